@@ -1,0 +1,162 @@
+"""Python front end of the fp64 CPU oracle (kda_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the CPU
+baseline leg of the benchmark; never by the HIP library or its binding.
+
+Every function takes numpy arrays in the packed token-major layout
+([TT, H, D], sequence boundaries in cu_seqlens) and computes in fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int
+        lib.kda_oracle_gate.argtypes = [i64, i32, i32, P, P, P]
+        lib.kda_oracle_gate.restype = None
+        lib.kda_oracle_gate_backward.argtypes = [i64, i32, i32, P, P, P, P, P, P]
+        lib.kda_oracle_gate_backward.restype = None
+        fwd = [i32, P, i32, i32, i32, P, P, P, P, P, P, i32, P, P, P, i32]
+        lib.kda_oracle_forward.argtypes = fwd
+        lib.kda_oracle_forward.restype = i32
+        lib.kda_oracle_forward_chunked.argtypes = fwd
+        lib.kda_oracle_forward_chunked.restype = i32
+        lib.kda_oracle_backward.argtypes = [i32, P, i32, i32, i32, P, P, P, P, P, P, P, P, i32,
+                                            P, P, P, P, P, P, P, i32]
+        lib.kda_oracle_backward.restype = i32
+        lib.kda_oracle_num_threads.argtypes = []
+        lib.kda_oracle_num_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _d(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _p(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().kda_oracle_num_threads())
+
+
+def _nchunks(cu, C):
+    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    return int(sum((int(l) + C - 1) // C for l in lens))
+
+
+def gate(g_raw, A_log):
+    """g = -exp(A_log[h]) * softplus(g_raw)."""
+    g_raw, A_log = _d(g_raw), _d(A_log)
+    TT, H, K = g_raw.shape
+    g = np.empty_like(g_raw)
+    _load().kda_oracle_gate(TT, H, K, _p(g_raw), _p(A_log), _p(g))
+    return g
+
+
+def gate_backward(g_raw, A_log, g, dg):
+    """dg_raw = dg * (-exp(A_log) sigmoid(g_raw));  dA_log[h] = sum dg * g."""
+    g_raw, A_log, g, dg = _d(g_raw), _d(A_log), _d(g), _d(dg)
+    TT, H, K = g_raw.shape
+    dg_raw = np.empty_like(g_raw)
+    dA = np.empty(H, dtype=np.float64)
+    _load().kda_oracle_gate_backward(TT, H, K, _p(g_raw), _p(A_log), _p(g), _p(dg), _p(dg_raw),
+                                     _p(dA))
+    return dg_raw, dA
+
+
+def _forward(fn, q, k, v, g, beta, h0, cu, chunk, want_states, nthreads):
+    q, k, v, g, beta, h0 = map(_d, (q, k, v, g, beta, h0))
+    cu = np.ascontiguousarray(cu, dtype=np.int64)
+    TT, H, K = q.shape
+    V = v.shape[2]
+    N = len(cu) - 1
+    o = np.empty((TT, H, V))
+    ht = np.empty((N, H, K, V))
+    states = np.empty((_nchunks(cu, chunk), H, K, V)) if want_states else None
+    rc = fn(N, _p(cu), H, K, V, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0), chunk, _p(o),
+            _p(ht), _p(states), nthreads)
+    if rc != 0:
+        raise RuntimeError("oracle forward failed: %d" % rc)
+    return o, ht, states
+
+
+def forward(q, k, v, g, beta, h0, cu, chunk=64, want_states=True, nthreads=0):
+    """Per-token recurrence. Returns (o, ht, states at chunk starts)."""
+    return _forward(_load().kda_oracle_forward, q, k, v, g, beta, h0, cu, chunk, want_states,
+                    nthreads)
+
+
+def forward_chunked(q, k, v, g, beta, h0, cu, chunk=64, want_states=True, nthreads=0):
+    """Chunk form of the same forward (independent code path)."""
+    return _forward(_load().kda_oracle_forward_chunked, q, k, v, g, beta, h0, cu, chunk,
+                    want_states, nthreads)
+
+
+def backward(q, k, v, g, beta, h0, dO, dht, cu, chunk=64, want_dstates=False, nthreads=0):
+    """Hand-derived per-token reverse mode. Gradients w.r.t. q, k, v, g, beta, h0,
+    and (optionally) dL/dS at the end of every chunk."""
+    q, k, v, g, beta, h0, dO, dht = map(_d, (q, k, v, g, beta, h0, dO, dht))
+    cu = np.ascontiguousarray(cu, dtype=np.int64)
+    TT, H, K = q.shape
+    V = v.shape[2]
+    N = len(cu) - 1
+    dq = np.empty((TT, H, K))
+    dk = np.empty((TT, H, K))
+    dv = np.empty((TT, H, V))
+    dg = np.empty((TT, H, K))
+    db = np.empty((TT, H))
+    dh0 = np.empty((N, H, K, V))
+    dst = np.empty((_nchunks(cu, chunk), H, K, V)) if want_dstates else None
+    rc = _load().kda_oracle_backward(N, _p(cu), H, K, V, _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                     _p(h0), _p(dO), _p(dht), chunk, _p(dq), _p(dk), _p(dv),
+                                     _p(dg), _p(db), _p(dh0), _p(dst), nthreads)
+    if rc != 0:
+        raise RuntimeError("oracle backward failed: %d" % rc)
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=db, dh0=dh0, dstates=dst)
+
+
+def kda_backward(inp: dict, want_dstates=False, want_states=False, nthreads=0) -> dict:
+    """Full backward from raw inputs (an input dict as produced by kda_inputs):
+    gate, per-token backward, gate chain rule.  Returns fp64 arrays dq, dk, dv,
+    dg_raw, dA_log, dbeta, dh0 (+ dstates / states on request)."""
+    g = gate(inp["g_raw"], inp["A_log"])
+    cu = inp["cu_seqlens"]
+    out = backward(inp["q"], inp["k"], inp["v"], g, inp["beta"], inp["h0"], inp["dO"],
+                   inp["dht"], cu, chunk=inp.get("chunk", 64), want_dstates=want_dstates,
+                   nthreads=nthreads)
+    dg_raw, dA = gate_backward(inp["g_raw"], inp["A_log"], g, out["dg"])
+    out["dg_raw"] = dg_raw
+    out["dA_log"] = dA
+    out["g"] = g
+    if want_states:
+        o, ht, st = forward(inp["q"], inp["k"], inp["v"], g, inp["beta"], inp["h0"], cu,
+                            chunk=inp.get("chunk", 64), want_states=True, nthreads=nthreads)
+        out["o"], out["ht"], out["states"] = o, ht, st
+    return out

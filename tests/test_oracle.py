@@ -1,0 +1,268 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: a hand-worked scalar
+example, closed forms of special cases, finite differences of its own forward,
+an independent autograd derivative, agreement between the per-token and the
+chunk forms, and library routines for the gate.  Shapes use K != V so that a
+transposed operand cannot pass.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_case(seed, lens, H, K, V, decay=0.5, with_state=True):
+    rng = np.random.default_rng(seed)
+    cu = np.zeros(len(lens) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lens)
+    TT = int(cu[-1])
+    N = len(lens)
+    q = rng.standard_normal((TT, H, K))
+    k = rng.standard_normal((TT, H, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((TT, H, V))
+    g_raw = rng.standard_normal((TT, H, K))
+    A_log = rng.uniform(-2.0, 0.5, size=H) + math.log(decay)
+    beta = rng.uniform(0.05, 0.95, size=(TT, H))
+    h0 = rng.standard_normal((N, H, K, V)) if with_state else None
+    dO = rng.standard_normal((TT, H, V))
+    dht = rng.standard_normal((N, H, K, V)) if with_state else None
+    return dict(cu=cu, q=q, k=k, v=v, g_raw=g_raw, A_log=A_log, beta=beta, h0=h0, dO=dO,
+                dht=dht)
+
+
+def _loss(c, **over):
+    d = dict(c)
+    d.update(over)
+    g = O.gate(d["g_raw"], d["A_log"])
+    o, ht, _ = O.forward(d["q"], d["k"], d["v"], g, d["beta"], d["h0"], d["cu"], chunk=4,
+                         want_states=False)
+    L = float(np.sum(o * d["dO"]))
+    if d["dht"] is not None:
+        L += float(np.sum(ht * d["dht"]))
+    return L
+
+
+def _full_backward(c, chunk=4):
+    g = O.gate(c["g_raw"], c["A_log"])
+    out = O.backward(c["q"], c["k"], c["v"], g, c["beta"], c["h0"], c["dO"], c["dht"], c["cu"],
+                     chunk=chunk, want_dstates=True)
+    dg_raw, dA = O.gate_backward(c["g_raw"], c["A_log"], g, out["dg"])
+    out["dg_raw"], out["dA_log"] = dg_raw, dA
+    return out
+
+
+def test_scalar_worked_example():
+    """K = V = 1, three tokens, every value derived by hand (golden fixture)."""
+    fx = json.load(open(os.path.join(GOLDEN, "scalar_recurrence.json")))
+    i, e = fx["inputs"], fx["expected"]
+    T = 3
+    sh = (T, 1, 1)
+    q = np.full(sh, i["q"])
+    k = np.full(sh, i["k"])
+    v = np.asarray(i["v"]).reshape(sh)
+    g = np.full(sh, math.log(i["a"]))
+    beta = np.full((T, 1), i["beta"])
+    h0 = np.full((1, 1, 1, 1), i["h0"])
+    dO = np.asarray(i["dO"]).reshape(sh)
+    dht = np.full((1, 1, 1, 1), i["dht"])
+    cu = np.array([0, T])
+    o, ht, _ = O.forward(q, k, v, g, beta, h0, cu)
+    np.testing.assert_allclose(o.ravel(), e["o"], rtol=1e-13)
+    np.testing.assert_allclose(ht.ravel(), [e["ht"]], rtol=1e-13)
+    out = O.backward(q, k, v, g, beta, h0, dO, dht, cu)
+    for key in ("dq", "dv", "dbeta", "dk", "dg"):
+        np.testing.assert_allclose(out[key].ravel(), e[key], rtol=1e-12, err_msg=key)
+    np.testing.assert_allclose(out["dh0"].ravel(), [e["dh0"]], rtol=1e-12)
+
+
+def test_delta_rule_write_property():
+    """beta = 1, g = 0, |k| = 1: the update writes v exactly, S_t^T k_t = v_t.
+    With q_t = k_t the output o_t equals v_t."""
+    rng = np.random.default_rng(3)
+    T, H, K, V = 9, 2, 6, 4
+    k = rng.standard_normal((T, H, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, V))
+    h0 = rng.standard_normal((1, H, K, V))
+    o, _, _ = O.forward(k, k, v, np.zeros((T, H, K)), np.ones((T, H)), h0, np.array([0, T]))
+    np.testing.assert_allclose(o, v, atol=1e-13)
+
+
+def test_zero_beta_is_pure_decay():
+    """beta = 0: S_t = Diag(exp(G_t)) h0 with G the running sum of g."""
+    rng = np.random.default_rng(4)
+    T, H, K, V = 11, 2, 5, 3
+    q = rng.standard_normal((T, H, K))
+    k = rng.standard_normal((T, H, K))
+    v = rng.standard_normal((T, H, V))
+    g = -rng.uniform(0, 0.7, size=(T, H, K))
+    h0 = rng.standard_normal((1, H, K, V))
+    o, ht, st = O.forward(q, k, v, g, np.zeros((T, H)), h0, np.array([0, T]), chunk=4)
+    G = np.cumsum(g, axis=0)
+    for t in range(T):
+        S_t = np.exp(G[t])[:, :, None] * h0[0]
+        np.testing.assert_allclose(o[t], np.einsum("hk,hkv->hv", q[t], S_t), atol=1e-13)
+    np.testing.assert_allclose(ht[0], np.exp(G[-1])[:, :, None] * h0[0], atol=1e-13)
+    np.testing.assert_allclose(st[1], np.exp(G[3])[:, :, None] * h0[0], atol=1e-13)
+
+
+def test_backward_closed_form_zero_beta_zero_gate():
+    """beta = 0, g = 0: S_t = h0 for every t, so
+    dq_t = h0 dO_t, dh0 = dht + sum_t q_t dO_t^T, dv = 0, dk = 0,
+    dbeta_t = k_t^T (dht + sum_{s>=t} q_s dO_s^T)(v_t - h0^T k_t),
+    dg_t = rowsum over j of (dht + sum_{s>=t} q_s dO_s^T) . h0."""
+    rng = np.random.default_rng(5)
+    T, H, K, V = 7, 1, 4, 3
+    q = rng.standard_normal((T, H, K))
+    k = rng.standard_normal((T, H, K))
+    v = rng.standard_normal((T, H, V))
+    h0 = rng.standard_normal((1, H, K, V))
+    dO = rng.standard_normal((T, H, V))
+    dht = rng.standard_normal((1, H, K, V))
+    out = O.backward(q, k, v, np.zeros((T, H, K)), np.zeros((T, H)), h0, dO, dht,
+                     np.array([0, T]))
+    S = h0[0, 0]
+    np.testing.assert_allclose(out["dq"][:, 0], dO[:, 0] @ S.T, atol=1e-12)
+    np.testing.assert_allclose(out["dh0"][0, 0], dht[0, 0] + q[:, 0].T @ dO[:, 0], atol=1e-12)
+    np.testing.assert_allclose(out["dv"], 0.0, atol=1e-14)
+    np.testing.assert_allclose(out["dk"], 0.0, atol=1e-14)
+    for t in range(T):
+        M = dht[0, 0] + q[t:, 0].T @ dO[t:, 0]
+        db = k[t, 0] @ M @ (v[t, 0] - S.T @ k[t, 0])
+        np.testing.assert_allclose(out["dbeta"][t, 0], db, atol=1e-12)
+        np.testing.assert_allclose(out["dg"][t, 0], np.sum(M * S, axis=1), atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 3, 4, 16, 64, 200])
+def test_chunked_forward_agrees(chunk):
+    """Per-token and chunk forms agree to rounding for any chunk size, ragged tails
+    included (lengths 1, 13, 64, 70)."""
+    c = _rand_case(7, [1, 13, 64, 70], H=2, K=6, V=5, decay=1.0)
+    g = O.gate(c["g_raw"], c["A_log"])
+    o1, h1, s1 = O.forward(c["q"], c["k"], c["v"], g, c["beta"], c["h0"], c["cu"], chunk=chunk)
+    o2, h2, s2 = O.forward_chunked(c["q"], c["k"], c["v"], g, c["beta"], c["h0"], c["cu"],
+                                   chunk=chunk)
+    scale = max(np.abs(o1).max(), 1.0)
+    assert np.abs(o1 - o2).max() / scale < 1e-12
+    assert np.abs(h1 - h2).max() / max(np.abs(h1).max(), 1.0) < 1e-12
+    assert np.abs(s1 - s2).max() / max(np.abs(s1).max(), 1.0) < 1e-12
+
+
+def test_chunked_forward_strong_decay_no_overflow():
+    """Strong decay (per-token log decay of tens): the chunk form uses only
+    non-positive exponents, so it stays finite and still agrees."""
+    c = _rand_case(8, [130], H=1, K=4, V=3)
+    c["A_log"] = np.array([math.log(16.0)])
+    c["g_raw"] = c["g_raw"] + 2.0
+    g = O.gate(c["g_raw"], c["A_log"])
+    assert g.min() < -40
+    o1, h1, _ = O.forward(c["q"], c["k"], c["v"], g, c["beta"], c["h0"], c["cu"])
+    o2, h2, _ = O.forward_chunked(c["q"], c["k"], c["v"], g, c["beta"], c["h0"], c["cu"])
+    assert np.all(np.isfinite(o2))
+    assert np.abs(o1 - o2).max() < 1e-12 * max(1.0, np.abs(o1).max())
+
+
+def test_finite_differences_all_inputs():
+    """Central differences of the oracle forward (eps = 1e-6) against the
+    hand-derived backward, for every scalar of q, k, v, g_raw, A_log, beta, h0
+    (two sequences of lengths 5 and 9, H = 2, K = 4, V = 3)."""
+    c = _rand_case(11, [5, 9], H=2, K=4, V=3)
+    out = _full_backward(c)
+    grads = dict(q="dq", k="dk", v="dv", g_raw="dg_raw", A_log="dA_log", beta="dbeta",
+                 h0="dh0")
+    eps = 1e-6
+    for name, gname in grads.items():
+        x = c[name]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy()
+            xp[idx] += eps
+            xm = x.copy()
+            xm[idx] -= eps
+            num[idx] = (_loss(c, **{name: xp}) - _loss(c, **{name: xm})) / (2 * eps)
+        err = np.abs(num - out[gname]).max() / np.abs(num).max()
+        assert err < 1e-7, (name, err)
+
+
+def test_autograd_and_boundary_state_gradients():
+    """An independent torch fp64 implementation of the recurrence, differentiated
+    by autograd, gives the same gradients, and the same dL/dS at every chunk end
+    (uses by later tokens only)."""
+    torch = pytest.importorskip("torch")
+    c = _rand_case(12, [7, 12], H=2, K=5, V=3)
+    C = 4
+    out = _full_backward(c, chunk=C)
+    T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    q, k, v, g_raw, A_log, beta, h0 = map(T, (c["q"], c["k"], c["v"], c["g_raw"], c["A_log"],
+                                              c["beta"], c["h0"]))
+    g = -torch.exp(A_log)[None, :, None] * torch.nn.functional.softplus(g_raw)
+    dO = torch.tensor(c["dO"])
+    dht = torch.tensor(c["dht"])
+    cu = c["cu"]
+    L = 0.0
+    bounds = []
+    for n in range(len(cu) - 1):
+        for h in range(q.shape[1]):
+            S = h0[n, h]
+            for t in range(int(cu[n]), int(cu[n + 1])):
+                kt, vt, qt = k[t, h], v[t, h], q[t, h]
+                St = torch.exp(g[t, h])[:, None] * S
+                St = St + beta[t, h] * torch.outer(kt, vt - St.T @ kt)
+                L = L + (St.T @ qt) @ dO[t, h]
+                local = t - int(cu[n])
+                if (local + 1) % C == 0 or t == int(cu[n + 1]) - 1:
+                    S = St * 1.0  # separate node: gradient from later tokens only
+                    S.retain_grad()
+                    bounds.append(((n, h, local // C), S))
+                else:
+                    S = St
+            L = L + torch.sum(S * dht[n, h])
+    L.backward()
+    for name, gname in dict(q="dq", k="dk", v="dv", g_raw="dg_raw", A_log="dA_log",
+                            beta="dbeta", h0="dh0").items():
+        ref = locals()[name].grad.numpy()
+        err = np.abs(ref - out[gname]).max() / np.abs(ref).max()
+        assert err < 1e-12, (name, err)
+    off = np.concatenate([[0], np.cumsum([(int(cu[i + 1] - cu[i]) + C - 1) // C
+                                          for i in range(len(cu) - 1)])])
+    for (n, h, ci), S in bounds:
+        ref = S.grad.numpy()
+        got = out["dstates"][off[n] + ci, h]
+        assert np.abs(ref - got).max() < 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_gate_against_library_routines():
+    """softplus against numpy's logaddexp; the gate chain rule against the
+    analytic derivative of logaddexp (the logistic function from scipy)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(13)
+    g_raw = rng.standard_normal((6, 3, 4)) * 5
+    A_log = rng.uniform(0, math.log(16), size=3)
+    g = O.gate(g_raw, A_log)
+    ref = -np.exp(A_log)[None, :, None] * np.logaddexp(0.0, g_raw)
+    np.testing.assert_allclose(g, ref, rtol=1e-14)
+    dg = rng.standard_normal(g.shape)
+    dg_raw, dA = O.gate_backward(g_raw, A_log, g, dg)
+    np.testing.assert_allclose(dg_raw, dg * (-np.exp(A_log)[None, :, None] * expit(g_raw)),
+                               rtol=1e-13)
+    np.testing.assert_allclose(dA, np.sum(dg * ref, axis=(0, 2)), rtol=1e-12)
+
+
+def test_parallel_matches_serial():
+    """OpenMP over (sequence, head) units does not change results."""
+    c = _rand_case(14, [30, 17, 40], H=3, K=8, V=6)
+    g = O.gate(c["g_raw"], c["A_log"])
+    a = O.backward(c["q"], c["k"], c["v"], g, c["beta"], c["h0"], c["dO"], c["dht"], c["cu"],
+                   nthreads=1)
+    b = O.backward(c["q"], c["k"], c["v"], g, c["beta"], c["h0"], c["dO"], c["dht"], c["cu"],
+                   nthreads=4)
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert np.array_equal(a[key], b[key]), key
