@@ -1,0 +1,163 @@
+/*
+ * kda.h -- C ABI of libkda.so: the chunkwise backward pass of KDA-style gated
+ * delta-rule linear attention on AMD Instinct MI355X (gfx950).
+ *
+ * Method.  Per (sequence n, head h), with S in R^{K x V}:
+ *   g_t = -exp(A_log[h]) * softplus(g_raw_t)                  (per key channel)
+ *   S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = S_t^T q_t,            S_{-1} = h0[n,h] (zero if absent)
+ * kda_bwd returns the gradients of  L = sum(dO . o) + sum(dht . S_T)  with respect
+ * to q, k, v, g_raw, A_log, beta and h0.  It is computed chunkwise (64 tokens):
+ * a serial reverse scan carries the state gradient dS back across chunks
+ * ("Kernel A", bwd-ncu-and-optimization-playbook, section 3.5 on split-V), then a
+ * data-parallel pass per chunk produces the per-token gradients, the gate
+ * gradient with its in-chunk reverse cumulative sum and the per-head dA_log sum
+ * ("Kernel B", bwd-kernelB-beginner-guide-full, part 2, B1/B2/B3).
+ *
+ * Layouts (all row-major, contiguous, no padding):
+ *   per-token tensors  [B, T, H, D]  (token stride H*D); with cu_seqlens, B = 1
+ *                      and the T tokens are the packed sequences back to back.
+ *   states             [.., H, K, V]  (V contiguous).
+ *   chunk-indexed      [NC, H, K, V]  where chunk c of sequence n has global index
+ *                      sum_{m<n} ceil(len_m / 64) + c  (kda_num_chunks gives NC).
+ *
+ * Dtypes: act_dtype (KDA_DTYPE_F32 or KDA_DTYPE_BF16) applies to q, k, v, dO, o,
+ * dq, dk, dv, h_saved and dstates.  g_raw, beta, A_log, h0, dht, ht, dg_raw, dbeta,
+ * dA_log and dh0 are always fp32.  All accumulation is fp32.
+ *
+ * Supported shapes in this build: chunk = 64; K == V; K in {64, 128} for bf16,
+ * K == 64 for fp32.  Anything else returns KDA_ERR_UNSUPPORTED.
+ *
+ * Ownership and synchronisation.  The caller owns every buffer (device memory)
+ * and the stream.  The library allocates no device memory and keeps no pointer
+ * after a call returns; scratch lives in the caller's workspace, sized by
+ * kda_workspace_size.  Calls are asynchronous on `stream` (a hipStream_t; NULL =
+ * the default stream) and enqueue work only after every argument has been
+ * validated: a non-OK return means nothing was launched.  Concurrent calls need
+ * distinct workspaces.  Outputs are overwritten, never accumulated.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define KDA_API __attribute__((visibility("default")))
+#else
+#define KDA_API
+#endif
+
+/* Status codes.  0 = success; negative = error (no work enqueued). */
+#define KDA_OK 0
+#define KDA_ERR_INVALID_ARGUMENT (-1) /* NULL required pointer, bad size, misaligned
+                                         pointer, non-monotone cu_seqlens, sum != T */
+#define KDA_ERR_UNSUPPORTED (-2)      /* shape or dtype outside this build */
+#define KDA_ERR_WORKSPACE_TOO_SMALL (-3)
+#define KDA_ERR_HIP (-4)              /* a HIP launch failed; kda_status_string(-4)
+                                         then names the HIP error of this thread */
+
+#define KDA_DTYPE_F32 0
+#define KDA_DTYPE_BF16 1
+
+/* Problem description.  Host memory; read during the call only. */
+typedef struct kda_problem {
+  int B, T, H, K, V;  /* batch, tokens per batch row, heads, key dim, value dim */
+  int chunk;          /* must be 64 */
+  int act_dtype;      /* KDA_DTYPE_F32 or KDA_DTYPE_BF16 */
+  int num_seqs;       /* with cu_seqlens: number of sequences N; else ignored (N = B) */
+  /* Optional variable-length packing: int32 [N+1], cu[0] = 0, non-decreasing,
+   * cu[N] = T, B must be 1.  Give both the host copy (sizes the grids; no device
+   * synchronisation is needed) and the device copy (indexed by the kernels), or
+   * neither. */
+  const int32_t* cu_seqlens_host;
+  const int32_t* cu_seqlens_dev;
+} kda_problem;
+
+/* Device pointers for kda_bwd.  16-byte aligned. */
+typedef struct kda_bwd_io {
+  /* inputs */
+  const void* q;        /* [B,T,H,K] act_dtype */
+  const void* k;        /* [B,T,H,K] act_dtype */
+  const void* v;        /* [B,T,H,V] act_dtype */
+  const float* g_raw;   /* [B,T,H,K] */
+  const float* beta;    /* [B,T,H]   (after the sigmoid) */
+  const float* A_log;   /* [H] */
+  const float* h0;      /* [N,H,K,V] or NULL (zero initial state) */
+  const void* dO;       /* [B,T,H,V] act_dtype */
+  const float* dht;     /* [N,H,K,V] or NULL (zero) */
+  const void* h_saved;  /* [NC,H,K,V] act_dtype: state at the start of every chunk,
+                           as kda_fwd_ref writes it; NULL = recomputed in-stream */
+  /* outputs (overwritten) */
+  void* dq;             /* [B,T,H,K] act_dtype */
+  void* dk;             /* [B,T,H,K] act_dtype */
+  void* dv;             /* [B,T,H,V] act_dtype */
+  float* dg_raw;        /* [B,T,H,K] */
+  float* dbeta;         /* [B,T,H] */
+  float* dA_log;        /* [H] */
+  float* dh0;           /* [N,H,K,V] or NULL (not produced) */
+  void* dstates;        /* [NC,H,K,V] act_dtype or NULL: if given, receives dL/dS at
+                           the end of every chunk (uses by later tokens only) */
+} kda_bwd_io;
+
+/* Device pointers for kda_fwd_ref (reference-quality forward that produces the
+ * chunk states the backward consumes). */
+typedef struct kda_fwd_io {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g_raw;
+  const float* beta;
+  const float* A_log;
+  const float* h0;      /* [N,H,K,V] or NULL */
+  void* o;              /* [B,T,H,V] act_dtype, or NULL */
+  float* ht;            /* [N,H,K,V] or NULL */
+  void* h_saved;        /* [NC,H,K,V] act_dtype, or NULL */
+} kda_fwd_io;
+
+#define KDA_WS_BWD 0
+#define KDA_WS_FWD 1
+
+/* Bytes of workspace kda_bwd (which = KDA_WS_BWD) or kda_fwd_ref (KDA_WS_FWD)
+ * needs for this problem.  Needs the host cu_seqlens when packed.  The bwd size
+ * with h_saved == NULL is the one returned (it is the larger). */
+KDA_API int kda_workspace_size(const kda_problem* p, int which, size_t* bytes);
+
+/* Total number of 64-token chunks NC over all sequences. */
+KDA_API int kda_num_chunks(const kda_problem* p, int64_t* nchunks);
+
+/* The backward pass (see the method above). */
+KDA_API int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t ws_bytes,
+            void* stream);
+
+/* Reference forward: o, ht and the per-chunk start states h_saved. */
+KDA_API int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t ws_bytes,
+                void* stream);
+
+/* Text for a status code (for KDA_ERR_HIP: the last HIP error of this thread). */
+KDA_API const char* kda_status_string(int status);
+
+KDA_API int kda_abi_version(void);
+
+/* Optional per-stage timing for measurement.  While enabled, kda_bwd brackets
+ * each kernel launch with HIP events on the call's stream.  kda_timing_read
+ * waits for the recorded events, writes per-stage totals (milliseconds) and
+ * launch counts for up to n stages, clears them, and returns the number of
+ * stages.  Stages: 0 chunk table, 1 prep, 2 state-gradient scan, 3 gradient
+ * pass (state side), 4 gradient pass (key side and gate epilogue), 5 dA_log
+ * reduction, 6 state recompute (h_saved == NULL).
+ * Not thread-safe; meant for benchmarks. */
+KDA_API int kda_timing_enable(int on);
+KDA_API int kda_timing_read(double* ms, int* launches, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

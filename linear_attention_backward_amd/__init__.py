@@ -1,0 +1,258 @@
+"""KDA (gated delta rule) chunkwise backward for MI355X -- Python binding.
+
+Thin ctypes front end of libkda.so (include/kda.h).  Torch tensors supply
+device memory and the current HIP stream; every step of the computation runs in
+the library's HIP kernels.  If libkda.so is missing or cannot be loaded every
+call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARGUMENT = -1
+KDA_ERR_UNSUPPORTED = -2
+KDA_ERR_WORKSPACE_TOO_SMALL = -3
+KDA_ERR_HIP = -4
+KDA_DTYPE_F32 = 0
+KDA_DTYPE_BF16 = 1
+KDA_WS_BWD = 0
+KDA_WS_FWD = 1
+CHUNK = 64
+
+STAGES = ("chunk_table", "prep", "scan", "grad_state", "grad_key", "dalog", "recompute")
+
+_P = ctypes.c_void_p
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("K", ctypes.c_int),
+                ("V", ctypes.c_int), ("chunk", ctypes.c_int), ("act_dtype", ctypes.c_int),
+                ("num_seqs", ctypes.c_int), ("cu_seqlens_host", _P), ("cu_seqlens_dev", _P)]
+
+
+class BwdIO(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("q", "k", "v", "g_raw", "beta", "A_log", "h0", "dO", "dht",
+                                  "h_saved", "dq", "dk", "dv", "dg_raw", "dbeta", "dA_log", "dh0",
+                                  "dstates")]
+
+
+class FwdIO(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("q", "k", "v", "g_raw", "beta", "A_log", "h0", "o", "ht",
+                                  "h_saved")]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("kda status %d: %s" % (status, msg))
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load libkda.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libkda.so not built: run `python -m linear_attention_backward_amd.build`"
+                              " (or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        PP = ctypes.POINTER(Problem)
+        lib.kda_abi_version.restype = ctypes.c_int
+        lib.kda_status_string.argtypes = [ctypes.c_int]
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_workspace_size.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        lib.kda_num_chunks.argtypes = [PP, ctypes.POINTER(ctypes.c_int64)]
+        lib.kda_bwd.argtypes = [PP, ctypes.POINTER(BwdIO), _P, ctypes.c_size_t, _P]
+        lib.kda_fwd_ref.argtypes = [PP, ctypes.POINTER(FwdIO), _P, ctypes.c_size_t, _P]
+        lib.kda_timing_enable.argtypes = [ctypes.c_int]
+        lib.kda_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int), ctypes.c_int]
+        for f in ("kda_workspace_size", "kda_num_chunks", "kda_bwd", "kda_fwd_ref",
+                  "kda_timing_enable", "kda_timing_read"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(st: int):
+    if st != KDA_OK:
+        raise KdaError(st, load_library().kda_status_string(st).decode())
+
+
+def status_string(st: int) -> str:
+    return load_library().kda_status_string(st).decode()
+
+
+def abi_version() -> int:
+    return load_library().kda_abi_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class _Prob:
+    """A kda_problem plus the host copy of cu_seqlens it points at."""
+
+    def __init__(self, B, T, H, K, V, dtype_code, cu_host=None, cu_dev=None):
+        self.cu_host = None
+        if cu_host is not None:
+            self.cu_host = (ctypes.c_int32 * len(cu_host))(*[int(x) for x in cu_host])
+        self.p = Problem(B, T, H, K, V, CHUNK, dtype_code,
+                         (len(cu_host) - 1) if cu_host is not None else 0,
+                         ctypes.cast(self.cu_host, _P) if self.cu_host is not None else None,
+                         _ptr(cu_dev) if cu_dev is not None else None)
+
+    def ref(self):
+        return ctypes.byref(self.p)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_F32
+    raise TypeError("activations must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _shape(q, v, cu_seqlens):
+    """(B, T, H, K, V) for [B,T,H,K] or packed [T,H,K] activations."""
+    if q.dim() == 4:
+        B, T, H, K = q.shape
+    elif q.dim() == 3:
+        B = 1
+        T, H, K = q.shape
+    else:
+        raise ValueError("q must be [B,T,H,K] or [T,H,K]")
+    V = v.shape[-1]
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed sequences need B == 1")
+    return B, T, H, K, V
+
+
+def _make_prob(q, v, cu_seqlens):
+    import torch
+    B, T, H, K, V = _shape(q, v, cu_seqlens)
+    cu_host = cu_dev = None
+    if cu_seqlens is not None:
+        cu_host = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist")
+                                    else cu_seqlens)]
+        cu_dev = torch.tensor(cu_host, dtype=torch.int32, device=q.device)
+    prob = _Prob(B, T, H, K, V, _dtype_code(q), cu_host, cu_dev)
+    prob.cu_dev_tensor = cu_dev  # keep alive
+    return prob, (B, T, H, K, V)
+
+
+def num_chunks(prob: _Prob) -> int:
+    n = ctypes.c_int64(0)
+    _check(load_library().kda_num_chunks(prob.ref(), ctypes.byref(n)))
+    return int(n.value)
+
+
+def workspace_size(prob: _Prob, which: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().kda_workspace_size(prob.ref(), which, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def kda_fwd_ref(q, k, v, g_raw, beta, A_log, h0=None, cu_seqlens=None, want_o=True,
+                want_ht=True, want_states=True, stream=None, workspace=None):
+    """Reference forward: returns dict(o, ht, h_saved)."""
+    import torch
+    _require_cuda(q, k, v, g_raw, beta, A_log, h0)
+    prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens)
+    N = (len(prob.cu_host) - 1) if prob.cu_host is not None else B
+    nc = num_chunks(prob)
+    dev = q.device
+    o = torch.empty_like(v) if want_o else None
+    ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if want_ht else None
+    hs = torch.empty((nc, H, K, V), dtype=q.dtype, device=dev) if want_states else None
+    ws_n = workspace_size(prob, KDA_WS_FWD)
+    ws = workspace if workspace is not None else torch.empty(max(ws_n, 1), dtype=torch.uint8,
+                                                             device=dev)
+    io = FwdIO(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta), _ptr(A_log), _ptr(h0),
+               _ptr(o), _ptr(ht), _ptr(hs))
+    _check(load_library().kda_fwd_ref(prob.ref(), ctypes.byref(io), _ptr(ws), ws.numel(),
+                                      _stream_ptr(stream)))
+    return dict(o=o, ht=ht, h_saved=hs)
+
+
+class BwdPlan:
+    """Pre-allocated outputs and workspace for repeated kda_bwd calls on fixed
+    shapes (used by the benchmark so the timed region allocates nothing)."""
+
+    def __init__(self, q, k, v, g_raw, beta, A_log, dO, h0=None, dht=None, h_saved=None,
+                 cu_seqlens=None, want_dh0=True, want_dstates=False):
+        import torch
+        _require_cuda(q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved)
+        self.prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens)
+        N = (len(self.prob.cu_host) - 1) if self.prob.cu_host is not None else B
+        dev = q.device
+        self.inputs = (q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved)
+        self.dq = torch.empty_like(q)
+        self.dk = torch.empty_like(k)
+        self.dv = torch.empty_like(v)
+        self.dg_raw = torch.empty_like(g_raw)
+        self.dbeta = torch.empty_like(beta)
+        self.dA_log = torch.empty_like(A_log)
+        self.dh0 = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if want_dh0 else None
+        self.nc = num_chunks(self.prob)
+        self.dstates = (torch.empty((self.nc, H, K, V), dtype=q.dtype, device=dev)
+                        if want_dstates else None)
+        ws_n = workspace_size(self.prob, KDA_WS_BWD)
+        self.ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+        self.io = BwdIO(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta), _ptr(A_log), _ptr(h0),
+                        _ptr(dO), _ptr(dht), _ptr(h_saved), _ptr(self.dq), _ptr(self.dk),
+                        _ptr(self.dv), _ptr(self.dg_raw), _ptr(self.dbeta), _ptr(self.dA_log),
+                        _ptr(self.dh0), _ptr(self.dstates))
+
+    def run(self, stream=None):
+        _check(load_library().kda_bwd(self.prob.ref(), ctypes.byref(self.io), _ptr(self.ws),
+                                      self.ws.numel(), _stream_ptr(stream)))
+
+    def outputs(self):
+        return dict(dq=self.dq, dk=self.dk, dv=self.dv, dg_raw=self.dg_raw, dbeta=self.dbeta,
+                    dA_log=self.dA_log, dh0=self.dh0, dstates=self.dstates)
+
+
+def kda_bwd(q, k, v, g_raw, beta, A_log, dO, h0=None, dht=None, h_saved=None, cu_seqlens=None,
+            want_dh0=True, want_dstates=False, stream=None):
+    """Backward pass.  Returns dict(dq, dk, dv, dg_raw, dbeta, dA_log, dh0, dstates)."""
+    plan = BwdPlan(q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved, cu_seqlens, want_dh0,
+                   want_dstates)
+    plan.run(stream)
+    return plan.outputs()
+
+
+def timing_enable(on: bool = True):
+    _check(load_library().kda_timing_enable(1 if on else 0))
+
+
+def timing_read():
+    """Per-stage (total ms, launches) since the last read, keyed by stage name."""
+    n = len(STAGES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    load_library().kda_timing_read(ms, cnt, n)
+    return {STAGES[i]: (ms[i], cnt[i]) for i in range(n)}

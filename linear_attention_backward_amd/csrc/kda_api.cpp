@@ -1,0 +1,297 @@
+// kda_api.cpp -- the C ABI of libkda.so (see include/kda.h).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kda.h"
+#include "kda_dev.h"
+#include "kda_launch.h"
+
+using namespace kda;
+
+namespace {
+
+thread_local std::string g_hip_msg;
+
+struct Region {
+  size_t off, size;
+};
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Everything derived from a kda_problem after validation.
+struct Plan {
+  Shape s;
+  int64_t NC = 0;
+  size_t es = 0;  // bytes per act element
+  // workspace regions
+  Region chunks, seq_off, Tm, PT, eGT, INV, INVT, MqkT, dstates, U, dvc, dAl, hsaved;
+  size_t fwd_bytes = 0, bwd_bytes = 0;
+};
+
+int count_chunks(const kda_problem* p, int64_t* nc) {
+  int64_t total = 0;
+  if (p->cu_seqlens_host) {
+    for (int n = 0; n < p->num_seqs; ++n) {
+      int64_t len = (int64_t)p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n];
+      total += (len + CH - 1) / CH;
+    }
+  } else {
+    total = (int64_t)p->B * ((p->T + CH - 1) / CH);
+  }
+  *nc = total;
+  return KDA_OK;
+}
+
+int validate_problem(const kda_problem* p) {
+  if (!p) return KDA_ERR_INVALID_ARGUMENT;
+  if (p->B < 1 || p->T < 0 || p->H < 1 || p->K < 1 || p->V < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (p->chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if (p->act_dtype != KDA_DTYPE_F32 && p->act_dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
+  if (p->K != p->V) return KDA_ERR_UNSUPPORTED;
+  if (p->act_dtype == KDA_DTYPE_BF16 && p->K != 64 && p->K != 128) return KDA_ERR_UNSUPPORTED;
+  if (p->act_dtype == KDA_DTYPE_F32 && p->K != 64) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)p->B * p->T >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  const bool hv = p->cu_seqlens_host != nullptr, dv = p->cu_seqlens_dev != nullptr;
+  if (hv != dv) return KDA_ERR_INVALID_ARGUMENT;
+  if (hv) {
+    if (p->B != 1 || p->num_seqs < 1) return KDA_ERR_INVALID_ARGUMENT;
+    if (p->cu_seqlens_host[0] != 0) return KDA_ERR_INVALID_ARGUMENT;
+    for (int n = 0; n < p->num_seqs; ++n)
+      if (p->cu_seqlens_host[n + 1] < p->cu_seqlens_host[n]) return KDA_ERR_INVALID_ARGUMENT;
+    if (p->cu_seqlens_host[p->num_seqs] != p->T) return KDA_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)p->cu_seqlens_dev & 3) != 0) return KDA_ERR_INVALID_ARGUMENT;
+  }
+  return KDA_OK;
+}
+
+int make_plan(const kda_problem* p, Plan* pl) {
+  int st = validate_problem(p);
+  if (st != KDA_OK) return st;
+  Shape& s = pl->s;
+  s.N = p->cu_seqlens_host ? p->num_seqs : p->B;
+  s.H = p->H;
+  s.D = p->K;
+  s.T = p->T;
+  s.bf16 = p->act_dtype == KDA_DTYPE_BF16;
+  s.cu = p->cu_seqlens_dev;
+  count_chunks(p, &pl->NC);
+  s.NC = pl->NC;
+  pl->es = s.bf16 ? 2 : 4;
+  const size_t NCH = (size_t)pl->NC * s.H;
+  const size_t D = s.D;
+  size_t off = 0;
+  auto take = [&](Region& r, size_t bytes) {
+    r.off = off;
+    r.size = bytes;
+    off = align_up(off + bytes);
+  };
+  take(pl->chunks, (size_t)pl->NC * sizeof(ChunkInfo));
+  take(pl->seq_off, ((size_t)s.N + 1) * sizeof(int));
+  pl->fwd_bytes = off;
+  take(pl->Tm, NCH * D * D * pl->es);
+  take(pl->PT, NCH * D * 64 * pl->es);
+  take(pl->eGT, NCH * D * 4);
+  take(pl->INV, NCH * 64 * 64 * pl->es);
+  take(pl->INVT, NCH * 64 * 64 * pl->es);
+  take(pl->MqkT, NCH * 64 * 64 * pl->es);
+  take(pl->dstates, NCH * D * D * pl->es);
+  take(pl->U, NCH * 64 * D * pl->es);
+  take(pl->dvc, NCH * 64 * D * pl->es);
+  take(pl->dAl, NCH * 4);
+  take(pl->hsaved, NCH * D * D * pl->es);
+  pl->bwd_bytes = off;
+  return KDA_OK;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+// ---- optional per-stage timing
+struct TimedLaunch {
+  int stage;
+  hipEvent_t a, b;
+};
+bool g_timing = false;
+std::vector<TimedLaunch> g_events;
+constexpr int kStages = 7;
+
+template <typename F>
+hipError_t timed(int stage, hipStream_t st, F&& launch) {
+  if (!g_timing) return launch();
+  TimedLaunch t{stage, nullptr, nullptr};
+  hipEventCreate(&t.a);
+  hipEventCreate(&t.b);
+  hipEventRecord(t.a, st);
+  hipError_t e = launch();
+  hipEventRecord(t.b, st);
+  g_events.push_back(t);
+  return e;
+}
+
+int hip_fail(hipError_t e) {
+  g_hip_msg = std::string("HIP error: ") + hipGetErrorName(e) + ": " + hipGetErrorString(e);
+  return KDA_ERR_HIP;
+}
+
+int vsplit_for(const Shape& s) {
+  const char* env = std::getenv("KDA_VSPLIT");
+  const int cap = s.D / 16;
+  if (env) {
+    int v = std::atoi(env);
+    if (v == 1 || v == 2 || v == 4 || v == 8) return v <= cap ? v : cap;
+  }
+  const int units = s.N * s.H;
+  int vs = 1;
+  while (vs < cap && units * vs < 1024) vs *= 2;
+  return vs;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KDA_ERR_HIP: return g_hip_msg.empty() ? "HIP error" : g_hip_msg.c_str();
+    default: return "unknown status";
+  }
+}
+
+int kda_num_chunks(const kda_problem* p, int64_t* nchunks) {
+  if (!nchunks) return KDA_ERR_INVALID_ARGUMENT;
+  int st = validate_problem(p);
+  if (st != KDA_OK) return st;
+  return count_chunks(p, nchunks);
+}
+
+int kda_workspace_size(const kda_problem* p, int which, size_t* bytes) {
+  if (!bytes || (which != KDA_WS_BWD && which != KDA_WS_FWD)) return KDA_ERR_INVALID_ARGUMENT;
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != KDA_OK) return st;
+  *bytes = which == KDA_WS_BWD ? pl.bwd_bytes : pl.fwd_bytes;
+  return KDA_OK;
+}
+
+int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t ws_bytes,
+                void* stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != KDA_OK) return st;
+  if (!io || !io->q || !io->k || !io->v || !io->g_raw || !io->beta || !io->A_log)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(io->q) || !aligned16(io->k) || !aligned16(io->v) || !aligned16(io->h_saved))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < pl.fwd_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (pl.fwd_bytes > 0 && !workspace) return KDA_ERR_INVALID_ARGUMENT;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  ChunkInfo* tab = (ChunkInfo*)(ws + pl.chunks.off);
+  int* seq_off = (int*)(ws + pl.seq_off.off);
+  hipError_t e = launch_chunk_table(pl.s, tab, seq_off, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_fwd_ref(pl.s, seq_off, io->q, io->k, io->v, io->g_raw, io->beta, io->A_log, io->h0,
+                     io->o, io->ht, io->h_saved, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return KDA_OK;
+}
+
+int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t ws_bytes,
+            void* stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != KDA_OK) return st;
+  if (!io) return KDA_ERR_INVALID_ARGUMENT;
+  if (!io->q || !io->k || !io->v || !io->g_raw || !io->beta || !io->A_log || !io->dO || !io->dq ||
+      !io->dk || !io->dv || !io->dg_raw || !io->dbeta || !io->dA_log)
+    return KDA_ERR_INVALID_ARGUMENT;
+  const void* al[] = {io->q, io->k, io->v, io->dO, io->g_raw, io->h_saved, io->h0, io->dht,
+                      io->dq, io->dk, io->dv, io->dg_raw, io->dh0, io->dstates};
+  for (const void* x : al)
+    if (!aligned16(x)) return KDA_ERR_INVALID_ARGUMENT;
+  size_t need = pl.bwd_bytes;
+  if (io->h_saved) need = pl.hsaved.off;  // the recompute region is the last one
+  if (ws_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !workspace) return KDA_ERR_INVALID_ARGUMENT;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  BwdPtrs b;
+  b.q = io->q; b.k = io->k; b.v = io->v; b.dO = io->dO;
+  b.g_raw = io->g_raw; b.beta = io->beta; b.A_log = io->A_log; b.h0 = io->h0; b.dht = io->dht;
+  b.dq = io->dq; b.dk = io->dk; b.dv = io->dv;
+  b.dg_raw = io->dg_raw; b.dbeta = io->dbeta; b.dA_log = io->dA_log; b.dh0 = io->dh0;
+  b.chunks = (const ChunkInfo*)(ws + pl.chunks.off);
+  b.seq_off = (const int*)(ws + pl.seq_off.off);
+  b.Tm = ws + pl.Tm.off;
+  b.PT = ws + pl.PT.off;
+  b.eGT = (float*)(ws + pl.eGT.off);
+  b.INV = ws + pl.INV.off;
+  b.INVT = ws + pl.INVT.off;
+  b.MqkT = ws + pl.MqkT.off;
+  b.dstates = io->dstates ? io->dstates : (void*)(ws + pl.dstates.off);
+  b.U = ws + pl.U.off;
+  b.dvc = ws + pl.dvc.off;
+  b.dAl_part = (float*)(ws + pl.dAl.off);
+  b.h_saved = io->h_saved ? io->h_saved : (const void*)(ws + pl.hsaved.off);
+  const Shape& sh = pl.s;
+  hipError_t e;
+  e = timed(0, s, [&] { return launch_chunk_table(sh, (ChunkInfo*)b.chunks, (int*)b.seq_off, s); });
+  if (e != hipSuccess) return hip_fail(e);
+  if (!io->h_saved) {
+    e = timed(6, s, [&] {
+      return launch_fwd_ref(sh, b.seq_off, io->q, io->k, io->v, io->g_raw, io->beta, io->A_log,
+                            io->h0, nullptr, nullptr, (void*)b.h_saved, s);
+    });
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  e = timed(1, s, [&] { return launch_prep(sh, b, s); });
+  if (e != hipSuccess) return hip_fail(e);
+  const int vs = vsplit_for(sh);
+  e = timed(2, s, [&] { return launch_scan(sh, b, vs, s); });
+  if (e != hipSuccess) return hip_fail(e);
+  e = timed(3, s, [&] { return launch_grad1(sh, b, s); });
+  if (e != hipSuccess) return hip_fail(e);
+  e = timed(4, s, [&] { return launch_grad2(sh, b, s); });
+  if (e != hipSuccess) return hip_fail(e);
+  e = timed(5, s, [&] { return launch_dalog(sh, b, s); });
+  if (e != hipSuccess) return hip_fail(e);
+  return KDA_OK;
+}
+
+int kda_timing_enable(int on) {
+  g_timing = on != 0;
+  return KDA_OK;
+}
+
+int kda_timing_read(double* ms, int* launches, int n) {
+  std::vector<double> tot(kStages, 0.0);
+  std::vector<int> cnt(kStages, 0);
+  for (auto& t : g_events) {
+    float x = 0.f;
+    if (hipEventSynchronize(t.b) == hipSuccess && hipEventElapsedTime(&x, t.a, t.b) == hipSuccess) {
+      tot[t.stage] += x;
+      cnt[t.stage] += 1;
+    }
+    hipEventDestroy(t.a);
+    hipEventDestroy(t.b);
+  }
+  g_events.clear();
+  for (int i = 0; i < n && i < kStages; ++i) {
+    if (ms) ms[i] = tot[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return kStages;
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// kda_dev.h -- device helpers shared by the KDA backward kernels (gfx950).
+//
+// MFMA conventions (CDNA3/CDNA4 16x16 family, wave64):
+//   A operand (16 x KS):  lane l holds row (l & 15), k = (l >> 4) * KPL + [0, KPL)
+//   B operand (KS x 16):  lane l holds col (l & 15), k = (l >> 4) * KPL + [0, KPL)
+//   C/D (16 x 16 fp32):   lane l holds col (l & 15), rows (l >> 4) * 4 + [0, 4)
+// bf16 uses v_mfma_f32_16x16x32_bf16 (KS = 32, KPL = 8); fp32 uses
+// v_mfma_f32_16x16x4_f32 (KS = 4, KPL = 1).  Every operand is therefore read from a
+// layout in which the contraction index is contiguous: A as [m][k], B as [n][k].
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int CH = 64;      // chunk length (tokens)
+constexpr int NTHR = 256;   // threads per workgroup (4 waves)
+constexpr float LOG2E = 1.4426950408889634f;
+
+// One row of the chunk table: a 64-token chunk of one sequence.
+struct ChunkInfo {
+  int t0;    // first token (packed index)
+  int len;   // valid rows, 1..64
+  int seq;   // sequence index
+  int cidx;  // chunk index inside the sequence
+};
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+// 2^x on the transcendental unit.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T> struct Mma;
+template <> struct Mma<bf16> {
+  static constexpr int KS = 32, KPL = 8;
+  typedef bf16x8 Frag;
+  __device__ static __forceinline__ f4 mma(Frag a, Frag b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ Frag load(const bf16* p) { return *(const bf16x8*)p; }
+  __device__ static __forceinline__ Frag from_f32(const float* p) {
+    f4 a = *(const f4*)p, b = *(const f4*)(p + 4);
+    Frag r;
+    r[0] = (bf16)a[0]; r[1] = (bf16)a[1]; r[2] = (bf16)a[2]; r[3] = (bf16)a[3];
+    r[4] = (bf16)b[0]; r[5] = (bf16)b[1]; r[6] = (bf16)b[2]; r[7] = (bf16)b[3];
+    return r;
+  }
+  __device__ static __forceinline__ Frag from_vals(const float* v) {
+    Frag r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (bf16)v[j];
+    return r;
+  }
+  __device__ static __forceinline__ float dot(Frag a, Frag b) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += (float)a[j] * (float)b[j];
+    return s;
+  }
+  // fp32-accurate product of fp32 operands on the bf16 unit: x = hi + lo with
+  // hi = bf16(x), lo = bf16(x - hi); a.b ~ hi.hi + hi.lo + lo.hi (the dropped
+  // lo.lo term is ~2^-16 relative).
+  __device__ static __forceinline__ f4 mma3(const float* a, const float* b, f4 c) {
+    Frag ah, al, bh, bl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ah[j] = (bf16)a[j];
+      al[j] = (bf16)(a[j] - (float)ah[j]);
+      bh[j] = (bf16)b[j];
+      bl[j] = (bf16)(b[j] - (float)bh[j]);
+    }
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {
+  static constexpr int KS = 4, KPL = 1;
+  typedef float Frag;
+  __device__ static __forceinline__ f4 mma(Frag a, Frag b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ Frag load(const float* p) { return *p; }
+  __device__ static __forceinline__ Frag from_f32(const float* p) { return *p; }
+  __device__ static __forceinline__ Frag from_vals(const float* v) { return v[0]; }
+  __device__ static __forceinline__ float dot(Frag a, Frag b) { return a * b; }
+  __device__ static __forceinline__ f4 mma3(const float* a, const float* b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+// Load KPL consecutive elements of type T as floats.
+template <typename T, int N> __device__ __forceinline__ void load_f(const T* p, float* out) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) out[j] = to_f(p[j]);
+}
+
+// Store a C tile (acc layout) into a row-major [m][n] array at (row0, col0).
+template <typename T>
+__device__ __forceinline__ void store_c(T* base, int pitch, int row0, int col0, f4 acc, int lane) {
+  int col = col0 + (lane & 15), r = row0 + (lane >> 4) * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) base[(r + j) * pitch + col] = from_f<T>(acc[j]);
+}
+// Store the transpose of a C tile: element (m, n) goes to base[n * pitch + m].
+// The 4 rows a lane holds become 4 contiguous elements.
+template <typename T>
+__device__ __forceinline__ void store_ct(T* base, int pitch, int row0, int col0, f4 acc, int lane);
+template <>
+__device__ __forceinline__ void store_ct<bf16>(bf16* base, int pitch, int row0, int col0, f4 acc,
+                                               int lane) {
+  int col = col0 + (lane & 15), r = row0 + (lane >> 4) * 4;
+  bf16x4 v;
+  v[0] = (bf16)acc[0]; v[1] = (bf16)acc[1]; v[2] = (bf16)acc[2]; v[3] = (bf16)acc[3];
+  *(bf16x4*)(base + col * pitch + r) = v;
+}
+template <>
+__device__ __forceinline__ void store_ct<float>(float* base, int pitch, int row0, int col0, f4 acc,
+                                                int lane) {
+  int col = col0 + (lane & 15), r = row0 + (lane >> 4) * 4;
+  *(f4*)(base + col * pitch + r) = acc;
+}
+
+// Sum over the 16 lanes that share (lane >> 4) (i.e. over the columns of a C tile).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+// Sum over the whole wave.
+__device__ __forceinline__ float sum64(float x) {
+  x = sum16(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Pitches (in elements) of the LDS tiles.  Natural token-major tiles [64][D] of T
+// get 16 bytes of row padding so that the 16 rows one MFMA operand reads start
+// in distinct 4-bank groups of the 64-bank LDS; transposed tiles [D][64] likewise.
+template <typename T, int D> struct Pitch {
+  static constexpr int N = D + 16 / (int)sizeof(T);  // [64][D] of T
+  static constexpr int NF = D + 4;                    // [64][D] of fp32
+  static constexpr int CC = 68;                       // [64][64] of fp32
+  static constexpr int TT = sizeof(T) == 2 ? 72 : 68; // [D][64] of T
+  static constexpr int CT = sizeof(T) == 2 ? 72 : 68; // [64][64] of T
+};
+
+}  // namespace kda

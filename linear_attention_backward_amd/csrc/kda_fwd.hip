@@ -1,0 +1,194 @@
+// kda_fwd.hip -- chunk table, reference forward (chunk start states) and the
+// per-head dA_log reduction.
+#include "kda_dev.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+// ---------------------------------------------------------------------------
+// Chunk table: one entry per 64-token chunk of every sequence, sequences back to
+// back (chunk c of sequence n at index seq_off[n] + c).  One workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_chunk_table(const int32_t* __restrict__ cu, int N, int T,
+                                                     ChunkInfo* __restrict__ tab,
+                                                     int* __restrict__ seq_off) {
+  __shared__ int part[256];
+  const int tid = threadIdx.x;
+  const int per = (N + 255) / 256;
+  const int n0 = min(N, tid * per), n1 = min(N, n0 + per);
+  int cnt = 0;
+  for (int n = n0; n < n1; ++n) {
+    int len = cu ? cu[n + 1] - cu[n] : T;
+    cnt += (len + CH - 1) / CH;
+  }
+  part[tid] = cnt;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      int x = part[i];
+      part[i] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  int off = part[tid];
+  for (int n = n0; n < n1; ++n) {
+    int start = cu ? cu[n] : n * T;
+    int len = cu ? cu[n + 1] - cu[n] : T;
+    seq_off[n] = off;
+    for (int c = 0; c * CH < len; ++c) {
+      ChunkInfo e;
+      e.t0 = start + c * CH;
+      e.len = min(CH, len - c * CH);
+      e.seq = n;
+      e.cidx = c;
+      tab[off + c] = e;
+    }
+    off += (len + CH - 1) / CH;
+  }
+  if (n0 < N && n1 == N) seq_off[N] = off;
+  if (N == 0 && tid == 0) seq_off[0] = 0;
+}
+
+__device__ __forceinline__ float softplus_f(float x) {
+  return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));
+}
+
+// ---------------------------------------------------------------------------
+// Reference forward, token by token.  One wave per (sequence, head, 64-column
+// slice of V); lane j keeps column j of the K x 64 state slice in registers, so
+// the rank-one update and both projections are per-lane loops over K with no
+// cross-lane reduction.  Writes the state at the start of every chunk (h_saved),
+// the outputs o and the final state.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_fwd_ref(const int* __restrict__ seq_off,
+                                                const int32_t* __restrict__ cu, int N, int H,
+                                                int Tn, const T* __restrict__ q,
+                                                const T* __restrict__ k,
+                                                const T* __restrict__ v,
+                                                const float* __restrict__ g_raw,
+                                                const float* __restrict__ beta,
+                                                const float* __restrict__ A_log,
+                                                const float* __restrict__ h0, T* __restrict__ o,
+                                                float* __restrict__ ht, T* __restrict__ h_saved) {
+  constexpr int NVS = D / 64;
+  constexpr int TB = 16;  // tokens staged per round
+  __shared__ float sk[TB][D], sq[TB][D], sa[TB][D], sb[TB];
+  const int b = blockIdx.x;
+  const int vs = b % NVS, u = b / NVS;
+  const int n = u / H, h = u % H;
+  const int j = threadIdx.x, d = vs * 64 + j;
+  const int start = cu ? cu[n] : n * Tn;
+  const int len = cu ? cu[n + 1] - cu[n] : Tn;
+  const size_t KV = (size_t)D * D;
+  float S[D];
+  if (h0) {
+    const float* src = h0 + ((size_t)n * H + h) * KV + d;
+#pragma unroll
+    for (int i = 0; i < D; ++i) S[i] = src[(size_t)i * D];
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) S[i] = 0.f;
+  }
+  const float aA = __expf(A_log[h]);
+  const int c0 = seq_off[n];
+  for (int tb = 0; tb < len; tb += TB) {
+    const int nt = min(TB, len - tb);
+    __syncthreads();
+    for (int idx = j; idx < TB * D; idx += 64) {
+      int r = idx / D, i = idx % D;
+      if (r < nt) {
+        size_t off = ((size_t)(start + tb + r) * H + h) * D + i;
+        sk[r][i] = to_f(k[off]);
+        sq[r][i] = to_f(q[off]);
+        sa[r][i] = __expf(-aA * softplus_f(g_raw[off]));
+      }
+    }
+    if (j < nt) sb[j] = beta[(size_t)(start + tb + j) * H + h];
+    __syncthreads();
+    for (int r = 0; r < nt; ++r) {
+      const int local = tb + r;
+      const size_t t = (size_t)(start + local);
+      if (h_saved && (local % CH) == 0) {
+        T* dst = h_saved + ((size_t)(c0 + local / CH) * H + h) * KV + d;
+#pragma unroll
+        for (int i = 0; i < D; ++i) dst[(size_t)i * D] = from_f<T>(S[i]);
+      }
+      const float vv = to_f(v[(t * H + h) * D + d]);
+      float uu = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        S[i] *= sa[r][i];
+        uu += S[i] * sk[r][i];
+      }
+      const float e = sb[r] * (vv - uu);
+      float oo = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        S[i] += sk[r][i] * e;
+        oo += S[i] * sq[r][i];
+      }
+      if (o) o[(t * H + h) * D + d] = from_f<T>(oo);
+    }
+  }
+  if (ht) {
+    float* dst = ht + ((size_t)n * H + h) * KV + d;
+#pragma unroll
+    for (int i = 0; i < D; ++i) dst[(size_t)i * D] = S[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dA_log[h] = sum over chunks of the per chunk-head partials (fixed order, so
+// the result is deterministic).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_dalog(const float* __restrict__ part, int64_t NC, int H,
+                                               float* __restrict__ out) {
+  __shared__ float red[4];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  float acc = 0.f;
+  for (int64_t c = tid; c < NC; c += 256) acc += part[c * H + h];
+  acc = sum64(acc);
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) out[h] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, hipStream_t st) {
+  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, st, s.cu, s.N, s.T, tab, seq_off);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t fwd_ref_t(const Shape& s, const int* seq_off, const void* q, const void* k,
+                            const void* v, const float* g_raw, const float* beta,
+                            const float* A_log, const float* h0, void* o, float* ht,
+                            void* h_saved, hipStream_t st) {
+  dim3 grid((unsigned)(s.N * s.H * (D / 64)));
+  hipLaunchKernelGGL((k_fwd_ref<T, D>), grid, dim3(64), 0, st, seq_off, s.cu, s.N, s.H, s.T,
+                     (const T*)q, (const T*)k, (const T*)v, g_raw, beta, A_log, h0, (T*)o, ht,
+                     (T*)h_saved);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, const void* k,
+                          const void* v, const float* g_raw, const float* beta,
+                          const float* A_log, const float* h0, void* o, float* ht,
+                          void* h_saved, hipStream_t st) {
+  if (s.N * s.H == 0) return hipSuccess;
+  if (s.bf16) {
+    if (s.D == 128)
+      return fwd_ref_t<bf16, 128>(s, seq_off, q, k, v, g_raw, beta, A_log, h0, o, ht, h_saved, st);
+    return fwd_ref_t<bf16, 64>(s, seq_off, q, k, v, g_raw, beta, A_log, h0, o, ht, h_saved, st);
+  }
+  return fwd_ref_t<float, 64>(s, seq_off, q, k, v, g_raw, beta, A_log, h0, o, ht, h_saved, st);
+}
+
+hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_dalog, dim3(s.H), dim3(256), 0, st, p.dAl_part, s.NC, s.H, p.dA_log);
+  return hipGetLastError();
+}
+
+}  // namespace kda

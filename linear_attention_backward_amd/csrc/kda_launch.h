@@ -1,0 +1,50 @@
+// kda_launch.h -- host-side launchers of the KDA kernels (internal to libkda.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct ChunkInfo;
+
+// Pointers of one backward call, as the kernels see them (device memory).
+struct BwdPtrs {
+  const void *q, *k, *v, *dO;
+  const float *g_raw, *beta, *A_log, *h0, *dht;
+  const void* h_saved;
+  void *dq, *dk, *dv;
+  float *dg_raw, *dbeta, *dA_log, *dh0;
+  // workspace
+  const ChunkInfo* chunks;
+  const int* seq_off;      // [N+1] first chunk of every sequence
+  void* Tm;                // [NC,H,K,K] act dtype : -W^T Kr (low-rank part of the chunk transition)
+  void* PT;                // [NC,H,K,64] act dtype: (Qd - Mqk W)^T
+  float* eGT;              // [NC,H,K]  exp(G_T)
+  void* INV;               // [NC,H,64,64] act dtype: (I + diag(beta) A)^{-1}
+  void* INVT;              // [NC,H,64,64] act dtype: its transpose
+  void* MqkT;              // [NC,H,64,64] act dtype: Mqk transposed
+  void* dstates;           // [NC,H,K,V] act dtype: dL/dS at the end of every chunk
+  void* U;                 // [NC,H,64,V] act dtype: INV diag(beta) (V - Kd S_in)
+  void* dvc;               // [NC,H,64,V] act dtype: INV^T dU
+  float* dAl_part;         // [NC,H] per chunk-head partial sums for dA_log
+};
+
+struct Shape {
+  int N, H, D, T;  // sequences, heads, K = V, tokens per row when not packed
+  int64_t NC;      // total chunks
+  int bf16;        // act dtype is bf16
+  const int32_t* cu;  // device cu_seqlens or nullptr (uniform rows of T tokens)
+};
+
+hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, hipStream_t st);
+hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, const void* k,
+                          const void* v, const float* g_raw, const float* beta,
+                          const float* A_log, const float* h0, void* o, float* ht,
+                          void* h_saved, hipStream_t st);
+hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st);
+hipError_t launch_scan(const Shape& s, const BwdPtrs& p, int vsplit, hipStream_t st);
+hipError_t launch_grad1(const Shape& s, const BwdPtrs& p, hipStream_t st);
+hipError_t launch_grad2(const Shape& s, const BwdPtrs& p, hipStream_t st);
+hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st);
+
+}  // namespace kda

@@ -16,24 +16,43 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+_LIB = os.path.join(_HERE, "liboracle.so")          # AVX2/FMA build
+_LIB_GENERIC = os.path.join(_HERE, "liboracle_generic.so")
 _lib = None
+# Summation order may be changed by the compiler (vectorised fp64 reductions);
+# that moves results by rounding only.
+_FAST = ["-O3", "-fno-math-errno", "-fassociative-math", "-fno-signed-zeros",
+         "-fno-trapping-math"]
+
+
+def _cpu_has_avx2() -> bool:
+    try:
+        flags = open("/proc/cpuinfo").read()
+    except OSError:
+        return False
+    return " avx2" in flags and " fma" in flags
+
+
+def _compile(out, extra):
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc"] + _FAST + extra + ["-fopenmp", "-fPIC", "-shared", "-o", tmp,
+                                                     _SRC, "-lm"])
+    os.replace(tmp, out)
 
 
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (fp64, OpenMP)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+    """Compile the oracle with gcc (fp64, OpenMP): an AVX2/FMA variant and a
+    baseline x86-64 variant; returns the one this CPU runs."""
+    for out, extra in ((_LIB, ["-march=x86-64-v3"]), (_LIB_GENERIC, [])):
+        if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+            _compile(out, extra)
+    return _LIB if _cpu_has_avx2() else _LIB_GENERIC
 
 
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(build())
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int
         lib.kda_oracle_gate.argtypes = [i64, i32, i32, P, P, P]

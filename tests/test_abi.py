@@ -1,0 +1,105 @@
+"""The C ABI on the CPU: the library loads, exports every function kda.h
+declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_backward_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    return sorted(set(re.findall(r"KDA_API\s+[\w\s\*]*?\b(kda_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = K.load_library()
+    names = _declared()
+    assert len(names) >= 8, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert K.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(K.status_string(code), str) and K.status_string(code)
+
+
+def _ws(prob, which=K.KDA_WS_BWD):
+    n = ctypes.c_size_t(0)
+    st = K.load_library().kda_workspace_size(prob.ref(), which, ctypes.byref(n))
+    return st, n.value
+
+
+def test_shape_validation():
+    ok = K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16)
+    st, n = _ws(ok)
+    assert st == 0 and n > 0
+    assert _ws(K._Prob(2, 100, 4, 96, 96, K.KDA_DTYPE_BF16))[0] == K.KDA_ERR_UNSUPPORTED
+    assert _ws(K._Prob(2, 100, 4, 128, 64, K.KDA_DTYPE_BF16))[0] == K.KDA_ERR_UNSUPPORTED
+    assert _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_F32))[0] == K.KDA_ERR_UNSUPPORTED
+    assert _ws(K._Prob(2, 100, 4, 64, 64, 7))[0] == K.KDA_ERR_UNSUPPORTED
+    assert _ws(K._Prob(0, 100, 4, 64, 64, 0))[0] == K.KDA_ERR_INVALID_ARGUMENT
+    assert _ws(K._Prob(1, 100, 0, 64, 64, 0))[0] == K.KDA_ERR_INVALID_ARGUMENT
+    p = K._Prob(1, 100, 4, 64, 64, 0)
+    p.p.chunk = 32
+    assert _ws(p)[0] == K.KDA_ERR_UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert K.load_library().kda_workspace_size(ok.ref(), 5, ctypes.byref(n)) == -1
+
+
+def test_cu_seqlens_validation():
+    fake_dev = ctypes.c_void_p(16)  # never dereferenced: validation fails or no launch happens
+    def prob(cu, T, B=1):
+        p = K._Prob(B, T, 2, 64, 64, K.KDA_DTYPE_F32, cu, None)
+        p.p.cu_seqlens_dev = fake_dev
+        return p
+    assert _ws(prob([0, 10, 100], 100))[0] == 0
+    assert _ws(prob([0, 10, 100], 101))[0] == K.KDA_ERR_INVALID_ARGUMENT  # sum != T
+    assert _ws(prob([0, 50, 40, 100], 100))[0] == K.KDA_ERR_INVALID_ARGUMENT  # not monotone
+    assert _ws(prob([1, 10, 100], 100))[0] == K.KDA_ERR_INVALID_ARGUMENT  # cu[0] != 0
+    assert _ws(prob([0, 10, 100], 100, B=2))[0] == K.KDA_ERR_INVALID_ARGUMENT
+    host_only = K._Prob(1, 100, 2, 64, 64, 0, [0, 10, 100], None)
+    assert _ws(host_only)[0] == K.KDA_ERR_INVALID_ARGUMENT  # host copy without device copy
+
+
+def test_num_chunks_and_workspace_monotone():
+    nc = ctypes.c_int64(0)
+    p = K._Prob(1, 1 + 63 + 64 + 65 + 0, 2, 64, 64, 0, [0, 1, 64, 128, 193, 193], None)
+    p.p.cu_seqlens_dev = ctypes.c_void_p(16)
+    assert K.load_library().kda_num_chunks(p.ref(), ctypes.byref(nc)) == 0
+    assert nc.value == 1 + 1 + 1 + 2 + 0
+    sizes = [_ws(K._Prob(1, T, 4, 128, 128, 1))[1] for T in (64, 128, 1000, 4096)]
+    assert sizes == sorted(sizes)
+    assert _ws(K._Prob(1, 64, 4, 128, 128, 1), K.KDA_WS_FWD)[1] <= sizes[0]
+
+
+def test_bwd_rejects_bad_calls_without_launching():
+    lib = K.load_library()
+    p = K._Prob(1, 64, 2, 64, 64, K.KDA_DTYPE_F32)
+    # NULL io
+    assert lib.kda_bwd(p.ref(), None, None, 0, None) == K.KDA_ERR_INVALID_ARGUMENT
+    io = K.BwdIO()
+    assert lib.kda_bwd(p.ref(), ctypes.byref(io), None, 0, None) == K.KDA_ERR_INVALID_ARGUMENT
+    # misaligned pointer
+    al = 256
+    for f in ("q", "k", "v", "g_raw", "beta", "A_log", "dO", "dq", "dk", "dv", "dg_raw", "dbeta",
+              "dA_log"):
+        setattr(io, f, al)
+    io.q = 258
+    assert lib.kda_bwd(p.ref(), ctypes.byref(io), None, 0, None) == K.KDA_ERR_INVALID_ARGUMENT
+    io.q = 256
+    # workspace too small
+    assert lib.kda_bwd(p.ref(), ctypes.byref(io), ctypes.c_void_p(256), 16, None) == \
+        K.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.kda_fwd_ref(p.ref(), None, None, 0, None) == K.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(K.KdaError):
+        K._check(K.KDA_ERR_UNSUPPORTED)
