@@ -1,0 +1,227 @@
+"""Benchmark: KDA backward tokens/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train_bf16]
+
+One step = one full kda_bwd call (chunk table, prep, reverse state-gradient
+scan, gradient pass, dA_log reduction) on the training-shape workload
+B=8, T=4096, H=32, K=V=128, bf16 activations, chunk 64, with the chunk start
+states (from the reference forward) already resident in HBM.  Prints ONE JSON
+line.  The CPU baseline is the fp64 oracle timed on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# Algorithmic bytes per token-head of each kernel's own compulsory traffic
+# (each operand read once, each result written once), bf16 activations,
+# K = V = 128, chunk 64.  Per chunk-head quantities are divided by 64.
+def kernel_bytes_per_token_head(D=128, es=2):
+    act = D * es          # one activation row
+    f32row = D * 4        # one fp32 row (g_raw, dg_raw)
+    state = D * D * es / 64.0   # one K x V state per chunk
+    sq = 64 * 64 * es / 64.0    # one 64 x 64 matrix per chunk
+    return {
+        # q, k, g_raw, beta -> Tm (KxK), PT (Kx64), eGT, INV, INV^T, Mqk^T
+        "prep": 2 * act + f32row + 4 + state + D * 64 * es / 64.0 + D * 4 / 64.0 + 3 * sq,
+        # Tm, PT, eGT, dO -> dS_out
+        "scan": state + D * 64 * es / 64.0 + D * 4 / 64.0 + act + state,
+        # k, v, dO, g_raw, beta, S_in, dS_out, INV, INV^T, Mqk^T -> dv, U, dvcorr, dbeta
+        "grad_state": 3 * act + f32row + 4 + 2 * state + 3 * sq + 3 * act + 4,
+        # q, k, dO, g_raw, beta, S_in, dS_out, U, dvcorr, dbeta -> dq, dk, dg_raw, dbeta, dA_log part
+        "grad_key": 2 * act + act + f32row + 4 + 2 * state + 2 * act + 4 + 2 * act + f32row + 4,
+    }
+
+
+# The whole path's algorithmic bytes per token-head: inputs q, k, v, dO, g_raw,
+# beta read once, outputs dq, dk, dv, dg_raw, dbeta written once, the chunk start
+# state read once and the state gradient handed from the scan to the gradient
+# pass once (written + read).
+def path_bytes_per_token_head(D=128, es=2):
+    return 4 * D * es + D * 4 + 4 + 3 * D * es + D * 4 + 4 + D * D * es / 64.0 * 3
+
+
+def kernel_sources_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_backward_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_stage):
+    """HBM traffic measured by rocprofv3 counters (profiles/traffic.json), only
+    if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("sources") != kernel_sources_digest():
+        return None
+    ent = d.get("kernels", {}).get(kernel_stage)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, target_s=12.0):
+    """Time the fp64 oracle on whole heads of the workload (every sequence of
+    each head), sized to roughly target_s seconds; scale to tokens/s."""
+    import numpy as np
+    import kda_inputs as KI
+    from oracle import oracle as O
+    threads = O.num_threads()
+    H = inp["H"]
+    TT = inp["q"].shape[0]
+    # probe: one head, the first sequence, its first 256 tokens
+    probe = KI.select_heads(KI.select_seqs(inp, [0]), [0])
+    n0 = min(256, int(probe["cu_seqlens"][-1]))
+    for key in ("q", "k", "v", "dO", "g_raw", "beta"):
+        probe[key] = probe[key][:n0]
+    probe["cu_seqlens"] = np.array([0, n0])
+    t = time.perf_counter()
+    O.kda_backward(probe, nthreads=1)
+    per_token_head = (time.perf_counter() - t) / n0
+    units_per_head = inp["N"]
+    est_per_head = per_token_head * TT / max(1, min(threads, units_per_head))
+    nh = int(max(1, min(H, round(target_s / max(est_per_head, 1e-9)))))
+    # keep all threads busy: whole heads, every sequence
+    sub = KI.select_heads(inp, list(range(nh)))
+    t = time.perf_counter()
+    O.kda_backward(sub)
+    dt = time.perf_counter() - t
+    token_heads = TT * nh
+    tok_s = token_heads / H / dt
+    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d heads x all %d tokens (%d token-heads), fp64, %.1f s"
+                      % (nh, H, TT, token_heads, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="train_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times) so that "
+                         "HBM counters can be scaled against a kernel of known traffic")
+    a = ap.parse_args()
+    if a.copy_calib:
+        import torch
+        n = a.copy_calib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "repeats": 3}))
+        return
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU; this build has no multi-GPU path (--gpus %d)" % a.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import kda_inputs as KI
+    import linear_attention_backward_amd as K
+    from tests import kda_case as KC
+
+    assert torch.cuda.is_available(), "needs a GPU"
+    K.load_library()
+    wl = KI.get_workload(a.workload)
+    t = time.perf_counter()
+    inp = KI.make_inputs(wl)
+    log("inputs generated in %.1f s" % (time.perf_counter() - t))
+    g = KC.to_gpu(inp)
+    cu = inp["cu_seqlens"] if inp["varlen"] else None
+    fwd = K.kda_fwd_ref(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], h0=g["h0"],
+                        cu_seqlens=cu, want_o=False, want_ht=False)
+    torch.cuda.synchronize()
+    plan = K.BwdPlan(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dO"],
+                     h0=g["h0"], dht=g["dht"], h_saved=fwd["h_saved"], cu_seqlens=cu)
+    stream = torch.cuda.current_stream()
+    for _ in range(a.warmup):
+        plan.run(stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(a.steps):
+        plan.run(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / a.steps
+    tokens = int(inp["q"].shape[0])
+    value = tokens / (ms / 1e3)
+    log("kda_bwd: %.3f ms/step (wall %.3f ms/step)" % (ms, t_wall * 1e3 / a.steps))
+
+    # per-kernel durations (HIP events around each launch, on the launch stream)
+    K.timing_enable(True)
+    nt = max(3, min(a.steps, 10))
+    for _ in range(nt):
+        plan.run(stream)
+    torch.cuda.synchronize()
+    st = K.timing_read()
+    K.timing_enable(False)
+    per = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in st.items()}
+    log("per-kernel ms: " + " ".join("%s=%.3f" % kv for kv in per.items() if kv[1] > 0))
+    dom = max(("prep", "scan", "grad_state", "grad_key"), key=lambda s: per[s])
+    H, D = inp["H"], inp["K"]
+    es = 2 if inp["dtype"] == "bf16" else 4
+    token_heads = tokens * H
+    kb = kernel_bytes_per_token_head(D, es)[dom] * token_heads
+    achieved = kb / (per[dom] / 1e3) / 1e9
+    traffic = load_traffic(dom)
+    path_bytes = path_bytes_per_token_head(D, es) * token_heads
+    out = {
+        "metric": "KDA backward tokens/s (H=32,K=V=128,bf16)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp["dtype"],
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": H, "K": D, "V": inp["V"],
+                   "chunk": 64, "h_saved": "given", "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "path_roofline": {"bound": "hbm", "algorithmic_bytes": path_bytes,
+                          "achieved": path_bytes / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": path_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "kernel_ms": per,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
