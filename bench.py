@@ -43,10 +43,9 @@ def kernel_bytes_per_token_head(D=128, es=2):
         "prep": 2 * act + f32row + 4 + state + D * 64 * es / 64.0 + D * 4 / 64.0 + 3 * sq,
         # Tm, PT, eGT, dO -> dS_out
         "scan": state + D * 64 * es / 64.0 + D * 4 / 64.0 + act + state,
-        # k, v, dO, g_raw, beta, S_in, dS_out, INV, INV^T, Mqk^T -> dv, U, dvcorr, dbeta
-        "grad_state": 3 * act + f32row + 4 + 2 * state + 3 * sq + 3 * act + 4,
-        # q, k, dO, g_raw, beta, S_in, dS_out, U, dvcorr, dbeta -> dq, dk, dg_raw, dbeta, dA_log part
-        "grad_key": 2 * act + act + f32row + 4 + 2 * state + 2 * act + 4 + 2 * act + f32row + 4,
+        # q, k, v, dO, g_raw, beta, S_in, dS_out, INV, INV^T, Mqk^T
+        #   -> dq, dk, dv, dg_raw, dbeta, dA_log partial
+        "grad": 4 * act + f32row + 4 + 2 * state + 3 * sq + 3 * act + f32row + 4 + 4 / 64.0,
     }
 
 
@@ -188,7 +187,7 @@ def main():
     K.timing_enable(False)
     per = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in st.items()}
     log("per-kernel ms: " + " ".join("%s=%.3f" % kv for kv in per.items() if kv[1] > 0))
-    dom = max(("prep", "scan", "grad_state", "grad_key"), key=lambda s: per[s])
+    dom = max(("prep", "scan", "grad"), key=lambda s: per[s])
     H, D = inp["H"], inp["K"]
     es = 2 if inp["dtype"] == "bf16" else 4
     token_heads = tokens * H

@@ -150,8 +150,7 @@ KDA_API int kda_abi_version(void);
  * waits for the recorded events, writes per-stage totals (milliseconds) and
  * launch counts for up to n stages, clears them, and returns the number of
  * stages.  Stages: 0 chunk table, 1 prep, 2 state-gradient scan, 3 gradient
- * pass (state side), 4 gradient pass (key side and gate epilogue), 5 dA_log
- * reduction, 6 state recompute (h_saved == NULL).
+ * pass, 4 dA_log reduction, 5 state recompute (h_saved == NULL).
  * Not thread-safe; meant for benchmarks. */
 KDA_API int kda_timing_enable(int on);
 KDA_API int kda_timing_read(double* ms, int* launches, int n);

@@ -25,7 +25,7 @@ KDA_WS_BWD = 0
 KDA_WS_FWD = 1
 CHUNK = 64
 
-STAGES = ("chunk_table", "prep", "scan", "grad_state", "grad_key", "dalog", "recompute")
+STAGES = ("chunk_table", "prep", "scan", "grad", "dalog", "recompute")
 
 _P = ctypes.c_void_p
 

@@ -29,7 +29,7 @@ struct Plan {
   int64_t NC = 0;
   size_t es = 0;  // bytes per act element
   // workspace regions
-  Region chunks, seq_off, Tm, PT, eGT, INV, INVT, MqkT, dstates, U, dvc, dAl, hsaved;
+  Region chunks, seq_off, Tm, PT, eGT, INV, INVT, MqkT, dstates, dAl, hsaved;
   size_t fwd_bytes = 0, bwd_bytes = 0;
 };
 
@@ -100,8 +100,6 @@ int make_plan(const kda_problem* p, Plan* pl) {
   take(pl->INVT, NCH * 64 * 64 * pl->es);
   take(pl->MqkT, NCH * 64 * 64 * pl->es);
   take(pl->dstates, NCH * D * D * pl->es);
-  take(pl->U, NCH * 64 * D * pl->es);
-  take(pl->dvc, NCH * 64 * D * pl->es);
   take(pl->dAl, NCH * 4);
   take(pl->hsaved, NCH * D * D * pl->es);
   pl->bwd_bytes = off;
@@ -117,7 +115,7 @@ struct TimedLaunch {
 };
 bool g_timing = false;
 std::vector<TimedLaunch> g_events;
-constexpr int kStages = 7;
+constexpr int kStages = 6;
 
 template <typename F>
 hipError_t timed(int stage, hipStream_t st, F&& launch) {
@@ -240,8 +238,6 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   b.INVT = ws + pl.INVT.off;
   b.MqkT = ws + pl.MqkT.off;
   b.dstates = io->dstates ? io->dstates : (void*)(ws + pl.dstates.off);
-  b.U = ws + pl.U.off;
-  b.dvc = ws + pl.dvc.off;
   b.dAl_part = (float*)(ws + pl.dAl.off);
   b.h_saved = io->h_saved ? io->h_saved : (const void*)(ws + pl.hsaved.off);
   const Shape& sh = pl.s;
@@ -249,7 +245,7 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   e = timed(0, s, [&] { return launch_chunk_table(sh, (ChunkInfo*)b.chunks, (int*)b.seq_off, s); });
   if (e != hipSuccess) return hip_fail(e);
   if (!io->h_saved) {
-    e = timed(6, s, [&] {
+    e = timed(5, s, [&] {
       return launch_fwd_ref(sh, b.seq_off, io->q, io->k, io->v, io->g_raw, io->beta, io->A_log,
                             io->h0, nullptr, nullptr, (void*)b.h_saved, s);
     });
@@ -260,11 +256,9 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   const int vs = vsplit_for(sh);
   e = timed(2, s, [&] { return launch_scan(sh, b, vs, s); });
   if (e != hipSuccess) return hip_fail(e);
-  e = timed(3, s, [&] { return launch_grad1(sh, b, s); });
+  e = timed(3, s, [&] { return launch_gradf(sh, b, s); });
   if (e != hipSuccess) return hip_fail(e);
-  e = timed(4, s, [&] { return launch_grad2(sh, b, s); });
-  if (e != hipSuccess) return hip_fail(e);
-  e = timed(5, s, [&] { return launch_dalog(sh, b, s); });
+  e = timed(4, s, [&] { return launch_dalog(sh, b, s); });
   if (e != hipSuccess) return hip_fail(e);
   return KDA_OK;
 }

@@ -49,6 +49,7 @@ template <> struct Mma<bf16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ Frag load(const bf16* p) { return *(const bf16x8*)p; }
+  __device__ static __forceinline__ float elem(Frag f, int j) { return (float)f[j]; }
   __device__ static __forceinline__ Frag from_f32(const float* p) {
     f4 a = *(const f4*)p, b = *(const f4*)(p + 4);
     Frag r;
@@ -92,6 +93,7 @@ template <> struct Mma<float> {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ Frag load(const float* p) { return *p; }
+  __device__ static __forceinline__ float elem(Frag f, int) { return f; }
   __device__ static __forceinline__ Frag from_f32(const float* p) { return *p; }
   __device__ static __forceinline__ Frag from_vals(const float* v) { return v[0]; }
   __device__ static __forceinline__ float dot(Frag a, Frag b) { return a * b; }
@@ -101,6 +103,74 @@ template <> struct Mma<float> {
 };
 
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+// 16-wide contractions (one 16-row block).  Lane group g = lane >> 4 supplies the
+// four contraction indices kidx(g, j), j = 0..3, of its row (A) or column (B):
+// bf16 uses one v_mfma_f32_16x16x16_bf16 (k = 4g + j), fp32 four
+// v_mfma_f32_16x16x4_f32 (step j contracts k = 4j + g).  mma_sb keeps A in the
+// act dtype and carries B at fp32 accuracy (bf16: B = hi + lo, two products).
+template <typename T> struct M16;
+template <> struct M16<bf16> {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  __device__ static __forceinline__ int kidx(int g, int j) { return 4 * g + j; }
+  __device__ static __forceinline__ void ld(const bf16* row, int g, float* out) {
+    const bf16x4 v = *(const bf16x4*)(row + 4 * g);
+    out[0] = (float)v[0]; out[1] = (float)v[1]; out[2] = (float)v[2]; out[3] = (float)v[3];
+  }
+  __device__ static __forceinline__ void ldf(const float* row, int g, float* out) {
+    const f4 v = *(const f4*)(row + 4 * g);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  }
+  __device__ static __forceinline__ f4 mma_sb(const float* a, const float* b, f4 c) {
+    bf16x4 ah, bh, bl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ah[j] = (bf16)a[j];
+      bh[j] = (bf16)b[j];
+      bl[j] = (bf16)(b[j] - (float)bh[j]);
+    }
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, ah),
+                                                   __builtin_bit_cast(s4, bl), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, ah),
+                                                      __builtin_bit_cast(s4, bh), c, 0, 0, 0);
+  }
+  // both operands at fp32 accuracy: ah.bh + ah.bl + al.bh
+  __device__ static __forceinline__ f4 mma_ss(const float* a, const float* b, f4 c) {
+    bf16x4 ah, al, bh, bl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ah[j] = (bf16)a[j];
+      al[j] = (bf16)(a[j] - (float)ah[j]);
+      bh[j] = (bf16)b[j];
+      bl[j] = (bf16)(b[j] - (float)bh[j]);
+    }
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, al),
+                                                   __builtin_bit_cast(s4, bh), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, ah),
+                                                   __builtin_bit_cast(s4, bl), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, ah),
+                                                      __builtin_bit_cast(s4, bh), c, 0, 0, 0);
+  }
+};
+template <> struct M16<float> {
+  __device__ static __forceinline__ int kidx(int g, int j) { return 4 * j + g; }
+  __device__ static __forceinline__ void ld(const float* row, int g, float* out) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = row[4 * j + g];
+  }
+  __device__ static __forceinline__ void ldf(const float* row, int g, float* out) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = row[4 * j + g];
+  }
+  __device__ static __forceinline__ f4 mma_sb(const float* a, const float* b, f4 c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+    return c;
+  }
+  __device__ static __forceinline__ f4 mma_ss(const float* a, const float* b, f4 c) {
+    return mma_sb(a, b, c);
+  }
+};
 
 // Load KPL consecutive elements of type T as floats.
 template <typename T, int N> __device__ __forceinline__ void load_f(const T* p, float* out) {

@@ -1,0 +1,750 @@
+// kda_gradf.hip -- fused gradient pass: one workgroup (D/16 waves) per chunk-head.
+//
+// Quantities per chunk (G: in-chunk cumulative gate; Kd = K e^G, Kr = K e^{G_T-G},
+// Qd = Q e^G; INV and Mqk from the prep pass; S_in the chunk start state; dS_out
+// the state gradient at the chunk end from the scan).  [KB] = the Kernel-B guide
+// ("bwd-kernelB-beginner-guide-full"), part 2.
+//   state side ([KB] B1, and the kdS / dbeta part of B2):
+//     Y = V - Kd S_in,  U = INV diag(beta) Y,
+//     dU = Mqk^T dO + Kr dS_out,  dvcorr = INV^T dU,  dv = beta . dvcorr,
+//     dbeta_r  = sum_d dvcorr_rd Y_rd
+//   key side ([KB] B2, B3 and the inlined gate epilogue K1):
+//     dKr = U dS_out^T,  dQd0 = dO S_in^T,  dKd0 = dvcorr S_in^T,
+//     p_i = sum_d S_in[i,d] dS_out[i,d]                       ([KB] B0, folded into B2)
+//     dMqk = tril(dO U^T),  dL = -stril(dvcorr U^T)
+//     dq   = e^G dQd0 + sum_{s<=r} dMqk_rs k_s e^{G_r-G_s}
+//     dk_d = beta_r (-e^G dKd0 + x2),  x2_r = sum_{s<r} dL_rs k_s e^{G_r-G_s}
+//     dk_i = sum_{r>=s} (dMqk_rs q_r + beta_r dL_rs k_r) e^{G_r-G_s}
+//     dk_r = e^{G_T-G} dKr,  dk = dk_d + dk_i + dk_r
+//     dbeta_r += sum_s dL_rs A_rs = sum_i k_ri x2_ri
+//     dG = q.dq + k.(dk_d - dk_i - dk_r);  dG_last += sum_r k.dk_r + e^{G_T}.p
+//     dg = reverse cumsum of dG (rows);  dg_raw = dg . (-e^{A_log} sigmoid(g_raw))
+//     dA_log partial = sum dg . g
+// The epilogue stays fp32 ([KB] B3: dk_d - dk_i - dk_r cancels strongly).  The
+// pairwise decays e^{G_r-G_s} never come from exp(-G) (it overflows): across
+// 16-row blocks and across 4-row sub-blocks inside a block they factor through an
+// anchor row between r and s (both factors <= 1) and run on MFMA with the decayed
+// operand carried at fp32 accuracy (hi + lo bf16); inside a 4x4 diagonal sub-block
+// they are products of per-token decays (VALU).
+#include "kda_dev.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+__device__ __forceinline__ void softplus_sigmoid(float x, float& sp, float& sg) {
+  const float e = __expf(-fabsf(x));
+  sp = fmaxf(x, 0.f) + __logf(1.f + e);
+  const float r = 1.f / (1.f + e);
+  sg = x >= 0.f ? r : e * r;
+}
+
+template <typename T, int D> struct GF {
+  using P = Pitch<T, D>;
+  static constexpr int NW = D / 16;  // waves
+  static constexpr int NT = NW * 64;
+  static constexpr int WPR = NW / 4;  // waves per 16-row block in the state side
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int PGT = 68;                // sGT  [D][PGT] fp32 (channel-major G)
+  static constexpr int PST = D + 16 / ES;       // sST  [D][PST] state transposed
+  static constexpr int PTT = P::TT;             // [D][64] token-minor tiles
+  static constexpr int PN = P::N;               // [64][D] token-major tiles
+  static constexpr int PCC = P::CT;             // [64][64] tiles
+  static constexpr int G_OFF = 0;
+  static constexpr int G_SZ = D * PGT * 4;
+  static constexpr int N_SZ = 64 * PN * ES;
+  static constexpr int U_OFF = G_OFF + G_SZ;    // v (phase 0-1), then U
+  static constexpr int DVC_OFF = U_OFF + N_SZ;  // dvcorr
+  static constexpr int X_OFF = DVC_OFF + N_SZ;
+  static constexpr int TT_SZ = D * PTT * ES;
+  static constexpr int CC_SZ = 64 * PCC * ES;
+  // state side
+  static constexpr int ST_OFF = X_OFF;
+  static constexpr int OT_OFF = ST_OFF + D * PST * ES;
+  static constexpr int YT_OFF = OT_OFF + TT_SZ;
+  static constexpr int X1_END = YT_OFF + TT_SZ;
+  // key side, first part: dO token-major
+  static constexpr int ON_OFF = X_OFF;
+  // key side, second part
+  static constexpr int KT_OFF = X_OFF;
+  static constexpr int QT_OFF = KT_OFF + TT_SZ;
+  static constexpr int DM_OFF = QT_OFF + TT_SZ;
+  static constexpr int DL_OFF = DM_OFF + CC_SZ;
+  static constexpr int DMT_OFF = DL_OFF + CC_SZ;
+  static constexpr int BLT_OFF = DMT_OFF + CC_SZ;
+  static constexpr int X3_END = BLT_OFF + CC_SZ;
+  static constexpr int X_END = X1_END > X3_END ? X1_END : X3_END;
+  static constexpr int B_OFF = (X_END + 15) / 16 * 16;     // beta [64]
+  static constexpr int DB1_OFF = B_OFF + 256;             // [WPR][64]
+  static constexpr int DB2_OFF = DB1_OFF + WPR * 256;     // [NW][64]
+  static constexpr int RED_OFF = DB2_OFF + NW * 256;      // [NW]
+  // fp32 copies of the four diagonal 16x16 blocks of dMqk, dL, dMqk^T, (beta dL)^T
+  // (only needed when the tiles above are bf16)
+  static constexpr int DG_OFF = (RED_OFF + NW * 4 + 15) / 16 * 16;
+  static constexpr int DG_SZ = ES == 2 ? 4 * 4 * 256 * 4 : 0;
+  static constexpr int TOTAL = DG_OFF + DG_SZ;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(4 * D) void k_gradf(
+    const ChunkInfo* __restrict__ chunks, int H, const T* __restrict__ q,
+    const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
+    const float* __restrict__ g_raw, const float* __restrict__ beta,
+    const float* __restrict__ A_log, const T* __restrict__ h_saved,
+    const T* __restrict__ dstates, const T* __restrict__ INV, const T* __restrict__ INVT,
+    const T* __restrict__ MqkT, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
+    float* __restrict__ dg_raw, float* __restrict__ dbeta, float* __restrict__ dAl_part) {
+  using L = GF<T, D>;
+  using MM = Mma<T>;
+  using MS = M16<T>;
+  typedef typename MM::Frag Frag;
+  constexpr int NW = L::NW, NT = L::NT, WPR = L::WPR;
+  constexpr int KS = MM::KS, KPL = MM::KPL;
+  constexpr int PGT = L::PGT, PST = L::PST, PTT = L::PTT, PN = L::PN, PCC = L::PCC;
+  constexpr int NKD = D / KS;  // k-steps over a D-long contraction
+  constexpr int NKC = 64 / KS; // k-steps over the chunk
+  constexpr int EPV = 16 / L::ES;
+  constexpr int VPR = D / EPV;              // 16-byte vectors per D-long row
+  constexpr int NLS = D * VPR / NT;         // vectors per thread for a D x D state
+  constexpr int NLT = 64 * VPR / NT;        // vectors per thread for a 64 x D tile
+  static_assert(D * VPR % NT == 0 && 64 * VPR % NT == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  float* sGT = (float*)(smem + L::G_OFF);
+  T* sU = (T*)(smem + L::U_OFF);
+  T* sV = sU;
+  T* sDVC = (T*)(smem + L::DVC_OFF);
+  T* sST = (T*)(smem + L::ST_OFF);
+  T* sOT = (T*)(smem + L::OT_OFF);
+  T* sYT = (T*)(smem + L::YT_OFF);
+  T* sON = (T*)(smem + L::ON_OFF);
+  T* sKT = (T*)(smem + L::KT_OFF);
+  T* sQT = (T*)(smem + L::QT_OFF);
+  T* sDM = (T*)(smem + L::DM_OFF);
+  T* sDL = (T*)(smem + L::DL_OFF);
+  T* sDMT = (T*)(smem + L::DMT_OFF);
+  T* sBLT = (T*)(smem + L::BLT_OFF);
+  float* sBeta = (float*)(smem + L::B_OFF);
+  float* sDB1 = (float*)(smem + L::DB1_OFF);
+  float* sDB2 = (float*)(smem + L::DB2_OFF);
+  float* sRed = (float*)(smem + L::RED_OFF);
+  // diagonal 16x16 blocks of dMqk, dL, dMqk^T, (beta dL)^T in fp32: block R at
+  // dg*[R * DGB + row * DGP + col]
+  float* dgM;
+  float* dgL;
+  float* dgMT;
+  float* dgBLT;
+  int DGP, DGB;
+  if constexpr (L::ES == 2) {
+    float* base = (float*)(smem + L::DG_OFF);
+    dgM = base;
+    dgL = base + 1024;
+    dgMT = base + 2048;
+    dgBLT = base + 3072;
+    DGP = 16;
+    DGB = 256;
+  } else {
+    dgM = (float*)(smem + L::DM_OFF);
+    dgL = (float*)(smem + L::DL_OFF);
+    dgMT = (float*)(smem + L::DMT_OFF);
+    dgBLT = (float*)(smem + L::BLT_OFF);
+    DGP = PCC;
+    DGB = 16 * PCC + 16;
+  }
+
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, cl = lane & 15;
+  const ChunkInfo ci = chunks[c];
+  const size_t t0 = ci.t0;
+  const int Lr = ci.len;
+  const size_t ch = (size_t)c * H + h;
+  const size_t DD = (size_t)D * D;
+  const size_t rs = (size_t)H * D;  // token stride of per-token tensors
+  const T* qh = q + t0 * rs + (size_t)h * D;
+  const T* kh = k + t0 * rs + (size_t)h * D;
+  const T* vh = v + t0 * rs + (size_t)h * D;
+  const T* oh = dO + t0 * rs + (size_t)h * D;
+  const float* grh = g_raw + t0 * rs + (size_t)h * D;
+  const T* Sin = h_saved + ch * DD;
+  const T* dSo = dstates + ch * DD;
+  const float aA = __expf(A_log[h]);
+
+  // ------------------------------------------------------------------ loads
+  uint4 rS[NLS], rD[NLS], rO[NLT], rV[NLT];
+#pragma unroll
+  for (int l = 0; l < NLS; ++l) {
+    const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
+    rS[l] = *(const uint4*)(Sin + (size_t)i * D + sv * EPV);
+    rD[l] = *(const uint4*)(dSo + (size_t)i * D + sv * EPV);
+  }
+#pragma unroll
+  for (int l = 0; l < NLT; ++l) {
+    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+    uint4 xo = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+    if (r < Lr) {
+      xo = *(const uint4*)(oh + r * rs + sv * EPV);
+      xv = *(const uint4*)(vh + r * rs + sv * EPV);
+    }
+    rO[l] = xo;
+    rV[l] = xv;
+  }
+  if (tid < 64) sBeta[tid] = tid < Lr ? beta[(t0 + tid) * H + h] : 0.f;
+  {  // in-chunk cumulative gate (log2 units), channel-major: sGT[i][r]
+    const int i = tid % D, part = tid / D;  // NT / D == 4 parts of 16 rows
+    float run = 0.f;
+#pragma unroll 4
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = part * 16 + rr;
+      float gg = 0.f;
+      if (r < Lr) {
+        float sp, sg;
+        softplus_sigmoid(grh[r * rs + i], sp, sg);
+        gg = -aA * sp;
+      }
+      run += gg * LOG2E;
+      sGT[i * PGT + r] = run;
+    }
+  }
+#pragma unroll
+  for (int l = 0; l < NLS; ++l) {  // S_in^T
+    const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
+    const T* e = (const T*)&rS[l];
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) sST[(sv * EPV + j) * PST + i] = e[j];
+  }
+#pragma unroll
+  for (int l = 0; l < NLT; ++l) {  // dO^T and v (token-major)
+    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+    const T* e = (const T*)&rO[l];
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) sOT[(sv * EPV + j) * PTT + r] = e[j];
+    *(uint4*)(sV + r * PN + sv * EPV) = rV[l];
+  }
+  __syncthreads();
+  {
+    const int i = tid % D, part = tid / D;
+    float add = 0.f;
+    for (int pp = 0; pp < part; ++pp) add += sGT[i * PGT + pp * 16 + 15];
+    __syncthreads();
+    if (part > 0)
+      for (int rr = 0; rr < 16; ++rr) sGT[i * PGT + part * 16 + rr] += add;
+  }
+  __syncthreads();
+
+  // ------------------------------------------------------------- state side
+  // wave w: rows of block R, value columns [64 half, 64 half + 64)
+  const int R1 = w / WPR, half = w % WPR;
+  const int arow = 16 * R1 + cl;            // A-operand row of this lane
+  const int crow = 16 * R1 + g4 * 4;        // first C row of this lane
+  const T* INVr = INV + ch * 4096 + arow * 64;
+  const T* INVTr = INVT + ch * 4096 + arow * 64;
+  const T* MqkTr = MqkT + ch * 4096 + arow * 64;
+  Frag kf[NKD];
+#pragma unroll
+  for (int kk = 0; kk < NKD; ++kk) {
+    if (arow < Lr) {
+      kf[kk] = MM::load(kh + arow * rs + kk * KS + g4 * KPL);
+    } else {
+      float z[KPL];
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) z[j] = 0.f;
+      kf[kk] = MM::from_vals(z);
+    }
+  }
+  // key-side B operands (natural rows of S_in and dS_out), prefetched
+  const int ic = 16 * w + cl;  // key channel of this lane in the key side
+  Frag bS[NKD], bD[NKD];
+#pragma unroll
+  for (int kk = 0; kk < NKD; ++kk) {
+    bS[kk] = MM::load(Sin + (size_t)ic * D + kk * KS + g4 * KPL);
+    bD[kk] = MM::load(dSo + (size_t)ic * D + kk * KS + g4 * KPL);
+  }
+  // Y = V - Kd S_in
+  f4 Y[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) Y[nt] = zero4();
+#pragma unroll
+  for (int kk = 0; kk < NKD; ++kk) {
+    float kd[KPL];
+    const int i0 = kk * KS + g4 * KPL;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) kd[j] = MM::elem(kf[kk], j) * ex2(sGT[(i0 + j) * PGT + arow]);
+    const Frag a = MM::from_vals(kd);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const Frag b = MM::load(sST + (64 * half + nt * 16 + cl) * PST + i0);
+      Y[nt] = MM::mma(a, b, Y[nt]);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int d = 64 * half + nt * 16 + cl;
+    f4 by;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      Y[nt][j] = to_f(sV[(crow + j) * PN + d]) - Y[nt][j];
+      by[j] = sBeta[crow + j] * Y[nt][j];
+    }
+    store_ct<T>(sYT, PTT, 16 * R1, 64 * half + nt * 16, by, lane);
+  }
+  __syncthreads();  // (beta Y)^T complete; S_in^T and v are dead
+#pragma unroll
+  for (int l = 0; l < NLS; ++l) {  // dS_out^T
+    const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
+    const T* e = (const T*)&rD[l];
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) sST[(sv * EPV + j) * PST + i] = e[j];
+  }
+  {  // U = INV (beta Y)
+    f4 U[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) U[nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NKC; ++ks) {
+      const Frag a = MM::load(INVr + ks * KS + g4 * KPL);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const Frag b = MM::load(sYT + (64 * half + nt * 16 + cl) * PTT + ks * KS + g4 * KPL);
+        U[nt] = MM::mma(a, b, U[nt]);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) store_c<T>(sU, PN, 16 * R1, 64 * half + nt * 16, U[nt], lane);
+  }
+  __syncthreads();  // dS_out^T in place; (beta Y)^T dead
+  {  // dU = Mqk^T dO + Kr dS_out  ->  dU^T
+    f4 dU[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) dU[nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NKC; ++ks) {
+      const Frag a = MM::load(MqkTr + ks * KS + g4 * KPL);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const Frag b = MM::load(sOT + (64 * half + nt * 16 + cl) * PTT + ks * KS + g4 * KPL);
+        dU[nt] = MM::mma(a, b, dU[nt]);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKD; ++kk) {
+      float kr[KPL];
+      const int i0 = kk * KS + g4 * KPL;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        kr[j] = MM::elem(kf[kk], j) *
+                ex2(sGT[(i0 + j) * PGT + 63] - sGT[(i0 + j) * PGT + arow]);
+      const Frag a = MM::from_vals(kr);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const Frag b = MM::load(sST + (64 * half + nt * 16 + cl) * PST + i0);
+        dU[nt] = MM::mma(a, b, dU[nt]);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) store_ct<T>(sYT, PTT, 16 * R1, 64 * half + nt * 16, dU[nt], lane);
+  }
+  __syncthreads();
+  {  // dvcorr = INV^T dU;  dv = beta . dvcorr;  dbeta (first part)
+    f4 dvc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) dvc[nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NKC; ++ks) {
+      const Frag a = MM::load(INVTr + ks * KS + g4 * KPL);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const Frag b = MM::load(sYT + (64 * half + nt * 16 + cl) * PTT + ks * KS + g4 * KPL);
+        dvc[nt] = MM::mma(a, b, dvc[nt]);
+      }
+    }
+    float db[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int d = 64 * half + nt * 16 + cl;
+      store_c<T>(sDVC, PN, 16 * R1, 64 * half + nt * 16, dvc[nt], lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = crow + j;
+        db[j] += dvc[nt][j] * Y[nt][j];
+        if (r < Lr) dv[(t0 + r) * rs + (size_t)h * D + d] = from_f<T>(sBeta[r] * dvc[nt][j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float s = sum16(db[j]);
+      if (cl == 0) sDB1[half * 64 + crow + j] = s;
+    }
+  }
+  __syncthreads();  // the state side is done: its tiles are dead
+#pragma unroll
+  for (int l = 0; l < NLT; ++l) {  // dO token-major for the key side
+    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+    *(uint4*)(sON + r * PN + sv * EPV) = rO[l];
+  }
+  // q, k for the epilogue (registers now, LDS after the next barrier)
+  uint4 rQ[NLT], rK[NLT];
+#pragma unroll
+  for (int l = 0; l < NLT; ++l) {
+    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+    uint4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
+    if (r < Lr) {
+      xq = *(const uint4*)(qh + r * rs + sv * EPV);
+      xk = *(const uint4*)(kh + r * rs + sv * EPV);
+    }
+    rQ[l] = xq;
+    rK[l] = xk;
+  }
+  __syncthreads();
+
+  // --------------------------------------------------------------- key side
+  // dKr = U dS_out^T, dQd0 = dO S_in^T, dKd0 = dvcorr S_in^T for key channels
+  // [16w, 16w+16) and all 64 rows; p for the same channels.
+  f4 aKr[4], aQd[4], aKd[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) aKr[rt] = aQd[rt] = aKd[rt] = zero4();
+  float pp = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NKD; ++kk) {
+    const int d0 = kk * KS + g4 * KPL;
+    pp += MM::dot(bS[kk], bD[kk]);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int r = rt * 16 + cl;
+      aKr[rt] = MM::mma(MM::load(sU + r * PN + d0), bD[kk], aKr[rt]);
+      aQd[rt] = MM::mma(MM::load(sON + r * PN + d0), bS[kk], aQd[rt]);
+      aKd[rt] = MM::mma(MM::load(sDVC + r * PN + d0), bS[kk], aKd[rt]);
+    }
+  }
+  pp += __shfl_xor(pp, 16);
+  pp += __shfl_xor(pp, 32);
+  // dMqk = tril(dO U^T), dL = -stril(dvcorr U^T): wave -> rows of block R1,
+  // column tiles [4/WPR * half, ...)
+  constexpr int CTW = 4 / WPR;
+  f4 am[CTW], al[CTW];
+#pragma unroll
+  for (int st = 0; st < CTW; ++st) am[st] = al[st] = zero4();
+#pragma unroll
+  for (int kk = 0; kk < NKD; ++kk) {
+    const int d0 = kk * KS + g4 * KPL;
+    const Frag ao = MM::load(sON + arow * PN + d0);
+    const Frag av = MM::load(sDVC + arow * PN + d0);
+#pragma unroll
+    for (int st = 0; st < CTW; ++st) {
+      const Frag b = MM::load(sU + ((CTW * half + st) * 16 + cl) * PN + d0);
+      am[st] = MM::mma(ao, b, am[st]);
+      al[st] = MM::mma(av, b, al[st]);
+    }
+  }
+  __syncthreads();  // dO token-major, U, dvcorr are dead
+  // dMqk, dL (masked) as act-dtype tiles, natural and transposed; beta folded into dL^T
+#pragma unroll
+  for (int st = 0; st < CTW; ++st) {
+    const int s = (CTW * half + st) * 16 + cl;
+    f4 m, l, bl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = crow + j;
+      m[j] = s <= r ? am[st][j] : 0.f;
+      l[j] = s < r ? -al[st][j] : 0.f;
+      bl[j] = sBeta[r] * l[j];
+    }
+    store_c<T>(sDM, PCC, 16 * R1, (CTW * half + st) * 16, m, lane);
+    store_c<T>(sDL, PCC, 16 * R1, (CTW * half + st) * 16, l, lane);
+    store_ct<T>(sDMT, PCC, 16 * R1, (CTW * half + st) * 16, m, lane);
+    store_ct<T>(sBLT, PCC, 16 * R1, (CTW * half + st) * 16, bl, lane);
+    if constexpr (L::ES == 2) {
+      if (CTW * half + st == R1) {  // diagonal block: keep fp32 copies
+        float* b0 = dgM + R1 * 256;
+        float* b1 = dgL + R1 * 256;
+        float* b2 = dgMT + R1 * 256;
+        float* b3 = dgBLT + R1 * 256;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rr = g4 * 4 + j;
+          b0[rr * 16 + cl] = m[j];
+          b1[rr * 16 + cl] = l[j];
+          b2[cl * 16 + rr] = m[j];
+          b3[cl * 16 + rr] = bl[j];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int l = 0; l < NLT; ++l) {  // q^T, k^T (channel-major)
+    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+    const T* eq = (const T*)&rQ[l];
+    const T* ek = (const T*)&rK[l];
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) {
+      sQT[(sv * EPV + j) * PTT + r] = eq[j];
+      sKT[(sv * EPV + j) * PTT + r] = ek[j];
+    }
+  }
+  __syncthreads();
+
+  // ------------------------------------------------ intra-chunk decay terms
+  const float* Gi = sGT + ic * PGT;  // G of this lane's column (channel ic), by row
+  const T* Ki = sKT + ic * PTT;
+  const T* Qi = sQT + ic * PTT;
+  const float gT = Gi[63];
+  float dG[4][4];
+  float dkr_col = 0.f, dal = 0.f;
+  float dbp[4][4];
+#pragma unroll 1
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r0 = 16 * rt;
+    const int ar = r0 + cl;  // A-operand row of this lane inside the tile
+    float Gr[4];
+    {
+      const f4 t = *(const f4*)(Gi + r0 + 4 * g4);
+      Gr[0] = t[0]; Gr[1] = t[1]; Gr[2] = t[2]; Gr[3] = t[3];
+    }
+    f4 X1a = zero4(), X2a = zero4(), Za = zero4();
+    f4 X1b = zero4(), X2b = zero4(), Zb = zero4();
+    // level 1: across 16-row blocks
+    //   rows r of this block, s in earlier blocks: anchor a = r0
+    if (rt > 0) {
+      const float ga = Gi[r0];
+      for (int S = 0; S < rt; ++S) {
+        float a1[4], a2[4], b[4], kv[4], gv[4];
+        MS::ld(sDM + ar * PCC + 16 * S, g4, a1);
+        MS::ld(sDL + ar * PCC + 16 * S, g4, a2);
+        MS::ld(Ki + 16 * S, g4, kv);
+        MS::ldf(Gi + 16 * S, g4, gv);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = kv[j] * ex2(ga - gv[j]);
+        X1a = MS::mma_sb(a1, b, X1a);
+        X2a = MS::mma_sb(a2, b, X2a);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sc = ex2(Gr[j] - ga);
+        X1a[j] *= sc;
+        X2a[j] *= sc;
+      }
+    }
+    //   rows s of this block, r in later blocks: anchor b = r0 + 16
+    if (rt < 3) {
+      const float gb = Gi[r0 + 16];
+      for (int R = rt + 1; R < 4; ++R) {
+        float a1[4], a2[4], bq[4], bk[4], qv[4], kv[4], gv[4];
+        MS::ld(sDMT + ar * PCC + 16 * R, g4, a1);
+        MS::ld(sBLT + ar * PCC + 16 * R, g4, a2);
+        MS::ld(Qi + 16 * R, g4, qv);
+        MS::ld(Ki + 16 * R, g4, kv);
+        MS::ldf(Gi + 16 * R, g4, gv);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float e = ex2(gv[j] - gb);
+          bq[j] = qv[j] * e;
+          bk[j] = kv[j] * e;
+        }
+        Za = MS::mma_sb(a1, bq, Za);
+        Za = MS::mma_sb(a2, bk, Za);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Za[j] *= ex2(gb - Gr[j]);
+    }
+    // level 2: 4-row sub-blocks inside this block (contraction index = row - r0)
+    {
+      float ma[4], la[4], mt[4], lt[4], kv[4], qv[4], gv[4];
+      MS::ldf(dgM + rt * DGB + cl * DGP, g4, ma);
+      MS::ldf(dgL + rt * DGB + cl * DGP, g4, la);
+      MS::ldf(dgMT + rt * DGB + cl * DGP, g4, mt);
+      MS::ldf(dgBLT + rt * DGB + cl * DGP, g4, lt);
+      MS::ld(Ki + r0, g4, kv);
+      MS::ld(Qi + r0, g4, qv);
+      MS::ldf(Gi + r0, g4, gv);
+      const int rsb = cl >> 2;  // sub-block of this lane's A row
+#pragma unroll
+      for (int rho = 1; rho < 4; ++rho) {
+        // rows in sub-block rho, s in earlier sub-blocks: anchor r0 + 4 rho
+        const float ga = Gi[r0 + 4 * rho];
+        float a1[4], a2[4], b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kx = MS::kidx(g4, j);
+          const bool ok = kx < 4 * rho;
+          a1[j] = (rsb == rho && ok) ? ma[j] : 0.f;
+          a2[j] = (rsb == rho && ok) ? la[j] : 0.f;
+          b[j] = ok ? kv[j] * ex2(ga - gv[j]) : 0.f;
+        }
+        X1b = MS::mma_ss(a1, b, X1b);
+        X2b = MS::mma_ss(a2, b, X2b);
+      }
+#pragma unroll
+      for (int sig = 0; sig < 3; ++sig) {
+        // rows s in sub-block sig, r in later sub-blocks: anchor r0 + 4 (sig + 1)
+        const float gb = Gi[r0 + 4 * (sig + 1)];
+        float a1[4], a2[4], bq[4], bk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kx = MS::kidx(g4, j);
+          const bool ok = kx >= 4 * (sig + 1);
+          const float e = ok ? ex2(gv[j] - gb) : 0.f;
+          a1[j] = (rsb == sig && ok) ? mt[j] : 0.f;
+          a2[j] = (rsb == sig && ok) ? lt[j] : 0.f;
+          bq[j] = qv[j] * e;
+          bk[j] = kv[j] * e;
+        }
+        Zb = MS::mma_ss(a1, bq, Zb);
+        Zb = MS::mma_ss(a2, bk, Zb);
+      }
+      // this lane's C rows are sub-block g4
+      if (g4 >= 1) {
+        const float ga = Gi[r0 + 4 * g4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sc = ex2(Gr[j] - ga);
+          X1b[j] *= sc;
+          X2b[j] *= sc;
+        }
+      }
+      if (g4 <= 2) {
+        const float gb = Gi[r0 + 4 * (g4 + 1)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Zb[j] *= ex2(gb - Gr[j]);
+      }
+    }
+    // level 3: the 4x4 diagonal sub-block of this lane's rows (VALU)
+    float x1d[4], x2d[4], zd[4];
+    {
+      const int rb = r0 + 4 * g4;
+      float kr[4], qr[4], br[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kr[j] = to_f(Ki[rb + j]);
+        qr[j] = to_f(Qi[rb + j]);
+        br[j] = sBeta[rb + j];
+      }
+      const float a1 = ex2(Gr[1] - Gr[0]), a2 = ex2(Gr[2] - Gr[1]), a3 = ex2(Gr[3] - Gr[2]);
+      // f[j][jj] = e^{G_{rb+j} - G_{rb+jj}}, jj <= j
+      float f[4][4];
+      f[0][0] = f[1][1] = f[2][2] = f[3][3] = 1.f;
+      f[1][0] = a1;
+      f[2][1] = a2;
+      f[2][0] = a1 * a2;
+      f[3][2] = a3;
+      f[3][1] = a2 * a3;
+      f[3][0] = f[2][0] * a3;
+      float mrow[4][4], lrow[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          mrow[j][jj] = dgM[rt * DGB + (4 * g4 + j) * DGP + 4 * g4 + jj];
+          lrow[j][jj] = dgL[rt * DGB + (4 * g4 + j) * DGP + 4 * g4 + jj];
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          if (jj <= j) {
+            s1 += mrow[j][jj] * kr[jj] * f[j][jj];
+            s2 += lrow[j][jj] * kr[jj] * f[j][jj];
+          }
+          if (jj >= j)
+            s3 += (mrow[jj][j] * qr[jj] + br[jj] * lrow[jj][j] * kr[jj]) * f[jj][j];
+        }
+        x1d[j] = s1;
+        x2d[j] = s2;
+        zd[j] = s3;
+      }
+    }
+    // combine and form the gate gradient of this tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = r0 + 4 * g4 + j;
+      const float eG = ex2(Gr[j]);
+      const float qv = to_f(Qi[r]), kv = to_f(Ki[r]);
+      const float br = sBeta[r];
+      const float x1 = X1a[j] + X1b[j] + x1d[j];
+      const float x2 = X2a[j] + X2b[j] + x2d[j];
+      const float dki = Za[j] + Zb[j] + zd[j];
+      const float dqv = eG * aQd[rt][j] + x1;
+      const float dkd = br * (-eG * aKd[rt][j] + x2);
+      const float dkr = ex2(gT - Gr[j]) * aKr[rt][j];
+      dG[rt][j] = qv * dqv + kv * (dkd - dki - dkr);
+      dkr_col += kv * dkr;
+      dbp[rt][j] = kv * x2;
+      if (r < Lr) {
+        const size_t o = (t0 + r) * rs + (size_t)h * D + ic;
+        dq[o] = from_f<T>(dqv);
+        dk[o] = from_f<T>(dkd + dki + dkr);
+      }
+    }
+  }
+  // last row: sum_r k.dk_r + e^{G_T} p
+  dkr_col += __shfl_xor(dkr_col, 16);
+  dkr_col += __shfl_xor(dkr_col, 32);
+  if (g4 == 3) dG[3][3] += dkr_col + ex2(gT) * pp;
+  // reverse cumsum over r = 16 rt + 4 g4 + j
+  float carry = 0.f;
+#pragma unroll
+  for (int rt = 3; rt >= 0; --rt) {
+    const float tot = dG[rt][0] + dG[rt][1] + dG[rt][2] + dG[rt][3];
+    const float t0v = __shfl(tot, cl), t1 = __shfl(tot, cl + 16);
+    const float t2 = __shfl(tot, cl + 32), t3 = __shfl(tot, cl + 48);
+    float run = carry;
+    if (g4 < 3) run += t3;
+    if (g4 < 2) run += t2;
+    if (g4 < 1) run += t1;
+    carry += t0v + t1 + t2 + t3;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      run += dG[rt][j];
+      const int r = rt * 16 + g4 * 4 + j;
+      if (r < Lr) {
+        const size_t o = (t0 + r) * rs + (size_t)h * D + ic;
+        float sp, sg;
+        softplus_sigmoid(grh[r * rs + ic], sp, sg);
+        dg_raw[o] = run * (-aA * sg);
+        dal += run * (-aA * sp);
+      }
+    }
+  }
+  // dbeta second part, reduced over this wave's channels
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float s = sum16(dbp[rt][j]);
+      if (cl == 0) sDB2[w * 64 + rt * 16 + g4 * 4 + j] = s;
+    }
+  dal = sum64(dal);
+  if (lane == 0) sRed[w] = dal;
+  __syncthreads();
+  if (tid < 64 && tid < Lr) {
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < WPR; ++x) s += sDB1[x * 64 + tid];
+#pragma unroll
+    for (int x = 0; x < NW; ++x) s += sDB2[x * 64 + tid];
+    dbeta[(t0 + tid) * H + h] = s;
+  }
+  if (tid == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) s += sRed[x];
+    dAl_part[ch] = s;
+  }
+}
+
+template <typename T, int D>
+static hipError_t gradf_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+  dim3 grid((unsigned)s.NC, (unsigned)s.H);
+  hipLaunchKernelGGL((k_gradf<T, D>), grid, dim3(GF<T, D>::NT), 0, st, p.chunks, s.H,
+                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dO, p.g_raw,
+                     p.beta, p.A_log, (const T*)p.h_saved, (const T*)p.dstates,
+                     (const T*)p.INV, (const T*)p.INVT, (const T*)p.MqkT, (T*)p.dq, (T*)p.dk,
+                     (T*)p.dv, p.dg_raw, p.dbeta, p.dAl_part);
+  return hipGetLastError();
+}
+
+hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+  if (s.NC == 0) return hipSuccess;
+  if (s.bf16) return s.D == 128 ? gradf_t<bf16, 128>(s, p, st) : gradf_t<bf16, 64>(s, p, st);
+  return gradf_t<float, 64>(s, p, st);
+}
+
+}  // namespace kda

@@ -24,8 +24,6 @@ struct BwdPtrs {
   void* INVT;              // [NC,H,64,64] act dtype: its transpose
   void* MqkT;              // [NC,H,64,64] act dtype: Mqk transposed
   void* dstates;           // [NC,H,K,V] act dtype: dL/dS at the end of every chunk
-  void* U;                 // [NC,H,64,V] act dtype: INV diag(beta) (V - Kd S_in)
-  void* dvc;               // [NC,H,64,V] act dtype: INV^T dU
   float* dAl_part;         // [NC,H] per chunk-head partial sums for dA_log
 };
 
@@ -43,8 +41,7 @@ hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, con
                           void* h_saved, hipStream_t st);
 hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_scan(const Shape& s, const BwdPtrs& p, int vsplit, hipStream_t st);
-hipError_t launch_grad1(const Shape& s, const BwdPtrs& p, hipStream_t st);
-hipError_t launch_grad2(const Shape& s, const BwdPtrs& p, hipStream_t st);
+hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st);
 
 }  // namespace kda
