@@ -112,6 +112,45 @@ __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 template <typename T> struct M16;
 template <> struct M16<bf16> {
   typedef short s4 __attribute__((ext_vector_type(4)));
+  // an operand carried as hi + lo bf16 (fp32 accuracy)
+  struct Op {
+    bf16x4 h, l;
+  };
+  __device__ static __forceinline__ Op split(const float* v) {
+    Op o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o.h[j] = (bf16)v[j];
+      o.l[j] = (bf16)(v[j] - (float)o.h[j]);
+    }
+    return o;
+  }
+  // an operand that is exactly bf16 (lo part zero), read straight from a row
+  __device__ static __forceinline__ Op ld_op(const bf16* row, int g) {
+    Op o;
+    o.h = *(const bf16x4*)(row + 4 * g);
+    o.l = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    return o;
+  }
+  __device__ static __forceinline__ Op keep_if(bool c, Op o) {
+    const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    Op r;
+    r.h = c ? o.h : z;
+    r.l = c ? o.l : z;
+    return r;
+  }
+  __device__ static __forceinline__ f4 mm(bf16x4 a, bf16x4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a),
+                                                      __builtin_bit_cast(s4, b), c, 0, 0, 0);
+  }
+  // A at act precision (hi only), B at fp32 accuracy
+  __device__ static __forceinline__ f4 op_sb(const Op& a, const Op& b, f4 c) {
+    return mm(a.h, b.h, mm(a.h, b.l, c));
+  }
+  // both at fp32 accuracy
+  __device__ static __forceinline__ f4 op_ss(const Op& a, const Op& b, f4 c) {
+    return mm(a.h, b.h, mm(a.h, b.l, mm(a.l, b.h, c)));
+  }
   __device__ static __forceinline__ int kidx(int g, int j) { return 4 * g + j; }
   __device__ static __forceinline__ void ld(const bf16* row, int g, float* out) {
     const bf16x4 v = *(const bf16x4*)(row + 4 * g);
@@ -153,6 +192,35 @@ template <> struct M16<bf16> {
   }
 };
 template <> struct M16<float> {
+  struct Op {
+    float v[4];
+  };
+  __device__ static __forceinline__ Op split(const float* v) {
+    Op o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.v[j] = v[j];
+    return o;
+  }
+  __device__ static __forceinline__ Op ld_op(const float* row, int g) {
+    Op o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.v[j] = row[4 * j + g];
+    return o;
+  }
+  __device__ static __forceinline__ Op keep_if(bool c, Op o) {
+    Op r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.v[j] = c ? o.v[j] : 0.f;
+    return r;
+  }
+  __device__ static __forceinline__ f4 op_sb(const Op& a, const Op& b, f4 c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+    return c;
+  }
+  __device__ static __forceinline__ f4 op_ss(const Op& a, const Op& b, f4 c) {
+    return op_sb(a, b, c);
+  }
   __device__ static __forceinline__ int kidx(int g, int j) { return 4 * j + g; }
   __device__ static __forceinline__ void ld(const float* row, int g, float* out) {
 #pragma unroll
@@ -204,12 +272,18 @@ __device__ __forceinline__ void store_ct<float>(float* base, int pitch, int row0
   *(f4*)(base + col * pitch + r) = acc;
 }
 
-// Sum over the 16 lanes that share (lane >> 4) (i.e. over the columns of a C tile).
+// DPP lane move inside a row of 16 lanes.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                                            0xF, true));
+}
+// Sum over the 16 lanes that share (lane >> 4) (i.e. over the columns of a C tile),
+// on DPP: swap neighbours, swap pairs, mirror halves of 8, mirror the row.
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
   return x;
 }
 // Sum over the whole wave.

@@ -34,7 +34,7 @@ namespace kda {
 __device__ __forceinline__ void softplus_sigmoid(float x, float& sp, float& sg) {
   const float e = __expf(-fabsf(x));
   sp = fmaxf(x, 0.f) + __logf(1.f + e);
-  const float r = 1.f / (1.f + e);
+  const float r = __builtin_amdgcn_rcpf(1.f + e);
   sg = x >= 0.f ? r : e * r;
 }
 
@@ -505,15 +505,16 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     if (rt > 0) {
       const float ga = Gi[r0];
       for (int S = 0; S < rt; ++S) {
-        float a1[4], a2[4], b[4], kv[4], gv[4];
-        MS::ld(sDM + ar * PCC + 16 * S, g4, a1);
-        MS::ld(sDL + ar * PCC + 16 * S, g4, a2);
+        float b[4], kv[4], gv[4];
+        const typename MS::Op a1 = MS::ld_op(sDM + ar * PCC + 16 * S, g4);
+        const typename MS::Op a2 = MS::ld_op(sDL + ar * PCC + 16 * S, g4);
         MS::ld(Ki + 16 * S, g4, kv);
         MS::ldf(Gi + 16 * S, g4, gv);
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = kv[j] * ex2(ga - gv[j]);
-        X1a = MS::mma_sb(a1, b, X1a);
-        X2a = MS::mma_sb(a2, b, X2a);
+        const typename MS::Op bo = MS::split(b);
+        X1a = MS::op_sb(a1, bo, X1a);
+        X2a = MS::op_sb(a2, bo, X2a);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -526,9 +527,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     if (rt < 3) {
       const float gb = Gi[r0 + 16];
       for (int R = rt + 1; R < 4; ++R) {
-        float a1[4], a2[4], bq[4], bk[4], qv[4], kv[4], gv[4];
-        MS::ld(sDMT + ar * PCC + 16 * R, g4, a1);
-        MS::ld(sBLT + ar * PCC + 16 * R, g4, a2);
+        float bq[4], bk[4], qv[4], kv[4], gv[4];
+        const typename MS::Op a1 = MS::ld_op(sDMT + ar * PCC + 16 * R, g4);
+        const typename MS::Op a2 = MS::ld_op(sBLT + ar * PCC + 16 * R, g4);
         MS::ld(Qi + 16 * R, g4, qv);
         MS::ld(Ki + 16 * R, g4, kv);
         MS::ldf(Gi + 16 * R, g4, gv);
@@ -538,13 +539,15 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
           bq[j] = qv[j] * e;
           bk[j] = kv[j] * e;
         }
-        Za = MS::mma_sb(a1, bq, Za);
-        Za = MS::mma_sb(a2, bk, Za);
+        Za = MS::op_sb(a1, MS::split(bq), Za);
+        Za = MS::op_sb(a2, MS::split(bk), Za);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) Za[j] *= ex2(gb - Gr[j]);
     }
-    // level 2: 4-row sub-blocks inside this block (contraction index = row - r0)
+    // level 2: 4-row sub-blocks inside this block (contraction index = row - r0).
+    // A rows outside the pass's sub-block are zeroed; the contraction range of the
+    // pass is cut on the B side.
     {
       float ma[4], la[4], mt[4], lt[4], kv[4], qv[4], gv[4];
       MS::ldf(dgM + rt * DGB + cl * DGP, g4, ma);
@@ -554,40 +557,34 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       MS::ld(Ki + r0, g4, kv);
       MS::ld(Qi + r0, g4, qv);
       MS::ldf(Gi + r0, g4, gv);
+      const typename MS::Op oma = MS::split(ma), ola = MS::split(la);
+      const typename MS::Op omt = MS::split(mt), olt = MS::split(lt);
       const int rsb = cl >> 2;  // sub-block of this lane's A row
 #pragma unroll
       for (int rho = 1; rho < 4; ++rho) {
         // rows in sub-block rho, s in earlier sub-blocks: anchor r0 + 4 rho
         const float ga = Gi[r0 + 4 * rho];
-        float a1[4], a2[4], b[4];
+        float b[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kx = MS::kidx(g4, j);
-          const bool ok = kx < 4 * rho;
-          a1[j] = (rsb == rho && ok) ? ma[j] : 0.f;
-          a2[j] = (rsb == rho && ok) ? la[j] : 0.f;
-          b[j] = ok ? kv[j] * ex2(ga - gv[j]) : 0.f;
-        }
-        X1b = MS::mma_ss(a1, b, X1b);
-        X2b = MS::mma_ss(a2, b, X2b);
+        for (int j = 0; j < 4; ++j)
+          b[j] = MS::kidx(g4, j) < 4 * rho ? kv[j] * ex2(ga - gv[j]) : 0.f;
+        const typename MS::Op bo = MS::split(b);
+        X1b = MS::op_ss(MS::keep_if(rsb == rho, oma), bo, X1b);
+        X2b = MS::op_ss(MS::keep_if(rsb == rho, ola), bo, X2b);
       }
 #pragma unroll
       for (int sig = 0; sig < 3; ++sig) {
         // rows s in sub-block sig, r in later sub-blocks: anchor r0 + 4 (sig + 1)
         const float gb = Gi[r0 + 4 * (sig + 1)];
-        float a1[4], a2[4], bq[4], bk[4];
+        float bq[4], bk[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int kx = MS::kidx(g4, j);
-          const bool ok = kx >= 4 * (sig + 1);
-          const float e = ok ? ex2(gv[j] - gb) : 0.f;
-          a1[j] = (rsb == sig && ok) ? mt[j] : 0.f;
-          a2[j] = (rsb == sig && ok) ? lt[j] : 0.f;
+          const float e = MS::kidx(g4, j) >= 4 * (sig + 1) ? ex2(gv[j] - gb) : 0.f;
           bq[j] = qv[j] * e;
           bk[j] = kv[j] * e;
         }
-        Zb = MS::mma_ss(a1, bq, Zb);
-        Zb = MS::mma_ss(a2, bk, Zb);
+        Zb = MS::op_ss(MS::keep_if(rsb == sig, omt), MS::split(bq), Zb);
+        Zb = MS::op_ss(MS::keep_if(rsb == sig, olt), MS::split(bk), Zb);
       }
       // this lane's C rows are sub-block g4
       if (g4 >= 1) {

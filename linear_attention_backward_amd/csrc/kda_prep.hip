@@ -159,21 +159,96 @@ __global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chun
         store_c<float>(sM, CC, 16 * R, 16 * S, zero4(), lane);
       }
     }
-    // diagonal block: pairwise decays, one (r, s) pair per lane and round
-    for (int p = lane; p < 256; p += 64) {
-      const int r = p >> 4, s = p & 15;
-      const int rr = 16 * R + r, ss = 16 * R + s;
-      float a = 0.f, m = 0.f;
-      if (s <= r) {
-        for (int i = 0; i < D; ++i) {
-          const float e = ex2(sG[rr * NF + i] - sG[ss * NF + i]);
-          const float ks = to_f(sK[ss * PN + i]) * e;
-          a += to_f(sK[rr * PN + i]) * ks;
-          m += to_f(sQ[rr * PN + i]) * ks;
+    // diagonal block (R, R), by 4-row sub-blocks:
+    //  (i) rows r of sub-block rho against s in earlier sub-blocks of the block,
+    //      anchored at a = 16R + 4 rho (between them): one MFMA pass per rho with
+    //      the A rows outside rho and the B columns at or after a set to zero;
+    //  (ii) pairs inside a 4x4 diagonal sub-block: pairwise decays on VALU, one
+    //      (sub-block, channel group) per lane, summed over the 16 groups.
+    {
+      const int r0 = 16 * R;
+      const int cl = lane & 15;
+      const int rA = r0 + cl;                  // A row of this lane
+      const int rho_l = cl >> 2;               // its sub-block
+      const int anc = r0 + 4 * rho_l;          // its anchor
+      f4 dA = zero4(), dM = zero4();
+      float zv[KPL];
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) zv[j] = 0.f;
+      const Frag ZF = MM::from_vals(zv);
+      for (int kk = 0; kk < D; kk += KS) {
+        const int i0 = kk + (lane >> 4) * KPL;
+        float kf[KPL], qf[KPL], ks[KPL], gs[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const float e = ex2(sG[rA * NF + i0 + j] - sG[anc * NF + i0 + j]);
+          kf[j] = to_f(sK[rA * PN + i0 + j]) * e;
+          qf[j] = to_f(sQ[rA * PN + i0 + j]) * e;
+          ks[j] = to_f(sK[rA * PN + i0 + j]);  // B column s = r0 + cl: same row data
+          gs[j] = sG[rA * NF + i0 + j];
+        }
+        const Frag KF = MM::from_vals(kf), QF = MM::from_vals(qf);
+#pragma unroll
+        for (int rho = 1; rho < 4; ++rho) {
+          const int a = r0 + 4 * rho;
+          const bool colok = cl < 4 * rho;
+          float kb[KPL];
+#pragma unroll
+          for (int j = 0; j < KPL; ++j)
+            kb[j] = colok ? ks[j] * ex2(sG[a * NF + i0 + j] - gs[j]) : 0.f;
+          const Frag KB = MM::from_vals(kb);
+          const bool rowok = rho_l == rho;
+          dA = MM::mma(rowok ? KF : ZF, KB, dA);
+          dM = MM::mma(rowok ? QF : ZF, KB, dM);
         }
       }
-      sA[rr * CC + ss] = (s < r) ? a : 0.f;
-      sM[rr * CC + ss] = (s <= r) ? m : 0.f;
+      {
+        constexpr int CPG = D / 16;
+        const int sb = lane >> 4, cg = lane & 15;
+        float pa[10], pm[10];
+#pragma unroll
+        for (int p = 0; p < 10; ++p) pa[p] = pm[p] = 0.f;
+        for (int c8 = 0; c8 < CPG; ++c8) {
+          const int i = cg * CPG + c8;
+          float kk4[4], qq4[4], gg4[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int r = r0 + 4 * sb + t;
+            kk4[t] = to_f(sK[r * PN + i]);
+            qq4[t] = to_f(sQ[r * PN + i]);
+            gg4[t] = sG[r * NF + i];
+          }
+#pragma unroll
+          for (int a_ = 0; a_ < 4; ++a_)
+#pragma unroll
+            for (int b_ = 0; b_ <= a_; ++b_) {
+              const int p = a_ * (a_ + 1) / 2 + b_;
+              const float kb = kk4[b_] * ex2(gg4[a_] - gg4[b_]);
+              pa[p] += kk4[a_] * kb;
+              pm[p] += qq4[a_] * kb;
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < 10; ++p) {
+          pa[p] = sum16(pa[p]);
+          pm[p] = sum16(pm[p]);
+        }
+        // C layout: lane holds rows 4 sb + j, column cl; the diagonal sub-block of
+        // those rows has columns 4 sb .. 4 sb + 3.
+        if ((cl >> 2) == sb) {
+          const int b_ = cl & 3;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (b_ <= j) {
+              const int p = j * (j + 1) / 2 + b_;
+              if (b_ < j) dA[j] += pa[p];
+              dM[j] += pm[p];
+            }
+          }
+        }
+      }
+      store_c<float>(sA, CC, r0, r0, dA, lane);
+      store_c<float>(sM, CC, r0, r0, dM, lane);
     }
   }
   __syncthreads();
