@@ -187,17 +187,57 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     rO[l] = xo;
     rV[l] = xv;
   }
+  // state side: wave w owns the rows of block R1, value columns [64 half, +64)
+  const int R1 = w / WPR, half = w % WPR;
+  const int arow = 16 * R1 + cl;            // A-operand row of this lane
+  const int crow = 16 * R1 + g4 * 4;        // first C row of this lane
+  Frag kf[NKD];                              // raw k of row arow
+#pragma unroll
+  for (int kk = 0; kk < NKD; ++kk) {
+    if (arow < Lr) {
+      kf[kk] = MM::load(kh + arow * rs + kk * KS + g4 * KPL);
+    } else {
+      float z[KPL];
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) z[j] = 0.f;
+      kf[kk] = MM::from_vals(z);
+    }
+  }
+  Frag fI[NKC], fIT[NKC], fMT[NKC];          // rows arow of INV, INV^T, Mqk^T
+#pragma unroll
+  for (int ks = 0; ks < NKC; ++ks) {
+    fI[ks] = MM::load(INV + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
+    fIT[ks] = MM::load(INVT + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
+    fMT[ks] = MM::load(MqkT + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
+  }
+  // key side: natural rows of S_in and dS_out for this lane's key channel
+  const int ic = 16 * w + cl;
+  Frag bS[NKD], bD[NKD];
+#pragma unroll
+  for (int kk = 0; kk < NKD; ++kk) {
+    bS[kk] = MM::load(Sin + (size_t)ic * D + kk * KS + g4 * KPL);
+    bD[kk] = MM::load(dSo + (size_t)ic * D + kk * KS + g4 * KPL);
+  }
+  float rg[16];  // g_raw of this thread's channel, 16 rows
+  {
+    const int i = tid % D, part = tid / D;  // NT / D == 4 parts of 16 rows
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = part * 16 + rr;
+      rg[rr] = r < Lr ? grh[r * rs + i] : 0.f;
+    }
+  }
   if (tid < 64) sBeta[tid] = tid < Lr ? beta[(t0 + tid) * H + h] : 0.f;
   {  // in-chunk cumulative gate (log2 units), channel-major: sGT[i][r]
-    const int i = tid % D, part = tid / D;  // NT / D == 4 parts of 16 rows
+    const int i = tid % D, part = tid / D;
     float run = 0.f;
-#pragma unroll 4
+#pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int r = part * 16 + rr;
       float gg = 0.f;
       if (r < Lr) {
         float sp, sg;
-        softplus_sigmoid(grh[r * rs + i], sp, sg);
+        softplus_sigmoid(rg[rr], sp, sg);
         gg = -aA * sp;
       }
       run += gg * LOG2E;
@@ -231,33 +271,6 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   __syncthreads();
 
   // ------------------------------------------------------------- state side
-  // wave w: rows of block R, value columns [64 half, 64 half + 64)
-  const int R1 = w / WPR, half = w % WPR;
-  const int arow = 16 * R1 + cl;            // A-operand row of this lane
-  const int crow = 16 * R1 + g4 * 4;        // first C row of this lane
-  const T* INVr = INV + ch * 4096 + arow * 64;
-  const T* INVTr = INVT + ch * 4096 + arow * 64;
-  const T* MqkTr = MqkT + ch * 4096 + arow * 64;
-  Frag kf[NKD];
-#pragma unroll
-  for (int kk = 0; kk < NKD; ++kk) {
-    if (arow < Lr) {
-      kf[kk] = MM::load(kh + arow * rs + kk * KS + g4 * KPL);
-    } else {
-      float z[KPL];
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) z[j] = 0.f;
-      kf[kk] = MM::from_vals(z);
-    }
-  }
-  // key-side B operands (natural rows of S_in and dS_out), prefetched
-  const int ic = 16 * w + cl;  // key channel of this lane in the key side
-  Frag bS[NKD], bD[NKD];
-#pragma unroll
-  for (int kk = 0; kk < NKD; ++kk) {
-    bS[kk] = MM::load(Sin + (size_t)ic * D + kk * KS + g4 * KPL);
-    bD[kk] = MM::load(dSo + (size_t)ic * D + kk * KS + g4 * KPL);
-  }
   // Y = V - Kd S_in
   f4 Y[4];
 #pragma unroll
@@ -300,7 +313,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     for (int nt = 0; nt < 4; ++nt) U[nt] = zero4();
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) {
-      const Frag a = MM::load(INVr + ks * KS + g4 * KPL);
+      const Frag a = fI[ks];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const Frag b = MM::load(sYT + (64 * half + nt * 16 + cl) * PTT + ks * KS + g4 * KPL);
@@ -317,7 +330,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     for (int nt = 0; nt < 4; ++nt) dU[nt] = zero4();
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) {
-      const Frag a = MM::load(MqkTr + ks * KS + g4 * KPL);
+      const Frag a = fMT[ks];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const Frag b = MM::load(sOT + (64 * half + nt * 16 + cl) * PTT + ks * KS + g4 * KPL);
@@ -349,7 +362,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     for (int nt = 0; nt < 4; ++nt) dvc[nt] = zero4();
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) {
-      const Frag a = MM::load(INVTr + ks * KS + g4 * KPL);
+      const Frag a = fIT[ks];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const Frag b = MM::load(sYT + (64 * half + nt * 16 + cl) * PTT + ks * KS + g4 * KPL);
@@ -489,6 +502,14 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   float dG[4][4];
   float dkr_col = 0.f, dal = 0.f;
   float dbp[4][4];
+  float tg[4][4];  // g_raw at this lane's C positions, for the epilogue (prefetched)
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = rt * 16 + g4 * 4 + j;
+      tg[rt][j] = r < Lr ? grh[r * rs + ic] : 0.f;
+    }
 #pragma unroll 1
   for (int rt = 0; rt < 4; ++rt) {
     const int r0 = 16 * rt;
@@ -694,7 +715,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       if (r < Lr) {
         const size_t o = (t0 + r) * rs + (size_t)h * D + ic;
         float sp, sg;
-        softplus_sigmoid(grh[r * rs + ic], sp, sg);
+        softplus_sigmoid(tg[rt][j], sp, sg);
         dg_raw[o] = run * (-aA * sg);
         dal += run * (-aA * sp);
       }

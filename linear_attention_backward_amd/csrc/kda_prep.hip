@@ -19,7 +19,7 @@
 namespace kda {
 
 __device__ __forceinline__ float softplus_p(float x) {
-  return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));
+  return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));
 }
 
 template <typename T, int D> struct PrepLds {
@@ -75,30 +75,52 @@ __global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chun
   const int t0 = ci.t0, Lr = ci.len;
   const size_t ch = (size_t)c * H + h;
 
-  // ---- load q, k (rows beyond the chunk are zero), beta, gate
+  // ---- load q, k (rows beyond the chunk are zero), beta, gate.  Every global
+  // load is issued before any of them is used.
   constexpr int VPR = D * (int)sizeof(T) / 16;
-  for (int idx = tid; idx < 64 * VPR; idx += NTHR) {
-    int r = idx / VPR, vv = idx % VPR;
-    uint4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
-    if (r < Lr) {
-      size_t off = ((size_t)(t0 + r) * H + h) * D;
-      xq = ((const uint4*)(q + off))[vv];
-      xk = ((const uint4*)(k + off))[vv];
+  constexpr int NLT = 64 * VPR / NTHR;
+  constexpr int PARTS = NTHR / D;
+  constexpr int RPP = 64 / PARTS;
+  const size_t rs = (size_t)H * D;
+  uint4 rq[NLT], rk[NLT];
+  float rg[RPP];
+  {
+    const T* qh = q + (size_t)t0 * rs + (size_t)h * D;
+    const T* kh = k + (size_t)t0 * rs + (size_t)h * D;
+#pragma unroll
+    for (int l = 0; l < NLT; ++l) {
+      const int idx = tid + l * NTHR, r = idx / VPR, vv = idx % VPR;
+      uint4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
+      if (r < Lr) {
+        xq = ((const uint4*)(qh + r * rs))[vv];
+        xk = ((const uint4*)(kh + r * rs))[vv];
+      }
+      rq[l] = xq;
+      rk[l] = xk;
     }
-    *(uint4*)((char*)(sQ + r * PN) + vv * 16) = xq;
-    *(uint4*)((char*)(sK + r * PN) + vv * 16) = xk;
+    const float* gh = g_raw + (size_t)t0 * rs + (size_t)h * D + tid % D;
+    const int part = tid / D;
+#pragma unroll
+    for (int rr = 0; rr < RPP; ++rr) {
+      const int r = part * RPP + rr;
+      rg[rr] = r < Lr ? gh[r * rs] : 0.f;
+    }
   }
   if (tid < 64) sBeta[tid] = tid < Lr ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
   const float aA = __expf(A_log[h]);
-  constexpr int PARTS = NTHR / D;
-  constexpr int RPP = 64 / PARTS;
+#pragma unroll
+  for (int l = 0; l < NLT; ++l) {
+    const int idx = tid + l * NTHR, r = idx / VPR, vv = idx % VPR;
+    *(uint4*)((char*)(sQ + r * PN) + vv * 16) = rq[l];
+    *(uint4*)((char*)(sK + r * PN) + vv * 16) = rk[l];
+  }
   {
     const int i = tid % D, part = tid / D;
     float run = 0.f;
+#pragma unroll
     for (int rr = 0; rr < RPP; ++rr) {
       const int r = part * RPP + rr;
-      float g = 0.f;
-      if (r < Lr) g = -aA * softplus_p(g_raw[((size_t)(t0 + r) * H + h) * D + i]);
+      const float g = r < Lr ? -aA * softplus_p(rg[rr]) : 0.f;
       run += g * LOG2E;
       sG[r * NF + i] = run;
     }
