@@ -41,6 +41,20 @@ template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16
 // 2^x on the transcendental unit.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Inside every group of 16 lanes, lane
+// 4a + b receives element b of the 8-byte chunks that lanes a, a + 4, a + 8, a + 12
+// of the group point at.  With lane 16G + s pointing at row k0 + (s >> 2), columns
+// n0 + 4 (s & 3) .. + 3 of a row-major [k][n] tile, lane 16G + n therefore receives
+// tile[k0 + e][n0 + n] for e = 0..3: a 4 x 16 block, read column-wise.  k0 is the
+// row of the lane's own group (callers add the group offset).
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4v lds_s4v;
+__device__ __forceinline__ bf16x4 ld_tr4(const bf16* tile, int pitch, int k0, int n0, int lane) {
+  const int s = lane & 15;
+  const bf16* p = tile + (k0 + (s >> 2)) * pitch + n0 + 4 * (s & 3);
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)p));
+}
+
 template <typename T> struct Mma;
 template <> struct Mma<bf16> {
   static constexpr int KS = 32, KPL = 8;
@@ -49,6 +63,28 @@ template <> struct Mma<bf16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ Frag load(const bf16* p) { return *(const bf16x8*)p; }
+  // Permuted contraction order for operands read across rows: lane group G holds
+  // k = kb + 4G + j (j < 4) and k = kb + 16 + 4G + (j - 4) (j >= 4), so that one
+  // fragment is two transposing reads of 16 consecutive rows each.  Both operands of
+  // a product must use the same order.
+  __device__ static __forceinline__ int kperm(int G, int j) {
+    return j < 4 ? 4 * G + j : 12 + 4 * G + j;
+  }
+  // fragment of a row-major [k][n] LDS tile, contraction over its rows (permuted order)
+  __device__ static __forceinline__ Frag ld_tr(const bf16* tile, int pitch, int kb, int n0,
+                                               int lane) {
+    const int G = lane >> 4;
+    const bf16x4 lo = ld_tr4(tile, pitch, kb + 4 * G, n0, lane);
+    const bf16x4 hi = ld_tr4(tile, pitch, kb + 16 + 4 * G, n0, lane);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // fragment of a row with contiguous k (any memory), permuted order
+  __device__ static __forceinline__ Frag ld_perm(const bf16* row, int kb, int lane) {
+    const int G = lane >> 4;
+    const bf16x4 lo = *(const bf16x4*)(row + kb + 4 * G);
+    const bf16x4 hi = *(const bf16x4*)(row + kb + 16 + 4 * G);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
   __device__ static __forceinline__ float elem(Frag f, int j) { return (float)f[j]; }
   __device__ static __forceinline__ Frag from_f32(const float* p) {
     f4 a = *(const f4*)p, b = *(const f4*)(p + 4);
@@ -93,6 +129,14 @@ template <> struct Mma<float> {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ Frag load(const float* p) { return *p; }
+  __device__ static __forceinline__ int kperm(int G, int) { return G; }
+  __device__ static __forceinline__ Frag ld_tr(const float* tile, int pitch, int kb, int n0,
+                                               int lane) {
+    return tile[(kb + (lane >> 4)) * pitch + n0 + (lane & 15)];
+  }
+  __device__ static __forceinline__ Frag ld_perm(const float* row, int kb, int lane) {
+    return row[kb + (lane >> 4)];
+  }
   __device__ static __forceinline__ float elem(Frag f, int) { return f; }
   __device__ static __forceinline__ Frag from_f32(const float* p) { return *p; }
   __device__ static __forceinline__ Frag from_vals(const float* v) { return v[0]; }
@@ -152,6 +196,19 @@ template <> struct M16<bf16> {
     return mm(a.h, b.h, mm(a.h, b.l, mm(a.l, b.h, c)));
   }
   __device__ static __forceinline__ int kidx(int g, int j) { return 4 * g + j; }
+  // operand of a row-major [k][n] LDS tile, contraction over its rows kb .. kb + 15
+  __device__ static __forceinline__ void ld_tr(const bf16* tile, int pitch, int kb, int n0,
+                                               int lane, float* out) {
+    const bf16x4 v = ld_tr4(tile, pitch, kb + 4 * (lane >> 4), n0, lane);
+    out[0] = (float)v[0]; out[1] = (float)v[1]; out[2] = (float)v[2]; out[3] = (float)v[3];
+  }
+  __device__ static __forceinline__ Op ld_tr_op(const bf16* tile, int pitch, int kb, int n0,
+                                                int lane) {
+    Op o;
+    o.h = ld_tr4(tile, pitch, kb + 4 * (lane >> 4), n0, lane);
+    o.l = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    return o;
+  }
   __device__ static __forceinline__ void ld(const bf16* row, int g, float* out) {
     const bf16x4 v = *(const bf16x4*)(row + 4 * g);
     out[0] = (float)v[0]; out[1] = (float)v[1]; out[2] = (float)v[2]; out[3] = (float)v[3];
@@ -222,6 +279,17 @@ template <> struct M16<float> {
     return op_sb(a, b, c);
   }
   __device__ static __forceinline__ int kidx(int g, int j) { return 4 * j + g; }
+  __device__ static __forceinline__ void ld_tr(const float* tile, int pitch, int kb, int n0,
+                                               int lane, float* out) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = tile[(kb + 4 * j + (lane >> 4)) * pitch + n0 + (lane & 15)];
+  }
+  __device__ static __forceinline__ Op ld_tr_op(const float* tile, int pitch, int kb, int n0,
+                                                int lane) {
+    Op o;
+    ld_tr(tile, pitch, kb, n0, lane, o.v);
+    return o;
+  }
   __device__ static __forceinline__ void ld(const float* row, int g, float* out) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[j] = row[4 * j + g];

@@ -39,49 +39,46 @@ __device__ __forceinline__ void softplus_sigmoid(float x, float& sp, float& sg) 
 }
 
 template <typename T, int D> struct GF {
-  using P = Pitch<T, D>;
   static constexpr int NW = D / 16;  // waves
   static constexpr int NT = NW * 64;
   static constexpr int WPR = NW / 4;  // waves per 16-row block in the state side
   static constexpr int ES = (int)sizeof(T);
-  static constexpr int PGT = 68;                // sGT  [D][PGT] fp32 (channel-major G)
-  static constexpr int PST = D + 16 / ES;       // sST  [D][PST] state transposed
-  static constexpr int PTT = P::TT;             // [D][64] token-minor tiles
-  static constexpr int PN = P::N;               // [64][D] token-major tiles
-  static constexpr int PCC = P::CT;             // [64][64] tiles
+  static constexpr int PG = 68;                 // sG  [D][PG] fp32 (channel-major G)
+  static constexpr int PN = D + 16 / ES;        // natural [rows][D] tiles of T
+  static constexpr int PT = ES == 2 ? 72 : 68;  // [D][64] token-minor tiles of T
+  static constexpr int PC = ES == 2 ? 72 : 68;  // [64][64] tiles of T
+  static constexpr int PDG = 20;                // fp32 diagonal-block tables [16][PDG]
+  static constexpr int PR = D + 4;              // dg_raw staging [64][PR] fp32
   static constexpr int G_OFF = 0;
-  static constexpr int G_SZ = D * PGT * 4;
+  static constexpr int G_SZ = D * PG * 4;
   static constexpr int N_SZ = 64 * PN * ES;
-  static constexpr int U_OFF = G_OFF + G_SZ;    // v (phase 0-1), then U
-  static constexpr int DVC_OFF = U_OFF + N_SZ;  // dvcorr
-  static constexpr int X_OFF = DVC_OFF + N_SZ;
-  static constexpr int TT_SZ = D * PTT * ES;
-  static constexpr int CC_SZ = 64 * PCC * ES;
-  // state side
-  static constexpr int ST_OFF = X_OFF;
-  static constexpr int OT_OFF = ST_OFF + D * PST * ES;
-  static constexpr int YT_OFF = OT_OFF + TT_SZ;
-  static constexpr int X1_END = YT_OFF + TT_SZ;
-  // key side, first part: dO token-major
-  static constexpr int ON_OFF = X_OFF;
-  // key side, second part
-  static constexpr int KT_OFF = X_OFF;
-  static constexpr int QT_OFF = KT_OFF + TT_SZ;
-  static constexpr int DM_OFF = QT_OFF + TT_SZ;
-  static constexpr int DL_OFF = DM_OFF + CC_SZ;
-  static constexpr int DMT_OFF = DL_OFF + CC_SZ;
-  static constexpr int BLT_OFF = DMT_OFF + CC_SZ;
-  static constexpr int X3_END = BLT_OFF + CC_SZ;
-  static constexpr int X_END = X1_END > X3_END ? X1_END : X3_END;
+  // dO (natural), v then U, dvcorr
+  static constexpr int O_OFF = G_OFF + G_SZ;
+  static constexpr int U_OFF = O_OFF + N_SZ;
+  static constexpr int DVC_OFF = U_OFF + N_SZ;
+  // state side: S_in then dS_out (natural), (beta Y)^T then dU^T; dv staging over S
+  static constexpr int S_OFF = DVC_OFF + N_SZ;
+  static constexpr int YT_OFF = S_OFF + D * PN * ES;
+  static constexpr int C_END = YT_OFF + D * PT * ES;
+  // intra-chunk phase, over the regions above once the key-side products are done
+  static constexpr int Q_OFF = O_OFF;
+  static constexpr int K_OFF = Q_OFF + N_SZ;
+  static constexpr int DM_OFF = K_OFF + N_SZ;
+  static constexpr int DL_OFF = DM_OFF + 64 * PC * ES;
+  static constexpr int DG_OFF = DL_OFF + 64 * PC * ES;
+  // fp32 copies of the four diagonal 16x16 blocks of dMqk and dL (bf16 tiles only)
+  static constexpr int DG_SZ = ES == 2 ? 2 * 4 * 16 * PDG * 4 : 0;
+  static constexpr int DQ_OFF = DG_OFF + DG_SZ;
+  static constexpr int DK_OFF = DQ_OFF + N_SZ;
+  static constexpr int P3_END = DK_OFF + N_SZ;
+  static constexpr int X_END = C_END > P3_END ? C_END : P3_END;
   static constexpr int B_OFF = (X_END + 15) / 16 * 16;     // beta [64]
   static constexpr int DB1_OFF = B_OFF + 256;             // [WPR][64]
   static constexpr int DB2_OFF = DB1_OFF + WPR * 256;     // [NW][64]
   static constexpr int RED_OFF = DB2_OFF + NW * 256;      // [NW]
-  // fp32 copies of the four diagonal 16x16 blocks of dMqk, dL, dMqk^T, (beta dL)^T
-  // (only needed when the tiles above are bf16)
-  static constexpr int DG_OFF = (RED_OFF + NW * 4 + 15) / 16 * 16;
-  static constexpr int DG_SZ = ES == 2 ? 4 * 4 * 256 * 4 : 0;
-  static constexpr int TOTAL = DG_OFF + DG_SZ;
+  static constexpr int TOTAL = RED_OFF + NW * 4;
+  static_assert(64 * PR * 4 <= G_SZ, "dg_raw staging fits the gate region");
+  static_assert(N_SZ <= D * PN * ES, "dv staging fits the state tile");
 };
 
 template <typename T, int D>
@@ -99,55 +96,51 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   typedef typename MM::Frag Frag;
   constexpr int NW = L::NW, NT = L::NT, WPR = L::WPR;
   constexpr int KS = MM::KS, KPL = MM::KPL;
-  constexpr int PGT = L::PGT, PST = L::PST, PTT = L::PTT, PN = L::PN, PCC = L::PCC;
+  constexpr int PG = L::PG, PN = L::PN, PT = L::PT, PC = L::PC, PR = L::PR;
   constexpr int NKD = D / KS;  // k-steps over a D-long contraction
   constexpr int NKC = 64 / KS; // k-steps over the chunk
   constexpr int EPV = 16 / L::ES;
   constexpr int VPR = D / EPV;              // 16-byte vectors per D-long row
   constexpr int NLS = D * VPR / NT;         // vectors per thread for a D x D state
   constexpr int NLT = 64 * VPR / NT;        // vectors per thread for a 64 x D tile
-  static_assert(D * VPR % NT == 0 && 64 * VPR % NT == 0, "tile split");
+  constexpr int NLR = 64 * D / 4 / NT;      // 16-byte vectors per thread, 64 x D fp32
+  static_assert(D * VPR % NT == 0 && 64 * VPR % NT == 0 && 16 * D % NT == 0, "tile split");
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-  float* sGT = (float*)(smem + L::G_OFF);
+  float* sG = (float*)(smem + L::G_OFF);
+  float* sR = sG;  // dg_raw staging at the end
+  T* sO = (T*)(smem + L::O_OFF);
   T* sU = (T*)(smem + L::U_OFF);
   T* sV = sU;
   T* sDVC = (T*)(smem + L::DVC_OFF);
-  T* sST = (T*)(smem + L::ST_OFF);
-  T* sOT = (T*)(smem + L::OT_OFF);
+  T* sS = (T*)(smem + L::S_OFF);
+  T* sDV = sS;
   T* sYT = (T*)(smem + L::YT_OFF);
-  T* sON = (T*)(smem + L::ON_OFF);
-  T* sKT = (T*)(smem + L::KT_OFF);
-  T* sQT = (T*)(smem + L::QT_OFF);
+  T* sQ = (T*)(smem + L::Q_OFF);
+  T* sK = (T*)(smem + L::K_OFF);
   T* sDM = (T*)(smem + L::DM_OFF);
   T* sDL = (T*)(smem + L::DL_OFF);
-  T* sDMT = (T*)(smem + L::DMT_OFF);
-  T* sBLT = (T*)(smem + L::BLT_OFF);
+  T* sDQ = (T*)(smem + L::DQ_OFF);
+  T* sDK = (T*)(smem + L::DK_OFF);
   float* sBeta = (float*)(smem + L::B_OFF);
   float* sDB1 = (float*)(smem + L::DB1_OFF);
   float* sDB2 = (float*)(smem + L::DB2_OFF);
   float* sRed = (float*)(smem + L::RED_OFF);
-  // diagonal 16x16 blocks of dMqk, dL, dMqk^T, (beta dL)^T in fp32: block R at
-  // dg*[R * DGB + row * DGP + col]
+  // diagonal 16x16 blocks of dMqk and dL in fp32, natural: block R, row rr, col cc at
+  // dg*[R * DGB + rr * DGP + cc]
   float* dgM;
   float* dgL;
-  float* dgMT;
-  float* dgBLT;
   int DGP, DGB;
   if constexpr (L::ES == 2) {
     float* base = (float*)(smem + L::DG_OFF);
     dgM = base;
-    dgL = base + 1024;
-    dgMT = base + 2048;
-    dgBLT = base + 3072;
-    DGP = 16;
-    DGB = 256;
+    dgL = base + 4 * 16 * L::PDG;
+    DGP = L::PDG;
+    DGB = 16 * L::PDG;
   } else {
-    dgM = (float*)(smem + L::DM_OFF);
-    dgL = (float*)(smem + L::DL_OFF);
-    dgMT = (float*)(smem + L::DMT_OFF);
-    dgBLT = (float*)(smem + L::BLT_OFF);
-    DGP = PCC;
-    DGB = 16 * PCC + 16;
+    dgM = (float*)sDM;
+    dgL = (float*)sDL;
+    DGP = PC;
+    DGB = 16 * PC + 16;
   }
 
   const int c = blockIdx.x, h = blockIdx.y;
@@ -159,11 +152,12 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const size_t ch = (size_t)c * H + h;
   const size_t DD = (size_t)D * D;
   const size_t rs = (size_t)H * D;  // token stride of per-token tensors
-  const T* qh = q + t0 * rs + (size_t)h * D;
-  const T* kh = k + t0 * rs + (size_t)h * D;
-  const T* vh = v + t0 * rs + (size_t)h * D;
-  const T* oh = dO + t0 * rs + (size_t)h * D;
-  const float* grh = g_raw + t0 * rs + (size_t)h * D;
+  const size_t hD = (size_t)h * D;
+  const T* qh = q + t0 * rs + hD;
+  const T* kh = k + t0 * rs + hD;
+  const T* vh = v + t0 * rs + hD;
+  const T* oh = dO + t0 * rs + hD;
+  const float* grh = g_raw + t0 * rs + hD;
   const T* Sin = h_saved + ch * DD;
   const T* dSo = dstates + ch * DD;
   const float aA = __expf(A_log[h]);
@@ -191,11 +185,11 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const int R1 = w / WPR, half = w % WPR;
   const int arow = 16 * R1 + cl;            // A-operand row of this lane
   const int crow = 16 * R1 + g4 * 4;        // first C row of this lane
-  Frag kf[NKD];                              // raw k of row arow
+  Frag kf[NKD];                              // raw k of row arow (permuted k order)
 #pragma unroll
   for (int kk = 0; kk < NKD; ++kk) {
     if (arow < Lr) {
-      kf[kk] = MM::load(kh + arow * rs + kk * KS + g4 * KPL);
+      kf[kk] = MM::ld_perm(kh + arow * rs, kk * KS, lane);
     } else {
       float z[KPL];
 #pragma unroll
@@ -208,15 +202,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   for (int ks = 0; ks < NKC; ++ks) {
     fI[ks] = MM::load(INV + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
     fIT[ks] = MM::load(INVT + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
-    fMT[ks] = MM::load(MqkT + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
-  }
-  // key side: natural rows of S_in and dS_out for this lane's key channel
-  const int ic = 16 * w + cl;
-  Frag bS[NKD], bD[NKD];
-#pragma unroll
-  for (int kk = 0; kk < NKD; ++kk) {
-    bS[kk] = MM::load(Sin + (size_t)ic * D + kk * KS + g4 * KPL);
-    bD[kk] = MM::load(dSo + (size_t)ic * D + kk * KS + g4 * KPL);
+    fMT[ks] = MM::ld_perm(MqkT + ch * 4096 + arow * 64, ks * KS, lane);
   }
   float rg[16];  // g_raw of this thread's channel, 16 rows
   {
@@ -228,65 +214,82 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     }
   }
   if (tid < 64) sBeta[tid] = tid < Lr ? beta[(t0 + tid) * H + h] : 0.f;
-  {  // in-chunk cumulative gate (log2 units), channel-major: sGT[i][r]
+  {  // in-chunk cumulative gate (log2 units), channel-major: sG[i][r]
     const int i = tid % D, part = tid / D;
     float run = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int r = part * 16 + rr;
-      float gg = 0.f;
-      if (r < Lr) {
-        float sp, sg;
-        softplus_sigmoid(rg[rr], sp, sg);
-        gg = -aA * sp;
+    for (int qq = 0; qq < 4; ++qq) {
+      f4 x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 4 * qq + j;
+        float gg = 0.f;
+        if (part * 16 + rr < Lr) {
+          float sp, sg;
+          softplus_sigmoid(rg[rr], sp, sg);
+          gg = -aA * sp;
+        }
+        run += gg * LOG2E;
+        x[j] = run;
       }
-      run += gg * LOG2E;
-      sGT[i * PGT + r] = run;
+      *(f4*)(sG + i * PG + part * 16 + 4 * qq) = x;
     }
   }
 #pragma unroll
-  for (int l = 0; l < NLS; ++l) {  // S_in^T
+  for (int l = 0; l < NLS; ++l) {  // S_in, natural
     const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
-    const T* e = (const T*)&rS[l];
-#pragma unroll
-    for (int j = 0; j < EPV; ++j) sST[(sv * EPV + j) * PST + i] = e[j];
+    *(uint4*)(sS + i * PN + sv * EPV) = rS[l];
   }
 #pragma unroll
-  for (int l = 0; l < NLT; ++l) {  // dO^T and v (token-major)
+  for (int l = 0; l < NLT; ++l) {  // dO and v, natural
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    const T* e = (const T*)&rO[l];
-#pragma unroll
-    for (int j = 0; j < EPV; ++j) sOT[(sv * EPV + j) * PTT + r] = e[j];
+    *(uint4*)(sO + r * PN + sv * EPV) = rO[l];
     *(uint4*)(sV + r * PN + sv * EPV) = rV[l];
   }
   __syncthreads();
   {
     const int i = tid % D, part = tid / D;
     float add = 0.f;
-    for (int pp = 0; pp < part; ++pp) add += sGT[i * PGT + pp * 16 + 15];
+    for (int pp = 0; pp < part; ++pp) add += sG[i * PG + pp * 16 + 15];
     __syncthreads();
-    if (part > 0)
-      for (int rr = 0; rr < 16; ++rr) sGT[i * PGT + part * 16 + rr] += add;
+    if (part > 0) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        f4* p = (f4*)(sG + i * PG + part * 16 + 4 * qq);
+        f4 x = *p;
+        x[0] += add; x[1] += add; x[2] += add; x[3] += add;
+        *p = x;
+      }
+    }
   }
   __syncthreads();
 
   // ------------------------------------------------------------- state side
+  // decayed key rows of this lane: Kd = K e^G (for Y), Kr = K e^{G_T - G} (for dU)
+  Frag akd[NKD], akr[NKD];
+#pragma unroll
+  for (int kk = 0; kk < NKD; ++kk) {
+    float kd[KPL], kr[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int i = kk * KS + MM::kperm(g4, j);
+      const float gg = sG[i * PG + arow], gt = sG[i * PG + 63];
+      const float kv = MM::elem(kf[kk], j);
+      kd[j] = kv * ex2(gg);
+      kr[j] = kv * ex2(gt - gg);
+    }
+    akd[kk] = MM::from_vals(kd);
+    akr[kk] = MM::from_vals(kr);
+  }
   // Y = V - Kd S_in
   f4 Y[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) Y[nt] = zero4();
 #pragma unroll
   for (int kk = 0; kk < NKD; ++kk) {
-    float kd[KPL];
-    const int i0 = kk * KS + g4 * KPL;
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) kd[j] = MM::elem(kf[kk], j) * ex2(sGT[(i0 + j) * PGT + arow]);
-    const Frag a = MM::from_vals(kd);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const Frag b = MM::load(sST + (64 * half + nt * 16 + cl) * PST + i0);
-      Y[nt] = MM::mma(a, b, Y[nt]);
-    }
+    for (int nt = 0; nt < 4; ++nt)
+      Y[nt] = MM::mma(akd[kk], MM::ld_tr(sS, PN, kk * KS, 64 * half + nt * 16, lane), Y[nt]);
   }
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
@@ -297,15 +300,18 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       Y[nt][j] = to_f(sV[(crow + j) * PN + d]) - Y[nt][j];
       by[j] = sBeta[crow + j] * Y[nt][j];
     }
-    store_ct<T>(sYT, PTT, 16 * R1, 64 * half + nt * 16, by, lane);
+    store_ct<T>(sYT, PT, 16 * R1, 64 * half + nt * 16, by, lane);
   }
-  __syncthreads();  // (beta Y)^T complete; S_in^T and v are dead
+  // key-side operands: S_in row of this lane's key channel
+  const int ic = 16 * w + cl;
+  Frag bS[NKD];
 #pragma unroll
-  for (int l = 0; l < NLS; ++l) {  // dS_out^T
+  for (int kk = 0; kk < NKD; ++kk) bS[kk] = MM::load(sS + ic * PN + kk * KS + g4 * KPL);
+  __syncthreads();  // (beta Y)^T complete; S_in and v are dead
+#pragma unroll
+  for (int l = 0; l < NLS; ++l) {  // dS_out, natural
     const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
-    const T* e = (const T*)&rD[l];
-#pragma unroll
-    for (int j = 0; j < EPV; ++j) sST[(sv * EPV + j) * PST + i] = e[j];
+    *(uint4*)(sS + i * PN + sv * EPV) = rD[l];
   }
   {  // U = INV (beta Y)
     f4 U[4];
@@ -316,47 +322,38 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const Frag a = fI[ks];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const Frag b = MM::load(sYT + (64 * half + nt * 16 + cl) * PTT + ks * KS + g4 * KPL);
+        const Frag b = MM::load(sYT + (64 * half + nt * 16 + cl) * PT + ks * KS + g4 * KPL);
         U[nt] = MM::mma(a, b, U[nt]);
       }
     }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) store_c<T>(sU, PN, 16 * R1, 64 * half + nt * 16, U[nt], lane);
   }
-  __syncthreads();  // dS_out^T in place; (beta Y)^T dead
+  __syncthreads();  // dS_out in place; U complete; (beta Y)^T dead
   {  // dU = Mqk^T dO + Kr dS_out  ->  dU^T
     f4 dU[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) dU[nt] = zero4();
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) {
-      const Frag a = fMT[ks];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const Frag b = MM::load(sOT + (64 * half + nt * 16 + cl) * PTT + ks * KS + g4 * KPL);
-        dU[nt] = MM::mma(a, b, dU[nt]);
-      }
+      for (int nt = 0; nt < 4; ++nt)
+        dU[nt] = MM::mma(fMT[ks], MM::ld_tr(sO, PN, ks * KS, 64 * half + nt * 16, lane), dU[nt]);
     }
 #pragma unroll
     for (int kk = 0; kk < NKD; ++kk) {
-      float kr[KPL];
-      const int i0 = kk * KS + g4 * KPL;
 #pragma unroll
-      for (int j = 0; j < KPL; ++j)
-        kr[j] = MM::elem(kf[kk], j) *
-                ex2(sGT[(i0 + j) * PGT + 63] - sGT[(i0 + j) * PGT + arow]);
-      const Frag a = MM::from_vals(kr);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const Frag b = MM::load(sST + (64 * half + nt * 16 + cl) * PST + i0);
-        dU[nt] = MM::mma(a, b, dU[nt]);
-      }
+      for (int nt = 0; nt < 4; ++nt)
+        dU[nt] = MM::mma(akr[kk], MM::ld_tr(sS, PN, kk * KS, 64 * half + nt * 16, lane), dU[nt]);
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) store_ct<T>(sYT, PTT, 16 * R1, 64 * half + nt * 16, dU[nt], lane);
+    for (int nt = 0; nt < 4; ++nt) store_ct<T>(sYT, PT, 16 * R1, 64 * half + nt * 16, dU[nt], lane);
   }
-  __syncthreads();
-  {  // dvcorr = INV^T dU;  dv = beta . dvcorr;  dbeta (first part)
+  Frag bD[NKD];  // dS_out row of this lane's key channel
+#pragma unroll
+  for (int kk = 0; kk < NKD; ++kk) bD[kk] = MM::load(sS + ic * PN + kk * KS + g4 * KPL);
+  __syncthreads();  // dU^T complete; dS_out is dead
+  {  // dvcorr = INV^T dU;  dv = beta . dvcorr (staged);  dbeta (first part)
     f4 dvc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) dvc[nt] = zero4();
@@ -365,21 +362,21 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const Frag a = fIT[ks];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const Frag b = MM::load(sYT + (64 * half + nt * 16 + cl) * PTT + ks * KS + g4 * KPL);
+        const Frag b = MM::load(sYT + (64 * half + nt * 16 + cl) * PT + ks * KS + g4 * KPL);
         dvc[nt] = MM::mma(a, b, dvc[nt]);
       }
     }
     float db[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int d = 64 * half + nt * 16 + cl;
       store_c<T>(sDVC, PN, 16 * R1, 64 * half + nt * 16, dvc[nt], lane);
+      f4 dvv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = crow + j;
         db[j] += dvc[nt][j] * Y[nt][j];
-        if (r < Lr) dv[(t0 + r) * rs + (size_t)h * D + d] = from_f<T>(sBeta[r] * dvc[nt][j]);
+        dvv[j] = sBeta[crow + j] * dvc[nt][j];
       }
+      store_c<T>(sDV, PN, 16 * R1, 64 * half + nt * 16, dvv, lane);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -387,13 +384,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       if (cl == 0) sDB1[half * 64 + crow + j] = s;
     }
   }
-  __syncthreads();  // the state side is done: its tiles are dead
-#pragma unroll
-  for (int l = 0; l < NLT; ++l) {  // dO token-major for the key side
-    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    *(uint4*)(sON + r * PN + sv * EPV) = rO[l];
-  }
-  // q, k for the epilogue (registers now, LDS after the next barrier)
+  // q, k for the intra-chunk phase (registers now, LDS once their tiles are free)
   uint4 rQ[NLT], rK[NLT];
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {
@@ -406,7 +397,12 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     rQ[l] = xq;
     rK[l] = xk;
   }
-  __syncthreads();
+  __syncthreads();  // dvcorr and dv staged
+#pragma unroll
+  for (int l = 0; l < NLT; ++l) {  // dv out, 16-byte vectors
+    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+    if (r < Lr) *(uint4*)(dv + (t0 + r) * rs + hD + sv * EPV) = *(const uint4*)(sDV + r * PN + sv * EPV);
+  }
 
   // --------------------------------------------------------------- key side
   // dKr = U dS_out^T, dQd0 = dO S_in^T, dKd0 = dvcorr S_in^T for key channels
@@ -423,7 +419,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     for (int rt = 0; rt < 4; ++rt) {
       const int r = rt * 16 + cl;
       aKr[rt] = MM::mma(MM::load(sU + r * PN + d0), bD[kk], aKr[rt]);
-      aQd[rt] = MM::mma(MM::load(sON + r * PN + d0), bS[kk], aQd[rt]);
+      aQd[rt] = MM::mma(MM::load(sO + r * PN + d0), bS[kk], aQd[rt]);
       aKd[rt] = MM::mma(MM::load(sDVC + r * PN + d0), bS[kk], aKd[rt]);
     }
   }
@@ -438,7 +434,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
   for (int kk = 0; kk < NKD; ++kk) {
     const int d0 = kk * KS + g4 * KPL;
-    const Frag ao = MM::load(sON + arow * PN + d0);
+    const Frag ao = MM::load(sO + arow * PN + d0);
     const Frag av = MM::load(sDVC + arow * PN + d0);
 #pragma unroll
     for (int st = 0; st < CTW; ++st) {
@@ -447,57 +443,44 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       al[st] = MM::mma(av, b, al[st]);
     }
   }
-  __syncthreads();  // dO token-major, U, dvcorr are dead
-  // dMqk, dL (masked) as act-dtype tiles, natural and transposed; beta folded into dL^T
+  __syncthreads();  // dO, U, dvcorr and the dv staging are dead
+  // dMqk, dL (masked, natural) as act-dtype tiles; fp32 copies of the diagonal blocks
 #pragma unroll
   for (int st = 0; st < CTW; ++st) {
     const int s = (CTW * half + st) * 16 + cl;
-    f4 m, l, bl;
+    f4 m, l;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = crow + j;
       m[j] = s <= r ? am[st][j] : 0.f;
       l[j] = s < r ? -al[st][j] : 0.f;
-      bl[j] = sBeta[r] * l[j];
     }
-    store_c<T>(sDM, PCC, 16 * R1, (CTW * half + st) * 16, m, lane);
-    store_c<T>(sDL, PCC, 16 * R1, (CTW * half + st) * 16, l, lane);
-    store_ct<T>(sDMT, PCC, 16 * R1, (CTW * half + st) * 16, m, lane);
-    store_ct<T>(sBLT, PCC, 16 * R1, (CTW * half + st) * 16, bl, lane);
+    store_c<T>(sDM, PC, 16 * R1, (CTW * half + st) * 16, m, lane);
+    store_c<T>(sDL, PC, 16 * R1, (CTW * half + st) * 16, l, lane);
     if constexpr (L::ES == 2) {
-      if (CTW * half + st == R1) {  // diagonal block: keep fp32 copies
-        float* b0 = dgM + R1 * 256;
-        float* b1 = dgL + R1 * 256;
-        float* b2 = dgMT + R1 * 256;
-        float* b3 = dgBLT + R1 * 256;
+      if (CTW * half + st == R1) {
+        float* b0 = dgM + R1 * DGB;
+        float* b1 = dgL + R1 * DGB;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int rr = g4 * 4 + j;
-          b0[rr * 16 + cl] = m[j];
-          b1[rr * 16 + cl] = l[j];
-          b2[cl * 16 + rr] = m[j];
-          b3[cl * 16 + rr] = bl[j];
+          b0[(g4 * 4 + j) * DGP + cl] = m[j];
+          b1[(g4 * 4 + j) * DGP + cl] = l[j];
         }
       }
     }
   }
 #pragma unroll
-  for (int l = 0; l < NLT; ++l) {  // q^T, k^T (channel-major)
+  for (int l = 0; l < NLT; ++l) {  // q, k natural
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    const T* eq = (const T*)&rQ[l];
-    const T* ek = (const T*)&rK[l];
-#pragma unroll
-    for (int j = 0; j < EPV; ++j) {
-      sQT[(sv * EPV + j) * PTT + r] = eq[j];
-      sKT[(sv * EPV + j) * PTT + r] = ek[j];
-    }
+    *(uint4*)(sQ + r * PN + sv * EPV) = rQ[l];
+    *(uint4*)(sK + r * PN + sv * EPV) = rK[l];
   }
   __syncthreads();
 
   // ------------------------------------------------ intra-chunk decay terms
-  const float* Gi = sGT + ic * PGT;  // G of this lane's column (channel ic), by row
-  const T* Ki = sKT + ic * PTT;
-  const T* Qi = sQT + ic * PTT;
+  // Lane: key channel ic (column of the C tiles), rows 16 rt + 4 g4 + j.
+  const float* Gi = sG + ic * PG;  // G of channel ic, by row
+  const int n0 = 16 * w;           // first key channel of this wave
   const float gT = Gi[63];
   float dG[4][4];
   float dkr_col = 0.f, dal = 0.f;
@@ -527,9 +510,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const float ga = Gi[r0];
       for (int S = 0; S < rt; ++S) {
         float b[4], kv[4], gv[4];
-        const typename MS::Op a1 = MS::ld_op(sDM + ar * PCC + 16 * S, g4);
-        const typename MS::Op a2 = MS::ld_op(sDL + ar * PCC + 16 * S, g4);
-        MS::ld(Ki + 16 * S, g4, kv);
+        const typename MS::Op a1 = MS::ld_op(sDM + ar * PC + 16 * S, g4);
+        const typename MS::Op a2 = MS::ld_op(sDL + ar * PC + 16 * S, g4);
+        MS::ld_tr(sK, PN, 16 * S, n0, lane, kv);
         MS::ldf(Gi + 16 * S, g4, gv);
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = kv[j] * ex2(ga - gv[j]);
@@ -544,21 +527,22 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
         X2a[j] *= sc;
       }
     }
-    //   rows s of this block, r in later blocks: anchor b = r0 + 16
+    //   rows s of this block, r in later blocks: anchor b = r0 + 16; A = dMqk^T and
+    //   dL^T read transposed from the natural tiles, beta_r folded into the k operand
     if (rt < 3) {
       const float gb = Gi[r0 + 16];
       for (int R = rt + 1; R < 4; ++R) {
         float bq[4], bk[4], qv[4], kv[4], gv[4];
-        const typename MS::Op a1 = MS::ld_op(sDMT + ar * PCC + 16 * R, g4);
-        const typename MS::Op a2 = MS::ld_op(sBLT + ar * PCC + 16 * R, g4);
-        MS::ld(Qi + 16 * R, g4, qv);
-        MS::ld(Ki + 16 * R, g4, kv);
+        const typename MS::Op a1 = MS::ld_tr_op(sDM, PC, 16 * R, r0, lane);
+        const typename MS::Op a2 = MS::ld_tr_op(sDL, PC, 16 * R, r0, lane);
+        MS::ld_tr(sQ, PN, 16 * R, n0, lane, qv);
+        MS::ld_tr(sK, PN, 16 * R, n0, lane, kv);
         MS::ldf(Gi + 16 * R, g4, gv);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float e = ex2(gv[j] - gb);
           bq[j] = qv[j] * e;
-          bk[j] = kv[j] * e;
+          bk[j] = sBeta[16 * R + MS::kidx(g4, j)] * kv[j] * e;
         }
         Za = MS::op_sb(a1, MS::split(bq), Za);
         Za = MS::op_sb(a2, MS::split(bk), Za);
@@ -573,10 +557,14 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       float ma[4], la[4], mt[4], lt[4], kv[4], qv[4], gv[4];
       MS::ldf(dgM + rt * DGB + cl * DGP, g4, ma);
       MS::ldf(dgL + rt * DGB + cl * DGP, g4, la);
-      MS::ldf(dgMT + rt * DGB + cl * DGP, g4, mt);
-      MS::ldf(dgBLT + rt * DGB + cl * DGP, g4, lt);
-      MS::ld(Ki + r0, g4, kv);
-      MS::ld(Qi + r0, g4, qv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = MS::kidx(g4, j);
+        mt[j] = dgM[rt * DGB + rr * DGP + cl];
+        lt[j] = sBeta[r0 + rr] * dgL[rt * DGB + rr * DGP + cl];
+      }
+      MS::ld_tr(sK, PN, r0, n0, lane, kv);
+      MS::ld_tr(sQ, PN, r0, n0, lane, qv);
       MS::ldf(Gi + r0, g4, gv);
       const typename MS::Op oma = MS::split(ma), ola = MS::split(la);
       const typename MS::Op omt = MS::split(mt), olt = MS::split(lt);
@@ -624,16 +612,16 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       }
     }
     // level 3: the 4x4 diagonal sub-block of this lane's rows (VALU)
+    const int rb = r0 + 4 * g4;
+    float kr[4], qr[4], br[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kr[j] = to_f(sK[(rb + j) * PN + ic]);
+      qr[j] = to_f(sQ[(rb + j) * PN + ic]);
+      br[j] = sBeta[rb + j];
+    }
     float x1d[4], x2d[4], zd[4];
     {
-      const int rb = r0 + 4 * g4;
-      float kr[4], qr[4], br[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kr[j] = to_f(Ki[rb + j]);
-        qr[j] = to_f(Qi[rb + j]);
-        br[j] = sBeta[rb + j];
-      }
       const float a1 = ex2(Gr[1] - Gr[0]), a2 = ex2(Gr[2] - Gr[1]), a3 = ex2(Gr[3] - Gr[2]);
       // f[j][jj] = e^{G_{rb+j} - G_{rb+jj}}, jj <= j
       float f[4][4];
@@ -672,31 +660,26 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     // combine and form the gate gradient of this tile
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = r0 + 4 * g4 + j;
+      const int r = rb + j;
       const float eG = ex2(Gr[j]);
-      const float qv = to_f(Qi[r]), kv = to_f(Ki[r]);
-      const float br = sBeta[r];
       const float x1 = X1a[j] + X1b[j] + x1d[j];
       const float x2 = X2a[j] + X2b[j] + x2d[j];
       const float dki = Za[j] + Zb[j] + zd[j];
       const float dqv = eG * aQd[rt][j] + x1;
-      const float dkd = br * (-eG * aKd[rt][j] + x2);
+      const float dkd = br[j] * (-eG * aKd[rt][j] + x2);
       const float dkr = ex2(gT - Gr[j]) * aKr[rt][j];
-      dG[rt][j] = qv * dqv + kv * (dkd - dki - dkr);
-      dkr_col += kv * dkr;
-      dbp[rt][j] = kv * x2;
-      if (r < Lr) {
-        const size_t o = (t0 + r) * rs + (size_t)h * D + ic;
-        dq[o] = from_f<T>(dqv);
-        dk[o] = from_f<T>(dkd + dki + dkr);
-      }
+      dG[rt][j] = qr[j] * dqv + kr[j] * (dkd - dki - dkr);
+      dkr_col += kr[j] * dkr;
+      dbp[rt][j] = kr[j] * x2;
+      sDQ[r * PN + ic] = from_f<T>(dqv);
+      sDK[r * PN + ic] = from_f<T>(dkd + dki + dkr);
     }
   }
   // last row: sum_r k.dk_r + e^{G_T} p
   dkr_col += __shfl_xor(dkr_col, 16);
   dkr_col += __shfl_xor(dkr_col, 32);
   if (g4 == 3) dG[3][3] += dkr_col + ex2(gT) * pp;
-  // reverse cumsum over r = 16 rt + 4 g4 + j
+  // reverse cumsum over r = 16 rt + 4 g4 + j; dG becomes dg_raw
   float carry = 0.f;
 #pragma unroll
   for (int rt = 3; rt >= 0; --rt) {
@@ -712,13 +695,10 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     for (int j = 3; j >= 0; --j) {
       run += dG[rt][j];
       const int r = rt * 16 + g4 * 4 + j;
-      if (r < Lr) {
-        const size_t o = (t0 + r) * rs + (size_t)h * D + ic;
-        float sp, sg;
-        softplus_sigmoid(tg[rt][j], sp, sg);
-        dg_raw[o] = run * (-aA * sg);
-        dal += run * (-aA * sp);
-      }
+      float sp, sg;
+      softplus_sigmoid(tg[rt][j], sp, sg);
+      dG[rt][j] = run * (-aA * sg);
+      if (r < Lr) dal += run * (-aA * sp);
     }
   }
   // dbeta second part, reduced over this wave's channels
@@ -731,7 +711,20 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     }
   dal = sum64(dal);
   if (lane == 0) sRed[w] = dal;
-  __syncthreads();
+  __syncthreads();  // dq, dk staged; the gate tile is dead
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sR[(rt * 16 + g4 * 4 + j) * PR + ic] = dG[rt][j];
+#pragma unroll
+  for (int l = 0; l < NLT; ++l) {  // dq, dk out, 16-byte vectors
+    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+    if (r < Lr) {
+      const size_t o = (t0 + r) * rs + hD + sv * EPV;
+      *(uint4*)(dq + o) = *(const uint4*)(sDQ + r * PN + sv * EPV);
+      *(uint4*)(dk + o) = *(const uint4*)(sDK + r * PN + sv * EPV);
+    }
+  }
   if (tid < 64 && tid < Lr) {
     float s = 0.f;
 #pragma unroll
@@ -745,6 +738,12 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
     for (int x = 0; x < NW; ++x) s += sRed[x];
     dAl_part[ch] = s;
+  }
+  __syncthreads();  // dg_raw staged
+#pragma unroll
+  for (int l = 0; l < NLR; ++l) {  // dg_raw out, 16-byte vectors
+    const int idx = tid + l * NT, r = idx / (D / 4), sv = idx % (D / 4);
+    if (r < Lr) *(f4*)(dg_raw + (t0 + r) * rs + hD + sv * 4) = *(const f4*)(sR + r * PR + sv * 4);
   }
 }
 
