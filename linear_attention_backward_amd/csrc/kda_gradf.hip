@@ -163,12 +163,24 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const float aA = __expf(A_log[h]);
 
   // ------------------------------------------------------------------ loads
+  // What the gate and the first product need is issued first; dS_out and the
+  // INV / Mqk rows follow once the gate is formed (they are first used after Y), so
+  // their transfer overlaps the gate, the LDS fills and the Y product.
+  float rg[16];  // g_raw of this thread's channel, 16 rows
+  {
+    const int i = tid % D, part = tid / D;  // NT / D == 4 parts of 16 rows
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = part * 16 + rr;
+      rg[rr] = r < Lr ? grh[r * rs + i] : 0.f;
+    }
+  }
+  const float rbeta = tid < Lr ? beta[(t0 + (tid & 63)) * H + h] : 0.f;
   uint4 rS[NLS], rD[NLS], rO[NLT], rV[NLT];
 #pragma unroll
   for (int l = 0; l < NLS; ++l) {
     const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
     rS[l] = *(const uint4*)(Sin + (size_t)i * D + sv * EPV);
-    rD[l] = *(const uint4*)(dSo + (size_t)i * D + sv * EPV);
   }
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {
@@ -197,23 +209,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       kf[kk] = MM::from_vals(z);
     }
   }
-  Frag fI[NKC], fIT[NKC], fMT[NKC];          // rows arow of INV, INV^T, Mqk^T
-#pragma unroll
-  for (int ks = 0; ks < NKC; ++ks) {
-    fI[ks] = MM::load(INV + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
-    fIT[ks] = MM::load(INVT + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
-    fMT[ks] = MM::ld_perm(MqkT + ch * 4096 + arow * 64, ks * KS, lane);
-  }
-  float rg[16];  // g_raw of this thread's channel, 16 rows
-  {
-    const int i = tid % D, part = tid / D;  // NT / D == 4 parts of 16 rows
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int r = part * 16 + rr;
-      rg[rr] = r < Lr ? grh[r * rs + i] : 0.f;
-    }
-  }
-  if (tid < 64) sBeta[tid] = tid < Lr ? beta[(t0 + tid) * H + h] : 0.f;
+  if (tid < 64) sBeta[tid] = rbeta;
   {  // in-chunk cumulative gate (log2 units), channel-major: sG[i][r]
     const int i = tid % D, part = tid / D;
     float run = 0.f;
@@ -245,6 +241,19 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
     *(uint4*)(sO + r * PN + sv * EPV) = rO[l];
     *(uint4*)(sV + r * PN + sv * EPV) = rV[l];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int l = 0; l < NLS; ++l) {
+    const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
+    rD[l] = *(const uint4*)(dSo + (size_t)i * D + sv * EPV);
+  }
+  Frag fI[NKC], fIT[NKC], fMT[NKC];          // rows arow of INV, INV^T, Mqk^T
+#pragma unroll
+  for (int ks = 0; ks < NKC; ++ks) {
+    fI[ks] = MM::load(INV + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
+    fMT[ks] = MM::ld_perm(MqkT + ch * 4096 + arow * 64, ks * KS, lane);
+    fIT[ks] = MM::load(INVT + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
   }
   __syncthreads();
   {
