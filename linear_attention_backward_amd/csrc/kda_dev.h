@@ -85,6 +85,16 @@ template <> struct Mma<bf16> {
     const bf16x4 hi = *(const bf16x4*)(row + kb + 16 + 4 * G);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+  // fragment of an fp32 row (any memory) in the permuted order, rounded to bf16
+  __device__ static __forceinline__ Frag ld_perm_f32(const float* row, int kb, int lane) {
+    const int G = lane >> 4;
+    const f4 lo = *(const f4*)(row + kb + 4 * G);
+    const f4 hi = *(const f4*)(row + kb + 16 + 4 * G);
+    Frag r;
+    r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
+    r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
+    return r;
+  }
   __device__ static __forceinline__ float elem(Frag f, int j) { return (float)f[j]; }
   __device__ static __forceinline__ Frag from_f32(const float* p) {
     f4 a = *(const f4*)p, b = *(const f4*)(p + 4);
@@ -135,6 +145,9 @@ template <> struct Mma<float> {
     return tile[(kb + (lane >> 4)) * pitch + n0 + (lane & 15)];
   }
   __device__ static __forceinline__ Frag ld_perm(const float* row, int kb, int lane) {
+    return row[kb + (lane >> 4)];
+  }
+  __device__ static __forceinline__ Frag ld_perm_f32(const float* row, int kb, int lane) {
     return row[kb + (lane >> 4)];
   }
   __device__ static __forceinline__ float elem(Frag f, int) { return f; }

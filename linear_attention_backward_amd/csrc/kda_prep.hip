@@ -22,136 +22,186 @@ __device__ __forceinline__ float softplus_p(float x) {
   return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));
 }
 
-template <typename T, int D> struct PrepLds {
-  using P = Pitch<T, D>;
-  static constexpr int G_SZ = 64 * P::NF * 4;
-  static constexpr int QK_SZ = 64 * P::N * (int)sizeof(T);
-  static constexpr int CC_SZ = 64 * P::CC * 4;
-  static constexpr int TT_SZ = D * P::TT * (int)sizeof(T);
-  static constexpr int U_SZ = CC_SZ > TT_SZ ? CC_SZ : TT_SZ;
+template <typename T, int D> struct PL {
+  static constexpr int NW = D / 16;               // waves
+  static constexpr int NT = NW * 64;
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int HALVES = NW / 4;           // column halves of W per row block
+  static constexpr int PGN = D + 4;               // sG [64][PGN] fp32, natural
+  static constexpr int PN = D + 16 / ES;          // [64][PN] tiles of T, natural
+  static constexpr int PC = 68;                   // [64][PC] fp32
+  static constexpr int PTM = D + 16 / ES;         // Tm staging [D][PTM] of T
+  static constexpr int PPT = 64 + 16 / ES;        // PT staging [D][PPT] of T
+  static constexpr int G_SZ = 64 * PGN * 4;
+  static constexpr int N_SZ = 64 * PN * ES;
+  static constexpr int C_SZ = 64 * PC * 4;
   static constexpr int G_OFF = 0;
   static constexpr int Q_OFF = G_OFF + G_SZ;
-  static constexpr int K_OFF = Q_OFF + QK_SZ;
-  static constexpr int M_OFF = K_OFF + QK_SZ;
-  static constexpr int INV_OFF = M_OFF + CC_SZ;  // later: W^T
-  static constexpr int A_OFF = INV_OFF + U_SZ;   // later: (beta Kd)^T
-  static constexpr int KRT_OFF = A_OFF + U_SZ;
-  static constexpr int BETA_OFF = KRT_OFF + TT_SZ;
-  static constexpr int SCR_OFF = BETA_OFF + 256;
-  static constexpr int TOTAL = SCR_OFF + 4 * 16 * 17 * 4;
+  static constexpr int K_OFF = Q_OFF + N_SZ;    // k, later W
+  static constexpr int M_OFF = K_OFF + N_SZ;    // Mqk
+  static constexpr int KR_OFF = M_OFF + C_SZ;   // Kr
+  static constexpr int A_OFF = KR_OFF + N_SZ;   // A
+  static constexpr int INV_OFF = A_OFF + C_SZ;  // INV
+  static constexpr int KD_OFF = INV_OFF + C_SZ; // beta Kd
+  static constexpr int SCR_OFF = KD_OFF + N_SZ; // INV block-substitution scratch
+  static constexpr int SCR_SZ = 4 * 16 * 17 * 4;
+  static constexpr int B_OFF = SCR_OFF + SCR_SZ;
+  static constexpr int TOTAL = B_OFF + 256;
+  // Tm and PT staging, over A, INV, Kd and the scratch once W is formed
+  static constexpr int TMS_OFF = A_OFF;
+  static constexpr int PTS_OFF = TMS_OFF + D * PTM * ES;
+  static_assert(PTS_OFF + D * PPT * ES <= B_OFF, "staging fits the dead region");
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chunks, int H,
-                                              const T* __restrict__ q, const T* __restrict__ k,
-                                              const float* __restrict__ g_raw,
-                                              const float* __restrict__ beta,
-                                              const float* __restrict__ A_log,
-                                              T* __restrict__ Tm, T* __restrict__ PT,
-                                              float* __restrict__ eGT, T* __restrict__ INVo,
-                                              T* __restrict__ INVTo, T* __restrict__ MqkTo) {
-  using L = PrepLds<T, D>;
-  using P = Pitch<T, D>;
+__global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ chunks, int H,
+                                                const T* __restrict__ q, const T* __restrict__ k,
+                                                const float* __restrict__ g_raw,
+                                                const float* __restrict__ beta,
+                                                const float* __restrict__ A_log,
+                                                T* __restrict__ Tm, T* __restrict__ PT,
+                                                float* __restrict__ eGT, T* __restrict__ INVo,
+                                                T* __restrict__ INVTo, T* __restrict__ MqkTo) {
+  using L = PL<T, D>;
   using MM = Mma<T>;
   typedef typename MM::Frag Frag;
+  constexpr int NW = L::NW, NT = L::NT, HALVES = L::HALVES;
   constexpr int KS = MM::KS, KPL = MM::KPL;
-  constexpr int NF = P::NF, PN = P::N, CC = P::CC, TT = P::TT;
+  constexpr int PGN = L::PGN, PN = L::PN, PC = L::PC, PTM = L::PTM, PPT = L::PPT;
+  constexpr int NKC = 64 / KS;
+  constexpr int DH = D / HALVES;           // columns of W per wave
+  constexpr int EPV = 16 / L::ES;          // elements per 16-byte vector
+  constexpr int VPR = D / EPV;             // vectors per D-long row
+  constexpr int NLT = 64 * VPR / NT;       // vectors per thread, 64 x D tile
+  static_assert(64 * VPR % NT == 0 && NT == 4 * D, "tile split");
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   float* sG = (float*)(smem + L::G_OFF);
   T* sQ = (T*)(smem + L::Q_OFF);
   T* sK = (T*)(smem + L::K_OFF);
+  T* sW = sK;
   float* sM = (float*)(smem + L::M_OFF);
-  float* sINV = (float*)(smem + L::INV_OFF);
-  T* sWT = (T*)(smem + L::INV_OFF);
+  T* sKr = (T*)(smem + L::KR_OFF);
   float* sA = (float*)(smem + L::A_OFF);
-  T* sKdT = (T*)(smem + L::A_OFF);
-  T* sKrT = (T*)(smem + L::KRT_OFF);
-  float* sBeta = (float*)(smem + L::BETA_OFF);
+  float* sINV = (float*)(smem + L::INV_OFF);
+  T* sKd = (T*)(smem + L::KD_OFF);
   float* sScr = (float*)(smem + L::SCR_OFF);
+  float* sBeta = (float*)(smem + L::B_OFF);
+  T* sTm = (T*)(smem + L::TMS_OFF);
+  T* sPT = (T*)(smem + L::PTS_OFF);
 
   const int c = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, cl = lane & 15;
   const ChunkInfo ci = chunks[c];
   const int t0 = ci.t0, Lr = ci.len;
   const size_t ch = (size_t)c * H + h;
-
-  // ---- load q, k (rows beyond the chunk are zero), beta, gate.  Every global
-  // load is issued before any of them is used.
-  constexpr int VPR = D * (int)sizeof(T) / 16;
-  constexpr int NLT = 64 * VPR / NTHR;
-  constexpr int PARTS = NTHR / D;
-  constexpr int RPP = 64 / PARTS;
   const size_t rs = (size_t)H * D;
-  uint4 rq[NLT], rk[NLT];
-  float rg[RPP];
+  const size_t hD = (size_t)h * D;
+
+  // ---- loads (all issued before first use): g_raw, beta, q, k; rows beyond the
+  // chunk are zero
+  float rg[16];
   {
-    const T* qh = q + (size_t)t0 * rs + (size_t)h * D;
-    const T* kh = k + (size_t)t0 * rs + (size_t)h * D;
+    const float* gh = g_raw + (size_t)t0 * rs + hD + tid % D;
+    const int part = tid / D;  // 4 parts of 16 rows
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = part * 16 + rr;
+      rg[rr] = r < Lr ? gh[r * rs] : 0.f;
+    }
+  }
+  const float rbeta = tid < Lr ? beta[(size_t)(t0 + (tid & 63)) * H + h] : 0.f;
+  uint4 rq[NLT], rk[NLT];
+  {
+    const T* qh = q + (size_t)t0 * rs + hD;
+    const T* kh = k + (size_t)t0 * rs + hD;
 #pragma unroll
     for (int l = 0; l < NLT; ++l) {
-      const int idx = tid + l * NTHR, r = idx / VPR, vv = idx % VPR;
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
       uint4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
       if (r < Lr) {
-        xq = ((const uint4*)(qh + r * rs))[vv];
-        xk = ((const uint4*)(kh + r * rs))[vv];
+        xq = *(const uint4*)(qh + r * rs + vv * EPV);
+        xk = *(const uint4*)(kh + r * rs + vv * EPV);
       }
       rq[l] = xq;
       rk[l] = xk;
     }
-    const float* gh = g_raw + (size_t)t0 * rs + (size_t)h * D + tid % D;
-    const int part = tid / D;
-#pragma unroll
-    for (int rr = 0; rr < RPP; ++rr) {
-      const int r = part * RPP + rr;
-      rg[rr] = r < Lr ? gh[r * rs] : 0.f;
-    }
   }
-  if (tid < 64) sBeta[tid] = tid < Lr ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
   const float aA = __expf(A_log[h]);
-#pragma unroll
-  for (int l = 0; l < NLT; ++l) {
-    const int idx = tid + l * NTHR, r = idx / VPR, vv = idx % VPR;
-    *(uint4*)((char*)(sQ + r * PN) + vv * 16) = rq[l];
-    *(uint4*)((char*)(sK + r * PN) + vv * 16) = rk[l];
-  }
-  {
+  if (tid < 64) sBeta[tid] = rbeta;
+  {  // in-chunk cumulative gate (log2 units), natural: sG[r][i]
     const int i = tid % D, part = tid / D;
     float run = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < RPP; ++rr) {
-      const int r = part * RPP + rr;
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = part * 16 + rr;
       const float g = r < Lr ? -aA * softplus_p(rg[rr]) : 0.f;
       run += g * LOG2E;
-      sG[r * NF + i] = run;
+      sG[r * PGN + i] = run;
     }
+  }
+#pragma unroll
+  for (int l = 0; l < NLT; ++l) {
+    const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+    *(uint4*)(sQ + r * PN + vv * EPV) = rq[l];
+    *(uint4*)(sK + r * PN + vv * EPV) = rk[l];
   }
   __syncthreads();
   {
     const int i = tid % D, part = tid / D;
     float add = 0.f;
-    for (int pp = 0; pp < part; ++pp) add += sG[(pp * RPP + RPP - 1) * NF + i];
+    for (int pp = 0; pp < part; ++pp) add += sG[(pp * 16 + 15) * PGN + i];
     __syncthreads();
     if (part > 0)
-      for (int rr = 0; rr < RPP; ++rr) sG[(part * RPP + rr) * NF + i] += add;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sG[(part * 16 + rr) * PGN + i] += add;
   }
   __syncthreads();
 
-  // ---- A and Mqk.  Wave w owns row block R = w.
-  {
+  // Kr = K exp(G_T - G), beta Kd = beta K exp(G): natural tiles of T
+  auto kr_kd = [&](int t, int n) {
+    for (int e = t; e < 64 * VPR; e += n) {
+      const int r = e / VPR, i0 = (e % VPR) * EPV;
+      float kv[EPV], gv[EPV], gt[EPV];
+      load_f<T, EPV>(sK + r * PN + i0, kv);
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) {
+        gv[j] = sG[r * PGN + i0 + j];
+        gt[j] = sG[63 * PGN + i0 + j];
+      }
+      const float br = sBeta[r];
+      T kr[EPV], kd[EPV];
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) {
+        kr[j] = from_f<T>(kv[j] * ex2(gt[j] - gv[j]));
+        kd[j] = from_f<T>(br * kv[j] * ex2(gv[j]));
+      }
+      *(uint4*)(sKr + r * PN + i0) = *(const uint4*)kr;
+      *(uint4*)(sKd + r * PN + i0) = *(const uint4*)kd;
+    }
+  };
+  if constexpr (NW == 8) {
+    if (w >= 4) kr_kd(tid - 256, NT - 256);
+  }
+
+  // ---- A and Mqk.  Wave R < 4 owns row block R (with eight waves, the other four
+  // form Kr and Kd meanwhile).
+  if (w < 4) {
     const int R = w;
-    const int arow = 16 * R;  // anchor: first row of the block
+    const int r0 = 16 * R;
+    const int rrow = r0 + cl;
     f4 accA[3], accM[3];
 #pragma unroll
     for (int S = 0; S < 3; ++S) accA[S] = accM[S] = zero4();
+    //   rows of block R against the earlier blocks: anchor r0 (first row of R)
     if (R > 0) {
-      const int rrow = 16 * R + (lane & 15);
       for (int kk = 0; kk < D; kk += KS) {
-        const int i0 = kk + (lane >> 4) * KPL;
+        const int i0 = kk + g4 * KPL;
         float kf[KPL], qf[KPL], ga[KPL];
 #pragma unroll
         for (int j = 0; j < KPL; ++j) {
-          ga[j] = sG[arow * NF + i0 + j];
-          const float e = ex2(sG[rrow * NF + i0 + j] - ga[j]);
+          ga[j] = sG[r0 * PGN + i0 + j];
+          const float e = ex2(sG[rrow * PGN + i0 + j] - ga[j]);
           kf[j] = to_f(sK[rrow * PN + i0 + j]) * e;
           qf[j] = to_f(sQ[rrow * PN + i0 + j]) * e;
         }
@@ -159,11 +209,11 @@ __global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chun
 #pragma unroll
         for (int S = 0; S < 3; ++S) {
           if (S < R) {
-            const int srow = 16 * S + (lane & 15);
+            const int srow = 16 * S + cl;
             float kb[KPL];
 #pragma unroll
             for (int j = 0; j < KPL; ++j)
-              kb[j] = to_f(sK[srow * PN + i0 + j]) * ex2(ga[j] - sG[srow * NF + i0 + j]);
+              kb[j] = to_f(sK[srow * PN + i0 + j]) * ex2(ga[j] - sG[srow * PGN + i0 + j]);
             const Frag KB = MM::from_vals(kb);
             accA[S] = MM::mma(KF, KB, accA[S]);
             accM[S] = MM::mma(QF, KB, accM[S]);
@@ -171,43 +221,30 @@ __global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chun
         }
       }
     }
-#pragma unroll
-    for (int S = 0; S < 4; ++S) {
-      if (S < R) {
-        store_c<float>(sA, CC, 16 * R, 16 * S, accA[S < 3 ? S : 0], lane);
-        store_c<float>(sM, CC, 16 * R, 16 * S, accM[S < 3 ? S : 0], lane);
-      } else if (S > R) {
-        store_c<float>(sA, CC, 16 * R, 16 * S, zero4(), lane);
-        store_c<float>(sM, CC, 16 * R, 16 * S, zero4(), lane);
-      }
-    }
     // diagonal block (R, R), by 4-row sub-blocks:
     //  (i) rows r of sub-block rho against s in earlier sub-blocks of the block,
-    //      anchored at a = 16R + 4 rho (between them): one MFMA pass per rho with
+    //      anchored at a = r0 + 4 rho (between them): one MFMA pass per rho with
     //      the A rows outside rho and the B columns at or after a set to zero;
     //  (ii) pairs inside a 4x4 diagonal sub-block: pairwise decays on VALU, one
     //      (sub-block, channel group) per lane, summed over the 16 groups.
+    f4 dA = zero4(), dM = zero4();
     {
-      const int r0 = 16 * R;
-      const int cl = lane & 15;
-      const int rA = r0 + cl;                  // A row of this lane
-      const int rho_l = cl >> 2;               // its sub-block
+      const int rho_l = cl >> 2;               // sub-block of this lane's A row
       const int anc = r0 + 4 * rho_l;          // its anchor
-      f4 dA = zero4(), dM = zero4();
       float zv[KPL];
 #pragma unroll
       for (int j = 0; j < KPL; ++j) zv[j] = 0.f;
       const Frag ZF = MM::from_vals(zv);
       for (int kk = 0; kk < D; kk += KS) {
-        const int i0 = kk + (lane >> 4) * KPL;
+        const int i0 = kk + g4 * KPL;
         float kf[KPL], qf[KPL], ks[KPL], gs[KPL];
 #pragma unroll
         for (int j = 0; j < KPL; ++j) {
-          const float e = ex2(sG[rA * NF + i0 + j] - sG[anc * NF + i0 + j]);
-          kf[j] = to_f(sK[rA * PN + i0 + j]) * e;
-          qf[j] = to_f(sQ[rA * PN + i0 + j]) * e;
-          ks[j] = to_f(sK[rA * PN + i0 + j]);  // B column s = r0 + cl: same row data
-          gs[j] = sG[rA * NF + i0 + j];
+          const float e = ex2(sG[rrow * PGN + i0 + j] - sG[anc * PGN + i0 + j]);
+          ks[j] = to_f(sK[rrow * PN + i0 + j]);  // B column s = r0 + cl: same row data
+          kf[j] = ks[j] * e;
+          qf[j] = to_f(sQ[rrow * PN + i0 + j]) * e;
+          gs[j] = sG[rrow * PGN + i0 + j];
         }
         const Frag KF = MM::from_vals(kf), QF = MM::from_vals(qf);
 #pragma unroll
@@ -217,7 +254,7 @@ __global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chun
           float kb[KPL];
 #pragma unroll
           for (int j = 0; j < KPL; ++j)
-            kb[j] = colok ? ks[j] * ex2(sG[a * NF + i0 + j] - gs[j]) : 0.f;
+            kb[j] = colok ? ks[j] * ex2(sG[a * PGN + i0 + j] - gs[j]) : 0.f;
           const Frag KB = MM::from_vals(kb);
           const bool rowok = rho_l == rho;
           dA = MM::mma(rowok ? KF : ZF, KB, dA);
@@ -226,7 +263,7 @@ __global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chun
       }
       {
         constexpr int CPG = D / 16;
-        const int sb = lane >> 4, cg = lane & 15;
+        const int sb = g4, cg = cl;
         float pa[10], pm[10];
 #pragma unroll
         for (int p = 0; p < 10; ++p) pa[p] = pm[p] = 0.f;
@@ -238,7 +275,7 @@ __global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chun
             const int r = r0 + 4 * sb + t;
             kk4[t] = to_f(sK[r * PN + i]);
             qq4[t] = to_f(sQ[r * PN + i]);
-            gg4[t] = sG[r * NF + i];
+            gg4[t] = sG[r * PGN + i];
           }
 #pragma unroll
           for (int a_ = 0; a_ < 4; ++a_)
@@ -269,15 +306,29 @@ __global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chun
           }
         }
       }
-      store_c<float>(sA, CC, r0, r0, dA, lane);
-      store_c<float>(sM, CC, r0, r0, dM, lane);
+    }
+    // block row R of A and Mqk: off-diagonal blocks, the diagonal block, zeros above
+#pragma unroll
+    for (int S = 0; S < 4; ++S) {
+      f4 a = zero4(), m = zero4();
+      if (S < R) {
+        a = accA[S < 3 ? S : 0];
+        m = accM[S < 3 ? S : 0];
+      } else if (S == R) {
+        a = dA;
+        m = dM;
+      }
+      store_c<float>(sA, PC, r0, 16 * S, a, lane);
+      store_c<float>(sM, PC, r0, 16 * S, m, lane);
     }
   }
+  if constexpr (NW == 4) kr_kd(tid, NT);
   __syncthreads();
 
   // ---- INV = (I + L)^{-1}, L = diag(beta) A (strictly lower), blocked by 16.
-  // Step 1: wave R inverts its unit lower-triangular diagonal block.
-  {
+  // Step 1: wave R < 4 inverts its unit lower-triangular diagonal block (forward
+  // substitution, one column per lane).
+  if (w < 4) {
     const int R = w;
     if (lane < 16) {
       float x[16];
@@ -286,21 +337,21 @@ __global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chun
         float acc = (r == lane) ? 1.f : 0.f;
         const float br = sBeta[16 * R + r];
 #pragma unroll
-        for (int s = 0; s < r; ++s) acc -= br * sA[(16 * R + r) * CC + 16 * R + s] * x[s];
+        for (int s = 0; s < r; ++s) acc -= br * sA[(16 * R + r) * PC + 16 * R + s] * x[s];
         x[r] = acc;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sINV[(16 * R + r) * CC + 16 * R + lane] = x[r];
+      for (int r = 0; r < 16; ++r) sINV[(16 * R + r) * PC + 16 * R + lane] = x[r];
     }
     for (int e = lane; e < 16 * 64; e += 64) {
       const int r = e >> 6, col = e & 63;
-      if (col >= 16 * (R + 1)) sINV[(16 * R + r) * CC + col] = 0.f;
+      if (col >= 16 * (R + 1)) sINV[(16 * R + r) * PC + col] = 0.f;
     }
   }
   __syncthreads();
-  // Step 2: wave S fills column block S below the diagonal, top to bottom:
+  // Step 2: wave S < 3 fills column block S below the diagonal, top to bottom:
   //   INV_{R,S} = -D_R * sum_{J=S}^{R-1} L_{R,J} INV_{J,S}.
-  {
+  if (w < 3) {
     const int S = w;
     float* scr = sScr + w * 16 * 17;
     for (int R = S + 1; R < 4; ++R) {
@@ -308,143 +359,129 @@ __global__ __launch_bounds__(256) void k_prep(const ChunkInfo* __restrict__ chun
       for (int J = S; J < R; ++J) {
 #pragma unroll
         for (int kk = 0; kk < 16; kk += 4) {
-          const int row = lane & 15, kx = kk + (lane >> 4);
-          const float a = sBeta[16 * R + row] * sA[(16 * R + row) * CC + 16 * J + kx];
-          const float b = sINV[(16 * J + kx) * CC + 16 * S + row];
+          const int row = cl, kx = kk + g4;
+          const float a = sBeta[16 * R + row] * sA[(16 * R + row) * PC + 16 * J + kx];
+          const float b = sINV[(16 * J + kx) * PC + 16 * S + row];
           X = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, X, 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) scr[((lane >> 4) * 4 + j) * 17 + (lane & 15)] = X[j];
+      for (int j = 0; j < 4; ++j) scr[(g4 * 4 + j) * 17 + cl] = X[j];
       __builtin_amdgcn_wave_barrier();
       f4 Y = zero4();
 #pragma unroll
       for (int kk = 0; kk < 16; kk += 4) {
-        const int row = lane & 15, kx = kk + (lane >> 4);
-        const float a = sINV[(16 * R + row) * CC + 16 * R + kx];
+        const int row = cl, kx = kk + g4;
+        const float a = sINV[(16 * R + row) * PC + 16 * R + kx];
         const float b = scr[kx * 17 + row];
         Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, Y, 0, 0, 0);
       }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sINV[(16 * R + (lane >> 4) * 4 + j) * CC + 16 * S + (lane & 15)] = -Y[j];
+      for (int j = 0; j < 4; ++j) sINV[(16 * R + g4 * 4 + j) * PC + 16 * S + cl] = -Y[j];
       __builtin_amdgcn_wave_barrier();
     }
   }
   __syncthreads();
 
-  // ---- write INV, INV^T, Mqk^T (act dtype) for the gradient pass
+  // ---- W = INV (beta Kd): wave w -> rows of block w % 4, columns [c0, c0 + DH)
   {
-    T* o1 = INVo + ch * 64 * 64;
-    T* o2 = INVTo + ch * 64 * 64;
-    T* o3 = MqkTo + ch * 64 * 64;
-    for (int e = tid; e < 64 * 64; e += NTHR) {
-      const int r = e >> 6, s = e & 63;
-      o1[e] = from_f<T>(sINV[r * CC + s]);
-      o2[e] = from_f<T>(sINV[s * CC + r]);
-      o3[e] = from_f<T>(sM[s * CC + r]);
+    const int R = w & 3, c0 = (w >> 2) * DH;
+    constexpr int NTW = DH / 16;
+    f4 acc[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) acc[nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NKC; ++ks) {
+      const Frag a = MM::ld_perm_f32(sINV + (16 * R + cl) * PC, ks * KS, lane);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+        acc[nt] = MM::mma(a, MM::ld_tr(sKd, PN, ks * KS, c0 + nt * 16, lane), acc[nt]);
     }
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) store_c<T>(sW, PN, 16 * R, c0 + nt * 16, acc[nt], lane);
   }
-  __syncthreads();  // sA (aliased by KdT) is dead from here on
-
-  // ---- (beta Kd)^T and Kr^T, [D][64]
-  for (int idx = tid; idx < 64 * D; idx += NTHR) {
-    const int s = idx / D, i = idx % D;
-    const float kv = to_f(sK[s * PN + i]);
-    const float G = sG[s * NF + i], GT = sG[63 * NF + i];
-    sKdT[i * TT + s] = from_f<T>(sBeta[s] * kv * ex2(G));
-    sKrT[i * TT + s] = from_f<T>(kv * ex2(GT - G));
+  // ---- INV, INV^T, Mqk^T (act dtype, natural rows) for the gradient pass
+  for (int e = tid; e < 64 * 8; e += NT) {
+    const int r = e >> 3, c8 = (e & 7) * 8;
+    float a[8], b[8], m[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a[j] = sINV[r * PC + c8 + j];
+      b[j] = sINV[(c8 + j) * PC + r];
+      m[j] = sM[(c8 + j) * PC + r];
+    }
+    T ta[8], tb[8], tm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ta[j] = from_f<T>(a[j]);
+      tb[j] = from_f<T>(b[j]);
+      tm[j] = from_f<T>(m[j]);
+    }
+    const size_t o = ch * 64 * 64 + r * 64 + c8;
+#pragma unroll
+    for (int v = 0; v < 8 * L::ES / 16; ++v) {
+      ((uint4*)(INVo + o))[v] = ((const uint4*)ta)[v];
+      ((uint4*)(INVTo + o))[v] = ((const uint4*)tb)[v];
+      ((uint4*)(MqkTo + o))[v] = ((const uint4*)tm)[v];
+    }
   }
   __syncthreads();
 
-  // ---- W = INV (beta Kd): wave R -> rows of block R, all D columns
+  // ---- Tm = -W^T Kr [D x D] and PT = Qd^T - W^T Mqk^T [D x 64], computed as their
+  // transposes (C tiles over rows j / r, columns i) so that a lane holds 4
+  // consecutive entries of one row; wave w -> key channels i in [16 w, 16 w + 16).
   {
-    const int R = w;
-    f4 acc[D / 16];
+    Frag bw[NKC];  // W[s][16 w + cl], s in the permuted order of k-step ks
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) acc[nt] = zero4();
-    for (int kk = 0; kk < 64; kk += KS) {
-      const Frag a = MM::from_f32(sINV + (16 * R + (lane & 15)) * CC + kk + (lane >> 4) * KPL);
+    for (int ks = 0; ks < NKC; ++ks) bw[ks] = MM::ld_tr(sW, PN, ks * KS, 16 * w, lane);
+#pragma unroll 2
+    for (int mt = 0; mt < NW; ++mt) {
+      f4 acc = zero4();
 #pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) {
-        const Frag b = MM::load(sKdT + (nt * 16 + (lane & 15)) * TT + kk + (lane >> 4) * KPL);
-        acc[nt] = MM::mma(a, b, acc[nt]);
-      }
+      for (int ks = 0; ks < NKC; ++ks)
+        acc = MM::mma(MM::ld_tr(sKr, PN, ks * KS, 16 * mt, lane), bw[ks], acc);
+      store_ct<T>(sTm, PTM, 16 * mt, 16 * w, -acc, lane);  // sTm[i][j] = Tm[i][j]
     }
-    __syncthreads();  // every wave is done reading INV before W^T overwrites it
+    const int i = 16 * w + cl;
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) store_ct<T>(sWT, TT, 16 * R, nt * 16, acc[nt], lane);
+    for (int mt = 0; mt < 4; ++mt) {
+      f4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < NKC; ++ks)
+        acc = MM::mma(MM::ld_perm_f32(sM + (16 * mt + cl) * PC, ks * KS, lane), bw[ks], acc);
+      f4 pt;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * mt + 4 * g4 + j;
+        pt[j] = to_f(sQ[r * PN + i]) * ex2(sG[r * PGN + i]) - acc[j];
+      }
+      store_ct<T>(sPT, PPT, 16 * mt, 16 * w, pt, lane);  // sPT[i][r] = PT[i][r]
+    }
   }
+  if (tid < D) eGT[ch * D + tid] = ex2(sG[63 * PGN + tid]);
   __syncthreads();
-
-  constexpr int RT = D / 64;  // row tiles per wave for D-row outputs
-  // ---- Tm = -W^T Kr  [D x D]
   {
-    f4 acc[RT][D / 16];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) acc[rt][nt] = zero4();
-    for (int kk = 0; kk < 64; kk += KS) {
-      Frag a[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        a[rt] = MM::load(sWT + ((w * RT + rt) * 16 + (lane & 15)) * TT + kk + (lane >> 4) * KPL);
-#pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) {
-        const Frag b = MM::load(sKrT + (nt * 16 + (lane & 15)) * TT + kk + (lane >> 4) * KPL);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = MM::mma(a[rt], b, acc[rt][nt]);
-      }
-    }
     T* dst = Tm + ch * D * D;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt)
-        store_c<T>(dst, D, (w * RT + rt) * 16, nt * 16, -acc[rt][nt], lane);
-  }
-  // ---- PT = Qd^T - W^T Mqk^T  [D x 64]
-  {
-    f4 acc[RT][4];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[rt][nt] = zero4();
-    for (int kk = 0; kk < 64; kk += KS) {
-      Frag a[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        a[rt] = MM::load(sWT + ((w * RT + rt) * 16 + (lane & 15)) * TT + kk + (lane >> 4) * KPL);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const Frag b = MM::from_f32(sM + (nt * 16 + (lane & 15)) * CC + kk + (lane >> 4) * KPL);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = MM::mma(a[rt], b, acc[rt][nt]);
-      }
+    for (int l = 0; l < D * VPR / NT; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      *(uint4*)(dst + r * D + vv * EPV) = *(const uint4*)(sTm + r * PTM + vv * EPV);
     }
-    T* dst = PT + ch * D * 64;
+    constexpr int VP = 64 / EPV;  // vectors per 64-long row
+    T* dp = PT + ch * D * 64;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int r = nt * 16 + (lane & 15);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = (w * RT + rt) * 16 + (lane >> 4) * 4 + j;
-          const float qd = to_f(sQ[r * PN + i]) * ex2(sG[r * NF + i]);
-          dst[i * 64 + r] = from_f<T>(qd - acc[rt][nt][j]);
-        }
-      }
+    for (int l = 0; l < D * VP / NT; ++l) {
+      const int idx = tid + l * NT, r = idx / VP, vv = idx % VP;
+      *(uint4*)(dp + r * 64 + vv * EPV) = *(const uint4*)(sPT + r * PPT + vv * EPV);
+    }
   }
-  if (tid < D) eGT[ch * D + tid] = ex2(sG[63 * NF + tid]);
 }
 
 template <typename T, int D>
 static hipError_t prep_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   dim3 grid((unsigned)s.NC, (unsigned)s.H);
-  hipLaunchKernelGGL((k_prep<T, D>), grid, dim3(NTHR), 0, st, p.chunks, s.H, (const T*)p.q,
+  hipLaunchKernelGGL((k_prep<T, D>), grid, dim3(PL<T, D>::NT), 0, st, p.chunks, s.H, (const T*)p.q,
                      (const T*)p.k, p.g_raw, p.beta, p.A_log, (T*)p.Tm, (T*)p.PT, p.eGT,
                      (T*)p.INV, (T*)p.INVT, (T*)p.MqkT);
   return hipGetLastError();
