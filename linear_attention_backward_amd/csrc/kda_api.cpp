@@ -3,6 +3,7 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -29,7 +30,8 @@ struct Plan {
   int64_t NC = 0;
   size_t es = 0;  // bytes per act element
   // workspace regions
-  Region chunks, seq_off, Tm, PT, eGT, INV, INVT, MqkT, dstates, dAl, hsaved;
+  Region chunks, seq_off, groups, grp_off, Tm, PT, eGT, INV, INVT, MqkT, dstates, dAl, Pg, Qg,
+      bnd, hsaved;
   size_t fwd_bytes = 0, bwd_bytes = 0;
 };
 
@@ -45,6 +47,26 @@ int count_chunks(const kda_problem* p, int64_t* nc) {
   }
   *nc = total;
   return KDA_OK;
+}
+
+int64_t seq_chunks(const kda_problem* p, int n) {
+  const int64_t len = p->cu_seqlens_host
+                          ? (int64_t)p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n]
+                          : (int64_t)p->T;
+  return (len + CH - 1) / CH;
+}
+
+// Chunks per group of the state-gradient scan.  A sequence of more than 128
+// chunks is scanned in groups of 64 (three passes, groups side by side); shorter
+// ones in one serial pass.  KDA_SCAN_GROUP=<chunks> overrides (0: never split).
+int scan_group_size(const kda_problem* p, int N) {
+  if (const char* env = std::getenv("KDA_SCAN_GROUP")) {
+    const int v = std::atoi(env);
+    if (v >= 0) return v;
+  }
+  int64_t mx = 0;
+  for (int n = 0; n < N; ++n) mx = std::max(mx, seq_chunks(p, n));
+  return mx > 128 ? 64 : 0;
 }
 
 int validate_problem(const kda_problem* p) {
@@ -81,8 +103,15 @@ int make_plan(const kda_problem* p, Plan* pl) {
   s.cu = p->cu_seqlens_dev;
   count_chunks(p, &pl->NC);
   s.NC = pl->NC;
+  s.gs = scan_group_size(p, s.N);
+  s.NG = 0;
+  for (int n = 0; n < s.N; ++n) {
+    const int64_t nck = seq_chunks(p, n);
+    s.NG += s.gs > 0 ? std::max<int64_t>(1, (nck + s.gs - 1) / s.gs) : 1;
+  }
   pl->es = s.bf16 ? 2 : 4;
   const size_t NCH = (size_t)pl->NC * s.H;
+  const size_t NGH = (size_t)s.NG * s.H;
   const size_t D = s.D;
   size_t off = 0;
   auto take = [&](Region& r, size_t bytes) {
@@ -93,6 +122,8 @@ int make_plan(const kda_problem* p, Plan* pl) {
   take(pl->chunks, (size_t)pl->NC * sizeof(ChunkInfo));
   take(pl->seq_off, ((size_t)s.N + 1) * sizeof(int));
   pl->fwd_bytes = off;
+  take(pl->groups, (size_t)s.NG * sizeof(GroupInfo));
+  take(pl->grp_off, ((size_t)s.N + 1) * sizeof(int));
   take(pl->Tm, NCH * D * D * pl->es);
   take(pl->PT, NCH * D * 64 * pl->es);
   take(pl->eGT, NCH * D * 4);
@@ -101,6 +132,10 @@ int make_plan(const kda_problem* p, Plan* pl) {
   take(pl->MqkT, NCH * 64 * 64 * pl->es);
   take(pl->dstates, NCH * D * D * pl->es);
   take(pl->dAl, NCH * 4);
+  const size_t split = s.gs > 0 ? 1 : 0;
+  take(pl->Pg, split * NGH * D * D * pl->es);
+  take(pl->Qg, split * NGH * D * D * 4);
+  take(pl->bnd, split * NGH * D * D * 4);
   take(pl->hsaved, NCH * D * D * pl->es);
   pl->bwd_bytes = off;
   return KDA_OK;
@@ -133,19 +168,6 @@ hipError_t timed(int stage, hipStream_t st, F&& launch) {
 int hip_fail(hipError_t e) {
   g_hip_msg = std::string("HIP error: ") + hipGetErrorName(e) + ": " + hipGetErrorString(e);
   return KDA_ERR_HIP;
-}
-
-int vsplit_for(const Shape& s) {
-  const char* env = std::getenv("KDA_VSPLIT");
-  const int cap = s.D / 16;
-  if (env) {
-    int v = std::atoi(env);
-    if (v == 1 || v == 2 || v == 4 || v == 8) return v <= cap ? v : cap;
-  }
-  const int units = s.N * s.H;
-  int vs = 1;
-  while (vs < cap && units * vs < 1024) vs *= 2;
-  return vs;
 }
 
 }  // namespace
@@ -196,7 +218,7 @@ int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, siz
   char* ws = (char*)workspace;
   ChunkInfo* tab = (ChunkInfo*)(ws + pl.chunks.off);
   int* seq_off = (int*)(ws + pl.seq_off.off);
-  hipError_t e = launch_chunk_table(pl.s, tab, seq_off, s);
+  hipError_t e = launch_chunk_table(pl.s, tab, seq_off, nullptr, nullptr, s);
   if (e != hipSuccess) return hip_fail(e);
   e = launch_fwd_ref(pl.s, seq_off, io->q, io->k, io->v, io->g_raw, io->beta, io->A_log, io->h0,
                      io->o, io->ht, io->h_saved, s);
@@ -240,9 +262,17 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   b.dstates = io->dstates ? io->dstates : (void*)(ws + pl.dstates.off);
   b.dAl_part = (float*)(ws + pl.dAl.off);
   b.h_saved = io->h_saved ? io->h_saved : (const void*)(ws + pl.hsaved.off);
+  b.groups = (const GroupInfo*)(ws + pl.groups.off);
+  b.grp_off = (const int*)(ws + pl.grp_off.off);
+  b.Pg = ws + pl.Pg.off;
+  b.Qg = (float*)(ws + pl.Qg.off);
+  b.bnd = (float*)(ws + pl.bnd.off);
   const Shape& sh = pl.s;
   hipError_t e;
-  e = timed(0, s, [&] { return launch_chunk_table(sh, (ChunkInfo*)b.chunks, (int*)b.seq_off, s); });
+  e = timed(0, s, [&] {
+    return launch_chunk_table(sh, (ChunkInfo*)b.chunks, (int*)b.seq_off, (GroupInfo*)b.groups,
+                              (int*)b.grp_off, s);
+  });
   if (e != hipSuccess) return hip_fail(e);
   if (!io->h_saved) {
     e = timed(5, s, [&] {
@@ -253,8 +283,7 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   }
   e = timed(1, s, [&] { return launch_prep(sh, b, s); });
   if (e != hipSuccess) return hip_fail(e);
-  const int vs = vsplit_for(sh);
-  e = timed(2, s, [&] { return launch_scan(sh, b, vs, s); });
+  e = timed(2, s, [&] { return launch_scan(sh, b, s); });
   if (e != hipSuccess) return hip_fail(e);
   e = timed(3, s, [&] { return launch_gradf(sh, b, s); });
   if (e != hipSuccess) return hip_fail(e);

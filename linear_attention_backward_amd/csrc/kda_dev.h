@@ -32,6 +32,16 @@ struct ChunkInfo {
   int cidx;  // chunk index inside the sequence
 };
 
+// One row of the group table: a run of consecutive chunks of one sequence that the
+// state-gradient scan treats as a unit (the whole sequence when it is not split).
+struct GroupInfo {
+  int c0;     // first chunk (index into the chunk table)
+  int cnt;    // chunks in the group (0 only for an empty sequence)
+  int seq;    // sequence index
+  int flags;  // GRP_FIRST: first group of its sequence; GRP_LAST: last group
+};
+constexpr int GRP_FIRST = 1, GRP_LAST = 2;
+
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f(float x);

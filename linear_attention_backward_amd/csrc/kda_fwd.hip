@@ -7,37 +7,52 @@ namespace kda {
 
 // ---------------------------------------------------------------------------
 // Chunk table: one entry per 64-token chunk of every sequence, sequences back to
-// back (chunk c of sequence n at index seq_off[n] + c).  One workgroup.
+// back (chunk c of sequence n at index seq_off[n] + c).  With a group table
+// requested, also the chunk groups of the state-gradient scan: runs of gs chunks
+// of one sequence (gs = 0: the whole sequence), at least one per sequence, with
+// grp_off[n] the first group of sequence n.  One workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_chunk_table(const int32_t* __restrict__ cu, int N, int T,
-                                                     ChunkInfo* __restrict__ tab,
-                                                     int* __restrict__ seq_off) {
-  __shared__ int part[256];
+                                                     int gs, ChunkInfo* __restrict__ tab,
+                                                     int* __restrict__ seq_off,
+                                                     GroupInfo* __restrict__ groups,
+                                                     int* __restrict__ grp_off) {
+  __shared__ int part[256], gpart[256];
   const int tid = threadIdx.x;
   const int per = (N + 255) / 256;
   const int n0 = min(N, tid * per), n1 = min(N, n0 + per);
-  int cnt = 0;
+  auto nchunks = [&](int n) {
+    const int len = cu ? cu[n + 1] - cu[n] : T;
+    return (len + CH - 1) / CH;
+  };
+  auto ngroups = [&](int nck) { return gs > 0 ? max(1, (nck + gs - 1) / gs) : 1; };
+  int cnt = 0, gcnt = 0;
   for (int n = n0; n < n1; ++n) {
-    int len = cu ? cu[n + 1] - cu[n] : T;
-    cnt += (len + CH - 1) / CH;
+    const int nck = nchunks(n);
+    cnt += nck;
+    gcnt += ngroups(nck);
   }
   part[tid] = cnt;
+  gpart[tid] = gcnt;
   __syncthreads();
   if (tid == 0) {
-    int run = 0;
+    int run = 0, grun = 0;
     for (int i = 0; i < 256; ++i) {
-      int x = part[i];
+      const int x = part[i], y = gpart[i];
       part[i] = run;
+      gpart[i] = grun;
       run += x;
+      grun += y;
     }
   }
   __syncthreads();
-  int off = part[tid];
+  int off = part[tid], goff = gpart[tid];
   for (int n = n0; n < n1; ++n) {
-    int start = cu ? cu[n] : n * T;
-    int len = cu ? cu[n + 1] - cu[n] : T;
+    const int start = cu ? cu[n] : n * T;
+    const int len = cu ? cu[n + 1] - cu[n] : T;
+    const int nck = (len + CH - 1) / CH;
     seq_off[n] = off;
-    for (int c = 0; c * CH < len; ++c) {
+    for (int c = 0; c < nck; ++c) {
       ChunkInfo e;
       e.t0 = start + c * CH;
       e.len = min(CH, len - c * CH);
@@ -45,10 +60,29 @@ __global__ __launch_bounds__(256) void k_chunk_table(const int32_t* __restrict__
       e.cidx = c;
       tab[off + c] = e;
     }
-    off += (len + CH - 1) / CH;
+    if (groups) {
+      const int ng = ngroups(nck);
+      grp_off[n] = goff;
+      for (int gi = 0; gi < ng; ++gi) {
+        GroupInfo gr;
+        gr.c0 = off + (gs > 0 ? gi * gs : 0);
+        gr.cnt = gs > 0 ? min(gs, nck - gi * gs) : nck;
+        gr.seq = n;
+        gr.flags = (gi == 0 ? GRP_FIRST : 0) | (gi == ng - 1 ? GRP_LAST : 0);
+        groups[goff + gi] = gr;
+      }
+      goff += ng;
+    }
+    off += nck;
   }
-  if (n0 < N && n1 == N) seq_off[N] = off;
-  if (N == 0 && tid == 0) seq_off[0] = 0;
+  if (n0 < N && n1 == N) {
+    seq_off[N] = off;
+    if (groups) grp_off[N] = goff;
+  }
+  if (N == 0 && tid == 0) {
+    seq_off[0] = 0;
+    if (groups) grp_off[0] = 0;
+  }
 }
 
 __device__ __forceinline__ float softplus_f(float x) {
@@ -156,8 +190,10 @@ __global__ __launch_bounds__(256) void k_dalog(const float* __restrict__ part, i
   if (tid == 0) out[h] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, hipStream_t st) {
-  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, st, s.cu, s.N, s.T, tab, seq_off);
+hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, GroupInfo* groups,
+                              int* grp_off, hipStream_t st) {
+  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, st, s.cu, s.N, s.T, s.gs, tab, seq_off,
+                     groups, grp_off);
   return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 namespace kda {
 
 struct ChunkInfo;
+struct GroupInfo;
 
 // Pointers of one backward call, as the kernels see them (device memory).
 struct BwdPtrs {
@@ -25,6 +26,11 @@ struct BwdPtrs {
   void* MqkT;              // [NC,H,64,64] act dtype: Mqk transposed
   void* dstates;           // [NC,H,K,V] act dtype: dL/dS at the end of every chunk
   float* dAl_part;         // [NC,H] per chunk-head partial sums for dA_log
+  const GroupInfo* groups; // [NG] chunk groups of the state-gradient scan
+  const int* grp_off;      // [N+1] first group of every sequence
+  void* Pg;                // [NG,H,K,K] act dtype: transition of every group (split scan only)
+  float* Qg;               // [NG,H,K,V] offset of every group (split scan only)
+  float* bnd;              // [NG,H,K,V] state gradient at the end of every group (split scan only)
 };
 
 struct Shape {
@@ -32,15 +38,18 @@ struct Shape {
   int64_t NC;      // total chunks
   int bf16;        // act dtype is bf16
   const int32_t* cu;  // device cu_seqlens or nullptr (uniform rows of T tokens)
+  int gs;          // chunks per scan group; 0: one group per sequence
+  int64_t NG;      // groups
 };
 
-hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, hipStream_t st);
+hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, GroupInfo* groups,
+                              int* grp_off, hipStream_t st);
 hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, const void* k,
                           const void* v, const float* g_raw, const float* beta,
                           const float* A_log, const float* h0, void* o, float* ht,
                           void* h_saved, hipStream_t st);
 hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st);
-hipError_t launch_scan(const Shape& s, const BwdPtrs& p, int vsplit, hipStream_t st);
+hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st);
 

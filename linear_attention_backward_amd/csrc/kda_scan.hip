@@ -1,212 +1,324 @@
 // kda_scan.hip -- reverse scan of the state gradient across chunks.
 //
-// For the chunks of one sequence, last to first ([PB] section 3: Kernel A is
-// the serial dstate scan; section 3.5 splits its V axis over workgroups):
+// For the chunks of one sequence, last to first ([PB] section 3: Kernel A is the
+// serial dstate scan):
 //   dS_out(c) = dS                       (stored for the gradient pass)
 //   dS       <- exp(G_T) . dS + Tm_c dS + PT_c dO_c
-// and dh0 = dS after the first chunk.  The recurrence is separable in the V
-// columns of dS, so each workgroup owns one (sequence, head, V-slice) and the
-// slices never communicate.  dS is carried in fp32 MFMA accumulators; the
-// operands Tm_c, PT_c (act dtype, from the prep pass) are read straight from
-// global memory into MFMA A-fragments and prefetched one chunk ahead.
+// and dh0 = dS after the first chunk.  The map is affine in dS with a K x K linear
+// part M_c = Diag(exp(G_T)) + Tm_c acting from the left, so every column of dS
+// evolves on its own and a run of chunks composes into one affine map.
+//
+// One workgroup carries the whole K x V state of a (chunk group, head) in fp32
+// MFMA accumulators and reads each chunk's Tm, PT, exp(G_T) and dO once.  The
+// state goes through LDS as a natural bf16 tile, read back transposed as the B
+// operand; Tm and PT rows are A fragments in the same permuted contraction order,
+// read straight from global memory one chunk ahead.
+//
+// Long sequences are split into groups of gs chunks and scanned in three passes
+// (the pages name context parallelism as the lever for long contexts; here the
+// groups run side by side on one GPU):
+//   1. every group from the boundary I (transition workgroups: P_g, no dO terms)
+//      and from 0 (offset workgroups: Q_g, with the dO terms), so that the state
+//      before the group is P_g B_g + Q_g for the state B_g at its end;
+//   2. per (sequence, head), the group boundaries B_g from the last group back;
+//   3. every group again from its true boundary, storing dS_out of every chunk.
 #include "kda_dev.h"
 #include "kda_launch.h"
 
 namespace kda {
 
-template <typename T, int D, int VS>
-__global__ __launch_bounds__(256) void k_scan(const ChunkInfo* __restrict__ chunks,
-                                              const int* __restrict__ seq_off, int H, int nunits,
-                                              const T* __restrict__ Tm, const T* __restrict__ PT,
-                                              const float* __restrict__ eGT,
-                                              const T* __restrict__ dO,
-                                              const float* __restrict__ dht,
-                                              T* __restrict__ dstates, float* __restrict__ dh0) {
+// Tiling of a scan workgroup: the K x V right-hand side, wave w owning row tiles of
+// row group w % 4 and column tiles of column group w / 4.
+template <typename T, int D> struct SL {
+  static constexpr int NW = D / 16;
+  static constexpr int NT = NW * 64;
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int CW = NW / 4;           // column groups
+  static constexpr int RTW = D / 64;          // row tiles per wave
+  static constexpr int CTW = D / 16 / CW;     // column tiles per wave
+  static constexpr int PS = D + 16 / ES;      // state tile pitch, natural [D][D]
+  static constexpr int PO = D + 16 / ES;      // dO tile pitch, natural [64][D]
+  static constexpr int S_SZ = D * PS * ES;
+  static constexpr int O_SZ = 64 * PO * ES;
+  static constexpr int TOTAL = 2 * S_SZ + 2 * O_SZ;
+};
+
+// PQ = false: scan a group from its boundary (dht for the last group of a
+// sequence, else bnd), store dS_out of every chunk and, for the first group, dh0.
+// PQ = true: blockIdx.z = 0 scans a group from I without the dO terms and stores
+// P_g (act dtype); blockIdx.z = 1 scans it from 0 and stores Q_g (fp32).
+template <typename T, int D, bool PQ>
+__global__ __launch_bounds__(4 * D) void k_scanw(
+    const ChunkInfo* __restrict__ chunks, const GroupInfo* __restrict__ groups, int H,
+    const T* __restrict__ Tm, const T* __restrict__ PT, const float* __restrict__ eGT,
+    const T* __restrict__ dO, const float* __restrict__ dht, const float* __restrict__ bnd,
+    T* __restrict__ dstates, float* __restrict__ dh0, T* __restrict__ Pg,
+    float* __restrict__ Qg) {
+  using L = SL<T, D>;
   using MM = Mma<T>;
   typedef typename MM::Frag Frag;
-  constexpr int KS = MM::KS, KPL = MM::KPL;
-  constexpr int VW = D / VS;       // value columns of this workgroup
-  constexpr int NCT = VW / 16;     // column tiles
-  constexpr int RT = D / 64;       // row tiles per wave (rows = key channels)
-  constexpr int PD = D + 16 / (int)sizeof(T);   // dS^T pitch  ([VW][D])
-  constexpr int PO = Pitch<T, D>::TT;           // dO^T pitch ([VW][64])
-  constexpr int EPV = 16 / (int)sizeof(T);      // elements per 16-byte vector
-  constexpr int VPR = VW / EPV;                 // vectors per dO row slice
-  constexpr int NLD = (64 * VPR + NTHR - 1) / NTHR;
-  __shared__ __attribute__((aligned(16))) T sdST[VW * PD];
-  __shared__ __attribute__((aligned(16))) T sdOT[2][VW * PO];
+  constexpr int NT = L::NT, RTW = L::RTW, CTW = L::CTW, PS = L::PS, PO = L::PO;
+  constexpr int KS = MM::KS;
+  constexpr int NKD = D / KS, NKC = 64 / KS;
+  constexpr int EPV = 16 / L::ES;
+  constexpr int VPR = D / EPV;                 // 16-byte vectors per D-long row
+  constexpr int NLO = 64 * VPR / NT;           // dO vectors per thread
+  constexpr int NLS = D * VPR / NT;            // state vectors per thread
+  static_assert(64 * VPR % NT == 0 && D * VPR % NT == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  T* sS0 = (T*)smem;
+  T* sO0 = (T*)(smem + 2 * L::S_SZ);
 
-  // Block -> (unit, slice): the VS slices of a unit get block ids congruent mod 8,
-  // so they are dispatched to the same XCD and share its L2 for Tm / PT.
-  const int b = blockIdx.x;
-  const int xcd = b & 7, y = b >> 3;
-  const int vs = y % VS, u = (y / VS) * 8 + xcd;
-  if (u >= nunits) return;
-  const int n = u / H, h = u % H;
+  const int g = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int cbeg = seq_off[n], nck = seq_off[n + 1] - cbeg;
-  const int col0 = vs * VW;
+  const int g4 = lane >> 4, cl = lane & 15;
+  const int rgp = w & 3, cgp = w >> 2;
+  const GroupInfo gi = groups[g];
   const size_t DD = (size_t)D * D;
+  const size_t uh = (size_t)gi.seq * H + h;  // (sequence, head)
+  const size_t gh = (size_t)g * H + h;       // (group, head)
+  const bool trans = PQ && blockIdx.z == 0;  // transition columns: identity start, no dO
 
-  f4 acc[RT][NCT];
+  f4 acc[RTW][CTW];
   {
-    const float* src = dht ? dht + ((size_t)n * H + h) * DD : nullptr;
+    const float* src = nullptr;
+    if constexpr (!PQ) src = (gi.flags & GRP_LAST) ? (dht ? dht + uh * DD : nullptr) : bnd + gh * DD;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int i = (w * RT + rt) * 16 + (lane >> 4) * 4;
-        const int d = col0 + ct * 16 + (lane & 15);
+      for (int ct = 0; ct < CTW; ++ct) {
+        const int i0 = (rgp * RTW + rt) * 16 + 4 * g4;
+        const int col = (cgp * CTW + ct) * 16 + cl;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[rt][ct][j] = src ? src[(size_t)(i + j) * D + d] : 0.f;
-      }
-  }
-
-  Frag ta[RT][D / KS], pa[RT][64 / KS];
-  f4 eg[RT];
-  uint4 dov[NLD];
-  auto load_ops = [&](int cg, Frag (&A)[RT][D / KS], Frag (&P)[RT][64 / KS], f4 (&E)[RT]) {
-    const size_t ch = (size_t)cg * H + h;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int i = (w * RT + rt) * 16 + (lane & 15);
-#pragma unroll
-      for (int kk = 0; kk < D / KS; ++kk)
-        A[rt][kk] = MM::load(Tm + ch * DD + (size_t)i * D + kk * KS + (lane >> 4) * KPL);
-#pragma unroll
-      for (int kk = 0; kk < 64 / KS; ++kk)
-        P[rt][kk] = MM::load(PT + ch * D * 64 + (size_t)i * 64 + kk * KS + (lane >> 4) * KPL);
-      E[rt] = *(const f4*)(eGT + ch * D + (w * RT + rt) * 16 + (lane >> 4) * 4);
-    }
-  };
-  auto load_do = [&](int cg, uint4 (&R)[NLD]) {
-    const ChunkInfo ci = chunks[cg];
-#pragma unroll
-    for (int l = 0; l < NLD; ++l) {
-      const int idx = tid + l * NTHR;
-      const int r = idx / VPR, sv = idx % VPR;
-      uint4 x = {0u, 0u, 0u, 0u};
-      if (idx < 64 * VPR && r < ci.len)
-        x = *(const uint4*)(dO + ((size_t)(ci.t0 + r) * H + h) * D + col0 + sv * EPV);
-      R[l] = x;
-    }
-  };
-  auto store_do = [&](const uint4 (&R)[NLD], T* dst) {
-#pragma unroll
-    for (int l = 0; l < NLD; ++l) {
-      const int idx = tid + l * NTHR;
-      if (idx < 64 * VPR) {
-        const int r = idx / VPR, sv = idx % VPR;
-        const T* e = (const T*)&R[l];
-#pragma unroll
-        for (int q = 0; q < EPV; ++q) dst[(sv * EPV + q) * PO + r] = e[q];
-      }
-    }
-  };
-
-  if (nck > 0) {
-    load_ops(cbeg + nck - 1, ta, pa, eg);
-    load_do(cbeg + nck - 1, dov);
-    store_do(dov, sdOT[0]);
-  }
-  int buf = 0;
-  for (int cc = nck - 1; cc >= 0; --cc) {
-    const int cg = cbeg + cc;
-    // dS_out of this chunk
-    {
-      T* dst = dstates + ((size_t)cg * H + h) * DD;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          store_c<T>(dst, D, (w * RT + rt) * 16, col0 + ct * 16, acc[rt][ct], lane);
-          store_ct<T>(sdST, PD, (w * RT + rt) * 16, ct * 16, acc[rt][ct], lane);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (PQ)
+            acc[rt][ct][j] = (trans && i0 + j == col) ? 1.f : 0.f;
+          else
+            acc[rt][ct][j] = src ? src[(size_t)(i0 + j) * D + col] : 0.f;
         }
+      }
+  }
+
+  Frag ta[RTW][NKD], pa[RTW][NKC];
+  f4 eg[RTW];
+  auto load_a = [&](int cgl, Frag (&A)[RTW][NKD], Frag (&P)[RTW][NKC], f4 (&E)[RTW]) {
+    const size_t ch = (size_t)cgl * H + h;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int i = (rgp * RTW + rt) * 16 + cl;
+#pragma unroll
+      for (int kk = 0; kk < NKD; ++kk) A[rt][kk] = MM::ld_perm(Tm + ch * DD + (size_t)i * D, kk * KS, lane);
+#pragma unroll
+      for (int kk = 0; kk < NKC; ++kk) P[rt][kk] = MM::ld_perm(PT + ch * D * 64 + (size_t)i * 64, kk * KS, lane);
+      E[rt] = *(const f4*)(eGT + ch * D + (rgp * RTW + rt) * 16 + 4 * g4);
     }
+  };
+  uint4 rdo[NLO];
+  auto load_do = [&](int cgl) {
+    const ChunkInfo ci = chunks[cgl];
+#pragma unroll
+    for (int l = 0; l < NLO; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      uint4 x = {0u, 0u, 0u, 0u};
+      if (r < ci.len && !trans) x = *(const uint4*)(dO + ((size_t)(ci.t0 + r) * H + h) * D + vv * EPV);
+      rdo[l] = x;
+    }
+  };
+  auto store_do = [&](T* dst) {
+#pragma unroll
+    for (int l = 0; l < NLO; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      *(uint4*)(dst + r * PO + vv * EPV) = rdo[l];
+    }
+  };
+
+  if (gi.cnt > 0) {
+    load_a(gi.c0 + gi.cnt - 1, ta, pa, eg);
+    load_do(gi.c0 + gi.cnt - 1);
+    store_do(sO0);
+  }
+  int sb = 0, ob = 0;
+  for (int cc = gi.cnt - 1; cc >= 0; --cc) {
+    const int cgl = gi.c0 + cc;
+    const size_t ch = (size_t)cgl * H + h;
+    T* sS = sS0 + sb * (PS * D);
+    const T* sO = sO0 + ob * (PO * 64);
+    // the state at the end of this chunk, as a natural act-dtype tile
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+        store_c<T>(sS, PS, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, acc[rt][ct], lane);
     __syncthreads();
-    Frag tn[RT][D / KS], pn[RT][64 / KS];
-    f4 en[RT];
+    if constexpr (!PQ) {  // dS_out of this chunk, 16-byte rows
+      T* dst = dstates + ch * DD;
+#pragma unroll
+      for (int l = 0; l < NLS; ++l) {
+        const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+        *(uint4*)(dst + (size_t)r * D + vv * EPV) = *(const uint4*)(sS + r * PS + vv * EPV);
+      }
+    }
+    Frag tn[RTW][NKD], pn[RTW][NKC];
+    f4 en[RTW];
     if (cc > 0) {
-      load_ops(cg - 1, tn, pn, en);
-      load_do(cg - 1, dov);
+      load_a(cgl - 1, tn, pn, en);
+      load_do(cgl - 1);
     }
     // dS <- exp(G_T) . dS + Tm dS + PT dO
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[rt][ct][j] *= eg[rt][j];
 #pragma unroll
-    for (int kk = 0; kk < D / KS; ++kk) {
+    for (int kk = 0; kk < NKD; ++kk) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const Frag bfr = MM::load(sdST + (ct * 16 + (lane & 15)) * PD + kk * KS + (lane >> 4) * KPL);
+      for (int ct = 0; ct < CTW; ++ct) {
+        const Frag b = MM::ld_tr(sS, PS, kk * KS, (cgp * CTW + ct) * 16, lane);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt][ct] = MM::mma(ta[rt][kk], bfr, acc[rt][ct]);
+        for (int rt = 0; rt < RTW; ++rt) acc[rt][ct] = MM::mma(ta[rt][kk], b, acc[rt][ct]);
       }
     }
-    const T* sO = sdOT[buf];
+    if (!trans) {
 #pragma unroll
-    for (int kk = 0; kk < 64 / KS; ++kk) {
+      for (int kk = 0; kk < NKC; ++kk) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const Frag bfr = MM::load(sO + (ct * 16 + (lane & 15)) * PO + kk * KS + (lane >> 4) * KPL);
+        for (int ct = 0; ct < CTW; ++ct) {
+          const Frag b = MM::ld_tr(sO, PO, kk * KS, (cgp * CTW + ct) * 16, lane);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt][ct] = MM::mma(pa[rt][kk], bfr, acc[rt][ct]);
+          for (int rt = 0; rt < RTW; ++rt) acc[rt][ct] = MM::mma(pa[rt][kk], b, acc[rt][ct]);
+        }
       }
     }
     if (cc > 0) {
-      store_do(dov, sdOT[buf ^ 1]);
+      store_do(sO0 + (ob ^ 1) * (PO * 64));
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
+      for (int rt = 0; rt < RTW; ++rt) {
 #pragma unroll
-        for (int kk = 0; kk < D / KS; ++kk) ta[rt][kk] = tn[rt][kk];
+        for (int kk = 0; kk < NKD; ++kk) ta[rt][kk] = tn[rt][kk];
 #pragma unroll
-        for (int kk = 0; kk < 64 / KS; ++kk) pa[rt][kk] = pn[rt][kk];
+        for (int kk = 0; kk < NKC; ++kk) pa[rt][kk] = pn[rt][kk];
         eg[rt] = en[rt];
       }
     }
-    buf ^= 1;
-    __syncthreads();
+    sb ^= 1;
+    ob ^= 1;
   }
-  if (dh0) {
-    float* dst = dh0 + ((size_t)n * H + h) * DD;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+  for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        store_c<float>(dst, D, (w * RT + rt) * 16, col0 + ct * 16, acc[rt][ct], lane);
-  }
+    for (int ct = 0; ct < CTW; ++ct) {
+      const int r0 = (rgp * RTW + rt) * 16;
+      const int c0 = (cgp * CTW + ct) * 16;
+      if constexpr (PQ) {
+        if (trans) store_c<T>(Pg + gh * DD, D, r0, c0, acc[rt][ct], lane);
+        else store_c<float>(Qg + gh * DD, D, r0, c0, acc[rt][ct], lane);
+      } else {
+        if ((gi.flags & GRP_FIRST) && dh0) store_c<float>(dh0 + uh * DD, D, r0, c0, acc[rt][ct], lane);
+      }
+    }
 }
 
-template <typename T, int D, int VS>
-static hipError_t scan_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
-  const int nunits = s.N * s.H;
-  const int groups = (nunits + 7) / 8;
-  dim3 grid((unsigned)(groups * 8 * VS));
-  hipLaunchKernelGGL((k_scan<T, D, VS>), grid, dim3(NTHR), 0, st, p.chunks, p.seq_off, s.H, nunits,
-                     (const T*)p.Tm, (const T*)p.PT, p.eGT, (const T*)p.dO, p.dht,
-                     (T*)p.dstates, p.dh0);
-  return hipGetLastError();
+// Group boundaries of one (sequence, head): B = dht at the end of the last group;
+// going back, bnd[g] = B (the state at the end of group g), then B <- P_g B + Q_g.
+template <typename T, int D>
+__global__ __launch_bounds__(4 * D) void k_scan_bnd(const GroupInfo* __restrict__ groups,
+                                                    const int* __restrict__ grp_off, int H,
+                                                    const T* __restrict__ Pg,
+                                                    const float* __restrict__ Qg,
+                                                    const float* __restrict__ dht,
+                                                    float* __restrict__ bnd) {
+  using L = SL<T, D>;
+  using MM = Mma<T>;
+  typedef typename MM::Frag Frag;
+  constexpr int RTW = L::RTW, CTW = L::CTW, PS = L::PS;
+  constexpr int KS = MM::KS, NKD = D / KS;
+  __shared__ __attribute__((aligned(16))) T sS[D * PS];
+  const int n = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, cl = lane & 15;
+  const int rgp = w & 3, cgp = w >> 2;
+  const size_t DD = (size_t)D * D;
+  const int gb = grp_off[n], ng = grp_off[n + 1] - gb;
+  f4 acc[RTW][CTW];
+  {
+    const float* src = dht ? dht + ((size_t)n * H + h) * DD : nullptr;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const int i0 = (rgp * RTW + rt) * 16 + 4 * g4;
+        const int col = (cgp * CTW + ct) * 16 + cl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[rt][ct][j] = src ? src[(size_t)(i0 + j) * D + col] : 0.f;
+      }
+  }
+  for (int gg = ng - 1; gg >= 1; --gg) {
+    const size_t gh = (size_t)(gb + gg) * H + h;
+    // the state at the end of group gb + gg - 1 is P_g B + Q_g
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+        store_c<T>(sS, PS, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, acc[rt][ct], lane);
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int i = (rgp * RTW + rt) * 16 + cl;
+      Frag a[NKD];
+#pragma unroll
+      for (int kk = 0; kk < NKD; ++kk) a[kk] = MM::ld_perm(Pg + gh * DD + (size_t)i * D, kk * KS, lane);
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const int i0 = (rgp * RTW + rt) * 16 + 4 * g4;
+        const int col = (cgp * CTW + ct) * 16 + cl;
+        f4 x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = Qg[gh * DD + (size_t)(i0 + j) * D + col];
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk)
+          x = MM::mma(a[kk], MM::ld_tr(sS, PS, kk * KS, (cgp * CTW + ct) * 16, lane), x);
+        acc[rt][ct] = x;
+      }
+    }
+    __syncthreads();
+    const size_t bh = (size_t)(gb + gg - 1) * H + h;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+        store_c<float>(bnd + bh * DD, D, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, acc[rt][ct],
+                       lane);
+  }
 }
 
 template <typename T, int D>
-static hipError_t scan_d(const Shape& s, const BwdPtrs& p, int vs, hipStream_t st) {
-  switch (vs) {
-    case 1: return scan_t<T, D, 1>(s, p, st);
-    case 2: return scan_t<T, D, 2>(s, p, st);
-    case 4: return scan_t<T, D, 4>(s, p, st);
-    default: break;
+static hipError_t scan_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+  const dim3 gg((unsigned)s.NG, (unsigned)s.H);
+  if (s.gs > 0) {
+    hipLaunchKernelGGL((k_scanw<T, D, true>), dim3((unsigned)s.NG, (unsigned)s.H, 2),
+                       dim3(SL<T, D>::NT), 0, st, p.chunks,
+                       p.groups, s.H, (const T*)p.Tm, (const T*)p.PT, p.eGT, (const T*)p.dO,
+                       nullptr, nullptr, nullptr, nullptr, (T*)p.Pg, p.Qg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_scan_bnd<T, D>), dim3((unsigned)s.N, (unsigned)s.H),
+                       dim3(SL<T, D>::NT), 0, st, p.groups, p.grp_off, s.H,
+                       (const T*)p.Pg, p.Qg, p.dht, p.bnd);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  if constexpr (D >= 128) return scan_t<T, D, 8>(s, p, st);
-  return scan_t<T, D, 4>(s, p, st);
+  hipLaunchKernelGGL((k_scanw<T, D, false>), gg, dim3(SL<T, D>::NT), 0, st, p.chunks,
+                     p.groups, s.H, (const T*)p.Tm, (const T*)p.PT, p.eGT, (const T*)p.dO, p.dht,
+                     p.bnd, (T*)p.dstates, p.dh0, nullptr, nullptr);
+  return hipGetLastError();
 }
 
-hipError_t launch_scan(const Shape& s, const BwdPtrs& p, int vsplit, hipStream_t st) {
-  if (s.N * s.H == 0) return hipSuccess;
-  if (s.bf16) return s.D == 128 ? scan_d<bf16, 128>(s, p, vsplit, st) : scan_d<bf16, 64>(s, p, vsplit, st);
-  return scan_d<float, 64>(s, p, vsplit, st);
+hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+  if (s.NG == 0) return hipSuccess;
+  if (s.bf16) return s.D == 128 ? scan_t<bf16, 128>(s, p, st) : scan_t<bf16, 64>(s, p, st);
+  return scan_t<float, 64>(s, p, st);
 }
 
 }  // namespace kda

@@ -84,3 +84,27 @@ def test_repeatable_bitwise():
     b = KC.run_gpu(inp)
     for key in GRADS + ["dstates"]:
         assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("name,group", [("weak_decay_bf16", 3), ("weak_decay_fp32", 2),
+                                        ("ragged_bf16", 1), ("ragged_fp32", 3),
+                                        ("single_seq_bf16", 5)])
+def test_split_scan(name, group, monkeypatch):
+    """The state-gradient scan split into groups of a few chunks (group maps, group
+    boundaries, re-scan from the boundaries) against the oracle; weak decay keeps
+    the cross-group terms large."""
+    monkeypatch.setenv("KDA_SCAN_GROUP", str(group))
+    print("\n[case] split scan %s, %d chunks per group" % (name, group), flush=True)
+    _check(name)
+
+
+def test_split_scan_zero_length(monkeypatch):
+    monkeypatch.setenv("KDA_SCAN_GROUP", "1")
+    wl = KI.Workload("zero_len", 1, 0 + 70 + 0 + 5 + 64, 2, 128, 128, "bf16", 1200, varlen_seqs=4,
+                     fixed_lengths=(0, 70, 0, 69), h0_std=0.3, dht_std=1.0)
+    inp = KI.make_inputs(wl)
+    print("\n[case] split scan zero_len", flush=True)
+    res = KC.run_gpu(inp)
+    ref = KC.oracle_for(inp)
+    ref["h_saved"] = ref["states"]
+    KC.compare(res, ref, GRADS + INTER, KC.TOL["bf16"], label="zero_len split")
