@@ -67,10 +67,14 @@ template <typename T, int D> struct GF {
   static constexpr int DL_OFF = DM_OFF + 64 * PC * ES;
   static constexpr int DG_OFF = DL_OFF + 64 * PC * ES;
   // fp32 copies of the four diagonal 16x16 blocks of dMqk and dL (bf16 tiles only)
-  static constexpr int DG_SZ = ES == 2 ? 2 * 4 * 16 * PDG * 4 : 0;
+  static constexpr int DGBS = 16 * PDG + 4;     // block stride of those tables
+  static constexpr int DG_SZ = ES == 2 ? 2 * 4 * DGBS * 4 : 0;
   static constexpr int DQ_OFF = DG_OFF + DG_SZ;
   static constexpr int DK_OFF = DQ_OFF + N_SZ;
   static constexpr int P3_END = DK_OFF + N_SZ;
+  // per-wave exchange slots [16 channels][PX] fp32 over the dq / dk staging tiles
+  static constexpr int PX = 68;
+  static_assert(NW * 16 * PX * 4 <= 2 * N_SZ, "exchange slots fit the dq / dk staging");
   static constexpr int X_END = C_END > P3_END ? C_END : P3_END;
   static constexpr int B_OFF = (X_END + 15) / 16 * 16;     // beta [64]
   static constexpr int DB1_OFF = B_OFF + 256;             // [WPR][64]
@@ -133,9 +137,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   if constexpr (L::ES == 2) {
     float* base = (float*)(smem + L::DG_OFF);
     dgM = base;
-    dgL = base + 4 * 16 * L::PDG;
+    dgL = base + 4 * L::DGBS;
     DGP = L::PDG;
-    DGB = 16 * L::PDG;
+    DGB = L::DGBS;
   } else {
     dgM = (float*)sDM;
     dgL = (float*)sDL;
@@ -487,13 +491,14 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   __syncthreads();
 
   // ------------------------------------------------ intra-chunk decay terms
-  // Lane: key channel ic (column of the C tiles), rows 16 rt + 4 g4 + j.
+  // Lane: key channel ic.  Pairs (r, s) inside one 16-row block are summed exactly
+  // in fp32 on VALU, one (channel, block) per lane, with the pairwise decays built
+  // as running products of per-token factors 2^{G_t - G_{t-1}} <= 1.  Pairs across
+  // blocks run on MFMA with anchored operands (formed once per block, reused for
+  // every row tile).
   const float* Gi = sG + ic * PG;  // G of channel ic, by row
   const int n0 = 16 * w;           // first key channel of this wave
   const float gT = Gi[63];
-  float dG[4][4];
-  float dkr_col = 0.f, dal = 0.f;
-  float dbp[4][4];
   float tg[4][4];  // g_raw at this lane's C positions, for the epilogue (prefetched)
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -502,7 +507,112 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const int r = rt * 16 + g4 * 4 + j;
       tg[rt][j] = r < Lr ? grh[r * rs + ic] : 0.f;
     }
-#pragma unroll 1
+  // (1) diagonal blocks: lane -> block g4 of channel ic (dec[s] = e^{G_r - G_s}).  x1_r = sum_{s<=r} dMqk_rs
+  //     k_s e^{G_r-G_s}, x2_r = the same with dL, z_s = sum_{r>=s} (dMqk_rs q_r +
+  //     beta_r dL_rs k_r) e^{G_r-G_s}; all rows and columns inside the block.
+  float x1d[4][4], x2d[4][4], zd[4][4];  // C layout: rows 16 rt + 4 g4 + j
+  {
+    const int rb = 16 * g4;
+    float Gb[16], kb[16], dec[16], x1[16], x2[16], z[16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f4 t = *(const f4*)(Gi + rb + 4 * m);
+      Gb[4 * m] = t[0]; Gb[4 * m + 1] = t[1]; Gb[4 * m + 2] = t[2]; Gb[4 * m + 3] = t[3];
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) kb[t] = to_f(sK[(rb + t) * PN + ic]);
+    const float* mb = dgM + g4 * DGB;
+    const float* lb = dgL + g4 * DGB;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float qr = to_f(sQ[(rb + r) * PN + ic]);
+      const float bkr = sBeta[rb + r] * kb[r];
+      if (r > 0) {
+        const float al = ex2(Gb[r] - Gb[r - 1]);
+#pragma unroll
+        for (int s = 0; s < r; ++s) dec[s] *= al;
+      }
+      dec[r] = 1.f;
+      z[r] = 0.f;
+      float mv[16], lv[16];
+#pragma unroll
+      for (int m = 0; m <= r / 4; ++m) {
+        const f4 a = *(const f4*)(mb + r * DGP + 4 * m);
+        const f4 b = *(const f4*)(lb + r * DGP + 4 * m);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mv[4 * m + e] = a[e];
+          lv[4 * m + e] = b[e];
+        }
+      }
+      float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+      for (int s = 0; s <= r; ++s) {
+        const float kd = kb[s] * dec[s];
+        a1 = fmaf(mv[s], kd, a1);
+        a2 = fmaf(lv[s], kd, a2);
+        z[s] = fmaf(fmaf(mv[s], qr, lv[s] * bkr), dec[s], z[s]);
+      }
+      x1[r] = a1;
+      x2[r] = a2;
+    }
+    // to the C layout through a per-wave LDS slot [16 channels][64 rows] (over the
+    // dq / dk staging tiles, which are written only after the next barrier)
+    float* xs = (float*)(smem + L::DQ_OFF) + w * 16 * L::PX;
+    auto exch = [&](const float (&src)[16], float (&dst)[4][4]) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        *(f4*)(xs + cl * L::PX + rb + 4 * m) =
+            f4{src[4 * m], src[4 * m + 1], src[4 * m + 2], src[4 * m + 3]};
+      __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in order
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const f4 t = *(const f4*)(xs + cl * L::PX + 16 * rt + 4 * g4);
+        dst[rt][0] = t[0]; dst[rt][1] = t[1]; dst[rt][2] = t[2]; dst[rt][3] = t[3];
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+    exch(x1, x1d);
+    exch(x2, x2d);
+    exch(z, zd);
+  }
+  // (2) operands of the cross-block products, anchored once per block:
+  //   X side (rows r of block R, s in block S < R):  k_s e^{G_e - G_s}, e = 16 S + 16;
+  //   Z side (rows s of block S, r in block R > S):  (q_r, beta_r k_r) e^{G_r - G_a},
+  //   a = 16 R.  The remaining factors e^{G_r - G_e} (X) and e^{G_a - G_s} (Z) are
+  //   split into a per-channel factor between anchors and a per-row factor.
+  typename MS::Op BX[3], BZq[4], BZk[4];
+#pragma unroll
+  for (int S = 0; S < 3; ++S) {
+    float kv[4], gv[4], b[4];
+    MS::ld_tr(sK, PN, 16 * S, n0, lane, kv);
+    MS::ldf(Gi + 16 * S, g4, gv);
+    const float ge = Gi[16 * S + 16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = kv[j] * ex2(ge - gv[j]);
+    BX[S] = MS::split(b);
+  }
+#pragma unroll
+  for (int R = 1; R < 4; ++R) {
+    float qv[4], kv[4], gv[4], bq[4], bk[4];
+    MS::ld_tr(sQ, PN, 16 * R, n0, lane, qv);
+    MS::ld_tr(sK, PN, 16 * R, n0, lane, kv);
+    MS::ldf(Gi + 16 * R, g4, gv);
+    const float ga = Gi[16 * R];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = ex2(gv[j] - ga);
+      bq[j] = qv[j] * e;
+      bk[j] = sBeta[16 * R + MS::kidx(g4, j)] * kv[j] * e;
+    }
+    BZq[R] = MS::split(bq);
+    BZk[R] = MS::split(bk);
+  }
+  __syncthreads();  // every wave's exchange slot is read: the dq / dk staging is free
+  float dG[4][4];
+  float dkr_col = 0.f, dal = 0.f;
+  float dbp[4][4];
+#pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const int r0 = 16 * rt;
     const int ar = r0 + cl;  // A-operand row of this lane inside the tile
@@ -512,22 +622,25 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       Gr[0] = t[0]; Gr[1] = t[1]; Gr[2] = t[2]; Gr[3] = t[3];
     }
     f4 X1a = zero4(), X2a = zero4(), Za = zero4();
-    f4 X1b = zero4(), X2b = zero4(), Zb = zero4();
-    // level 1: across 16-row blocks
-    //   rows r of this block, s in earlier blocks: anchor a = r0
     if (rt > 0) {
       const float ga = Gi[r0];
+#pragma unroll
       for (int S = 0; S < rt; ++S) {
-        float b[4], kv[4], gv[4];
         const typename MS::Op a1 = MS::ld_op(sDM + ar * PC + 16 * S, g4);
         const typename MS::Op a2 = MS::ld_op(sDL + ar * PC + 16 * S, g4);
-        MS::ld_tr(sK, PN, 16 * S, n0, lane, kv);
-        MS::ldf(Gi + 16 * S, g4, gv);
+        if (S == rt - 1) {
+          X1a = MS::op_sb(a1, BX[S], X1a);
+          X2a = MS::op_sb(a2, BX[S], X2a);
+        } else {
+          const f4 p1 = MS::op_sb(a1, BX[S], zero4());
+          const f4 p2 = MS::op_sb(a2, BX[S], zero4());
+          const float m = ex2(ga - Gi[16 * S + 16]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = kv[j] * ex2(ga - gv[j]);
-        const typename MS::Op bo = MS::split(b);
-        X1a = MS::op_sb(a1, bo, X1a);
-        X2a = MS::op_sb(a2, bo, X2a);
+          for (int j = 0; j < 4; ++j) {
+            X1a[j] = fmaf(m, p1[j], X1a[j]);
+            X2a[j] = fmaf(m, p2[j], X2a[j]);
+          }
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -536,150 +649,44 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
         X2a[j] *= sc;
       }
     }
-    //   rows s of this block, r in later blocks: anchor b = r0 + 16; A = dMqk^T and
-    //   dL^T read transposed from the natural tiles, beta_r folded into the k operand
     if (rt < 3) {
       const float gb = Gi[r0 + 16];
+#pragma unroll
       for (int R = rt + 1; R < 4; ++R) {
-        float bq[4], bk[4], qv[4], kv[4], gv[4];
         const typename MS::Op a1 = MS::ld_tr_op(sDM, PC, 16 * R, r0, lane);
         const typename MS::Op a2 = MS::ld_tr_op(sDL, PC, 16 * R, r0, lane);
-        MS::ld_tr(sQ, PN, 16 * R, n0, lane, qv);
-        MS::ld_tr(sK, PN, 16 * R, n0, lane, kv);
-        MS::ldf(Gi + 16 * R, g4, gv);
+        if (R == rt + 1) {
+          Za = MS::op_sb(a1, BZq[R], Za);
+          Za = MS::op_sb(a2, BZk[R], Za);
+        } else {
+          f4 p = MS::op_sb(a1, BZq[R], zero4());
+          p = MS::op_sb(a2, BZk[R], p);
+          const float m = ex2(Gi[16 * R] - gb);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e = ex2(gv[j] - gb);
-          bq[j] = qv[j] * e;
-          bk[j] = sBeta[16 * R + MS::kidx(g4, j)] * kv[j] * e;
+          for (int j = 0; j < 4; ++j) Za[j] = fmaf(m, p[j], Za[j]);
         }
-        Za = MS::op_sb(a1, MS::split(bq), Za);
-        Za = MS::op_sb(a2, MS::split(bk), Za);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) Za[j] *= ex2(gb - Gr[j]);
     }
-    // level 2: 4-row sub-blocks inside this block (contraction index = row - r0).
-    // A rows outside the pass's sub-block are zeroed; the contraction range of the
-    // pass is cut on the B side.
-    {
-      float ma[4], la[4], mt[4], lt[4], kv[4], qv[4], gv[4];
-      MS::ldf(dgM + rt * DGB + cl * DGP, g4, ma);
-      MS::ldf(dgL + rt * DGB + cl * DGP, g4, la);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = MS::kidx(g4, j);
-        mt[j] = dgM[rt * DGB + rr * DGP + cl];
-        lt[j] = sBeta[r0 + rr] * dgL[rt * DGB + rr * DGP + cl];
-      }
-      MS::ld_tr(sK, PN, r0, n0, lane, kv);
-      MS::ld_tr(sQ, PN, r0, n0, lane, qv);
-      MS::ldf(Gi + r0, g4, gv);
-      const typename MS::Op oma = MS::split(ma), ola = MS::split(la);
-      const typename MS::Op omt = MS::split(mt), olt = MS::split(lt);
-      const int rsb = cl >> 2;  // sub-block of this lane's A row
-#pragma unroll
-      for (int rho = 1; rho < 4; ++rho) {
-        // rows in sub-block rho, s in earlier sub-blocks: anchor r0 + 4 rho
-        const float ga = Gi[r0 + 4 * rho];
-        float b[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b[j] = MS::kidx(g4, j) < 4 * rho ? kv[j] * ex2(ga - gv[j]) : 0.f;
-        const typename MS::Op bo = MS::split(b);
-        X1b = MS::op_ss(MS::keep_if(rsb == rho, oma), bo, X1b);
-        X2b = MS::op_ss(MS::keep_if(rsb == rho, ola), bo, X2b);
-      }
-#pragma unroll
-      for (int sig = 0; sig < 3; ++sig) {
-        // rows s in sub-block sig, r in later sub-blocks: anchor r0 + 4 (sig + 1)
-        const float gb = Gi[r0 + 4 * (sig + 1)];
-        float bq[4], bk[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e = MS::kidx(g4, j) >= 4 * (sig + 1) ? ex2(gv[j] - gb) : 0.f;
-          bq[j] = qv[j] * e;
-          bk[j] = kv[j] * e;
-        }
-        Zb = MS::op_ss(MS::keep_if(rsb == sig, omt), MS::split(bq), Zb);
-        Zb = MS::op_ss(MS::keep_if(rsb == sig, olt), MS::split(bk), Zb);
-      }
-      // this lane's C rows are sub-block g4
-      if (g4 >= 1) {
-        const float ga = Gi[r0 + 4 * g4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float sc = ex2(Gr[j] - ga);
-          X1b[j] *= sc;
-          X2b[j] *= sc;
-        }
-      }
-      if (g4 <= 2) {
-        const float gb = Gi[r0 + 4 * (g4 + 1)];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Zb[j] *= ex2(gb - Gr[j]);
-      }
-    }
-    // level 3: the 4x4 diagonal sub-block of this lane's rows (VALU)
-    const int rb = r0 + 4 * g4;
-    float kr[4], qr[4], br[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kr[j] = to_f(sK[(rb + j) * PN + ic]);
-      qr[j] = to_f(sQ[(rb + j) * PN + ic]);
-      br[j] = sBeta[rb + j];
-    }
-    float x1d[4], x2d[4], zd[4];
-    {
-      const float a1 = ex2(Gr[1] - Gr[0]), a2 = ex2(Gr[2] - Gr[1]), a3 = ex2(Gr[3] - Gr[2]);
-      // f[j][jj] = e^{G_{rb+j} - G_{rb+jj}}, jj <= j
-      float f[4][4];
-      f[0][0] = f[1][1] = f[2][2] = f[3][3] = 1.f;
-      f[1][0] = a1;
-      f[2][1] = a2;
-      f[2][0] = a1 * a2;
-      f[3][2] = a3;
-      f[3][1] = a2 * a3;
-      f[3][0] = f[2][0] * a3;
-      float mrow[4][4], lrow[4][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          mrow[j][jj] = dgM[rt * DGB + (4 * g4 + j) * DGP + 4 * g4 + jj];
-          lrow[j][jj] = dgL[rt * DGB + (4 * g4 + j) * DGP + 4 * g4 + jj];
-        }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          if (jj <= j) {
-            s1 += mrow[j][jj] * kr[jj] * f[j][jj];
-            s2 += lrow[j][jj] * kr[jj] * f[j][jj];
-          }
-          if (jj >= j)
-            s3 += (mrow[jj][j] * qr[jj] + br[jj] * lrow[jj][j] * kr[jj]) * f[jj][j];
-        }
-        x1d[j] = s1;
-        x2d[j] = s2;
-        zd[j] = s3;
-      }
-    }
     // combine and form the gate gradient of this tile
+    const int rb = r0 + 4 * g4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = rb + j;
+      const float kr = to_f(sK[r * PN + ic]);
+      const float qr = to_f(sQ[r * PN + ic]);
+      const float br = sBeta[r];
       const float eG = ex2(Gr[j]);
-      const float x1 = X1a[j] + X1b[j] + x1d[j];
-      const float x2 = X2a[j] + X2b[j] + x2d[j];
-      const float dki = Za[j] + Zb[j] + zd[j];
+      const float x1 = X1a[j] + x1d[rt][j];
+      const float x2 = X2a[j] + x2d[rt][j];
+      const float dki = Za[j] + zd[rt][j];
       const float dqv = eG * aQd[rt][j] + x1;
-      const float dkd = br[j] * (-eG * aKd[rt][j] + x2);
+      const float dkd = br * (-eG * aKd[rt][j] + x2);
       const float dkr = ex2(gT - Gr[j]) * aKr[rt][j];
-      dG[rt][j] = qr[j] * dqv + kr[j] * (dkd - dki - dkr);
-      dkr_col += kr[j] * dkr;
-      dbp[rt][j] = kr[j] * x2;
+      dG[rt][j] = qr * dqv + kr * (dkd - dki - dkr);
+      dkr_col += kr * dkr;
+      dbp[rt][j] = kr * x2;
       sDQ[r * PN + ic] = from_f<T>(dqv);
       sDK[r * PN + ic] = from_f<T>(dkd + dki + dkr);
     }
