@@ -180,21 +180,17 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       *(uint4*)(sKd + r * PN + i0) = *(const uint4*)kd;
     }
   };
-  if constexpr (NW == 8) {
-    if (w >= 4) kr_kd(tid - 256, NT - 256);
-  }
-
-  // ---- A and Mqk.  Wave R < 4 owns row block R (with eight waves, the other four
-  // form Kr and Kd meanwhile).
-  if (w < 4) {
-    const int R = w;
+  // ---- A and Mqk, by 16-row blocks.
+  //   offdiag(R, S0, S1): blocks (R, S), S0 <= S < S1 < R, anchored at the first row
+  //   of block R; diag(R): block (R, R) and the zero blocks right of it.
+  auto offdiag = [&](const int R, const int S0, const int S1) {
     const int r0 = 16 * R;
     const int rrow = r0 + cl;
     f4 accA[3], accM[3];
 #pragma unroll
     for (int S = 0; S < 3; ++S) accA[S] = accM[S] = zero4();
     //   rows of block R against the earlier blocks: anchor r0 (first row of R)
-    if (R > 0) {
+    {
       for (int kk = 0; kk < D; kk += KS) {
         const int i0 = kk + g4 * KPL;
         float kf[KPL], qf[KPL], ga[KPL];
@@ -208,7 +204,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
         const Frag KF = MM::from_vals(kf), QF = MM::from_vals(qf);
 #pragma unroll
         for (int S = 0; S < 3; ++S) {
-          if (S < R) {
+          if (S >= S0 && S < S1) {
             const int srow = 16 * S + cl;
             float kb[KPL];
 #pragma unroll
@@ -221,6 +217,16 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
         }
       }
     }
+#pragma unroll
+    for (int S = 0; S < 3; ++S)
+      if (S >= S0 && S < S1) {
+        store_c<float>(sA, PC, r0, 16 * S, accA[S], lane);
+        store_c<float>(sM, PC, r0, 16 * S, accM[S], lane);
+      }
+  };
+  auto diag = [&](const int R) {
+    const int r0 = 16 * R;
+    const int rrow = r0 + cl;
     // diagonal block (R, R), by 4-row sub-blocks:
     //  (i) rows r of sub-block rho against s in earlier sub-blocks of the block,
     //      anchored at a = r0 + 4 rho (between them): one MFMA pass per rho with
@@ -307,19 +313,33 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
         }
       }
     }
-    // block row R of A and Mqk: off-diagonal blocks, the diagonal block, zeros above
 #pragma unroll
     for (int S = 0; S < 4; ++S) {
-      f4 a = zero4(), m = zero4();
-      if (S < R) {
-        a = accA[S < 3 ? S : 0];
-        m = accM[S < 3 ? S : 0];
-      } else if (S == R) {
-        a = dA;
-        m = dM;
-      }
+      if (S < R) continue;
+      const f4 a = S == R ? dA : zero4();
+      const f4 m = S == R ? dM : zero4();
       store_c<float>(sA, PC, r0, 16 * S, a, lane);
       store_c<float>(sM, PC, r0, 16 * S, m, lane);
+    }
+  };
+  if constexpr (NW == 8) {
+    // waves 0-3: the diagonal blocks; waves 4-7: the six blocks below them, in
+    // shares of about equal cost (one anchored row-block operand per block row)
+    if (w < 4) {
+      diag(w);
+    } else if (w == 4) {
+      offdiag(3, 0, 2);
+    } else if (w == 5) {
+      offdiag(3, 2, 3);
+    } else if (w == 6) {
+      offdiag(2, 0, 2);
+    } else {
+      offdiag(1, 0, 1);
+    }
+  } else {
+    if (w < 4) {
+      if (w > 0) offdiag(w, 0, w);
+      diag(w);
     }
   }
   if constexpr (NW == 4) kr_kd(tid, NT);
@@ -327,7 +347,11 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 
   // ---- INV = (I + L)^{-1}, L = diag(beta) A (strictly lower), blocked by 16.
   // Step 1: wave R < 4 inverts its unit lower-triangular diagonal block (forward
-  // substitution, one column per lane).
+  // substitution, one column per lane); with eight waves, waves 4-7 form Kr and Kd
+  // meanwhile.
+  if constexpr (NW == 8) {
+    if (w >= 4) kr_kd(tid - 256, NT - 256);
+  }
   if (w < 4) {
     const int R = w;
     if (lane < 16) {
