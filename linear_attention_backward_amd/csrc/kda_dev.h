@@ -363,6 +363,44 @@ __device__ __forceinline__ void store_ct<float>(float* base, int pitch, int row0
   *(f4*)(base + col * pitch + r) = acc;
 }
 
+// Direct global -> LDS copy of a [ROWS][D] tile of T (global row stride `rs`
+// elements) into an LDS tile of pitch D + 16 / sizeof(T) elements, i.e. one 16-byte
+// pad granule per row.  global_load_lds moves 16 bytes per lane and lands lane l at
+// the wave-uniform LDS base + 16 l, so each wave fills 64-granule slices of the
+// padded tile (wave w: slices w, w + NW, ...) without passing through registers.
+// Pad granules receive a copy of the row's last granule (never read); rows at or
+// beyond `valid` are zero-filled with ordinary LDS stores instead.  The caller
+// waits for vmcnt(0) and synchronises before the tile is read.
+typedef __attribute__((address_space(3))) void lds_void;
+template <typename T, int D, int ROWS, int NW>
+__device__ __forceinline__ void g2l_tile(T* lds_tile, const T* src, size_t rs, int valid, int w,
+                                         int lane) {
+  constexpr int GPR = D * (int)sizeof(T) / 16;  // data granules per row
+  constexpr int GP = GPR + 1;                   // granules per padded LDS row
+  constexpr int NG = ROWS * GP;
+  constexpr int EPG = 16 / (int)sizeof(T);
+  constexpr int NSL = (NG + 63) / 64;           // slices
+#pragma unroll
+  for (int n = 0; n < (NSL + NW - 1) / NW; ++n) {
+    const int base = (w + n * NW) * 64;
+    if (base < NG) {
+      const int p = base + lane;
+      const int row = p / GP, gc = p - row * GP;
+      if (p < NG) {
+        if (row < valid) {
+          const T* g = src + (size_t)row * rs + (gc < GPR ? gc : GPR - 1) * EPG;
+          __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)((char*)lds_tile + base * 16),
+                                           16, 0, 0);
+        } else {
+          *(uint4*)((char*)lds_tile + p * 16) = uint4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  }
+}
+// Wait until this wave's global loads (including global -> LDS copies) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 // DPP lane move inside a row of 16 lanes.
 template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,

@@ -180,23 +180,10 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     }
   }
   const float rbeta = tid < Lr ? beta[(t0 + (tid & 63)) * H + h] : 0.f;
-  uint4 rS[NLS], rD[NLS], rO[NLT], rV[NLT];
-#pragma unroll
-  for (int l = 0; l < NLS; ++l) {
-    const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
-    rS[l] = *(const uint4*)(Sin + (size_t)i * D + sv * EPV);
-  }
-#pragma unroll
-  for (int l = 0; l < NLT; ++l) {
-    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    uint4 xo = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-    if (r < Lr) {
-      xo = *(const uint4*)(oh + r * rs + sv * EPV);
-      xv = *(const uint4*)(vh + r * rs + sv * EPV);
-    }
-    rO[l] = xo;
-    rV[l] = xv;
-  }
+  // S_in, dO and v straight into their LDS tiles (natural, padded rows)
+  g2l_tile<T, D, D, NW>(sS, Sin, D, D, w, lane);
+  g2l_tile<T, D, 64, NW>(sO, oh, rs, Lr, w, lane);
+  g2l_tile<T, D, 64, NW>(sV, vh, rs, Lr, w, lane);
   // state side: wave w owns the rows of block R1, value columns [64 half, +64)
   const int R1 = w / WPR, half = w % WPR;
   const int arow = 16 * R1 + cl;            // A-operand row of this lane
@@ -235,23 +222,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       *(f4*)(sG + i * PG + part * 16 + 4 * qq) = x;
     }
   }
-#pragma unroll
-  for (int l = 0; l < NLS; ++l) {  // S_in, natural
-    const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
-    *(uint4*)(sS + i * PN + sv * EPV) = rS[l];
-  }
-#pragma unroll
-  for (int l = 0; l < NLT; ++l) {  // dO and v, natural
-    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    *(uint4*)(sO + r * PN + sv * EPV) = rO[l];
-    *(uint4*)(sV + r * PN + sv * EPV) = rV[l];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int l = 0; l < NLS; ++l) {
-    const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
-    rD[l] = *(const uint4*)(dSo + (size_t)i * D + sv * EPV);
-  }
+  wait_vmem();
+  __syncthreads();
   Frag fI[NKC], fIT[NKC], fMT[NKC];          // rows arow of INV, INV^T, Mqk^T
 #pragma unroll
   for (int ks = 0; ks < NKC; ++ks) {
@@ -259,7 +231,6 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     fMT[ks] = MM::ld_perm(MqkT + ch * 4096 + arow * 64, ks * KS, lane);
     fIT[ks] = MM::load(INVT + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
   }
-  __syncthreads();
   {
     const int i = tid % D, part = tid / D;
     float add = 0.f;
@@ -321,11 +292,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
   for (int kk = 0; kk < NKD; ++kk) bS[kk] = MM::load(sS + ic * PN + kk * KS + g4 * KPL);
   __syncthreads();  // (beta Y)^T complete; S_in and v are dead
-#pragma unroll
-  for (int l = 0; l < NLS; ++l) {  // dS_out, natural
-    const int idx = tid + l * NT, i = idx / VPR, sv = idx % VPR;
-    *(uint4*)(sS + i * PN + sv * EPV) = rD[l];
-  }
+  g2l_tile<T, D, D, NW>(sS, dSo, D, D, w, lane);  // dS_out, natural (lands during U)
   {  // U = INV (beta Y)
     f4 U[4];
 #pragma unroll
@@ -342,6 +309,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) store_c<T>(sU, PN, 16 * R1, 64 * half + nt * 16, U[nt], lane);
   }
+  wait_vmem();
   __syncthreads();  // dS_out in place; U complete; (beta Y)^T dead
   {  // dU = Mqk^T dO + Kr dS_out  ->  dU^T
     f4 dU[4];
