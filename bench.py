@@ -112,6 +112,61 @@ def cpu_baseline(inp, target_s=12.0):
                       % (nh, H, TT, token_heads, dt)}
 
 
+KERNEL_STAGE = (("k_prep", "prep"), ("k_scanw", "scan"), ("k_gradf", "grad"))
+
+
+def _stage_of(name):
+    for key, stage in KERNEL_STAGE:
+        if key in name:
+            return stage
+    return None
+
+
+def _pmc_kib(csv_path, counter):
+    """Average counter value (KiB) per dispatch of every backward kernel stage; the
+    scan stage sums its launches (group maps and the scan proper) per step."""
+    import csv
+    per = {}
+    for row in csv.DictReader(open(csv_path)):
+        if row["Counter_Name"] != counter:
+            continue
+        stage = _stage_of(row["Kernel_Name"])
+        if stage is None:
+            continue
+        per.setdefault(stage, []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def _copy_kib(csv_path, counter):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+    return sum(vals) / len(vals)
+
+
+def summarize_profiles(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, copy_mib):
+    """Write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of
+    this benchmark and of its --copy-calib mode (a copy of copy_mib MiB): each counter
+    is scaled by (bytes the copy moves) / (what the counter read for it)."""
+    nbytes = copy_mib << 20
+    fs = nbytes / (_copy_kib(calib_fetch_csv, "FETCH_SIZE") * 1024.0)
+    ws = nbytes / (_copy_kib(calib_write_csv, "WRITE_SIZE") * 1024.0)
+    fk = _pmc_kib(fetch_csv, "FETCH_SIZE")
+    wk = _pmc_kib(write_csv, "WRITE_SIZE")
+    out = {"sources": kernel_sources_digest(),
+           "workload": "train_bf16 (B=8,T=4096,H=32,K=V=128,bf16)",
+           "fetch_scale": fs, "write_scale": ws, "kernels": {}}
+    for stage in sorted(set(fk) & set(wk)):
+        rb = fk[stage] * 1024.0 * fs
+        wb = wk[stage] * 1024.0 * ws
+        out["kernels"][stage] = {"fetch_kib_raw": fk[stage], "write_kib_raw": wk[stage],
+                                 "read_bytes": rb, "write_bytes": wb, "bytes_per_launch": rb + wb}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,7 +177,14 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) so that "
                          "HBM counters can be scaled against a kernel of known traffic")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                             "CALIB_FETCH_CSV", "CALIB_WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 counter CSVs of this "
+                         "benchmark and of --copy-calib 1024 (no GPU needed)")
     a = ap.parse_args()
+    if a.summarize_traffic:
+        print(json.dumps(summarize_profiles(*a.summarize_traffic, copy_mib=1024), indent=1))
+        return
     if a.copy_calib:
         import torch
         n = a.copy_calib << 20

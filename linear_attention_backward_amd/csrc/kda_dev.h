@@ -19,6 +19,7 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes in registers
 
 constexpr int CH = 64;      // chunk length (tokens)
 constexpr int NTHR = 256;   // threads per workgroup (4 waves)

@@ -184,22 +184,13 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   g2l_tile<T, D, D, NW>(sS, Sin, D, D, w, lane);
   g2l_tile<T, D, 64, NW>(sO, oh, rs, Lr, w, lane);
   g2l_tile<T, D, 64, NW>(sV, vh, rs, Lr, w, lane);
+  // k, once, over the dvcorr tile (unused until the state side's last product)
+  T* sK0 = sDVC;
+  g2l_tile<T, D, 64, NW>(sK0, kh, rs, Lr, w, lane);
   // state side: wave w owns the rows of block R1, value columns [64 half, +64)
   const int R1 = w / WPR, half = w % WPR;
   const int arow = 16 * R1 + cl;            // A-operand row of this lane
   const int crow = 16 * R1 + g4 * 4;        // first C row of this lane
-  Frag kf[NKD];                              // raw k of row arow (permuted k order)
-#pragma unroll
-  for (int kk = 0; kk < NKD; ++kk) {
-    if (arow < Lr) {
-      kf[kk] = MM::ld_perm(kh + arow * rs, kk * KS, lane);
-    } else {
-      float z[KPL];
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) z[j] = 0.f;
-      kf[kk] = MM::from_vals(z);
-    }
-  }
   if (tid < 64) sBeta[tid] = rbeta;
   {  // in-chunk cumulative gate (log2 units), channel-major: sG[i][r]
     const int i = tid % D, part = tid / D;
@@ -224,6 +215,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   }
   wait_vmem();
   __syncthreads();
+  Frag kf[NKD];                              // raw k of row arow (permuted k order)
+#pragma unroll
+  for (int kk = 0; kk < NKD; ++kk) kf[kk] = MM::ld_perm(sK0 + arow * PN, kk * KS, lane);
   Frag fI[NKC], fIT[NKC], fMT[NKC];          // rows arow of INV, INV^T, Mqk^T
 #pragma unroll
   for (int ks = 0; ks < NKC; ++ks) {
@@ -330,6 +324,12 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) store_ct<T>(sYT, PT, 16 * R1, 64 * half + nt * 16, dU[nt], lane);
   }
+  u32x4 rK[NLT];  // k for the intra-chunk phase, before the dvcorr tile is overwritten
+#pragma unroll
+  for (int l = 0; l < NLT; ++l) {
+    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+    rK[l] = *(const u32x4*)(sK0 + r * PN + sv * EPV);
+  }
   Frag bD[NKD];  // dS_out row of this lane's key channel
 #pragma unroll
   for (int kk = 0; kk < NKD; ++kk) bD[kk] = MM::load(sS + ic * PN + kk * KS + g4 * KPL);
@@ -365,18 +365,14 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       if (cl == 0) sDB1[half * 64 + crow + j] = s;
     }
   }
-  // q, k for the intra-chunk phase (registers now, LDS once their tiles are free)
-  uint4 rQ[NLT], rK[NLT];
+  // q for the intra-chunk phase (registers now, LDS once its tile is free)
+  uint4 rQ[NLT];
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    uint4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
-    if (r < Lr) {
-      xq = *(const uint4*)(qh + r * rs + sv * EPV);
-      xk = *(const uint4*)(kh + r * rs + sv * EPV);
-    }
+    uint4 xq = {0u, 0u, 0u, 0u};
+    if (r < Lr) xq = *(const uint4*)(qh + r * rs + sv * EPV);
     rQ[l] = xq;
-    rK[l] = xk;
   }
   __syncthreads();  // dvcorr and dv staged
 #pragma unroll
@@ -454,7 +450,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   for (int l = 0; l < NLT; ++l) {  // q, k natural
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
     *(uint4*)(sQ + r * PN + sv * EPV) = rQ[l];
-    *(uint4*)(sK + r * PN + sv * EPV) = rK[l];
+    *(u32x4*)(sK + r * PN + sv * EPV) = rK[l];
   }
   __syncthreads();
 
@@ -467,14 +463,6 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const float* Gi = sG + ic * PG;  // G of channel ic, by row
   const int n0 = 16 * w;           // first key channel of this wave
   const float gT = Gi[63];
-  float tg[4][4];  // g_raw at this lane's C positions, for the epilogue (prefetched)
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = rt * 16 + g4 * 4 + j;
-      tg[rt][j] = r < Lr ? grh[r * rs + ic] : 0.f;
-    }
   // (1) diagonal blocks: lane -> block g4 of channel ic (dec[s] = e^{G_r - G_s}).  x1_r = sum_{s<=r} dMqk_rs
   //     k_s e^{G_r-G_s}, x2_r = the same with dL, z_s = sum_{r>=s} (dMqk_rs q_r +
   //     beta_r dL_rs k_r) e^{G_r-G_s}; all rows and columns inside the block.
@@ -663,7 +651,11 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   dkr_col += __shfl_xor(dkr_col, 16);
   dkr_col += __shfl_xor(dkr_col, 32);
   if (g4 == 3) dG[3][3] += dkr_col + ex2(gT) * pp;
-  // reverse cumsum over r = 16 rt + 4 g4 + j; dG becomes dg_raw
+  // reverse cumsum over r = 16 rt + 4 g4 + j; dG becomes dg_raw.  The gate's own
+  // derivative comes from the cumulative gate: with d = G_r - G_{r-1} = g_r log2(e),
+  // softplus(g_raw) = -g_r / e^{A_log} and sigmoid(g_raw) = 1 - e^{-softplus}, so
+  // dg_raw = dg . e^{A_log} (2^{d / e^{A_log}} - 1) and the dA_log term is dg . d ln 2.
+  const float inv_aA = 1.f / aA;
   float carry = 0.f;
 #pragma unroll
   for (int rt = 3; rt >= 0; --rt) {
@@ -675,14 +667,20 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     if (g4 < 2) run += t2;
     if (g4 < 1) run += t1;
     carry += t0v + t1 + t2 + t3;
+    float gq[5];  // G at rows rb - 1 .. rb + 3 of this lane (rb = 16 rt + 4 g4)
+    {
+      const int rb = rt * 16 + g4 * 4;
+      const f4 t = *(const f4*)(Gi + rb);
+      gq[0] = rb > 0 ? Gi[rb - 1] : 0.f;
+      gq[1] = t[0]; gq[2] = t[1]; gq[3] = t[2]; gq[4] = t[3];
+    }
 #pragma unroll
     for (int j = 3; j >= 0; --j) {
       run += dG[rt][j];
       const int r = rt * 16 + g4 * 4 + j;
-      float sp, sg;
-      softplus_sigmoid(tg[rt][j], sp, sg);
-      dG[rt][j] = run * (-aA * sg);
-      if (r < Lr) dal += run * (-aA * sp);
+      const float d = gq[j + 1] - gq[j];
+      dG[rt][j] = run * (aA * (ex2(d * inv_aA) - 1.f));
+      if (r < Lr) dal += run * (d * 0.69314718055994531f);
     }
   }
   // dbeta second part, reduced over this wave's channels
