@@ -99,8 +99,10 @@ __global__ __launch_bounds__(4 * D) void k_scanw(
       }
   }
 
-  Frag ta[RTW][NKD], pa[RTW][NKC];
-  f4 eg[RTW];
+  // Operands of one chunk: Tm and PT rows (A fragments), exp(G_T) of this lane's
+  // rows, and the chunk's dO tile (16-byte vectors, stored to LDS one step later).
+  // Two sets alternate so that the loads for the next chunk, issued before this
+  // chunk's products, are first waited on in the next step.
   auto load_a = [&](int cgl, Frag (&A)[RTW][NKD], Frag (&P)[RTW][NKC], f4 (&E)[RTW]) {
     const size_t ch = (size_t)cgl * H + h;
 #pragma unroll
@@ -108,47 +110,46 @@ __global__ __launch_bounds__(4 * D) void k_scanw(
       const int i = (rgp * RTW + rt) * 16 + cl;
 #pragma unroll
       for (int kk = 0; kk < NKD; ++kk) A[rt][kk] = MM::ld_perm(Tm + ch * DD + (size_t)i * D, kk * KS, lane);
+      if (!trans) {
 #pragma unroll
-      for (int kk = 0; kk < NKC; ++kk) P[rt][kk] = MM::ld_perm(PT + ch * D * 64 + (size_t)i * 64, kk * KS, lane);
+        for (int kk = 0; kk < NKC; ++kk) P[rt][kk] = MM::ld_perm(PT + ch * D * 64 + (size_t)i * 64, kk * KS, lane);
+      }
       E[rt] = *(const f4*)(eGT + ch * D + (rgp * RTW + rt) * 16 + 4 * g4);
     }
   };
-  uint4 rdo[NLO];
-  auto load_do = [&](int cgl) {
+  auto load_do = [&](int cgl, u32x4 (&R)[NLO]) {
     const ChunkInfo ci = chunks[cgl];
 #pragma unroll
     for (int l = 0; l < NLO; ++l) {
       const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
-      uint4 x = {0u, 0u, 0u, 0u};
-      if (r < ci.len && !trans) x = *(const uint4*)(dO + ((size_t)(ci.t0 + r) * H + h) * D + vv * EPV);
-      rdo[l] = x;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r < ci.len && !trans) x = *(const u32x4*)(dO + ((size_t)(ci.t0 + r) * H + h) * D + vv * EPV);
+      R[l] = x;
     }
   };
-  auto store_do = [&](T* dst) {
-#pragma unroll
-    for (int l = 0; l < NLO; ++l) {
-      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
-      *(uint4*)(dst + r * PO + vv * EPV) = rdo[l];
-    }
-  };
-
-  if (gi.cnt > 0) {
-    load_a(gi.c0 + gi.cnt - 1, ta, pa, eg);
-    load_do(gi.c0 + gi.cnt - 1);
-    store_do(sO0);
-  }
-  int sb = 0, ob = 0;
-  for (int cc = gi.cnt - 1; cc >= 0; --cc) {
+  // One chunk, last to first: issue the next chunk's loads, publish the state (and
+  // this chunk's dO tile), store dS_out, then dS <- exp(G_T) . dS + Tm dS + PT dO.
+  auto step = [&](int cc, Frag (&ta)[RTW][NKD], Frag (&pa)[RTW][NKC], f4 (&eg)[RTW],
+                  u32x4 (&ro)[NLO], Frag (&tn)[RTW][NKD], Frag (&pn)[RTW][NKC], f4 (&en)[RTW],
+                  u32x4 (&rn)[NLO]) {
     const int cgl = gi.c0 + cc;
     const size_t ch = (size_t)cgl * H + h;
-    T* sS = sS0 + sb * (PS * D);
-    const T* sO = sO0 + ob * (PO * 64);
-    // the state at the end of this chunk, as a natural act-dtype tile
+    T* sS = sS0 + (cc & 1) * (PS * D);
+    T* sO = sO0 + (cc & 1) * (PO * 64);
+    if (cc > 0) {  // the next chunk's operands, into the set the previous step used
+      load_a(cgl - 1, tn, pn, en);
+      load_do(cgl - 1, rn);
+    }
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
       for (int ct = 0; ct < CTW; ++ct)
         store_c<T>(sS, PS, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, acc[rt][ct], lane);
+#pragma unroll
+    for (int l = 0; l < NLO; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      *(u32x4*)(sO + r * PO + vv * EPV) = ro[l];
+    }
     __syncthreads();
     if constexpr (!PQ) {  // dS_out of this chunk, 16-byte rows
       T* dst = dstates + ch * DD;
@@ -158,13 +159,6 @@ __global__ __launch_bounds__(4 * D) void k_scanw(
         *(uint4*)(dst + (size_t)r * D + vv * EPV) = *(const uint4*)(sS + r * PS + vv * EPV);
       }
     }
-    Frag tn[RTW][NKD], pn[RTW][NKC];
-    f4 en[RTW];
-    if (cc > 0) {
-      load_a(cgl - 1, tn, pn, en);
-      load_do(cgl - 1);
-    }
-    // dS <- exp(G_T) . dS + Tm dS + PT dO
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -191,20 +185,20 @@ __global__ __launch_bounds__(4 * D) void k_scanw(
         }
       }
     }
-    if (cc > 0) {
-      store_do(sO0 + (ob ^ 1) * (PO * 64));
-#pragma unroll
-      for (int rt = 0; rt < RTW; ++rt) {
-#pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) ta[rt][kk] = tn[rt][kk];
-#pragma unroll
-        for (int kk = 0; kk < NKC; ++kk) pa[rt][kk] = pn[rt][kk];
-        eg[rt] = en[rt];
-      }
-    }
-    sb ^= 1;
-    ob ^= 1;
+  };
+  Frag ta0[RTW][NKD], pa0[RTW][NKC], ta1[RTW][NKD], pa1[RTW][NKC];
+  f4 eg0[RTW], eg1[RTW];
+  u32x4 ro0[NLO], ro1[NLO];
+  int cc = gi.cnt - 1;
+  if (cc >= 0) {
+    load_a(gi.c0 + cc, ta0, pa0, eg0);
+    load_do(gi.c0 + cc, ro0);
   }
+  for (; cc >= 1; cc -= 2) {
+    step(cc, ta0, pa0, eg0, ro0, ta1, pa1, eg1, ro1);
+    step(cc - 1, ta1, pa1, eg1, ro1, ta0, pa0, eg0, ro0);
+  }
+  if (cc == 0) step(0, ta0, pa0, eg0, ro0, ta1, pa1, eg1, ro1);
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
