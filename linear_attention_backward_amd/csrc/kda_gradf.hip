@@ -31,13 +31,6 @@
 
 namespace kda {
 
-__device__ __forceinline__ void softplus_sigmoid(float x, float& sp, float& sg) {
-  const float e = __expf(-fabsf(x));
-  sp = fmaxf(x, 0.f) + __logf(1.f + e);
-  const float r = __builtin_amdgcn_rcpf(1.f + e);
-  sg = x >= 0.f ? r : e * r;
-}
-
 template <typename T, int D> struct GF {
   static constexpr int NW = D / 16;  // waves
   static constexpr int NT = NW * 64;
@@ -176,7 +169,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int r = part * 16 + rr;
-      rg[rr] = r < Lr ? grh[r * rs + i] : 0.f;
+      rg[rr] = grh[(r < Lr ? r : Lr - 1) * rs + i];  // rows past the chunk: masked below
     }
   }
   const float rbeta = tid < Lr ? beta[(t0 + (tid & 63)) * H + h] : 0.f;
@@ -201,12 +194,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = 4 * qq + j;
-        float gg = 0.f;
-        if (part * 16 + rr < Lr) {
-          float sp, sg;
-          softplus_sigmoid(rg[rr], sp, sg);
-          gg = -aA * sp;
-        }
+        const float e = __expf(-fabsf(rg[rr]));
+        const float sp = fmaxf(rg[rr], 0.f) + __logf(1.f + e);  // softplus
+        const float gg = part * 16 + rr < Lr ? -aA * sp : 0.f;
         run += gg * LOG2E;
         x[j] = run;
       }

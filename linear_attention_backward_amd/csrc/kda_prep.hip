@@ -107,7 +107,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int r = part * 16 + rr;
-      rg[rr] = r < Lr ? gh[r * rs] : 0.f;
+      rg[rr] = gh[(r < Lr ? r : Lr - 1) * rs];  // rows past the chunk: masked below
     }
   }
   const float rbeta = tid < Lr ? beta[(size_t)(t0 + (tid & 63)) * H + h] : 0.f;
@@ -135,7 +135,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int r = part * 16 + rr;
-      const float g = r < Lr ? -aA * softplus_p(rg[rr]) : 0.f;
+      const float gv = -aA * softplus_p(rg[rr]);
+      const float g = r < Lr ? gv : 0.f;
       run += g * LOG2E;
       sG[r * PGN + i] = run;
     }
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
           float kb[KPL];
 #pragma unroll
           for (int j = 0; j < KPL; ++j)
-            kb[j] = colok ? ks[j] * ex2(sG[a * PGN + i0 + j] - gs[j]) : 0.f;
+            kb[j] = (colok ? ks[j] : 0.f) * ex2(fminf(sG[a * PGN + i0 + j] - gs[j], 0.f));
           const Frag KB = MM::from_vals(kb);
           const bool rowok = rho_l == rho;
           dA = MM::mma(rowok ? KF : ZF, KB, dA);
