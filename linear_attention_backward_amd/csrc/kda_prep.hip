@@ -284,12 +284,22 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
             qq4[t] = to_f(sQ[r * PN + i]);
             gg4[t] = sG[r * PGN + i];
           }
+          // pairwise decays inside the sub-block from the per-token factors
+          const float a1 = ex2(gg4[1] - gg4[0]), a2 = ex2(gg4[2] - gg4[1]), a3 = ex2(gg4[3] - gg4[2]);
+          float dec[4][4];
+          dec[0][0] = dec[1][1] = dec[2][2] = dec[3][3] = 1.f;
+          dec[1][0] = a1;
+          dec[2][1] = a2;
+          dec[2][0] = a1 * a2;
+          dec[3][2] = a3;
+          dec[3][1] = a2 * a3;
+          dec[3][0] = dec[2][0] * a3;
 #pragma unroll
           for (int a_ = 0; a_ < 4; ++a_)
 #pragma unroll
             for (int b_ = 0; b_ <= a_; ++b_) {
               const int p = a_ * (a_ + 1) / 2 + b_;
-              const float kb = kk4[b_] * ex2(gg4[a_] - gg4[b_]);
+              const float kb = kk4[b_] * dec[a_][b_];
               pa[p] += kk4[a_] * kb;
               pm[p] += qq4[a_] * kb;
             }
