@@ -89,6 +89,19 @@ template <> struct Mma<bf16> {
     const bf16x4 hi = ld_tr4(tile, pitch, kb + 16 + 4 * G, n0, lane);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+  // Natural contraction order (lane group G holds k = kb + 8G + j): a fragment of a
+  // row with contiguous k is one 16-byte load, and the matching fragment of a
+  // row-major [k][n] LDS tile two transposing reads of 4 rows each.
+  __device__ static __forceinline__ Frag ld_tr_nat(const bf16* tile, int pitch, int kb, int n0,
+                                                   int lane) {
+    const int G = lane >> 4;
+    const bf16x4 lo = ld_tr4(tile, pitch, kb + 8 * G, n0, lane);
+    const bf16x4 hi = ld_tr4(tile, pitch, kb + 8 * G + 4, n0, lane);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  __device__ static __forceinline__ Frag ld_nat(const bf16* row, int kb, int lane) {
+    return *(const bf16x8*)(row + kb + 8 * (lane >> 4));
+  }
   // fragment of a row with contiguous k (any memory), permuted order
   __device__ static __forceinline__ Frag ld_perm(const bf16* row, int kb, int lane) {
     const int G = lane >> 4;
@@ -157,6 +170,13 @@ template <> struct Mma<float> {
   }
   __device__ static __forceinline__ Frag ld_perm(const float* row, int kb, int lane) {
     return row[kb + (lane >> 4)];
+  }
+  __device__ static __forceinline__ Frag ld_tr_nat(const float* tile, int pitch, int kb, int n0,
+                                                   int lane) {
+    return ld_tr(tile, pitch, kb, n0, lane);
+  }
+  __device__ static __forceinline__ Frag ld_nat(const float* row, int kb, int lane) {
+    return ld_perm(row, kb, lane);
   }
   __device__ static __forceinline__ Frag ld_perm_f32(const float* row, int kb, int lane) {
     return row[kb + (lane >> 4)];

@@ -11,8 +11,8 @@
 // One workgroup carries the whole K x V state of a (chunk group, head) in fp32
 // MFMA accumulators and reads each chunk's Tm, PT, exp(G_T) and dO once.  The
 // state goes through LDS as a natural bf16 tile, read back transposed as the B
-// operand; Tm and PT rows are A fragments in the same permuted contraction order,
-// read straight from global memory one chunk ahead.
+// operand; Tm and PT rows are A fragments in the natural contraction order (one
+// 16-byte load per lane), read straight from global memory one chunk ahead.
 //
 // Long sequences are split into groups of gs chunks and scanned in three passes
 // (the pages name context parallelism as the lever for long contexts; here the
@@ -109,10 +109,10 @@ __global__ __launch_bounds__(4 * D) void k_scanw(
     for (int rt = 0; rt < RTW; ++rt) {
       const int i = (rgp * RTW + rt) * 16 + cl;
 #pragma unroll
-      for (int kk = 0; kk < NKD; ++kk) A[rt][kk] = MM::ld_perm(Tm + ch * DD + (size_t)i * D, kk * KS, lane);
+      for (int kk = 0; kk < NKD; ++kk) A[rt][kk] = MM::ld_nat(Tm + ch * DD + (size_t)i * D, kk * KS, lane);
       if (!trans) {
 #pragma unroll
-        for (int kk = 0; kk < NKC; ++kk) P[rt][kk] = MM::ld_perm(PT + ch * D * 64 + (size_t)i * 64, kk * KS, lane);
+        for (int kk = 0; kk < NKC; ++kk) P[rt][kk] = MM::ld_nat(PT + ch * D * 64 + (size_t)i * 64, kk * KS, lane);
       }
       E[rt] = *(const f4*)(eGT + ch * D + (rgp * RTW + rt) * 16 + 4 * g4);
     }
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(4 * D) void k_scanw(
     for (int kk = 0; kk < NKD; ++kk) {
 #pragma unroll
       for (int ct = 0; ct < CTW; ++ct) {
-        const Frag b = MM::ld_tr(sS, PS, kk * KS, (cgp * CTW + ct) * 16, lane);
+        const Frag b = MM::ld_tr_nat(sS, PS, kk * KS, (cgp * CTW + ct) * 16, lane);
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt) acc[rt][ct] = MM::mma(ta[rt][kk], b, acc[rt][ct]);
       }
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(4 * D) void k_scanw(
       for (int kk = 0; kk < NKC; ++kk) {
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
-          const Frag b = MM::ld_tr(sO, PO, kk * KS, (cgp * CTW + ct) * 16, lane);
+          const Frag b = MM::ld_tr_nat(sO, PO, kk * KS, (cgp * CTW + ct) * 16, lane);
 #pragma unroll
           for (int rt = 0; rt < RTW; ++rt) acc[rt][ct] = MM::mma(pa[rt][kk], b, acc[rt][ct]);
         }
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(4 * D) void k_scan_bnd(const GroupInfo* __restrict_
       const int i = (rgp * RTW + rt) * 16 + cl;
       Frag a[NKD];
 #pragma unroll
-      for (int kk = 0; kk < NKD; ++kk) a[kk] = MM::ld_perm(Pg + gh * DD + (size_t)i * D, kk * KS, lane);
+      for (int kk = 0; kk < NKD; ++kk) a[kk] = MM::ld_nat(Pg + gh * DD + (size_t)i * D, kk * KS, lane);
 #pragma unroll
       for (int ct = 0; ct < CTW; ++ct) {
         const int i0 = (rgp * RTW + rt) * 16 + 4 * g4;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(4 * D) void k_scan_bnd(const GroupInfo* __restrict_
         for (int j = 0; j < 4; ++j) x[j] = Qg[gh * DD + (size_t)(i0 + j) * D + col];
 #pragma unroll
         for (int kk = 0; kk < NKD; ++kk)
-          x = MM::mma(a[kk], MM::ld_tr(sS, PS, kk * KS, (cgp * CTW + ct) * 16, lane), x);
+          x = MM::mma(a[kk], MM::ld_tr_nat(sS, PS, kk * KS, (cgp * CTW + ct) * 16, lane), x);
         acc[rt][ct] = x;
       }
     }
