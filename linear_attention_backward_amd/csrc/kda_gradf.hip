@@ -163,14 +163,14 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   // What the gate and the first product need is issued first; dS_out and the
   // INV / Mqk rows follow once the gate is formed (they are first used after Y), so
   // their transfer overlaps the gate, the LDS fills and the Y product.
-  float rg[16];  // g_raw of this thread's channel, 16 rows
-  {
-    const int i = tid % D, part = tid / D;  // NT / D == 4 parts of 16 rows
+  // gate layout: lane (g4, cl) of wave w owns key channel 16 w + cl, rows 16 g4 .. + 15,
+  // so that the four row parts of a channel sit in one wave
+  const int gch = 16 * w + cl;
+  float rg[16];  // g_raw of this lane's channel, 16 rows
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int r = part * 16 + rr;
-      rg[rr] = grh[(r < Lr ? r : Lr - 1) * rs + i];  // rows past the chunk: masked below
-    }
+  for (int rr = 0; rr < 16; ++rr) {
+    const int r = g4 * 16 + rr;
+    rg[rr] = grh[(r < Lr ? r : Lr - 1) * rs + gch];  // rows past the chunk: masked below
   }
   const float rbeta = tid < Lr ? beta[(t0 + (tid & 63)) * H + h] : 0.f;
   // S_in, dO and v straight into their LDS tiles (natural, padded rows)
@@ -185,23 +185,24 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const int arow = 16 * R1 + cl;            // A-operand row of this lane
   const int crow = 16 * R1 + g4 * 4;        // first C row of this lane
   if (tid < 64) sBeta[tid] = rbeta;
-  {  // in-chunk cumulative gate (log2 units), channel-major: sG[i][r]
-    const int i = tid % D, part = tid / D;
+  {  // in-chunk cumulative gate (log2 units), channel-major: sG[i][r]; the sums of
+     // the earlier row parts come from the lanes that hold them (same wave)
+    float x[16];
     float run = 0.f;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      f4 x;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = 4 * qq + j;
-        const float e = __expf(-fabsf(rg[rr]));
-        const float sp = fmaxf(rg[rr], 0.f) + __logf(1.f + e);  // softplus
-        const float gg = part * 16 + rr < Lr ? -aA * sp : 0.f;
-        run += gg * LOG2E;
-        x[j] = run;
-      }
-      *(f4*)(sG + i * PG + part * 16 + 4 * qq) = x;
+    for (int rr = 0; rr < 16; ++rr) {
+      const float e = __expf(-fabsf(rg[rr]));
+      const float sp = fmaxf(rg[rr], 0.f) + __logf(1.f + e);  // softplus
+      const float gg = g4 * 16 + rr < Lr ? -aA * sp : 0.f;
+      run += gg * LOG2E;
+      x[rr] = run;
     }
+    const float t0p = __shfl(run, cl), t1p = __shfl(run, cl + 16), t2p = __shfl(run, cl + 32);
+    const float add = (g4 > 0 ? t0p : 0.f) + (g4 > 1 ? t1p : 0.f) + (g4 > 2 ? t2p : 0.f);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      *(f4*)(sG + gch * PG + g4 * 16 + 4 * qq) =
+          f4{x[4 * qq] + add, x[4 * qq + 1] + add, x[4 * qq + 2] + add, x[4 * qq + 3] + add};
   }
   wait_vmem();
   __syncthreads();
@@ -215,22 +216,6 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     fMT[ks] = MM::ld_perm(MqkT + ch * 4096 + arow * 64, ks * KS, lane);
     fIT[ks] = MM::load(INVT + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
   }
-  {
-    const int i = tid % D, part = tid / D;
-    float add = 0.f;
-    for (int pp = 0; pp < part; ++pp) add += sG[i * PG + pp * 16 + 15];
-    __syncthreads();
-    if (part > 0) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        f4* p = (f4*)(sG + i * PG + part * 16 + 4 * qq);
-        f4 x = *p;
-        x[0] += add; x[1] += add; x[2] += add; x[3] += add;
-        *p = x;
-      }
-    }
-  }
-  __syncthreads();
 
   // ------------------------------------------------------------- state side
   // decayed key rows of this lane: Kd = K e^G (for Y), Kr = K e^{G_T - G} (for dU)
