@@ -5,6 +5,7 @@
 #include <cstdlib>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -171,6 +172,40 @@ int hip_fail(hipError_t e) {
 }
 
 }  // namespace
+
+namespace kda {
+
+hipError_t resident_blocks(const void* kernel, int threads, int* out) {
+  struct Entry {
+    int dev;
+    const void* fn;
+    int threads, blocks;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    for (const Entry& x : cache)
+      if (x.dev == dev && x.fn == kernel && x.threads == threads) {
+        *out = x.blocks;
+        return hipSuccess;
+      }
+  }
+  int ncu = 0, per = 0;
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0);
+  if (e != hipSuccess) return e;
+  const int blocks = std::max(1, ncu * per);
+  std::lock_guard<std::mutex> lk(mu);
+  cache.push_back({dev, kernel, threads, blocks});
+  *out = blocks;
+  return hipSuccess;
+}
+
+}  // namespace kda
 
 extern "C" {
 

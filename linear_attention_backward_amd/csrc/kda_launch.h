@@ -48,6 +48,10 @@ hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, con
                           const void* v, const float* g_raw, const float* beta,
                           const float* A_log, const float* h0, void* o, float* ht,
                           void* h_saved, hipStream_t st);
+// Workgroups of `kernel` (block of `threads`) that the current device holds at
+// once: CU count times the per-CU occupancy; cached per device and kernel.
+hipError_t resident_blocks(const void* kernel, int threads, int* out);
+
 hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st);

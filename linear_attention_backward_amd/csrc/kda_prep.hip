@@ -54,7 +54,7 @@ template <typename T, int D> struct PL {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ chunks, int H,
+__global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ chunks, int NC, int H,
                                                 const T* __restrict__ q, const T* __restrict__ k,
                                                 const float* __restrict__ g_raw,
                                                 const float* __restrict__ beta,
@@ -89,44 +89,53 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   T* sTm = (T*)(smem + L::TMS_OFF);
   T* sPT = (T*)(smem + L::PTS_OFF);
 
-  const int c = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g4 = lane >> 4, cl = lane & 15;
-  const ChunkInfo ci = chunks[c];
-  const int t0 = ci.t0, Lr = ci.len;
-  const size_t ch = (size_t)c * H + h;
   const size_t rs = (size_t)H * D;
-  const size_t hD = (size_t)h * D;
+  const int items = NC * H;
+  const int tid0 = threadIdx.x;
 
-  // ---- loads (all issued before first use): g_raw, beta, q, k; rows beyond the
-  // chunk are zero
-  float rg[16];
-  {
-    const float* gh = g_raw + (size_t)t0 * rs + hD + tid % D;
-    const int part = tid / D;  // 4 parts of 16 rows
+  // Persistent: one workgroup fills a CU's LDS, so each workgroup walks the
+  // (chunk, head) items with stride gridDim.x and holds the next item's g_raw,
+  // beta, q and k in registers while it works on the current one. Rows beyond
+  // the chunk are zero (q, k) or masked at the cumsum (g_raw).
+  float rg[16], rbeta;
+  uint4 rq[NLT], rk[NLT];
+  auto issue_loads = [&](int it) {
+    const int c = it % NC, h = it / NC;
+    const ChunkInfo ci = chunks[c];
+    const size_t hD = (size_t)h * D;
+    const float* gh = g_raw + (size_t)ci.t0 * rs + hD + tid0 % D;
+    const int part = tid0 / D;  // 4 parts of 16 rows
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int r = part * 16 + rr;
-      rg[rr] = gh[(r < Lr ? r : Lr - 1) * rs];  // rows past the chunk: masked below
+      rg[rr] = gh[(r < ci.len ? r : ci.len - 1) * rs];
     }
-  }
-  const float rbeta = tid < Lr ? beta[(size_t)(t0 + (tid & 63)) * H + h] : 0.f;
-  uint4 rq[NLT], rk[NLT];
-  {
-    const T* qh = q + (size_t)t0 * rs + hD;
-    const T* kh = k + (size_t)t0 * rs + hD;
+    rbeta = tid0 < ci.len ? beta[(size_t)(ci.t0 + (tid0 & 63)) * H + h] : 0.f;
+    const T* qh = q + (size_t)ci.t0 * rs + hD;
+    const T* kh = k + (size_t)ci.t0 * rs + hD;
 #pragma unroll
     for (int l = 0; l < NLT; ++l) {
-      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      const int idx = tid0 + l * NT, r = idx / VPR, vv = idx % VPR;
       uint4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
-      if (r < Lr) {
+      if (r < ci.len) {
         xq = *(const uint4*)(qh + r * rs + vv * EPV);
         xk = *(const uint4*)(kh + r * rs + vv * EPV);
       }
       rq[l] = xq;
       rk[l] = xk;
     }
-  }
+  };
+  if ((int)blockIdx.x < items) issue_loads(blockIdx.x);
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+  // thread indices re-derived per item so that the lane-dependent LDS addresses
+  // below stay inside the loop instead of being held in registers across it
+  int tid = tid0;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, cl = lane & 15;
+  const int c = it % NC, h = it / NC;
+  const int Lr = chunks[c].len;
+  const size_t ch = (size_t)c * H + h;
   const float aA = __expf(A_log[h]);
   if (tid < 64) sBeta[tid] = rbeta;
   {  // in-chunk cumulative gate (log2 units), natural: sG[r][i]
@@ -147,6 +156,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     *(uint4*)(sQ + r * PN + vv * EPV) = rq[l];
     *(uint4*)(sK + r * PN + vv * EPV) = rk[l];
   }
+  if (it + (int)gridDim.x < items) issue_loads(it + gridDim.x);
   __syncthreads();
   {
     const int i = tid % D, part = tid / D;
@@ -511,12 +521,18 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       *(uint4*)(dp + r * 64 + vv * EPV) = *(const uint4*)(sPT + r * PPT + vv * EPV);
     }
   }
+  // the next item writes sG, sQ, sK and sBeta only: no reader of those is left
+  }
 }
 
 template <typename T, int D>
 static hipError_t prep_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
-  dim3 grid((unsigned)s.NC, (unsigned)s.H);
-  hipLaunchKernelGGL((k_prep<T, D>), grid, dim3(PL<T, D>::NT), 0, st, p.chunks, s.H, (const T*)p.q,
+  const int items = s.NC * s.H;
+  int resident = 0;
+  hipError_t e = resident_blocks((const void*)k_prep<T, D>, PL<T, D>::NT, &resident);
+  if (e != hipSuccess) return e;
+  const int grid = items < resident ? items : resident;
+  hipLaunchKernelGGL((k_prep<T, D>), dim3(grid), dim3(PL<T, D>::NT), 0, st, p.chunks, s.NC, s.H, (const T*)p.q,
                      (const T*)p.k, p.g_raw, p.beta, p.A_log, (T*)p.Tm, (T*)p.PT, p.eGT,
                      (T*)p.INV, (T*)p.INVT, (T*)p.MqkT);
   return hipGetLastError();
