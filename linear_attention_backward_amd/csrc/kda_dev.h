@@ -393,6 +393,15 @@ __device__ __forceinline__ void store_ct<float>(float* base, int pitch, int row0
 // beyond `valid` are zero-filled with ordinary LDS stores instead.  The caller
 // waits for vmcnt(0) and synchronises before the tile is read.
 typedef __attribute__((address_space(3))) void lds_void;
+// One 16-byte global -> LDS copy per active lane: lane l writes LDS bytes
+// [lds + 16 l, lds + 16 l + 16) (lds: a wave-uniform LDS byte address, via M0).
+// Issued as inline asm so that the compiler does not hold every later LDS access
+// of the wave until the copy lands: a reader of the destination calls wait_vmem()
+// and then a workgroup barrier. The kernels that use it set M0 nowhere else.
+__device__ __forceinline__ void g2l16(const void* g, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory");
+}
 template <typename T, int D, int ROWS, int NW>
 __device__ __forceinline__ void g2l_tile(T* lds_tile, const T* src, size_t rs, int valid, int w,
                                          int lane) {
@@ -410,8 +419,8 @@ __device__ __forceinline__ void g2l_tile(T* lds_tile, const T* src, size_t rs, i
       if (p < NG) {
         if (row < valid) {
           const T* g = src + (size_t)row * rs + (gc < GPR ? gc : GPR - 1) * EPG;
-          __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)((char*)lds_tile + base * 16),
-                                           16, 0, 0);
+          g2l16(g, __builtin_amdgcn_readfirstlane(
+                       (unsigned)(uintptr_t)(lds_void*)((char*)lds_tile + base * 16)));
         } else {
           *(uint4*)((char*)lds_tile + p * 16) = uint4{0u, 0u, 0u, 0u};
         }

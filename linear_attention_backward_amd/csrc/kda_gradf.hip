@@ -80,7 +80,7 @@ template <typename T, int D> struct GF {
 
 template <typename T, int D>
 __global__ __launch_bounds__(4 * D) void k_gradf(
-    const ChunkInfo* __restrict__ chunks, int H, const T* __restrict__ q,
+    const ChunkInfo* __restrict__ chunks, int NC, int H, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
     const float* __restrict__ g_raw, const float* __restrict__ beta,
     const float* __restrict__ A_log, const T* __restrict__ h_saved,
@@ -140,46 +140,69 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     DGB = 16 * PC + 16;
   }
 
-  const int c = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const size_t DD = (size_t)D * D;
+  const size_t rs = (size_t)H * D;  // token stride of per-token tensors
+  const int items = NC * H;
+  const int tid0 = threadIdx.x;
+  // k for the intra-chunk phase goes through the dvcorr tile (unused until the
+  // state side's last product)
+  T* sK0 = sDVC;
+
+  // ------------------------------------------------------------------ loads
+  // Persistent: one workgroup fills a CU's LDS, so each workgroup walks the
+  // (chunk, head) items with stride gridDim.x and issues the next item's loads
+  // while it finishes the current one: g_raw and beta into registers and dO, v, k
+  // straight into their LDS tiles once the intra-chunk phase is done with those
+  // regions, S_in once the dq / dk staging over its tile has been read out.
+  // gate layout: lane (g4, cl) of wave w owns key channel 16 w + cl, rows 16 g4 .. + 15,
+  // so that the four row parts of a channel sit in one wave
+  float rg[16];  // g_raw of this lane's channel, 16 rows (rows past the chunk: masked later)
+  float rbeta;
+  // (t: this thread's index, passed in so that the address arithmetic is redone per
+  // item rather than held across the loop)
+  auto issue_front = [&](int it, int t) {
+    const int c = it % NC, h = it / NC;
+    const ChunkInfo ci = chunks[c];
+    const size_t base = (size_t)ci.t0 * rs + (size_t)h * D;
+    const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const float* grh = g_raw + base + 16 * w + (lane & 15);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = (lane >> 4) * 16 + rr;
+      rg[rr] = grh[(r < ci.len ? r : ci.len - 1) * rs];
+    }
+    rbeta = t < ci.len ? beta[((size_t)ci.t0 + lane) * H + h] : 0.f;
+    g2l_tile<T, D, 64, NW>(sO, dO + base, rs, ci.len, w, lane);
+    g2l_tile<T, D, 64, NW>(sV, v + base, rs, ci.len, w, lane);
+    g2l_tile<T, D, 64, NW>(sK0, k + base, rs, ci.len, w, lane);
+  };
+  auto issue_state = [&](int it, int t) {
+    const size_t ch = (size_t)(it % NC) * H + it / NC;
+    g2l_tile<T, D, D, NW>(sS, h_saved + ch * DD, D, D, __builtin_amdgcn_readfirstlane(t >> 6),
+                          t & 63);
+  };
+  if ((int)blockIdx.x < items) {
+    issue_front(blockIdx.x, tid0);
+    issue_state(blockIdx.x, tid0);
+  }
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+  // thread indices re-derived per item so that the lane-dependent LDS addresses
+  // below stay inside the loop instead of being held in registers across it
+  int tid = tid0;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, cl = lane & 15;
+  const int c = it % NC, h = it / NC;
+  const int nxt = it + (int)gridDim.x;
   const ChunkInfo ci = chunks[c];
   const size_t t0 = ci.t0;
   const int Lr = ci.len;
   const size_t ch = (size_t)c * H + h;
-  const size_t DD = (size_t)D * D;
-  const size_t rs = (size_t)H * D;  // token stride of per-token tensors
   const size_t hD = (size_t)h * D;
   const T* qh = q + t0 * rs + hD;
-  const T* kh = k + t0 * rs + hD;
-  const T* vh = v + t0 * rs + hD;
-  const T* oh = dO + t0 * rs + hD;
-  const float* grh = g_raw + t0 * rs + hD;
-  const T* Sin = h_saved + ch * DD;
   const T* dSo = dstates + ch * DD;
   const float aA = __expf(A_log[h]);
-
-  // ------------------------------------------------------------------ loads
-  // What the gate and the first product need is issued first; dS_out and the
-  // INV / Mqk rows follow once the gate is formed (they are first used after Y), so
-  // their transfer overlaps the gate, the LDS fills and the Y product.
-  // gate layout: lane (g4, cl) of wave w owns key channel 16 w + cl, rows 16 g4 .. + 15,
-  // so that the four row parts of a channel sit in one wave
   const int gch = 16 * w + cl;
-  float rg[16];  // g_raw of this lane's channel, 16 rows
-#pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    const int r = g4 * 16 + rr;
-    rg[rr] = grh[(r < Lr ? r : Lr - 1) * rs + gch];  // rows past the chunk: masked below
-  }
-  const float rbeta = tid < Lr ? beta[(t0 + (tid & 63)) * H + h] : 0.f;
-  // S_in, dO and v straight into their LDS tiles (natural, padded rows)
-  g2l_tile<T, D, D, NW>(sS, Sin, D, D, w, lane);
-  g2l_tile<T, D, 64, NW>(sO, oh, rs, Lr, w, lane);
-  g2l_tile<T, D, 64, NW>(sV, vh, rs, Lr, w, lane);
-  // k, once, over the dvcorr tile (unused until the state side's last product)
-  T* sK0 = sDVC;
-  g2l_tile<T, D, 64, NW>(sK0, kh, rs, Lr, w, lane);
   // state side: wave w owns the rows of block R1, value columns [64 half, +64)
   const int R1 = w / WPR, half = w % WPR;
   const int arow = 16 * R1 + cl;            // A-operand row of this lane
@@ -669,6 +692,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   dal = sum64(dal);
   if (lane == 0) sRed[w] = dal;
   __syncthreads();  // dq, dk staged; the gate tile is dead
+  if (nxt < items) issue_front(nxt, tid);  // dO, v, k regions: dead since the intra phase
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -697,17 +721,24 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     dAl_part[ch] = s;
   }
   __syncthreads();  // dg_raw staged
+  if (nxt < items) issue_state(nxt, tid);  // the dq / dk staging over the state tile is read out
 #pragma unroll
   for (int l = 0; l < NLR; ++l) {  // dg_raw out, 16-byte vectors
     const int idx = tid + l * NT, r = idx / (D / 4), sv = idx % (D / 4);
     if (r < Lr) *(f4*)(dg_raw + (t0 + r) * rs + hD + sv * 4) = *(const f4*)(sR + r * PR + sv * 4);
   }
+  __syncthreads();  // the gate tile (dg_raw staging) is read out before the next gate
+  }
 }
 
 template <typename T, int D>
 static hipError_t gradf_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
-  dim3 grid((unsigned)s.NC, (unsigned)s.H);
-  hipLaunchKernelGGL((k_gradf<T, D>), grid, dim3(GF<T, D>::NT), 0, st, p.chunks, s.H,
+  const int items = s.NC * s.H;
+  int resident = 0;
+  hipError_t e = resident_blocks((const void*)k_gradf<T, D>, GF<T, D>::NT, &resident);
+  if (e != hipSuccess) return e;
+  const int grid = items < resident ? items : resident;
+  hipLaunchKernelGGL((k_gradf<T, D>), dim3(grid), dim3(GF<T, D>::NT), 0, st, p.chunks, s.NC, s.H,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dO, p.g_raw,
                      p.beta, p.A_log, (const T*)p.h_saved, (const T*)p.dstates,
                      (const T*)p.INV, (const T*)p.INVT, (const T*)p.MqkT, (T*)p.dq, (T*)p.dk,

@@ -99,23 +99,23 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   // the chunk are zero (q, k) or masked at the cumsum (g_raw).
   float rg[16], rbeta;
   uint4 rq[NLT], rk[NLT];
-  auto issue_loads = [&](int it) {
+  auto issue_loads = [&](int it, int t) {
     const int c = it % NC, h = it / NC;
     const ChunkInfo ci = chunks[c];
     const size_t hD = (size_t)h * D;
-    const float* gh = g_raw + (size_t)ci.t0 * rs + hD + tid0 % D;
-    const int part = tid0 / D;  // 4 parts of 16 rows
+    const float* gh = g_raw + (size_t)ci.t0 * rs + hD + t % D;
+    const int part = t / D;  // 4 parts of 16 rows
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int r = part * 16 + rr;
       rg[rr] = gh[(r < ci.len ? r : ci.len - 1) * rs];
     }
-    rbeta = tid0 < ci.len ? beta[(size_t)(ci.t0 + (tid0 & 63)) * H + h] : 0.f;
+    rbeta = t < ci.len ? beta[(size_t)(ci.t0 + (t & 63)) * H + h] : 0.f;
     const T* qh = q + (size_t)ci.t0 * rs + hD;
     const T* kh = k + (size_t)ci.t0 * rs + hD;
 #pragma unroll
     for (int l = 0; l < NLT; ++l) {
-      const int idx = tid0 + l * NT, r = idx / VPR, vv = idx % VPR;
+      const int idx = t + l * NT, r = idx / VPR, vv = idx % VPR;
       uint4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
       if (r < ci.len) {
         xq = *(const uint4*)(qh + r * rs + vv * EPV);
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       rk[l] = xk;
     }
   };
-  if ((int)blockIdx.x < items) issue_loads(blockIdx.x);
+  if ((int)blockIdx.x < items) issue_loads(blockIdx.x, tid0);
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
   // thread indices re-derived per item so that the lane-dependent LDS addresses
   // below stay inside the loop instead of being held in registers across it
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     *(uint4*)(sQ + r * PN + vv * EPV) = rq[l];
     *(uint4*)(sK + r * PN + vv * EPV) = rk[l];
   }
-  if (it + (int)gridDim.x < items) issue_loads(it + gridDim.x);
+  if (it + (int)gridDim.x < items) issue_loads(it + gridDim.x, tid);
   __syncthreads();
   {
     const int i = tid % D, part = tid / D;
