@@ -431,6 +431,22 @@ __device__ __forceinline__ void g2l_tile(T* lds_tile, const T* src, size_t rs, i
 // Wait until this wave's global loads (including global -> LDS copies) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// Registers filled by loads issued well before their use (a prefetch for the next
+// work item): passing them through an empty asm makes the compiler wait for those
+// loads here, at a point chosen where they have landed and no stores are queued
+// behind them, instead of at the first use, where its wait would also cover every
+// store issued in between.
+__device__ __forceinline__ void settle(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void settle(u32x4& x) { asm volatile("" : "+v"(x)); }
+template <int N> __device__ __forceinline__ void settle(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) settle(x[i]);
+}
+template <int N> __device__ __forceinline__ void settle(u32x4 (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) settle(x[i]);
+}
+
 // DPP lane move inside a row of 16 lanes.
 template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,

@@ -185,6 +185,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     issue_front(blockIdx.x, tid0);
     issue_state(blockIdx.x, tid0);
   }
+  settle(rg);
+  settle(rbeta);
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
   // thread indices re-derived per item so that the lane-dependent LDS addresses
   // below stay inside the loop instead of being held in registers across it
@@ -363,20 +365,22 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       if (cl == 0) sDB1[half * 64 + crow + j] = s;
     }
   }
-  // q for the intra-chunk phase (registers now, LDS once its tile is free)
-  uint4 rQ[NLT];
+  // q for the intra-chunk phase (registers now, LDS once its tile is free); rows
+  // past the chunk read the last row and are zeroed when stored
+  u32x4 rQ[NLT];
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    uint4 xq = {0u, 0u, 0u, 0u};
-    if (r < Lr) xq = *(const uint4*)(qh + r * rs + sv * EPV);
-    rQ[l] = xq;
+    rQ[l] = *(const u32x4*)(qh + (size_t)(r < Lr ? r : Lr - 1) * rs + sv * EPV);
   }
   __syncthreads();  // dvcorr and dv staged
+  // Output copies: rows past the chunk store row Lr - 1 again (the same bytes as
+  // the lane that owns it), so that every lane issues the same stores.
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {  // dv out, 16-byte vectors
-    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    if (r < Lr) *(uint4*)(dv + (t0 + r) * rs + hD + sv * EPV) = *(const uint4*)(sDV + r * PN + sv * EPV);
+    const int idx = tid + l * NT, r0 = idx / VPR, sv = idx % VPR;
+    const int r = r0 < Lr ? r0 : Lr - 1;
+    *(u32x4*)(dv + (t0 + r) * rs + hD + sv * EPV) = *(const u32x4*)(sDV + r * PN + sv * EPV);
   }
 
   // --------------------------------------------------------------- key side
@@ -447,7 +451,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {  // q, k natural
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    *(uint4*)(sQ + r * PN + sv * EPV) = rQ[l];
+    *(u32x4*)(sQ + r * PN + sv * EPV) = rQ[l] & (r < Lr ? ~0u : 0u);
     *(u32x4*)(sK + r * PN + sv * EPV) = rK[l];
   }
   __syncthreads();
@@ -699,12 +703,11 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     for (int j = 0; j < 4; ++j) sR[(rt * 16 + g4 * 4 + j) * PR + ic] = dG[rt][j];
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {  // dq, dk out, 16-byte vectors
-    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    if (r < Lr) {
-      const size_t o = (t0 + r) * rs + hD + sv * EPV;
-      *(uint4*)(dq + o) = *(const uint4*)(sDQ + r * PN + sv * EPV);
-      *(uint4*)(dk + o) = *(const uint4*)(sDK + r * PN + sv * EPV);
-    }
+    const int idx = tid + l * NT, r0 = idx / VPR, sv = idx % VPR;
+    const int r = r0 < Lr ? r0 : Lr - 1;
+    const size_t o = (t0 + r) * rs + hD + sv * EPV;
+    *(u32x4*)(dq + o) = *(const u32x4*)(sDQ + r * PN + sv * EPV);
+    *(u32x4*)(dk + o) = *(const u32x4*)(sDK + r * PN + sv * EPV);
   }
   if (tid < 64 && tid < Lr) {
     float s = 0.f;
@@ -721,12 +724,15 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     dAl_part[ch] = s;
   }
   __syncthreads();  // dg_raw staged
-  if (nxt < items) issue_state(nxt, tid);  // the dq / dk staging over the state tile is read out
 #pragma unroll
   for (int l = 0; l < NLR; ++l) {  // dg_raw out, 16-byte vectors
-    const int idx = tid + l * NT, r = idx / (D / 4), sv = idx % (D / 4);
-    if (r < Lr) *(f4*)(dg_raw + (t0 + r) * rs + hD + sv * 4) = *(const f4*)(sR + r * PR + sv * 4);
+    const int idx = tid + l * NT, r0 = idx / (D / 4), sv = idx % (D / 4);
+    const int r = r0 < Lr ? r0 : Lr - 1;
+    *(f4*)(dg_raw + (t0 + r) * rs + hD + sv * 4) = *(const f4*)(sR + r * PR + sv * 4);
   }
+  // the dq / dk staging over the state tile is read out; issued after this item's
+  // last stores so that the next item's first wait on its registers skips it
+  if (nxt < items) issue_state(nxt, tid);
   __syncthreads();  // the gate tile (dg_raw staging) is read out before the next gate
   }
 }

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   // beta, q and k in registers while it works on the current one. Rows beyond
   // the chunk are zero (q, k) or masked at the cumsum (g_raw).
   float rg[16], rbeta;
-  uint4 rq[NLT], rk[NLT];
+  u32x4 rq[NLT], rk[NLT];
   auto issue_loads = [&](int it, int t) {
     const int c = it % NC, h = it / NC;
     const ChunkInfo ci = chunks[c];
@@ -114,18 +114,21 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     const T* qh = q + (size_t)ci.t0 * rs + hD;
     const T* kh = k + (size_t)ci.t0 * rs + hD;
 #pragma unroll
-    for (int l = 0; l < NLT; ++l) {
+    for (int l = 0; l < NLT; ++l) {  // rows past the chunk: zeroed when stored
       const int idx = t + l * NT, r = idx / VPR, vv = idx % VPR;
-      uint4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
-      if (r < ci.len) {
-        xq = *(const uint4*)(qh + r * rs + vv * EPV);
-        xk = *(const uint4*)(kh + r * rs + vv * EPV);
-      }
-      rq[l] = xq;
-      rk[l] = xk;
+      const size_t o = (size_t)(r < ci.len ? r : ci.len - 1) * rs + vv * EPV;
+      rq[l] = *(const u32x4*)(qh + o);
+      rk[l] = *(const u32x4*)(kh + o);
     }
   };
+  auto settle_loads = [&]() {
+    settle(rg);
+    settle(rbeta);
+    settle(rq);
+    settle(rk);
+  };
   if ((int)blockIdx.x < items) issue_loads(blockIdx.x, tid0);
+  settle_loads();
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
   // thread indices re-derived per item so that the lane-dependent LDS addresses
   // below stay inside the loop instead of being held in registers across it
@@ -153,8 +156,9 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {
     const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
-    *(uint4*)(sQ + r * PN + vv * EPV) = rq[l];
-    *(uint4*)(sK + r * PN + vv * EPV) = rk[l];
+    const unsigned m = r < Lr ? ~0u : 0u;
+    *(u32x4*)(sQ + r * PN + vv * EPV) = rq[l] & m;
+    *(u32x4*)(sK + r * PN + vv * EPV) = rk[l] & m;
   }
   if (it + (int)gridDim.x < items) issue_loads(it + gridDim.x, tid);
   __syncthreads();
@@ -428,6 +432,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     }
   }
   __syncthreads();
+
+  settle_loads();  // the next item's inputs, before this item's first stores
 
   // ---- W = INV (beta Kd): wave w -> rows of block w % 4, columns [c0, c0 + DH)
   {
