@@ -52,6 +52,15 @@ template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16
 // 2^x on the transcendental unit.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Per-token log decay in log2 units, g log2(e) with g = -e^{A_log} softplus(x)
+// (aA = e^{A_log}).  softplus(x) log2(e) = max(x, 0) log2(e) + log2(1 + 2^{-|x| log2(e)}):
+// the log's argument lies in [1, 2] and the exponent is <= 0, so the bare hardware
+// log2 / exp2 apply with no range reduction.
+__device__ __forceinline__ float gate_log2(float x, float aA) {
+  const float t = __builtin_amdgcn_exp2f(-fabsf(x) * LOG2E);
+  return -aA * fmaf(fmaxf(x, 0.f), LOG2E, __builtin_amdgcn_logf(1.f + t));
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Inside every group of 16 lanes, lane
 // 4a + b receives element b of the 8-byte chunks that lanes a, a + 4, a + 8, a + 12
 // of the group point at.  With lane 16G + s pointing at row k0 + (s >> 2), columns

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const int r = (lane >> 4) * 16 + rr;
       rg[rr] = grh[(r < ci.len ? r : ci.len - 1) * rs];
     }
-    rbeta = t < ci.len ? beta[((size_t)ci.t0 + lane) * H + h] : 0.f;
+    rbeta = beta[((size_t)ci.t0 + (lane < ci.len ? lane : ci.len - 1)) * H + h];
     g2l_tile<T, D, 64, NW>(sO, dO + base, rs, ci.len, w, lane);
     g2l_tile<T, D, 64, NW>(sV, v + base, rs, ci.len, w, lane);
     g2l_tile<T, D, 64, NW>(sK0, k + base, rs, ci.len, w, lane);
@@ -209,17 +209,15 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const int R1 = w / WPR, half = w % WPR;
   const int arow = 16 * R1 + cl;            // A-operand row of this lane
   const int crow = 16 * R1 + g4 * 4;        // first C row of this lane
-  if (tid < 64) sBeta[tid] = rbeta;
+  if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
   {  // in-chunk cumulative gate (log2 units), channel-major: sG[i][r]; the sums of
      // the earlier row parts come from the lanes that hold them (same wave)
     float x[16];
     float run = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const float e = __expf(-fabsf(rg[rr]));
-      const float sp = fmaxf(rg[rr], 0.f) + __logf(1.f + e);  // softplus
-      const float gg = g4 * 16 + rr < Lr ? -aA * sp : 0.f;
-      run += gg * LOG2E;
+      const float gv = gate_log2(rg[rr], aA);
+      run += g4 * 16 + rr < Lr ? gv : 0.f;
       x[rr] = run;
     }
     const float t0p = __shfl(run, cl), t1p = __shfl(run, cl + 16), t2p = __shfl(run, cl + 32);

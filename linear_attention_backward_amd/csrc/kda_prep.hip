@@ -18,10 +18,6 @@
 
 namespace kda {
 
-__device__ __forceinline__ float softplus_p(float x) {
-  return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));
-}
-
 template <typename T, int D> struct PL {
   static constexpr int NW = D / 16;               // waves
   static constexpr int NT = NW * 64;
@@ -99,9 +95,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   // the chunk are zero (q, k) or masked at the cumsum (g_raw).
   float rg[16], rbeta;
   u32x4 rq[NLT], rk[NLT];
-  auto issue_loads = [&](int it, int t) {
-    const int c = it % NC, h = it / NC;
-    const ChunkInfo ci = chunks[c];
+  auto issue_loads = [&](int it, int t, const ChunkInfo ci) {
+    const int h = it / NC;
     const size_t hD = (size_t)h * D;
     const float* gh = g_raw + (size_t)ci.t0 * rs + hD + t % D;
     const int part = t / D;  // 4 parts of 16 rows
@@ -110,7 +105,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       const int r = part * 16 + rr;
       rg[rr] = gh[(r < ci.len ? r : ci.len - 1) * rs];
     }
-    rbeta = t < ci.len ? beta[(size_t)(ci.t0 + (t & 63)) * H + h] : 0.f;
+    rbeta = beta[(size_t)(ci.t0 + ((t & 63) < ci.len ? (t & 63) : ci.len - 1)) * H + h];
     const T* qh = q + (size_t)ci.t0 * rs + hD;
     const T* kh = k + (size_t)ci.t0 * rs + hD;
 #pragma unroll
@@ -127,7 +122,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     settle(rq);
     settle(rk);
   };
-  if ((int)blockIdx.x < items) issue_loads(blockIdx.x, tid0);
+  if ((int)blockIdx.x < items) issue_loads(blockIdx.x, tid0, chunks[blockIdx.x % NC]);
   settle_loads();
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
   // thread indices re-derived per item so that the lane-dependent LDS addresses
@@ -138,18 +133,19 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   const int g4 = lane >> 4, cl = lane & 15;
   const int c = it % NC, h = it / NC;
   const int Lr = chunks[c].len;
+  const int nxt = it + (int)gridDim.x;
+  const ChunkInfo cnx = chunks[(nxt < items ? nxt : it) % NC];  // early: scalar-load latency
   const size_t ch = (size_t)c * H + h;
   const float aA = __expf(A_log[h]);
-  if (tid < 64) sBeta[tid] = rbeta;
+  if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
   {  // in-chunk cumulative gate (log2 units), natural: sG[r][i]
     const int i = tid % D, part = tid / D;
     float run = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int r = part * 16 + rr;
-      const float gv = -aA * softplus_p(rg[rr]);
-      const float g = r < Lr ? gv : 0.f;
-      run += g * LOG2E;
+      const float gv = gate_log2(rg[rr], aA);
+      run += r < Lr ? gv : 0.f;
       sG[r * PGN + i] = run;
     }
   }
@@ -160,7 +156,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     *(u32x4*)(sQ + r * PN + vv * EPV) = rq[l] & m;
     *(u32x4*)(sK + r * PN + vv * EPV) = rk[l] & m;
   }
-  if (it + (int)gridDim.x < items) issue_loads(it + gridDim.x, tid);
+  if (nxt < items) issue_loads(nxt, tid, cnx);
   __syncthreads();
   {
     const int i = tid % D, part = tid / D;
