@@ -411,9 +411,11 @@ __device__ __forceinline__ void g2l16(const void* g, unsigned lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
                : "memory");
 }
+//   lds0: LDS byte address of the tile (wave-uniform), lds_tile: the same tile seen
+//   through a generic pointer (for the zero fill).
 template <typename T, int D, int ROWS, int NW>
-__device__ __forceinline__ void g2l_tile(T* lds_tile, const T* src, size_t rs, int valid, int w,
-                                         int lane) {
+__device__ __forceinline__ void g2l_tile(unsigned lds0, T* lds_tile, const T* src, size_t rs,
+                                         int valid, int w, int lane) {
   constexpr int GPR = D * (int)sizeof(T) / 16;  // data granules per row
   constexpr int GP = GPR + 1;                   // granules per padded LDS row
   constexpr int NG = ROWS * GP;
@@ -428,10 +430,11 @@ __device__ __forceinline__ void g2l_tile(T* lds_tile, const T* src, size_t rs, i
       if (p < NG) {
         if (row < valid) {
           const T* g = src + (size_t)row * rs + (gc < GPR ? gc : GPR - 1) * EPG;
-          g2l16(g, __builtin_amdgcn_readfirstlane(
-                       (unsigned)(uintptr_t)(lds_void*)((char*)lds_tile + base * 16)));
+          g2l16(g, lds0 + base * 16);
         } else {
-          *(uint4*)((char*)lds_tile + p * 16) = uint4{0u, 0u, 0u, 0u};
+          unsigned z;  // made here: a zero quad kept across the caller's loop gets spilled
+          asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+          *(u32x4*)((char*)lds_tile + p * 16) = u32x4{z, z, z, z};
         }
       }
     }
@@ -439,6 +442,12 @@ __device__ __forceinline__ void g2l_tile(T* lds_tile, const T* src, size_t rs, i
 }
 // Wait until this wave's global loads (including global -> LDS copies) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Wait until at most N of this wave's vector memory operations are outstanding.
+// They complete in issue order, so everything issued before the last N is done.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Registers filled by loads issued well before their use (a prefetch for the next
 // work item): passing them through an empty asm makes the compiler wait for those

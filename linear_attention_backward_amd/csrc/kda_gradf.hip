@@ -45,35 +45,40 @@ template <typename T, int D> struct GF {
   static constexpr int G_OFF = 0;
   static constexpr int G_SZ = D * PG * 4;
   static constexpr int N_SZ = 64 * PN * ES;
-  // dO (natural), v then U, dvcorr
-  static constexpr int O_OFF = G_OFF + G_SZ;
-  static constexpr int U_OFF = O_OFF + N_SZ;
-  static constexpr int DVC_OFF = U_OFF + N_SZ;
-  // state side: S_in then dS_out (natural), (beta Y)^T then dU^T; dv staging over S
-  static constexpr int S_OFF = DVC_OFF + N_SZ;
-  static constexpr int YT_OFF = S_OFF + D * PN * ES;
-  static constexpr int C_END = YT_OFF + D * PT * ES;
-  // intra-chunk phase, over the regions above once the key-side products are done
-  static constexpr int Q_OFF = O_OFF;
-  static constexpr int K_OFF = Q_OFF + N_SZ;
-  static constexpr int DM_OFF = K_OFF + N_SZ;
-  static constexpr int DL_OFF = DM_OFF + 64 * PC * ES;
-  static constexpr int DG_OFF = DL_OFF + 64 * PC * ES;
+  static constexpr int S_SZ = D * PN * ES;
+  static constexpr int YT_SZ = D * PT * ES;
+  static constexpr int PCT = 64 * PC * ES;  // one [64][PC] tile
   // fp32 copies of the four diagonal 16x16 blocks of dMqk and dL (bf16 tiles only)
   static constexpr int DGBS = 16 * PDG + 4;     // block stride of those tables
   static constexpr int DG_SZ = ES == 2 ? 2 * 4 * DGBS * 4 : 0;
-  static constexpr int DQ_OFF = DG_OFF + DG_SZ;
-  static constexpr int DK_OFF = DQ_OFF + N_SZ;
-  static constexpr int P3_END = DK_OFF + N_SZ;
-  // per-wave exchange slots [16 channels][PX] fp32 over the dq / dk staging tiles
-  static constexpr int PX = 68;
-  static_assert(NW * 16 * PX * 4 <= 2 * N_SZ, "exchange slots fit the dq / dk staging");
-  static constexpr int X_END = C_END > P3_END ? C_END : P3_END;
-  static constexpr int B_OFF = (X_END + 15) / 16 * 16;     // beta [64]
+  // Regions by phase (state side / intra-chunk phase):
+  //   O : dO                  / q, then dq staged in place
+  //   YT: (beta Y)^T, dU^T    / k, then dk staged in place; past it dMqk, dL and
+  //                             the diagonal tables
+  //   K0: k, then dvcorr      / (under dMqk, dL; refilled once the intra phase is done)
+  //   S : S_in, dS_out, dv    / -
+  //   V : v, then U           / -
+  // S and V lie above every intra-phase tile, so the next chunk-head's S_in and v
+  // stream in during the whole intra phase.
+  static constexpr int O_OFF = G_OFF + G_SZ;
+  static constexpr int YT_OFF = O_OFF + N_SZ;
+  static constexpr int Q_OFF = O_OFF;
+  static constexpr int K_OFF = YT_OFF;
+  static constexpr int DM_OFF = K_OFF + N_SZ;
+  static constexpr int DL_OFF = DM_OFF + PCT;
+  static constexpr int DG_OFF = DL_OFF + PCT;
+  static constexpr int I_END = DG_OFF + DG_SZ;
+  static constexpr int K0_OFF = YT_OFF + (N_SZ > YT_SZ ? N_SZ : YT_SZ);
+  static constexpr int S_OFF = K0_OFF + N_SZ > I_END ? K0_OFF + N_SZ : I_END;
+  static constexpr int V_OFF = S_OFF + S_SZ;
+  static constexpr int C_END = V_OFF + N_SZ;
+  static constexpr int B_OFF = (C_END + 15) / 16 * 16;     // beta [64]
   static constexpr int DB1_OFF = B_OFF + 256;             // [WPR][64]
   static constexpr int DB2_OFF = DB1_OFF + WPR * 256;     // [NW][64]
   static constexpr int RED_OFF = DB2_OFF + NW * 256;      // [NW]
   static constexpr int TOTAL = RED_OFF + NW * 4;
+  static_assert(S_OFF >= I_END && K0_OFF >= DM_OFF, "prefetch tiles clear the intra phase");
+  static_assert(TOTAL <= 160 * 1024, "LDS");
   static_assert(64 * PR * 4 <= G_SZ, "dg_raw staging fits the gate region");
   static_assert(N_SZ <= D * PN * ES, "dv staging fits the state tile");
 };
@@ -106,9 +111,10 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   float* sG = (float*)(smem + L::G_OFF);
   float* sR = sG;  // dg_raw staging at the end
   T* sO = (T*)(smem + L::O_OFF);
-  T* sU = (T*)(smem + L::U_OFF);
-  T* sV = sU;
-  T* sDVC = (T*)(smem + L::DVC_OFF);
+  T* sV = (T*)(smem + L::V_OFF);
+  T* sU = sV;
+  T* sK0 = (T*)(smem + L::K0_OFF);  // k for the intra-chunk phase, then dvcorr
+  T* sDVC = sK0;
   T* sS = (T*)(smem + L::S_OFF);
   T* sDV = sS;
   T* sYT = (T*)(smem + L::YT_OFF);
@@ -116,8 +122,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   T* sK = (T*)(smem + L::K_OFF);
   T* sDM = (T*)(smem + L::DM_OFF);
   T* sDL = (T*)(smem + L::DL_OFF);
-  T* sDQ = (T*)(smem + L::DQ_OFF);
-  T* sDK = (T*)(smem + L::DK_OFF);
+  T* sDQ = sQ;  // dq, dk staged in place of q, k: each lane overwrites only the
+  T* sDK = sK;  // entries (row, own channel) it has just read
   float* sBeta = (float*)(smem + L::B_OFF);
   float* sDB1 = (float*)(smem + L::DB1_OFF);
   float* sDB2 = (float*)(smem + L::DB2_OFF);
@@ -144,27 +150,33 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const size_t rs = (size_t)H * D;  // token stride of per-token tensors
   const int items = NC * H;
   const int tid0 = threadIdx.x;
-  // k for the intra-chunk phase goes through the dvcorr tile (unused until the
-  // state side's last product)
-  T* sK0 = sDVC;
+  const unsigned lds0 = (unsigned)(uintptr_t)(lds_void*)smem;  // LDS byte address of smem
 
   // ------------------------------------------------------------------ loads
   // Persistent: one workgroup fills a CU's LDS, so each workgroup walks the
-  // (chunk, head) items with stride gridDim.x and issues the next item's loads
-  // while it finishes the current one: g_raw and beta into registers and dO, v, k
-  // straight into their LDS tiles once the intra-chunk phase is done with those
-  // regions, S_in once the dq / dk staging over its tile has been read out.
+  // (chunk, head) items with stride gridDim.x and copies the next item's tiles
+  // straight into LDS as soon as their regions are dead: S_in and v when the key
+  // side is done (they then land during the intra phase), k, g_raw and beta once
+  // the intra phase is done, dO once the dq staging over its tile is read out.
   // gate layout: lane (g4, cl) of wave w owns key channel 16 w + cl, rows 16 g4 .. + 15,
   // so that the four row parts of a channel sit in one wave
   float rg[16];  // g_raw of this lane's channel, 16 rows (rows past the chunk: masked later)
   float rbeta;
   // (t: this thread's index, passed in so that the address arithmetic is redone per
   // item rather than held across the loop)
+  auto issue_early = [&](int it, int t) {
+    const int c = it % NC, h = it / NC;
+    const ChunkInfo ci = chunks[c];
+    const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    g2l_tile<T, D, D, NW>(lds0 + L::S_OFF, sS, h_saved + ((size_t)c * H + h) * DD, D, D, w, lane);
+    g2l_tile<T, D, 64, NW>(lds0 + L::V_OFF, sV, v + (size_t)ci.t0 * rs + (size_t)h * D, rs, ci.len, w, lane);
+  };
   auto issue_front = [&](int it, int t) {
     const int c = it % NC, h = it / NC;
     const ChunkInfo ci = chunks[c];
     const size_t base = (size_t)ci.t0 * rs + (size_t)h * D;
     const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    g2l_tile<T, D, 64, NW>(lds0 + L::K0_OFF, sK0, k + base, rs, ci.len, w, lane);
     const float* grh = g_raw + base + 16 * w + (lane & 15);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -172,20 +184,19 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       rg[rr] = grh[(r < ci.len ? r : ci.len - 1) * rs];
     }
     rbeta = beta[((size_t)ci.t0 + (lane < ci.len ? lane : ci.len - 1)) * H + h];
-    g2l_tile<T, D, 64, NW>(sO, dO + base, rs, ci.len, w, lane);
-    g2l_tile<T, D, 64, NW>(sV, v + base, rs, ci.len, w, lane);
-    g2l_tile<T, D, 64, NW>(sK0, k + base, rs, ci.len, w, lane);
   };
-  auto issue_state = [&](int it, int t) {
-    const size_t ch = (size_t)(it % NC) * H + it / NC;
-    g2l_tile<T, D, D, NW>(sS, h_saved + ch * DD, D, D, __builtin_amdgcn_readfirstlane(t >> 6),
-                          t & 63);
+  auto issue_late = [&](int it, int t) {
+    const int c = it % NC, h = it / NC;
+    const ChunkInfo ci = chunks[c];
+    g2l_tile<T, D, 64, NW>(lds0 + L::O_OFF, sO, dO + (size_t)ci.t0 * rs + (size_t)h * D, rs, ci.len,
+                           __builtin_amdgcn_readfirstlane(t >> 6), t & 63);
   };
   if ((int)blockIdx.x < items) {
+    issue_early(blockIdx.x, tid0);
     issue_front(blockIdx.x, tid0);
-    issue_state(blockIdx.x, tid0);
+    issue_late(blockIdx.x, tid0);
   }
-  settle(rg);
+  settle(rg);  // waits for all of the first item's copies as well
   settle(rbeta);
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
   // thread indices re-derived per item so that the lane-dependent LDS addresses
@@ -227,7 +238,10 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       *(f4*)(sG + gch * PG + g4 * 16 + 4 * qq) =
           f4{x[4 * qq] + add, x[4 * qq + 1] + add, x[4 * qq + 2] + add, x[4 * qq + 3] + add};
   }
-  wait_vmem();
+  // S_in, v and k have landed: every copy of them is followed by at least the
+  // previous item's 2 NLT + NLR unconditional output stores (dO may still be in
+  // flight; it is waited for with dS_out)
+  wait_vmcnt<2 * NLT + NLR>();
   __syncthreads();
   Frag kf[NKD];                              // raw k of row arow (permuted k order)
 #pragma unroll
@@ -284,7 +298,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
   for (int kk = 0; kk < NKD; ++kk) bS[kk] = MM::load(sS + ic * PN + kk * KS + g4 * KPL);
   __syncthreads();  // (beta Y)^T complete; S_in and v are dead
-  g2l_tile<T, D, D, NW>(sS, dSo, D, D, w, lane);  // dS_out, natural (lands during U)
+  g2l_tile<T, D, D, NW>(lds0 + L::S_OFF, sS, dSo, D, D, w, lane);  // dS_out, natural (lands during U)
   {  // U = INV (beta Y)
     f4 U[4];
 #pragma unroll
@@ -421,6 +435,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     }
   }
   __syncthreads();  // dO, U, dvcorr and the dv staging are dead
+  if (nxt < items) issue_early(nxt, tid);  // S_in, v: their tiles are clear of the intra phase
   // dMqk, dL (masked, natural) as act-dtype tiles; fp32 copies of the diagonal blocks
 #pragma unroll
   for (int st = 0; st < CTW; ++st) {
@@ -512,21 +527,24 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       x1[r] = a1;
       x2[r] = a2;
     }
-    // to the C layout through a per-wave LDS slot [16 channels][64 rows] (over the
-    // dq / dk staging tiles, which are written only after the next barrier)
-    float* xs = (float*)(smem + L::DQ_OFF) + w * 16 * L::PX;
+    // to the C layout: lane (g4, cl) holds rows 16 g4 + t and wants rows
+    // 16 rt + 4 g4 + j, i.e. a transpose of 4-row chunks across the four 16-lane rows
+    // of the wave: one 32-lane swap stage and one 16-lane swap stage per element.
+    // The swaps are inline asm with both registers read and written: this compiler
+    // returns the first register for both results of the swap builtins.
     auto exch = [&](const float (&src)[16], float (&dst)[4][4]) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        *(f4*)(xs + cl * L::PX + rb + 4 * m) =
-            f4{src[4 * m], src[4 * m + 1], src[4 * m + 2], src[4 * m + 3]};
-      __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in order
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const f4 t = *(const f4*)(xs + cl * L::PX + 16 * rt + 4 * g4);
-        dst[rt][0] = t[0]; dst[rt][1] = t[1]; dst[rt][2] = t[2]; dst[rt][3] = t[3];
+      for (int e = 0; e < 4; ++e) {
+        float x0 = src[e], x1 = src[4 + e], x2 = src[8 + e], x3 = src[12 + e];
+        asm volatile("v_permlane32_swap_b32 %0, %1" : "+v"(x0), "+v"(x2));
+        asm volatile("v_permlane32_swap_b32 %0, %1" : "+v"(x1), "+v"(x3));
+        asm volatile("v_permlane16_swap_b32 %0, %1" : "+v"(x0), "+v"(x1));
+        asm volatile("v_permlane16_swap_b32 %0, %1" : "+v"(x2), "+v"(x3));
+        dst[0][e] = x0;
+        dst[1][e] = x1;
+        dst[2][e] = x2;
+        dst[3][e] = x3;
       }
-      __builtin_amdgcn_wave_barrier();
     };
     exch(x1, x1d);
     exch(x2, x2d);
@@ -564,7 +582,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     BZq[R] = MS::split(bq);
     BZk[R] = MS::split(bk);
   }
-  __syncthreads();  // every wave's exchange slot is read: the dq / dk staging is free
+  __builtin_amdgcn_sched_barrier(0);  // keep the operand set-up out of the tile loop
   float dG[4][4];
   float dkr_col = 0.f, dal = 0.f;
   float dbp[4][4];
@@ -694,7 +712,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   dal = sum64(dal);
   if (lane == 0) sRed[w] = dal;
   __syncthreads();  // dq, dk staged; the gate tile is dead
-  if (nxt < items) issue_front(nxt, tid);  // dO, v, k regions: dead since the intra phase
+  if (nxt < items) issue_front(nxt, tid);  // k over dMqk / dL, dead since the intra phase
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -728,9 +746,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const int r = r0 < Lr ? r0 : Lr - 1;
     *(f4*)(dg_raw + (t0 + r) * rs + hD + sv * 4) = *(const f4*)(sR + r * PR + sv * 4);
   }
-  // the dq / dk staging over the state tile is read out; issued after this item's
-  // last stores so that the next item's first wait on its registers skips it
-  if (nxt < items) issue_state(nxt, tid);
+  // dO over the dq staging, which is read out; issued after this item's last stores
+  // so that the next item's first waits skip it
+  if (nxt < items) issue_late(nxt, tid);
   __syncthreads();  // the gate tile (dg_raw staging) is read out before the next gate
   }
 }
