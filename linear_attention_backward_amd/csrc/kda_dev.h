@@ -460,6 +460,11 @@ template <int N> __device__ __forceinline__ void settle(float (&x)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) settle(x[i]);
 }
+__device__ __forceinline__ void settle(f4& x) { asm volatile("" : "+v"(x)); }
+template <int N> __device__ __forceinline__ void settle(f4 (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) settle(x[i]);
+}
 template <int N> __device__ __forceinline__ void settle(u32x4 (&x)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) settle(x[i]);

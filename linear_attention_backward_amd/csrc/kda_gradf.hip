@@ -158,9 +158,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   // straight into LDS as soon as their regions are dead: S_in and v when the key
   // side is done (they then land during the intra phase), k, g_raw and beta once
   // the intra phase is done, dO once the dq staging over its tile is read out.
-  // gate layout: lane (g4, cl) of wave w owns key channel 16 w + cl, rows 16 g4 .. + 15,
-  // so that the four row parts of a channel sit in one wave
-  float rg[16];  // g_raw of this lane's channel, 16 rows (rows past the chunk: masked later)
+  // g_raw of wave w's 16 channels in 16-byte quads: lane l holds rows 16 t + (l >> 2),
+  // channels 16 w + 4 (l & 3) .. + 3, t = 0..3 (rows past the chunk: masked later)
+  f4 rg[4];
   float rbeta;
   // (t: this thread's index, passed in so that the address arithmetic is redone per
   // item rather than held across the loop)
@@ -177,11 +177,11 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const size_t base = (size_t)ci.t0 * rs + (size_t)h * D;
     const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     g2l_tile<T, D, 64, NW>(lds0 + L::K0_OFF, sK0, k + base, rs, ci.len, w, lane);
-    const float* grh = g_raw + base + 16 * w + (lane & 15);
+    const float* grw = g_raw + base + 16 * w + 4 * (lane & 3);
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int r = (lane >> 4) * 16 + rr;
-      rg[rr] = grh[(r < ci.len ? r : ci.len - 1) * rs];
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const int r = 16 * t4 + (lane >> 2);
+      rg[t4] = *(const f4*)(grw + (size_t)(r < ci.len ? r : ci.len - 1) * rs);
     }
     rbeta = beta[((size_t)ci.t0 + (lane < ci.len ? lane : ci.len - 1)) * H + h];
   };
@@ -221,14 +221,27 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const int arow = 16 * R1 + cl;            // A-operand row of this lane
   const int crow = 16 * R1 + g4 * 4;        // first C row of this lane
   if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
-  {  // in-chunk cumulative gate (log2 units), channel-major: sG[i][r]; the sums of
-     // the earlier row parts come from the lanes that hold them (same wave)
+  {  // in-chunk cumulative gate (log2 units), channel-major: sG[i][r].  The per-token
+     // gates go into this wave's 16 channel rows of the tile (written and read back by
+     // this wave only), then lane (g4, cl) sums channel 16 w + cl over rows 16 g4 .. + 15
+     // and the sums of the earlier row parts come from the lanes that hold them
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const int r = 16 * t4 + (lane >> 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sG[(16 * w + 4 * (lane & 3) + e) * PG + r] = r < Lr ? gate_log2(rg[t4][e], aA) : 0.f;
+    }
     float x[16];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const f4 t = *(const f4*)(sG + gch * PG + g4 * 16 + 4 * qq);
+      x[4 * qq] = t[0]; x[4 * qq + 1] = t[1]; x[4 * qq + 2] = t[2]; x[4 * qq + 3] = t[3];
+    }
     float run = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const float gv = gate_log2(rg[rr], aA);
-      run += g4 * 16 + rr < Lr ? gv : 0.f;
+      run += x[rr];
       x[rr] = run;
     }
     const float t0p = __shfl(run, cl), t1p = __shfl(run, cl + 16), t2p = __shfl(run, cl + 32);
