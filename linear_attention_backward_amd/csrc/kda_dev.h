@@ -413,7 +413,8 @@ __device__ __forceinline__ void g2l16(const void* g, unsigned lds) {
 }
 //   lds0: LDS byte address of the tile (wave-uniform), lds_tile: the same tile seen
 //   through a generic pointer (for the zero fill).
-template <typename T, int D, int ROWS, int NW>
+//   [N0, N1): the part of the wave's slices to issue (a tile may be issued in parts).
+template <typename T, int D, int ROWS, int NW, int N0 = 0, int N1 = 1 << 20>
 __device__ __forceinline__ void g2l_tile(unsigned lds0, T* lds_tile, const T* src, size_t rs,
                                          int valid, int w, int lane) {
   constexpr int GPR = D * (int)sizeof(T) / 16;  // data granules per row
@@ -421,8 +422,9 @@ __device__ __forceinline__ void g2l_tile(unsigned lds0, T* lds_tile, const T* sr
   constexpr int NG = ROWS * GP;
   constexpr int EPG = 16 / (int)sizeof(T);
   constexpr int NSL = (NG + 63) / 64;           // slices
+  constexpr int NPW = (NSL + NW - 1) / NW;      // slices per wave (at most)
 #pragma unroll
-  for (int n = 0; n < (NSL + NW - 1) / NW; ++n) {
+  for (int n = N0; n < (N1 < NPW ? N1 : NPW); ++n) {
     const int base = (w + n * NW) * 64;
     if (base < NG) {
       const int p = base + lane;

@@ -164,12 +164,18 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   float rbeta;
   // (t: this thread's index, passed in so that the address arithmetic is redone per
   // item rather than held across the loop)
-  auto issue_early = [&](int it, int t) {
+  // (part: 0 = all of S_in and v; 1..3 = the pieces that the intra phase spreads over its
+  // row tiles, so that the copies do not queue up ahead of the epilogue's loads and stores)
+  auto issue_early = [&](int it, int t, int part) {
     const int c = it % NC, h = it / NC;
     const ChunkInfo ci = chunks[c];
     const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
-    g2l_tile<T, D, D, NW>(lds0 + L::S_OFF, sS, h_saved + ((size_t)c * H + h) * DD, D, D, w, lane);
-    g2l_tile<T, D, 64, NW>(lds0 + L::V_OFF, sV, v + (size_t)ci.t0 * rs + (size_t)h * D, rs, ci.len, w, lane);
+    const T* sin = h_saved + ((size_t)c * H + h) * DD;
+    if (part == 0 || part == 1) g2l_tile<T, D, D, NW, 0, 2>(lds0 + L::S_OFF, sS, sin, D, D, w, lane);
+    if (part == 0 || part == 2) g2l_tile<T, D, D, NW, 2>(lds0 + L::S_OFF, sS, sin, D, D, w, lane);
+    if (part == 0 || part == 3)
+      g2l_tile<T, D, 64, NW>(lds0 + L::V_OFF, sV, v + (size_t)ci.t0 * rs + (size_t)h * D, rs,
+                             ci.len, w, lane);
   };
   auto issue_front = [&](int it, int t) {
     const int c = it % NC, h = it / NC;
@@ -192,7 +198,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
                            __builtin_amdgcn_readfirstlane(t >> 6), t & 63);
   };
   if ((int)blockIdx.x < items) {
-    issue_early(blockIdx.x, tid0);
+    issue_early(blockIdx.x, tid0, 0);
     issue_front(blockIdx.x, tid0);
     issue_late(blockIdx.x, tid0);
   }
@@ -448,7 +454,6 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     }
   }
   __syncthreads();  // dO, U, dvcorr and the dv staging are dead
-  if (nxt < items) issue_early(nxt, tid);  // S_in, v: their tiles are clear of the intra phase
   // dMqk, dL (masked, natural) as act-dtype tiles; fp32 copies of the diagonal blocks
 #pragma unroll
   for (int st = 0; st < CTW; ++st) {
@@ -677,6 +682,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       sDQ[r * PN + ic] = from_f<T>(dqv);
       sDK[r * PN + ic] = from_f<T>(dkd + dki + dkr);
     }
+    // the next item's S_in and v, in pieces (their tiles are clear of the intra phase)
+    if (rt < 3 && nxt < items) issue_early(nxt, tid, rt + 1);
   }
   // last row: sum_r k.dk_r + e^{G_T} p
   dkr_col += __shfl_xor(dkr_col, 16);
