@@ -84,6 +84,10 @@ EXTRA = {
     "ragged_fp32": Workload("ragged_fp32", 1, 1 + 63 + 64 + 65 + 200, 2, 64, 64, "f32",
                             1105, varlen_seqs=5, fixed_lengths=(1, 63, 64, 65, 200),
                             h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0),
+    # bf16 with K = V = 64 (the other supported bf16 head size)
+    "ragged_bf16_d64": Workload("ragged_bf16_d64", 1, 1 + 63 + 64 + 65 + 200, 4, 64, 64, "bf16",
+                                1106, varlen_seqs=5, fixed_lengths=(1, 63, 64, 65, 200),
+                                h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0),
 }
 
 

@@ -183,25 +183,28 @@ hipError_t resident_blocks(const void* kernel, int threads, int* out) {
   };
   static std::mutex mu;
   static std::vector<Entry> cache;
+  // KDA_GRID_CAP=<n> caps the result (tests: a few workgroups walk many items)
+  int cap = 0;
+  if (const char* env = std::getenv("KDA_GRID_CAP")) cap = std::atoi(env);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  int blocks = 0;
   {
     std::lock_guard<std::mutex> lk(mu);
     for (const Entry& x : cache)
-      if (x.dev == dev && x.fn == kernel && x.threads == threads) {
-        *out = x.blocks;
-        return hipSuccess;
-      }
+      if (x.dev == dev && x.fn == kernel && x.threads == threads) blocks = x.blocks;
   }
-  int ncu = 0, per = 0;
-  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0);
-  if (e != hipSuccess) return e;
-  const int blocks = std::max(1, ncu * per);
-  std::lock_guard<std::mutex> lk(mu);
-  cache.push_back({dev, kernel, threads, blocks});
-  *out = blocks;
+  if (blocks == 0) {
+    int ncu = 0, per = 0;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0);
+    if (e != hipSuccess) return e;
+    blocks = std::max(1, ncu * per);
+    std::lock_guard<std::mutex> lk(mu);
+    cache.push_back({dev, kernel, threads, blocks});
+  }
+  *out = cap > 0 && cap < blocks ? cap : blocks;
   return hipSuccess;
 }
 

@@ -49,7 +49,8 @@ hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, con
                           const float* A_log, const float* h0, void* o, float* ht,
                           void* h_saved, hipStream_t st);
 // Workgroups of `kernel` (block of `threads`) that the current device holds at
-// once: CU count times the per-CU occupancy; cached per device and kernel.
+// once: CU count times the per-CU occupancy; cached per device and kernel.  The
+// environment variable KDA_GRID_CAP, when set to n > 0, caps it at n.
 hipError_t resident_blocks(const void* kernel, int threads, int* out);
 
 hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st);

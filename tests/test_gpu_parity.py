@@ -47,7 +47,7 @@ def test_parity_fp32(name):
 
 
 @pytest.mark.parametrize("name", ["single_seq_bf16", "weak_decay_bf16", "strong_decay_bf16",
-                                  "ragged_bf16"])
+                                  "ragged_bf16", "ragged_bf16_d64"])
 def test_parity_bf16(name):
     _check(name)
 
@@ -108,3 +108,22 @@ def test_split_scan_zero_length(monkeypatch):
     ref = KC.oracle_for(inp)
     ref["h_saved"] = ref["states"]
     KC.compare(res, ref, GRADS + INTER, KC.TOL["bf16"], label="zero_len split")
+
+
+@pytest.mark.parametrize("name,cap", [("ragged_fp32", 3), ("ragged_bf16", 3),
+                                      ("ragged_bf16_d64", 2), ("weak_decay_bf16", 5)])
+def test_persistent_walk(name, cap, monkeypatch):
+    """Prep and the gradient pass with a grid of `cap` workgroups: each workgroup walks
+    many (chunk, head) items and hands the prefetched tiles of the next item over
+    across ragged chunks.  Results match the oracle and, bit for bit, a run with the
+    full grid (an item's arithmetic does not depend on which workgroup runs it)."""
+    inp = KI.make_inputs(KI.get_workload(name))
+    print("\n[case] persistent walk %s, grid capped at %d" % (name, cap), flush=True)
+    full = KC.run_gpu(inp)
+    monkeypatch.setenv("KDA_GRID_CAP", str(cap))
+    capped = KC.run_gpu(inp)
+    ref = KC.oracle_for(inp)
+    ref["h_saved"] = ref["states"]
+    KC.compare(capped, ref, GRADS + INTER, KC.TOL[inp["dtype"]], label=name + " capped")
+    for key in GRADS + ["dstates"]:
+        assert np.array_equal(full[key], capped[key]), key
