@@ -226,6 +226,14 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const int R1 = w / WPR, half = w % WPR;
   const int arow = 16 * R1 + cl;            // A-operand row of this lane
   const int crow = 16 * R1 + g4 * 4;        // first C row of this lane
+  // dS_out into registers now (the gate, Kd / Kr and Y hide the load); it goes to LDS
+  // over S_in once Y is done
+  u32x4 rD[NLS];
+#pragma unroll
+  for (int l = 0; l < NLS; ++l) {
+    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+    rD[l] = *(const u32x4*)(dSo + (size_t)r * D + sv * EPV);
+  }
   if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
   {  // in-chunk cumulative gate (log2 units), channel-major: sG[i][r].  The per-token
      // gates go into this wave's 16 channel rows of the tile (written and read back by
@@ -257,10 +265,11 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       *(f4*)(sG + gch * PG + g4 * 16 + 4 * qq) =
           f4{x[4 * qq] + add, x[4 * qq + 1] + add, x[4 * qq + 2] + add, x[4 * qq + 3] + add};
   }
-  // S_in, v and k have landed: every copy of them is followed by at least the
-  // previous item's 2 NLT + NLR unconditional output stores (dO may still be in
-  // flight; it is waited for with dS_out)
-  wait_vmcnt<2 * NLT + NLR>();
+  // S_in, v and k have landed: every copy of them is followed by at least g_raw and
+  // beta (5 loads), the previous item's 2 NLT + NLR unconditional output stores and this
+  // item's NLS dS_out loads (dO and dS_out may still be in flight; the dS_out stores to
+  // LDS wait for both, in issue order)
+  wait_vmcnt<2 * NLT + NLR + NLS>();
   __syncthreads();
   Frag kf[NKD];                              // raw k of row arow (permuted k order)
 #pragma unroll
@@ -317,7 +326,11 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
   for (int kk = 0; kk < NKD; ++kk) bS[kk] = MM::load(sS + ic * PN + kk * KS + g4 * KPL);
   __syncthreads();  // (beta Y)^T complete; S_in and v are dead
-  g2l_tile<T, D, D, NW>(lds0 + L::S_OFF, sS, dSo, D, D, w, lane);  // dS_out, natural (lands during U)
+#pragma unroll
+  for (int l = 0; l < NLS; ++l) {  // dS_out over S_in, natural
+    const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+    *(u32x4*)(sS + r * PN + sv * EPV) = rD[l];
+  }
   {  // U = INV (beta Y)
     f4 U[4];
 #pragma unroll
@@ -334,7 +347,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) store_c<T>(sU, PN, 16 * R1, 64 * half + nt * 16, U[nt], lane);
   }
-  wait_vmem();
+  wait_vmem();      // (dO: already waited for by the dS_out stores, which follow it)
   __syncthreads();  // dS_out in place; U complete; (beta Y)^T dead
   {  // dU = Mqk^T dO + Kr dS_out  ->  dU^T
     f4 dU[4];
