@@ -31,7 +31,7 @@ struct Plan {
   int64_t NC = 0;
   size_t es = 0;  // bytes per act element
   // workspace regions
-  Region chunks, seq_off, groups, grp_off, Tm, PT, eGT, INV, INVT, MqkT, dstates, dAl, Pg, Qg,
+  Region chunks, seq_off, groups, grp_off, Tm, PT, eGT, INV, MqkT, dstates, dAl, Pg, Qg,
       bnd, hsaved;
   size_t fwd_bytes = 0, bwd_bytes = 0;
 };
@@ -129,7 +129,6 @@ int make_plan(const kda_problem* p, Plan* pl) {
   take(pl->PT, NCH * D * 64 * pl->es);
   take(pl->eGT, NCH * D * 4);
   take(pl->INV, NCH * 64 * 64 * pl->es);
-  take(pl->INVT, NCH * 64 * 64 * pl->es);
   take(pl->MqkT, NCH * 64 * 64 * pl->es);
   take(pl->dstates, NCH * D * D * pl->es);
   take(pl->dAl, NCH * 4);
@@ -295,7 +294,6 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   b.PT = ws + pl.PT.off;
   b.eGT = (float*)(ws + pl.eGT.off);
   b.INV = ws + pl.INV.off;
-  b.INVT = ws + pl.INVT.off;
   b.MqkT = ws + pl.MqkT.off;
   b.dstates = io->dstates ? io->dstates : (void*)(ws + pl.dstates.off);
   b.dAl_part = (float*)(ws + pl.dAl.off);

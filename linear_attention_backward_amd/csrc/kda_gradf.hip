@@ -72,7 +72,14 @@ template <typename T, int D> struct GF {
   static constexpr int S_OFF = K0_OFF + N_SZ > I_END ? K0_OFF + N_SZ : I_END;
   static constexpr int V_OFF = S_OFF + S_SZ;
   static constexpr int C_END = V_OFF + N_SZ;
-  static constexpr int B_OFF = (C_END + 15) / 16 * 16;     // beta [64]
+  // INV [64][PC] (act dtype; INV^T is read out of it with transposing reads): over the
+  // diagonal tables for bf16 (they are dead from the intra tile loop until the key
+  // side writes them, after INV's last use), past the state tiles for fp32
+  static constexpr int IV_SZ = PCT;
+  static constexpr int IV_OFF = ES == 2 ? DG_OFF : C_END;
+  static constexpr int L_END = ES == 2 ? C_END : C_END + IV_SZ;
+  static_assert(ES != 2 || IV_SZ <= DG_SZ, "INV fits the diagonal-table region");
+  static constexpr int B_OFF = (L_END + 15) / 16 * 16;     // beta [64]
   static constexpr int DB1_OFF = B_OFF + 256;             // [WPR][64]
   static constexpr int DB2_OFF = DB1_OFF + WPR * 256;     // [NW][64]
   static constexpr int RED_OFF = DB2_OFF + NW * 256;      // [NW]
@@ -89,7 +96,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
     const float* __restrict__ g_raw, const float* __restrict__ beta,
     const float* __restrict__ A_log, const T* __restrict__ h_saved,
-    const T* __restrict__ dstates, const T* __restrict__ INV, const T* __restrict__ INVT,
+    const T* __restrict__ dstates, const T* __restrict__ INV,
     const T* __restrict__ MqkT, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
     float* __restrict__ dg_raw, float* __restrict__ dbeta, float* __restrict__ dAl_part) {
   using L = GF<T, D>;
@@ -120,6 +127,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   T* sYT = (T*)(smem + L::YT_OFF);
   T* sQ = (T*)(smem + L::Q_OFF);
   T* sK = (T*)(smem + L::K_OFF);
+  T* sIV = (T*)(smem + L::IV_OFF);
   T* sDM = (T*)(smem + L::DM_OFF);
   T* sDL = (T*)(smem + L::DL_OFF);
   T* sDQ = sQ;  // dq, dk staged in place of q, k: each lane overwrites only the
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   float rbeta;
   // (t: this thread's index, passed in so that the address arithmetic is redone per
   // item rather than held across the loop)
-  // (part: 0 = all of S_in and v; 1..3 = the pieces that the intra phase spreads over its
+  // (part: 0 = all of S_in, v and INV; 1..3 = the pieces that the intra phase spreads over its
   // row tiles, so that the copies do not queue up ahead of the epilogue's loads and stores)
   auto issue_early = [&](int it, int t, int part) {
     const int c = it % NC, h = it / NC;
@@ -173,9 +181,12 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const T* sin = h_saved + ((size_t)c * H + h) * DD;
     if (part == 0 || part == 1) g2l_tile<T, D, D, NW, 0, 2>(lds0 + L::S_OFF, sS, sin, D, D, w, lane);
     if (part == 0 || part == 2) g2l_tile<T, D, D, NW, 2>(lds0 + L::S_OFF, sS, sin, D, D, w, lane);
-    if (part == 0 || part == 3)
+    if (part == 0 || part == 3) {
       g2l_tile<T, D, 64, NW>(lds0 + L::V_OFF, sV, v + (size_t)ci.t0 * rs + (size_t)h * D, rs,
                              ci.len, w, lane);
+      g2l_tile<T, 64, 64, NW>(lds0 + L::IV_OFF, sIV, INV + ((size_t)c * H + h) * 4096, 64, 64, w,
+                              lane);
+    }
   };
   auto issue_front = [&](int it, int t) {
     const int c = it % NC, h = it / NC;
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       *(f4*)(sG + gch * PG + g4 * 16 + 4 * qq) =
           f4{x[4 * qq] + add, x[4 * qq + 1] + add, x[4 * qq + 2] + add, x[4 * qq + 3] + add};
   }
-  // S_in, v and k have landed: every copy of them is followed by at least g_raw and
+  // S_in, v, INV and k have landed: every copy of them is followed by at least g_raw and
   // beta (5 loads), the previous item's 2 NLT + NLR unconditional output stores and this
   // item's NLS dS_out loads (dO and dS_out may still be in flight; the dS_out stores to
   // LDS wait for both, in issue order)
@@ -277,9 +288,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   Frag fI[NKC], fIT[NKC], fMT[NKC];          // rows arow of INV, INV^T, Mqk^T
 #pragma unroll
   for (int ks = 0; ks < NKC; ++ks) {
-    fI[ks] = MM::load(INV + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
+    fI[ks] = MM::load(sIV + arow * PC + ks * KS + g4 * KPL);
     fMT[ks] = MM::ld_perm(MqkT + ch * 4096 + arow * 64, ks * KS, lane);
-    fIT[ks] = MM::load(INVT + ch * 4096 + arow * 64 + ks * KS + g4 * KPL);
+    fIT[ks] = MM::ld_tr_nat(sIV, PC, ks * KS, 16 * R1, lane);  // row arow of INV^T
   }
 
   // ------------------------------------------------------------- state side
@@ -796,7 +807,7 @@ static hipError_t gradf_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   hipLaunchKernelGGL((k_gradf<T, D>), dim3(grid), dim3(GF<T, D>::NT), 0, st, p.chunks, s.NC, s.H,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dO, p.g_raw,
                      p.beta, p.A_log, (const T*)p.h_saved, (const T*)p.dstates,
-                     (const T*)p.INV, (const T*)p.INVT, (const T*)p.MqkT, (T*)p.dq, (T*)p.dk,
+                     (const T*)p.INV, (const T*)p.MqkT, (T*)p.dq, (T*)p.dk,
                      (T*)p.dv, p.dg_raw, p.dbeta, p.dAl_part);
   return hipGetLastError();
 }

@@ -22,7 +22,6 @@ struct BwdPtrs {
   void* PT;                // [NC,H,K,64] act dtype: (Qd - Mqk W)^T
   float* eGT;              // [NC,H,K]  exp(G_T)
   void* INV;               // [NC,H,64,64] act dtype: (I + diag(beta) A)^{-1}
-  void* INVT;              // [NC,H,64,64] act dtype: its transpose
   void* MqkT;              // [NC,H,64,64] act dtype: Mqk transposed
   void* dstates;           // [NC,H,K,V] act dtype: dL/dS at the end of every chunk
   float* dAl_part;         // [NC,H] per chunk-head partial sums for dA_log

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
                                                 const float* __restrict__ A_log,
                                                 T* __restrict__ Tm, T* __restrict__ PT,
                                                 float* __restrict__ eGT, T* __restrict__ INVo,
-                                                T* __restrict__ INVTo, T* __restrict__ MqkTo) {
+                                                T* __restrict__ MqkTo) {
   using L = PL<T, D>;
   using MM = Mma<T>;
   typedef typename MM::Frag Frag;
@@ -448,28 +448,26 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) store_c<T>(sW, PN, 16 * R, c0 + nt * 16, acc[nt], lane);
   }
-  // ---- INV, INV^T, Mqk^T (act dtype, natural rows) for the gradient pass
+  // ---- INV and Mqk^T (act dtype, natural rows) for the gradient pass (which reads
+  // INV^T out of its copy of INV)
   for (int e = tid; e < 64 * 8; e += NT) {
     const int r = e >> 3, c8 = (e & 7) * 8;
-    float a[8], b[8], m[8];
+    float a[8], m[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       a[j] = sINV[r * PC + c8 + j];
-      b[j] = sINV[(c8 + j) * PC + r];
       m[j] = sM[(c8 + j) * PC + r];
     }
-    T ta[8], tb[8], tm[8];
+    T ta[8], tm[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       ta[j] = from_f<T>(a[j]);
-      tb[j] = from_f<T>(b[j]);
       tm[j] = from_f<T>(m[j]);
     }
     const size_t o = ch * 64 * 64 + r * 64 + c8;
 #pragma unroll
     for (int v = 0; v < 8 * L::ES / 16; ++v) {
       ((uint4*)(INVo + o))[v] = ((const uint4*)ta)[v];
-      ((uint4*)(INVTo + o))[v] = ((const uint4*)tb)[v];
       ((uint4*)(MqkTo + o))[v] = ((const uint4*)tm)[v];
     }
   }
@@ -536,7 +534,7 @@ static hipError_t prep_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const int grid = items < resident ? items : resident;
   hipLaunchKernelGGL((k_prep<T, D>), dim3(grid), dim3(PL<T, D>::NT), 0, st, p.chunks, s.NC, s.H, (const T*)p.q,
                      (const T*)p.k, p.g_raw, p.beta, p.A_log, (T*)p.Tm, (T*)p.PT, p.eGT,
-                     (T*)p.INV, (T*)p.INVT, (T*)p.MqkT);
+                     (T*)p.INV, (T*)p.MqkT);
   return hipGetLastError();
 }
 
