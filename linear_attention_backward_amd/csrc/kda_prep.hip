@@ -480,7 +480,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     Frag bw[NKC];  // W[s][16 w + cl], s in the permuted order of k-step ks
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) bw[ks] = MM::ld_tr(sW, PN, ks * KS, 16 * w, lane);
-#pragma unroll 2
+#pragma unroll
     for (int mt = 0; mt < NW; ++mt) {
       f4 acc = zero4();
 #pragma unroll
