@@ -39,13 +39,13 @@ def kernel_bytes_per_token_head(D=128, es=2):
     state = D * D * es / 64.0   # one K x V state per chunk
     sq = 64 * 64 * es / 64.0    # one 64 x 64 matrix per chunk
     return {
-        # q, k, g_raw, beta -> Tm (KxK), PT (Kx64), eGT, INV, INV^T, Mqk^T
-        "prep": 2 * act + f32row + 4 + state + D * 64 * es / 64.0 + D * 4 / 64.0 + 3 * sq,
+        # q, k, g_raw, beta -> Tm (KxK), PT (Kx64), eGT, INV, Mqk^T
+        "prep": 2 * act + f32row + 4 + state + D * 64 * es / 64.0 + D * 4 / 64.0 + 2 * sq,
         # Tm, PT, eGT, dO -> dS_out
         "scan": state + D * 64 * es / 64.0 + D * 4 / 64.0 + act + state,
-        # q, k, v, dO, g_raw, beta, S_in, dS_out, INV, INV^T, Mqk^T
+        # q, k, v, dO, g_raw, beta, S_in, dS_out, INV, Mqk^T
         #   -> dq, dk, dv, dg_raw, dbeta, dA_log partial
-        "grad": 4 * act + f32row + 4 + 2 * state + 3 * sq + 3 * act + f32row + 4 + 4 / 64.0,
+        "grad": 4 * act + f32row + 4 + 2 * state + 2 * sq + 3 * act + f32row + 4 + 4 / 64.0,
     }
 
 
