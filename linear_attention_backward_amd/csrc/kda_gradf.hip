@@ -1,4 +1,5 @@
-// kda_gradf.hip -- fused gradient pass: one workgroup (D/16 waves) per chunk-head.
+// kda_gradf.hip -- fused gradient pass: workgroups of D/16 waves, each walking a share of
+// the chunk-heads (persistent; the next one's tiles are fetched during the current one).
 //
 // Quantities per chunk (G: in-chunk cumulative gate; Kd = K e^G, Kr = K e^{G_T-G},
 // Qd = Q e^G; INV and Mqk from the prep pass; S_in the chunk start state; dS_out
@@ -21,11 +22,11 @@
 //     dg = reverse cumsum of dG (rows);  dg_raw = dg . (-e^{A_log} sigmoid(g_raw))
 //     dA_log partial = sum dg . g
 // The epilogue stays fp32 ([KB] B3: dk_d - dk_i - dk_r cancels strongly).  The
-// pairwise decays e^{G_r-G_s} never come from exp(-G) (it overflows): across
-// 16-row blocks and across 4-row sub-blocks inside a block they factor through an
-// anchor row between r and s (both factors <= 1) and run on MFMA with the decayed
-// operand carried at fp32 accuracy (hi + lo bf16); inside a 4x4 diagonal sub-block
-// they are products of per-token decays (VALU).
+// pairwise decays e^{G_r-G_s} never come from exp(-G) (it overflows): across 16-row
+// blocks they factor through an anchor row between r and s (both factors <= 1) and
+// run on MFMA with the decayed operand carried at fp32 accuracy (hi + lo bf16); inside
+// a 16-row diagonal block they are running products of per-token decays, summed
+// exactly in fp32 on VALU.
 #include "kda_dev.h"
 #include "kda_launch.h"
 
