@@ -84,6 +84,13 @@ EXTRA = {
     "ragged_fp32": Workload("ragged_fp32", 1, 1 + 63 + 64 + 65 + 200, 2, 64, 64, "f32",
                             1105, varlen_seqs=5, fixed_lengths=(1, 63, 64, 65, 200),
                             h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0),
+    # several sequences of a length that is not a multiple of the chunk (no cu_seqlens:
+    # every sequence ends in a ragged chunk), odd head count
+    "multi_ragged_bf16": Workload("multi_ragged_bf16", 3, 100, 3, 128, 128, "bf16", 1107,
+                                  h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0),
+    # one token per sequence
+    "single_token_fp32": Workload("single_token_fp32", 2, 1, 1, 64, 64, "f32", 1108,
+                                  h0_std=0.5, dht_std=1.0),
     # bf16 with K = V = 64 (the other supported bf16 head size)
     "ragged_bf16_d64": Workload("ragged_bf16_d64", 1, 1 + 63 + 64 + 65 + 200, 4, 64, 64, "bf16",
                                 1106, varlen_seqs=5, fixed_lengths=(1, 63, 64, 65, 200),

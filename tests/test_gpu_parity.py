@@ -41,13 +41,14 @@ def _check(name, heads=None, use_h_saved=True):
     return res
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "weak_decay_fp32", "ragged_fp32"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "weak_decay_fp32", "ragged_fp32",
+                                  "single_token_fp32"])
 def test_parity_fp32(name):
     _check(name)
 
 
 @pytest.mark.parametrize("name", ["single_seq_bf16", "weak_decay_bf16", "strong_decay_bf16",
-                                  "ragged_bf16", "ragged_bf16_d64"])
+                                  "ragged_bf16", "ragged_bf16_d64", "multi_ragged_bf16"])
 def test_parity_bf16(name):
     _check(name)
 
@@ -111,7 +112,8 @@ def test_split_scan_zero_length(monkeypatch):
 
 
 @pytest.mark.parametrize("name,cap", [("ragged_fp32", 3), ("ragged_bf16", 3),
-                                      ("ragged_bf16_d64", 2), ("weak_decay_bf16", 5)])
+                                      ("ragged_bf16_d64", 2), ("weak_decay_bf16", 5),
+                                      ("multi_ragged_bf16", 2)])
 def test_persistent_walk(name, cap, monkeypatch):
     """Prep and the gradient pass with a grid of `cap` workgroups: each workgroup walks
     many (chunk, head) items and hands the prefetched tiles of the next item over
