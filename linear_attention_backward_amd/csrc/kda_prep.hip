@@ -98,12 +98,13 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   auto issue_loads = [&](int it, int t, const ChunkInfo ci) {
     const int h = it / NC;
     const size_t hD = (size_t)h * D;
-    const float* gh = g_raw + (size_t)ci.t0 * rs + hD + t % D;
+    const float* gh = g_raw + (size_t)ci.t0 * rs + hD;  // uniform; 32-bit lane offsets
     const int part = t / D;  // 4 parts of 16 rows
+    const unsigned urs = (unsigned)rs;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int r = part * 16 + rr;
-      rg[rr] = gh[(r < ci.len ? r : ci.len - 1) * rs];
+      rg[rr] = gh[(unsigned)(r < ci.len ? r : ci.len - 1) * urs + (unsigned)(t % D)];
     }
     rbeta = beta[(size_t)(ci.t0 + ((t & 63) < ci.len ? (t & 63) : ci.len - 1)) * H + h];
     const T* qh = q + (size_t)ci.t0 * rs + hD;
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 #pragma unroll
     for (int l = 0; l < NLT; ++l) {  // rows past the chunk: zeroed when stored
       const int idx = t + l * NT, r = idx / VPR, vv = idx % VPR;
-      const size_t o = (size_t)(r < ci.len ? r : ci.len - 1) * rs + vv * EPV;
+      const unsigned o = (unsigned)(r < ci.len ? r : ci.len - 1) * (unsigned)rs + vv * EPV;
       rq[l] = *(const u32x4*)(qh + o);
       rk[l] = *(const u32x4*)(kh + o);
     }
