@@ -42,7 +42,8 @@ template <typename T, int D> struct PL {
   static constexpr int SCR_OFF = KD_OFF + N_SZ; // INV block-substitution scratch
   static constexpr int SCR_SZ = 4 * 16 * 17 * 4;
   static constexpr int B_OFF = SCR_OFF + SCR_SZ;
-  static constexpr int TOTAL = B_OFF + 256;
+  static constexpr int TOT_OFF = B_OFF + 256;     // gate totals of the 4 row parts [4][D]
+  static constexpr int TOTAL = TOT_OFF + 4 * D * 4;
   // Tm and PT staging, over A, INV, Kd and the scratch once W is formed
   static constexpr int TMS_OFF = A_OFF;
   static constexpr int PTS_OFF = TMS_OFF + D * PTM * ES;
@@ -139,7 +140,12 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   const size_t ch = (size_t)c * H + h;
   const float aA = __expf(A_log[h]);
   if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
-  {  // in-chunk cumulative gate (log2 units), natural: sG[r][i]
+  // in-chunk cumulative gate (log2 units), natural: sG[r][i].  Thread (part, i) sums
+  // channel i over rows 16 part .. + 15 in registers and publishes the part's total;
+  // after the barrier it adds the totals of the earlier parts and writes its rows.
+  float* sTot = (float*)(smem + L::TOT_OFF);
+  float gx[16];
+  {
     const int i = tid % D, part = tid / D;
     float run = 0.f;
 #pragma unroll
@@ -147,8 +153,9 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       const int r = part * 16 + rr;
       const float gv = gate_log2(rg[rr], aA);
       run += r < Lr ? gv : 0.f;
-      sG[r * PGN + i] = run;
+      gx[rr] = run;
     }
+    sTot[part * D + i] = run;
   }
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {
@@ -162,11 +169,9 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   {
     const int i = tid % D, part = tid / D;
     float add = 0.f;
-    for (int pp = 0; pp < part; ++pp) add += sG[(pp * 16 + 15) * PGN + i];
-    __syncthreads();
-    if (part > 0)
+    for (int pp = 0; pp < part; ++pp) add += sTot[pp * D + i];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sG[(part * 16 + rr) * PGN + i] += add;
+    for (int rr = 0; rr < 16; ++rr) sG[(part * 16 + rr) * PGN + i] = gx[rr] + add;
   }
   __syncthreads();
 
