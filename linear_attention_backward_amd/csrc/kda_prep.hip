@@ -96,26 +96,34 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   // the chunk are zero (q, k) or masked at the cumsum (g_raw).
   float rg[16], rbeta;
   u32x4 rq[NLT], rk[NLT];
-  auto issue_loads = [&](int it, int t, const ChunkInfo ci) {
+  // parts: 1 = g_raw rows 0-7 of the thread's 16 and beta, 2 = g_raw rows 8-15,
+  // 4 = q, 8 = k.  A CU keeps a bounded number of cache lines in flight and a wave
+  // stalls at issue once that is reached, so the loads go out in two portions,
+  // at the start and at the end of the A/Mqk phase, not in one burst.
+  auto issue_loads = [&](int it, int t, const ChunkInfo ci, const int parts) {
     const int h = it / NC;
     const size_t hD = (size_t)h * D;
-    const float* gh = g_raw + (size_t)ci.t0 * rs + hD;  // uniform; 32-bit lane offsets
-    const int part = t / D;  // 4 parts of 16 rows
-    const unsigned urs = (unsigned)rs;
+    // 4 parts of 16 rows; a part is one (D = 64) or two (D = 128) whole waves, so
+    // the row addresses are uniform and the 16 loads share one lane offset
+    const int part = __builtin_amdgcn_readfirstlane(t / D);
+    const float* gh = g_raw + (size_t)ci.t0 * rs + hD;
+    const unsigned lo = (unsigned)(t % D);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
+      if (!(parts & (rr < 8 ? 1 : 2))) continue;
       const int r = part * 16 + rr;
-      rg[rr] = gh[(unsigned)(r < ci.len ? r : ci.len - 1) * urs + (unsigned)(t % D)];
+      const float* rowp = gh + (unsigned)((r < ci.len ? r : ci.len - 1) * (int)rs);
+      rg[rr] = rowp[lo];
     }
-    rbeta = beta[(size_t)(ci.t0 + ((t & 63) < ci.len ? (t & 63) : ci.len - 1)) * H + h];
+    if (parts & 1) rbeta = beta[(size_t)(ci.t0 + ((t & 63) < ci.len ? (t & 63) : ci.len - 1)) * H + h];
     const T* qh = q + (size_t)ci.t0 * rs + hD;
     const T* kh = k + (size_t)ci.t0 * rs + hD;
 #pragma unroll
     for (int l = 0; l < NLT; ++l) {  // rows past the chunk: zeroed when stored
       const int idx = t + l * NT, r = idx / VPR, vv = idx % VPR;
       const unsigned o = (unsigned)(r < ci.len ? r : ci.len - 1) * (unsigned)rs + vv * EPV;
-      rq[l] = *(const u32x4*)(qh + o);
-      rk[l] = *(const u32x4*)(kh + o);
+      if (parts & 4) rq[l] = *(const u32x4*)(qh + o);
+      if (parts & 8) rk[l] = *(const u32x4*)(kh + o);
     }
   };
   auto settle_loads = [&]() {
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     settle(rq);
     settle(rk);
   };
-  if ((int)blockIdx.x < items) issue_loads(blockIdx.x, tid0, chunks[blockIdx.x % NC]);
+  if ((int)blockIdx.x < items) issue_loads(blockIdx.x, tid0, chunks[blockIdx.x % NC], 15);
   settle_loads();
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
   // thread indices re-derived per item so that the lane-dependent LDS addresses
@@ -164,7 +172,6 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     *(u32x4*)(sQ + r * PN + vv * EPV) = rq[l] & m;
     *(u32x4*)(sK + r * PN + vv * EPV) = rk[l] & m;
   }
-  if (nxt < items) issue_loads(nxt, tid, cnx);
   __syncthreads();
   {
     const int i = tid % D, part = tid / D;
@@ -174,6 +181,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     for (int rr = 0; rr < 16; ++rr) sG[(part * 16 + rr) * PGN + i] = gx[rr] + add;
   }
   __syncthreads();
+  if (nxt < items) issue_loads(nxt, tid, cnx, 1 | 4);  // g_raw rows 0-7, beta, q
 
   // Kr = K exp(G_T - G), beta Kd = beta K exp(G): natural tiles of T
   auto kr_kd = [&](int t, int n) {
@@ -371,6 +379,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   }
   if constexpr (NW == 4) kr_kd(tid, NT);
   __syncthreads();
+  if (nxt < items) issue_loads(nxt, tid, cnx, 2 | 8);  // g_raw rows 8-15, k
 
   // ---- INV = (I + L)^{-1}, L = diag(beta) A (strictly lower), blocked by 16.
   // Step 1: wave R < 4 inverts its unit lower-triangular diagonal block (forward
