@@ -444,12 +444,6 @@ __device__ __forceinline__ void g2l_tile(unsigned lds0, T* lds_tile, const T* sr
 }
 // Wait until this wave's global loads (including global -> LDS copies) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-// Wait until at most N of this wave's vector memory operations are outstanding.
-// They complete in issue order, so everything issued before the last N is done.
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
-}
 
 // Registers filled by loads issued well before their use (a prefetch for the next
 // work item): passing them through an empty asm makes the compiler wait for those

@@ -277,11 +277,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       *(f4*)(sG + gch * PG + g4 * 16 + 4 * qq) =
           f4{x[4 * qq] + add, x[4 * qq + 1] + add, x[4 * qq + 2] + add, x[4 * qq + 3] + add};
   }
-  // S_in, v, INV and k have landed: every copy of them is followed by at least g_raw and
-  // beta (5 loads), the previous item's 2 NLT + NLR unconditional output stores and this
-  // item's NLS dS_out loads (dO and dS_out may still be in flight; the dS_out stores to
+  // S_in, v, INV and k have landed: they were issued before g_raw and beta, which the
+  // previous item waited for (dO and dS_out may still be in flight; the dS_out stores to
   // LDS wait for both, in issue order)
-  wait_vmcnt<2 * NLT + NLR + NLS>();
   __syncthreads();
   Frag kf[NKD];                              // raw k of row arow (permuted k order)
 #pragma unroll
@@ -791,6 +789,11 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const int r = r0 < Lr ? r0 : Lr - 1;
     *(f4*)(dg_raw + (t0 + r) * rs + hD + sv * 4) = *(const f4*)(sR + r * PR + sv * 4);
   }
+  // The next item's g_raw and beta (and so, in issue order, its k, S_in, v and INV)
+  // are waited for here, before the dO copy: the compiler does not see that copy, so a
+  // wait at their first use would also cover this item's dq and dk stores.
+  settle(rg);
+  settle(rbeta);
   // dO over the dq staging, which is read out; issued after this item's last stores
   // so that the next item's first waits skip it
   if (nxt < items) issue_late(nxt, tid);
