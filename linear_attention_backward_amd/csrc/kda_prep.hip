@@ -383,25 +383,25 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 
   // ---- INV = (I + L)^{-1}, L = diag(beta) A (strictly lower), blocked by 16.
   // Step 1: wave R < 4 inverts its unit lower-triangular diagonal block (forward
-  // substitution, one column per lane); with eight waves, waves 4-7 form Kr and Kd
-  // meanwhile.
-  if constexpr (NW == 8) {
-    if (w >= 4) kr_kd(tid - 256, NT - 256);
-  }
+  // substitution, one column per lane).
   if (w < 4) {
     const int R = w;
     if (lane < 16) {
-      float x[16];
+      // right-looking: once x_s is final it is taken off every later row, so the
+      // dependent chain is one FMA per row; each row still sums its terms in the
+      // order s = 0, 1, ...
+      float acc[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == lane) ? 1.f : 0.f;
-        const float br = sBeta[16 * R + r];
+      for (int r = 0; r < 16; ++r) acc[r] = (r == lane) ? 1.f : 0.f;
 #pragma unroll
-        for (int s = 0; s < r; ++s) acc -= br * sA[(16 * R + r) * PC + 16 * R + s] * x[s];
-        x[r] = acc;
+      for (int s = 0; s < 16; ++s) {
+        const float xs = acc[s];
+#pragma unroll
+        for (int r = s + 1; r < 16; ++r)
+          acc[r] -= sBeta[16 * R + r] * sA[(16 * R + r) * PC + 16 * R + s] * xs;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sINV[(16 * R + r) * PC + 16 * R + lane] = x[r];
+      for (int r = 0; r < 16; ++r) sINV[(16 * R + r) * PC + 16 * R + lane] = acc[r];
     }
     for (int e = lane; e < 16 * 64; e += 64) {
       const int r = e >> 6, col = e & 63;
@@ -410,7 +410,11 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   }
   __syncthreads();
   // Step 2: wave S < 3 fills column block S below the diagonal, top to bottom:
-  //   INV_{R,S} = -D_R * sum_{J=S}^{R-1} L_{R,J} INV_{J,S}.
+  //   INV_{R,S} = -D_R * sum_{J=S}^{R-1} L_{R,J} INV_{J,S};
+  // with eight waves, waves 3-7 form Kr and Kd meanwhile (first read by W and Tm).
+  if constexpr (NW == 8) {
+    if (w >= 3) kr_kd(tid - 192, NT - 192);
+  }
   if (w < 3) {
     const int S = w;
     float* scr = sScr + w * 16 * 17;
