@@ -18,6 +18,10 @@
  *
  *   g_t   = -exp(A_log[h]) * softplus(g_raw_t)              (per key channel, <= 0)
  *   S_t   = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *
+ * Gate variants ([KB] part 2, the gate epilogue K1 and its dt_bias reduction): a
+ * per-channel bias inside the softplus, and a gate given in log2 units (decay 2^g);
+ * both live in the gate map and its chain rule below.
  *   o_t   = S_t^T q_t
  *
  * with S in R^{K x V}, S_{-1} = h0 (or 0), one recurrence per (sequence, head).
@@ -72,28 +76,44 @@ int kda_oracle_num_threads(void) {
 #endif
 }
 
-/* g = -exp(A_log[h]) * softplus(g_raw); softplus(x) = max(x,0) + log1p(exp(-|x|)). */
+/* Gate map.  The gate of token t, head h, key channel i is
+ *   g' = -exp(A_log[h]) * softplus(g_raw + dt_bias[h][i]),   dt_bias absent = 0,
+ * softplus(x) = max(x,0) + log1p(exp(-|x|)).  The per-step decay is exp(g') for a
+ * gate in natural-log units (unit = 1) and 2^{g'} = exp(g' ln 2) for a gate in log2
+ * units (unit = ln 2).  Returned: g = unit * g', the natural-log exponent the
+ * recurrence applies. */
 void kda_oracle_gate(int64_t TT, int H, int K, const double* g_raw, const double* A_log,
-                     double* g) {
+                     const double* dt_bias, double unit, double* g) {
   for (int64_t t = 0; t < TT; ++t)
     for (int h = 0; h < H; ++h) {
       double a = exp(A_log[h]);
-      for (int i = 0; i < K; ++i) g[IDX3(t, h, i, H, K)] = -a * softplus(g_raw[IDX3(t, h, i, H, K)]);
+      for (int i = 0; i < K; ++i) {
+        double x = g_raw[IDX3(t, h, i, H, K)] + (dt_bias ? dt_bias[(int64_t)h * K + i] : 0.0);
+        g[IDX3(t, h, i, H, K)] = unit * (-a * softplus(x));
+      }
     }
 }
 
-/* Chain rule through the gate: dg_raw = dg * (-exp(A_log) * sigmoid(g_raw)),
- * dA_log[h] = sum over all tokens and key channels of dg * g  (dg/dA_log = g). */
+/* Chain rule through the gate map, from dg = dL/dg (g as returned above):
+ *   dg_raw = dg * unit * (-exp(A_log) * sigmoid(g_raw + dt_bias)),
+ *   dA_log[h] = sum over tokens and key channels of dg * g   (dg/dA_log = g),
+ *   ddt_bias[h][i] = sum over tokens of dg_raw                (NULL = not wanted). */
 void kda_oracle_gate_backward(int64_t TT, int H, int K, const double* g_raw, const double* A_log,
-                              const double* g, const double* dg, double* dg_raw, double* dA_log) {
+                              const double* dt_bias, double unit, const double* g,
+                              const double* dg, double* dg_raw, double* dA_log,
+                              double* ddt_bias) {
   for (int h = 0; h < H; ++h) {
     double a = exp(A_log[h]);
     double acc = 0.0;
+    if (ddt_bias)
+      for (int i = 0; i < K; ++i) ddt_bias[(int64_t)h * K + i] = 0.0;
     for (int64_t t = 0; t < TT; ++t)
       for (int i = 0; i < K; ++i) {
         int64_t x = IDX3(t, h, i, H, K);
-        dg_raw[x] = dg[x] * (-a * sigmoid(g_raw[x]));
+        double xr = g_raw[x] + (dt_bias ? dt_bias[(int64_t)h * K + i] : 0.0);
+        dg_raw[x] = dg[x] * unit * (-a * sigmoid(xr));
         acc += dg[x] * g[x];
+        if (ddt_bias) ddt_bias[(int64_t)h * K + i] += dg_raw[x];
       }
     dA_log[h] = acc;
   }

@@ -9,6 +9,7 @@ Every function takes numpy arrays in the packed token-major layout
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -55,9 +56,10 @@ def _load():
         lib = ctypes.CDLL(build())
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int
-        lib.kda_oracle_gate.argtypes = [i64, i32, i32, P, P, P]
+        lib.kda_oracle_gate.argtypes = [i64, i32, i32, P, P, P, ctypes.c_double, P]
         lib.kda_oracle_gate.restype = None
-        lib.kda_oracle_gate_backward.argtypes = [i64, i32, i32, P, P, P, P, P, P]
+        lib.kda_oracle_gate_backward.argtypes = [i64, i32, i32, P, P, P, ctypes.c_double, P, P, P,
+                                                 P, P]
         lib.kda_oracle_gate_backward.restype = None
         fwd = [i32, P, i32, i32, i32, P, P, P, P, P, P, i32, P, P, P, i32]
         lib.kda_oracle_forward.argtypes = fwd
@@ -90,24 +92,31 @@ def _nchunks(cu, C):
     return int(sum((int(l) + C - 1) // C for l in lens))
 
 
-def gate(g_raw, A_log):
-    """g = -exp(A_log[h]) * softplus(g_raw)."""
+def gate(g_raw, A_log, dt_bias=None, log2_units=False):
+    """g = unit * (-exp(A_log[h]) * softplus(g_raw + dt_bias[h])), the natural-log decay
+    exponent per token and key channel; unit = ln 2 for a gate in log2 units, else 1."""
     g_raw, A_log = _d(g_raw), _d(A_log)
     TT, H, K = g_raw.shape
     g = np.empty_like(g_raw)
-    _load().kda_oracle_gate(TT, H, K, _p(g_raw), _p(A_log), _p(g))
+    db = None if dt_bias is None else _d(np.broadcast_to(dt_bias, (H, K)))
+    _load().kda_oracle_gate(TT, H, K, _p(g_raw), _p(A_log), _p(db),
+                            math.log(2.0) if log2_units else 1.0, _p(g))
     return g
 
 
-def gate_backward(g_raw, A_log, g, dg):
-    """dg_raw = dg * (-exp(A_log) sigmoid(g_raw));  dA_log[h] = sum dg * g."""
+def gate_backward(g_raw, A_log, g, dg, dt_bias=None, log2_units=False):
+    """dg_raw = dg * unit * (-exp(A_log) sigmoid(g_raw + dt_bias));  dA_log[h] = sum dg * g;
+    ddt_bias[h, i] = sum over tokens of dg_raw.  Returns (dg_raw, dA_log, ddt_bias)."""
     g_raw, A_log, g, dg = _d(g_raw), _d(A_log), _d(g), _d(dg)
     TT, H, K = g_raw.shape
     dg_raw = np.empty_like(g_raw)
     dA = np.empty(H, dtype=np.float64)
-    _load().kda_oracle_gate_backward(TT, H, K, _p(g_raw), _p(A_log), _p(g), _p(dg), _p(dg_raw),
-                                     _p(dA))
-    return dg_raw, dA
+    ddt = np.empty((H, K), dtype=np.float64)
+    db = None if dt_bias is None else _d(np.broadcast_to(dt_bias, (H, K)))
+    _load().kda_oracle_gate_backward(TT, H, K, _p(g_raw), _p(A_log), _p(db),
+                                     math.log(2.0) if log2_units else 1.0, _p(g), _p(dg),
+                                     _p(dg_raw), _p(dA), _p(ddt))
+    return dg_raw, dA, ddt
 
 
 def _forward(fn, q, k, v, g, beta, h0, cu, chunk, want_states, nthreads):
@@ -164,15 +173,19 @@ def backward(q, k, v, g, beta, h0, dO, dht, cu, chunk=64, want_dstates=False, nt
 def kda_backward(inp: dict, want_dstates=False, want_states=False, nthreads=0) -> dict:
     """Full backward from raw inputs (an input dict as produced by kda_inputs):
     gate, per-token backward, gate chain rule.  Returns fp64 arrays dq, dk, dv,
-    dg_raw, dA_log, dbeta, dh0 (+ dstates / states on request)."""
-    g = gate(inp["g_raw"], inp["A_log"])
+    dg_raw, dA_log, dbeta, dh0, ddt_bias (+ dstates / states on request).  Optional
+    entries: dt_bias [H, K] (added inside the softplus) and gate_log2 (the gate is in
+    log2 units: the decay per step is 2^g)."""
+    gkw = dict(dt_bias=inp.get("dt_bias"), log2_units=bool(inp.get("gate_log2", False)))
+    g = gate(inp["g_raw"], inp["A_log"], **gkw)
     cu = inp["cu_seqlens"]
     out = backward(inp["q"], inp["k"], inp["v"], g, inp["beta"], inp["h0"], inp["dO"],
                    inp["dht"], cu, chunk=inp.get("chunk", 64), want_dstates=want_dstates,
                    nthreads=nthreads)
-    dg_raw, dA = gate_backward(inp["g_raw"], inp["A_log"], g, out["dg"])
+    dg_raw, dA, ddt = gate_backward(inp["g_raw"], inp["A_log"], g, out["dg"], **gkw)
     out["dg_raw"] = dg_raw
     out["dA_log"] = dA
+    out["ddt_bias"] = ddt
     out["g"] = g
     if want_states:
         o, ht, st = forward(inp["q"], inp["k"], inp["v"], g, inp["beta"], inp["h0"], cu,

@@ -41,7 +41,8 @@ def _rand_case(seed, lens, H, K, V, decay=0.5, with_state=True):
 def _loss(c, **over):
     d = dict(c)
     d.update(over)
-    g = O.gate(d["g_raw"], d["A_log"])
+    g = O.gate(d["g_raw"], d["A_log"], dt_bias=d.get("dt_bias"),
+               log2_units=bool(d.get("gate_log2", False)))
     o, ht, _ = O.forward(d["q"], d["k"], d["v"], g, d["beta"], d["h0"], d["cu"], chunk=4,
                          want_states=False)
     L = float(np.sum(o * d["dO"]))
@@ -54,7 +55,7 @@ def _full_backward(c, chunk=4):
     g = O.gate(c["g_raw"], c["A_log"])
     out = O.backward(c["q"], c["k"], c["v"], g, c["beta"], c["h0"], c["dO"], c["dht"], c["cu"],
                      chunk=chunk, want_dstates=True)
-    dg_raw, dA = O.gate_backward(c["g_raw"], c["A_log"], g, out["dg"])
+    dg_raw, dA, _ = O.gate_backward(c["g_raw"], c["A_log"], g, out["dg"])
     out["dg_raw"], out["dA_log"] = dg_raw, dA
     return out
 
@@ -250,7 +251,7 @@ def test_gate_against_library_routines():
     ref = -np.exp(A_log)[None, :, None] * np.logaddexp(0.0, g_raw)
     np.testing.assert_allclose(g, ref, rtol=1e-14)
     dg = rng.standard_normal(g.shape)
-    dg_raw, dA = O.gate_backward(g_raw, A_log, g, dg)
+    dg_raw, dA, _ = O.gate_backward(g_raw, A_log, g, dg)
     np.testing.assert_allclose(dg_raw, dg * (-np.exp(A_log)[None, :, None] * expit(g_raw)),
                                rtol=1e-13)
     np.testing.assert_allclose(dA, np.sum(dg * ref, axis=(0, 2)), rtol=1e-12)
@@ -266,3 +267,82 @@ def test_parallel_matches_serial():
                    nthreads=4)
     for key in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
         assert np.array_equal(a[key], b[key]), key
+
+
+def _as_inputs(c, **over):
+    d = dict(c)
+    d.update(over)
+    return dict(q=d["q"], k=d["k"], v=d["v"], g_raw=d["g_raw"], A_log=d["A_log"], beta=d["beta"],
+                h0=d["h0"], dO=d["dO"], dht=d["dht"], cu_seqlens=d["cu"], chunk=4,
+                dt_bias=d.get("dt_bias"), gate_log2=d.get("gate_log2", False))
+
+
+_GRADS = ("dq", "dk", "dv", "dg_raw", "dA_log", "dbeta", "dh0")
+
+
+def test_gate_variants_against_library_routines():
+    """The gate map with a per-channel bias and in log2 units against numpy's
+    logaddexp; its chain rule against scipy's logistic function; the bias gradient
+    against numpy's sum over tokens."""
+    from scipy.special import expit
+    rng = np.random.default_rng(21)
+    g_raw = rng.standard_normal((7, 3, 4)) * 4
+    A_log = rng.uniform(-1, math.log(16), size=3)
+    db = rng.standard_normal((3, 4))
+    for log2_units, unit in ((False, 1.0), (True, math.log(2.0))):
+        x = g_raw + db[None]
+        g = O.gate(g_raw, A_log, dt_bias=db, log2_units=log2_units)
+        ref = unit * (-np.exp(A_log)[None, :, None] * np.logaddexp(0.0, x))
+        np.testing.assert_allclose(g, ref, rtol=1e-14)
+        dg = rng.standard_normal(g.shape)
+        dg_raw, dA, ddt = O.gate_backward(g_raw, A_log, g, dg, dt_bias=db, log2_units=log2_units)
+        ref_raw = dg * unit * (-np.exp(A_log)[None, :, None] * expit(x))
+        np.testing.assert_allclose(dg_raw, ref_raw, rtol=1e-13)
+        np.testing.assert_allclose(dA, np.sum(dg * ref, axis=(0, 2)), rtol=1e-12)
+        np.testing.assert_allclose(ddt, ref_raw.sum(axis=0), rtol=1e-12, atol=1e-15)
+
+
+def test_log2_gate_is_a_shifted_A_log():
+    """A gate in log2 units decays by 2^g = exp(g ln 2), and ln 2 e^{A_log} =
+    e^{A_log + ln ln 2}: every output equals that of the natural-log gate with A_log
+    shifted by ln(ln 2), gradients included (dA_log too, the shift being additive)."""
+    c = _rand_case(22, [6, 11], H=2, K=4, V=3)
+    a = O.kda_backward(_as_inputs(c, gate_log2=True))
+    b = O.kda_backward(_as_inputs(c, A_log=c["A_log"] + math.log(math.log(2.0))))
+    for name in _GRADS + ("ddt_bias",):
+        np.testing.assert_allclose(a[name], b[name], rtol=1e-11, atol=1e-13, err_msg=name)
+
+
+def test_dt_bias_is_a_shifted_g_raw():
+    """A bias inside the softplus is the same as adding it to g_raw: every output
+    agrees with the unbiased problem on g_raw + dt_bias, and ddt_bias is the sum of
+    dg_raw over all tokens."""
+    c = _rand_case(23, [6, 11], H=2, K=4, V=3)
+    db = np.random.default_rng(24).standard_normal((2, 4))
+    a = O.kda_backward(_as_inputs(c, dt_bias=db))
+    b = O.kda_backward(_as_inputs(c, g_raw=c["g_raw"] + db[None]))
+    for name in _GRADS:
+        np.testing.assert_allclose(a[name], b[name], rtol=1e-12, atol=1e-14, err_msg=name)
+    np.testing.assert_allclose(a["ddt_bias"], b["dg_raw"].sum(axis=0), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("gate_log2", [False, True])
+def test_finite_differences_gate_variants(gate_log2):
+    """Central differences of the oracle forward against its backward for dt_bias,
+    g_raw and A_log, with a bias present and the gate in either unit."""
+    c = _rand_case(25, [5, 7], H=2, K=4, V=3)
+    c["dt_bias"] = np.random.default_rng(26).standard_normal((2, 4))
+    c["gate_log2"] = gate_log2
+    out = O.kda_backward(_as_inputs(c))
+    eps = 1e-6
+    for name, gname in (("dt_bias", "ddt_bias"), ("g_raw", "dg_raw"), ("A_log", "dA_log")):
+        x = c[name]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy()
+            xp[idx] += eps
+            xm = x.copy()
+            xm[idx] -= eps
+            num[idx] = (_loss(c, **{name: xp}) - _loss(c, **{name: xm})) / (2 * eps)
+        err = np.abs(num - out[gname]).max() / np.abs(num).max()
+        assert err < 1e-7, (name, err)
