@@ -3,11 +3,14 @@
  * delta-rule linear attention on AMD Instinct MI355X (gfx950).
  *
  * Method.  Per (sequence n, head h), with S in R^{K x V}:
- *   g_t = -exp(A_log[h]) * softplus(g_raw_t)                  (per key channel)
+ *   g_t = -exp(A_log[h]) * softplus(g_raw_t + dt_bias[h])      (per key channel)
  *   S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
  *   o_t = S_t^T q_t,            S_{-1} = h0[n,h] (zero if absent)
- * kda_bwd returns the gradients of  L = sum(dO . o) + sum(dht . S_T)  with respect
- * to q, k, v, g_raw, A_log, beta and h0.  It is computed chunkwise (64 tokens):
+ * dt_bias [H,K] is optional (zero if absent).  With gate_units = KDA_GATE_LOG2 the
+ * gate is in log2 units: Diag(2^g_t) replaces Diag(exp g_t) (bwd-kernelB-beginner-
+ * guide-full, R1, applies the gate with exp2; its K1 reduces ddt_bias).  kda_bwd
+ * returns the gradients of  L = sum(dO . o) + sum(dht . S_T)  with respect to q, k, v,
+ * g_raw, A_log, beta, h0 and dt_bias.  It is computed chunkwise (64 tokens):
  * a serial reverse scan carries the state gradient dS back across chunks
  * ("Kernel A", bwd-ncu-and-optimization-playbook, section 3.5 on split-V), then a
  * data-parallel pass per chunk produces the per-token gradients, the gate
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define KDA_API __attribute__((visibility("default")))
@@ -66,6 +69,10 @@ extern "C" {
 #define KDA_DTYPE_F32 0
 #define KDA_DTYPE_BF16 1
 
+/* Units of the gate g (kda_problem.gate_units). */
+#define KDA_GATE_LN 0   /* decay exp(g) per step */
+#define KDA_GATE_LOG2 1 /* decay 2^g per step */
+
 /* Problem description.  Host memory; read during the call only. */
 typedef struct kda_problem {
   int B, T, H, K, V;  /* batch, tokens per batch row, heads, key dim, value dim */
@@ -78,6 +85,7 @@ typedef struct kda_problem {
    * neither. */
   const int32_t* cu_seqlens_host;
   const int32_t* cu_seqlens_dev;
+  int gate_units;     /* KDA_GATE_LN or KDA_GATE_LOG2 (anything else: invalid) */
 } kda_problem;
 
 /* Device pointers for kda_bwd.  16-byte aligned. */
@@ -104,6 +112,9 @@ typedef struct kda_bwd_io {
   float* dh0;           /* [N,H,K,V] or NULL (not produced) */
   void* dstates;        /* [NC,H,K,V] act_dtype or NULL: if given, receives dL/dS at
                            the end of every chunk (uses by later tokens only) */
+  const float* dt_bias; /* [H,K] or NULL (zero bias) -- input */
+  float* ddt_bias;      /* [H,K] or NULL (not produced) -- output: the sum of dg_raw over
+                           all tokens of every sequence */
 } kda_bwd_io;
 
 /* Device pointers for kda_fwd_ref (reference-quality forward that produces the
@@ -119,6 +130,7 @@ typedef struct kda_fwd_io {
   void* o;              /* [B,T,H,V] act_dtype, or NULL */
   float* ht;            /* [N,H,K,V] or NULL */
   void* h_saved;        /* [NC,H,K,V] act_dtype, or NULL */
+  const float* dt_bias; /* [H,K] or NULL (zero bias) */
 } kda_fwd_io;
 
 #define KDA_WS_BWD 0

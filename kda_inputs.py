@@ -50,6 +50,8 @@ class Workload:
     alog_hi: float = math.log(16.0)
     graw_mean: float = 0.0
     fixed_lengths: Optional[tuple] = None  # explicit packed lengths
+    dt_bias_std: float = 0.0  # >0: a per-(head, channel) gate bias of this scale
+    gate_log2: bool = False   # gate in log2 units (decay 2^g per step)
 
     @property
     def tokens(self) -> int:
@@ -95,6 +97,18 @@ EXTRA = {
     "ragged_bf16_d64": Workload("ragged_bf16_d64", 1, 1 + 63 + 64 + 65 + 200, 4, 64, 64, "bf16",
                                 1106, varlen_seqs=5, fixed_lengths=(1, 63, 64, 65, 200),
                                 h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0),
+    # gate variants: a per-channel bias inside the softplus, gates in log2 units
+    "gate_bias_bf16": Workload("gate_bias_bf16", 1, 1 + 63 + 64 + 65 + 200, 4, 128, 128, "bf16",
+                               1109, varlen_seqs=5, fixed_lengths=(1, 63, 64, 65, 200),
+                               h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0,
+                               dt_bias_std=1.0),
+    "gate_log2_fp32": Workload("gate_log2_fp32", 1, 1 + 63 + 64 + 65 + 200, 2, 64, 64, "f32",
+                               1110, varlen_seqs=5, fixed_lengths=(1, 63, 64, 65, 200),
+                               h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0,
+                               dt_bias_std=1.0, gate_log2=True),
+    "gate_log2_bf16": Workload("gate_log2_bf16", 3, 100, 3, 128, 128, "bf16", 1111,
+                               h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0,
+                               gate_log2=True),
 }
 
 
@@ -182,11 +196,15 @@ def make_inputs(wl: Workload) -> dict:
         h0 = (rng.standard_normal((N, H, K, V), dtype=np.float32) * np.float32(wl.h0_std))
     if wl.dht_std > 0:
         dht = (rng.standard_normal((N, H, K, V), dtype=np.float32) * np.float32(wl.dht_std))
+    dt_bias = None
+    if wl.dt_bias_std > 0:  # drawn last: the other inputs do not depend on it
+        dt_bias = rng.standard_normal((H, K), dtype=np.float32) * np.float32(wl.dt_bias_std)
     if wl.dtype == "bf16":
         q, k, v, dO = round_bf16(q), round_bf16(k), round_bf16(v), round_bf16(dO)
     return dict(name=wl.name, dtype=wl.dtype, B=wl.B, T=wl.T, H=H, K=K, V=V, N=N,
                 chunk=CHUNK, cu_seqlens=cu, lens=lens, varlen=wl.varlen_seqs > 0,
-                q=q, k=k, v=v, dO=dO, g_raw=g_raw, beta=beta, A_log=A_log, h0=h0, dht=dht)
+                q=q, k=k, v=v, dO=dO, g_raw=g_raw, beta=beta, A_log=A_log, h0=h0, dht=dht,
+                dt_bias=dt_bias, gate_log2=wl.gate_log2)
 
 
 def select_heads(inp: dict, heads) -> dict:
@@ -199,6 +217,8 @@ def select_heads(inp: dict, heads) -> dict:
     for key in ("h0", "dht"):
         if inp[key] is not None:
             out[key] = np.ascontiguousarray(inp[key][:, heads])
+    if inp.get("dt_bias") is not None:
+        out["dt_bias"] = np.ascontiguousarray(inp["dt_bias"][heads])
     out["H"] = len(heads)
     return out
 

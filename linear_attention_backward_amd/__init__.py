@@ -23,6 +23,8 @@ KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 KDA_WS_BWD = 0
 KDA_WS_FWD = 1
+KDA_GATE_LN = 0
+KDA_GATE_LOG2 = 1
 CHUNK = 64
 
 STAGES = ("chunk_table", "prep", "scan", "grad", "dalog", "recompute")
@@ -33,18 +35,19 @@ _P = ctypes.c_void_p
 class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("K", ctypes.c_int),
                 ("V", ctypes.c_int), ("chunk", ctypes.c_int), ("act_dtype", ctypes.c_int),
-                ("num_seqs", ctypes.c_int), ("cu_seqlens_host", _P), ("cu_seqlens_dev", _P)]
+                ("num_seqs", ctypes.c_int), ("cu_seqlens_host", _P), ("cu_seqlens_dev", _P),
+                ("gate_units", ctypes.c_int)]
 
 
 class BwdIO(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("q", "k", "v", "g_raw", "beta", "A_log", "h0", "dO", "dht",
                                   "h_saved", "dq", "dk", "dv", "dg_raw", "dbeta", "dA_log", "dh0",
-                                  "dstates")]
+                                  "dstates", "dt_bias", "ddt_bias")]
 
 
 class FwdIO(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("q", "k", "v", "g_raw", "beta", "A_log", "h0", "o", "ht",
-                                  "h_saved")]
+                                  "h_saved", "dt_bias")]
 
 
 class KdaError(RuntimeError):
@@ -108,14 +111,14 @@ def _stream_ptr(stream=None):
 class _Prob:
     """A kda_problem plus the host copy of cu_seqlens it points at."""
 
-    def __init__(self, B, T, H, K, V, dtype_code, cu_host=None, cu_dev=None):
+    def __init__(self, B, T, H, K, V, dtype_code, cu_host=None, cu_dev=None, gate_units=0):
         self.cu_host = None
         if cu_host is not None:
             self.cu_host = (ctypes.c_int32 * len(cu_host))(*[int(x) for x in cu_host])
         self.p = Problem(B, T, H, K, V, CHUNK, dtype_code,
                          (len(cu_host) - 1) if cu_host is not None else 0,
                          ctypes.cast(self.cu_host, _P) if self.cu_host is not None else None,
-                         _ptr(cu_dev) if cu_dev is not None else None)
+                         _ptr(cu_dev) if cu_dev is not None else None, gate_units)
 
     def ref(self):
         return ctypes.byref(self.p)
@@ -145,7 +148,7 @@ def _shape(q, v, cu_seqlens):
     return B, T, H, K, V
 
 
-def _make_prob(q, v, cu_seqlens):
+def _make_prob(q, v, cu_seqlens, gate_log2=False):
     import torch
     B, T, H, K, V = _shape(q, v, cu_seqlens)
     cu_host = cu_dev = None
@@ -153,7 +156,8 @@ def _make_prob(q, v, cu_seqlens):
         cu_host = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist")
                                     else cu_seqlens)]
         cu_dev = torch.tensor(cu_host, dtype=torch.int32, device=q.device)
-    prob = _Prob(B, T, H, K, V, _dtype_code(q), cu_host, cu_dev)
+    prob = _Prob(B, T, H, K, V, _dtype_code(q), cu_host, cu_dev,
+                 KDA_GATE_LOG2 if gate_log2 else KDA_GATE_LN)
     prob.cu_dev_tensor = cu_dev  # keep alive
     return prob, (B, T, H, K, V)
 
@@ -177,11 +181,13 @@ def _require_cuda(*ts):
 
 
 def kda_fwd_ref(q, k, v, g_raw, beta, A_log, h0=None, cu_seqlens=None, want_o=True,
-                want_ht=True, want_states=True, stream=None, workspace=None):
-    """Reference forward: returns dict(o, ht, h_saved)."""
+                want_ht=True, want_states=True, stream=None, workspace=None, dt_bias=None,
+                gate_log2=False):
+    """Reference forward: returns dict(o, ht, h_saved).  dt_bias [H, K] (optional) is
+    added inside the softplus; gate_log2 = True takes the gate in log2 units."""
     import torch
-    _require_cuda(q, k, v, g_raw, beta, A_log, h0)
-    prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens)
+    _require_cuda(q, k, v, g_raw, beta, A_log, h0, dt_bias)
+    prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens, gate_log2)
     N = (len(prob.cu_host) - 1) if prob.cu_host is not None else B
     nc = num_chunks(prob)
     dev = q.device
@@ -192,7 +198,7 @@ def kda_fwd_ref(q, k, v, g_raw, beta, A_log, h0=None, cu_seqlens=None, want_o=Tr
     ws = workspace if workspace is not None else torch.empty(max(ws_n, 1), dtype=torch.uint8,
                                                              device=dev)
     io = FwdIO(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta), _ptr(A_log), _ptr(h0),
-               _ptr(o), _ptr(ht), _ptr(hs))
+               _ptr(o), _ptr(ht), _ptr(hs), _ptr(dt_bias))
     _check(load_library().kda_fwd_ref(prob.ref(), ctypes.byref(io), _ptr(ws), ws.numel(),
                                       _stream_ptr(stream)))
     return dict(o=o, ht=ht, h_saved=hs)
@@ -203,13 +209,18 @@ class BwdPlan:
     shapes (used by the benchmark so the timed region allocates nothing)."""
 
     def __init__(self, q, k, v, g_raw, beta, A_log, dO, h0=None, dht=None, h_saved=None,
-                 cu_seqlens=None, want_dh0=True, want_dstates=False):
+                 cu_seqlens=None, want_dh0=True, want_dstates=False, dt_bias=None,
+                 gate_log2=False, want_ddt_bias=None):
         import torch
-        _require_cuda(q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved)
-        self.prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens)
+        _require_cuda(q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved, dt_bias)
+        self.prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens, gate_log2)
         N = (len(self.prob.cu_host) - 1) if self.prob.cu_host is not None else B
         dev = q.device
-        self.inputs = (q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved)
+        self.inputs = (q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved, dt_bias)
+        if want_ddt_bias is None:
+            want_ddt_bias = dt_bias is not None
+        self.ddt_bias = (torch.empty((H, K), dtype=torch.float32, device=dev) if want_ddt_bias
+                         else None)
         self.dq = torch.empty_like(q)
         self.dk = torch.empty_like(k)
         self.dv = torch.empty_like(v)
@@ -225,7 +236,7 @@ class BwdPlan:
         self.io = BwdIO(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta), _ptr(A_log), _ptr(h0),
                         _ptr(dO), _ptr(dht), _ptr(h_saved), _ptr(self.dq), _ptr(self.dk),
                         _ptr(self.dv), _ptr(self.dg_raw), _ptr(self.dbeta), _ptr(self.dA_log),
-                        _ptr(self.dh0), _ptr(self.dstates))
+                        _ptr(self.dh0), _ptr(self.dstates), _ptr(dt_bias), _ptr(self.ddt_bias))
 
     def run(self, stream=None):
         _check(load_library().kda_bwd(self.prob.ref(), ctypes.byref(self.io), _ptr(self.ws),
@@ -233,14 +244,16 @@ class BwdPlan:
 
     def outputs(self):
         return dict(dq=self.dq, dk=self.dk, dv=self.dv, dg_raw=self.dg_raw, dbeta=self.dbeta,
-                    dA_log=self.dA_log, dh0=self.dh0, dstates=self.dstates)
+                    dA_log=self.dA_log, dh0=self.dh0, dstates=self.dstates,
+                    ddt_bias=self.ddt_bias)
 
 
 def kda_bwd(q, k, v, g_raw, beta, A_log, dO, h0=None, dht=None, h_saved=None, cu_seqlens=None,
-            want_dh0=True, want_dstates=False, stream=None):
-    """Backward pass.  Returns dict(dq, dk, dv, dg_raw, dbeta, dA_log, dh0, dstates)."""
+            want_dh0=True, want_dstates=False, stream=None, dt_bias=None, gate_log2=False):
+    """Backward pass.  Returns dict(dq, dk, dv, dg_raw, dbeta, dA_log, dh0, dstates,
+    ddt_bias); ddt_bias is produced when dt_bias is given."""
     plan = BwdPlan(q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved, cu_seqlens, want_dh0,
-                   want_dstates)
+                   want_dstates, dt_bias, gate_log2)
     plan.run(stream)
     return plan.outputs()
 

@@ -31,7 +31,7 @@ struct Plan {
   int64_t NC = 0;
   size_t es = 0;  // bytes per act element
   // workspace regions
-  Region chunks, seq_off, groups, grp_off, Tm, PT, eGT, INV, MqkT, dstates, dAl, Pg, Qg,
+  Region chunks, seq_off, groups, grp_off, Tm, PT, eGT, INV, MqkT, dstates, dAl, ddt, Pg, Qg,
       bnd, hsaved;
   size_t fwd_bytes = 0, bwd_bytes = 0;
 };
@@ -74,6 +74,7 @@ int validate_problem(const kda_problem* p) {
   if (!p) return KDA_ERR_INVALID_ARGUMENT;
   if (p->B < 1 || p->T < 0 || p->H < 1 || p->K < 1 || p->V < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (p->chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if (p->gate_units != KDA_GATE_LN && p->gate_units != KDA_GATE_LOG2) return KDA_ERR_INVALID_ARGUMENT;
   if (p->act_dtype != KDA_DTYPE_F32 && p->act_dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
   if (p->K != p->V) return KDA_ERR_UNSUPPORTED;
   if (p->act_dtype == KDA_DTYPE_BF16 && p->K != 64 && p->K != 128) return KDA_ERR_UNSUPPORTED;
@@ -102,6 +103,7 @@ int make_plan(const kda_problem* p, Plan* pl) {
   s.T = p->T;
   s.bf16 = p->act_dtype == KDA_DTYPE_BF16;
   s.cu = p->cu_seqlens_dev;
+  s.gu = p->gate_units == KDA_GATE_LOG2 ? 0.69314718055994531f : 1.f;
   count_chunks(p, &pl->NC);
   s.NC = pl->NC;
   s.gs = scan_group_size(p, s.N);
@@ -132,6 +134,7 @@ int make_plan(const kda_problem* p, Plan* pl) {
   take(pl->MqkT, NCH * 64 * 64 * pl->es);
   take(pl->dstates, NCH * D * D * pl->es);
   take(pl->dAl, NCH * 4);
+  take(pl->ddt, NCH * D * 4);
   const size_t split = s.gs > 0 ? 1 : 0;
   take(pl->Pg, split * NGH * D * D * pl->es);
   take(pl->Qg, split * NGH * D * D * 4);
@@ -247,7 +250,8 @@ int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, siz
   if (st != KDA_OK) return st;
   if (!io || !io->q || !io->k || !io->v || !io->g_raw || !io->beta || !io->A_log)
     return KDA_ERR_INVALID_ARGUMENT;
-  if (!aligned16(io->q) || !aligned16(io->k) || !aligned16(io->v) || !aligned16(io->h_saved))
+  if (!aligned16(io->q) || !aligned16(io->k) || !aligned16(io->v) || !aligned16(io->h_saved) ||
+      !aligned16(io->dt_bias))
     return KDA_ERR_INVALID_ARGUMENT;
   if (ws_bytes < pl.fwd_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
   if (pl.fwd_bytes > 0 && !workspace) return KDA_ERR_INVALID_ARGUMENT;
@@ -257,8 +261,8 @@ int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, siz
   int* seq_off = (int*)(ws + pl.seq_off.off);
   hipError_t e = launch_chunk_table(pl.s, tab, seq_off, nullptr, nullptr, s);
   if (e != hipSuccess) return hip_fail(e);
-  e = launch_fwd_ref(pl.s, seq_off, io->q, io->k, io->v, io->g_raw, io->beta, io->A_log, io->h0,
-                     io->o, io->ht, io->h_saved, s);
+  e = launch_fwd_ref(pl.s, seq_off, io->q, io->k, io->v, io->g_raw, io->beta, io->A_log,
+                     io->dt_bias, io->h0, io->o, io->ht, io->h_saved, s);
   if (e != hipSuccess) return hip_fail(e);
   return KDA_OK;
 }
@@ -273,9 +277,10 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
       !io->dk || !io->dv || !io->dg_raw || !io->dbeta || !io->dA_log)
     return KDA_ERR_INVALID_ARGUMENT;
   const void* al[] = {io->q, io->k, io->v, io->dO, io->g_raw, io->h_saved, io->h0, io->dht,
-                      io->dq, io->dk, io->dv, io->dg_raw, io->dh0, io->dstates};
+                      io->dq, io->dk, io->dv, io->dg_raw, io->dh0, io->dstates, io->dt_bias};
   for (const void* x : al)
     if (!aligned16(x)) return KDA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)io->ddt_bias & 3) != 0) return KDA_ERR_INVALID_ARGUMENT;
   size_t need = pl.bwd_bytes;
   if (io->h_saved) need = pl.hsaved.off;  // the recompute region is the last one
   if (ws_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
@@ -286,6 +291,9 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   BwdPtrs b;
   b.q = io->q; b.k = io->k; b.v = io->v; b.dO = io->dO;
   b.g_raw = io->g_raw; b.beta = io->beta; b.A_log = io->A_log; b.h0 = io->h0; b.dht = io->dht;
+  b.dt_bias = io->dt_bias ? io->dt_bias : io->g_raw;
+  b.has_db = io->dt_bias != nullptr;
+  b.ddt_bias = io->ddt_bias;
   b.dq = io->dq; b.dk = io->dk; b.dv = io->dv;
   b.dg_raw = io->dg_raw; b.dbeta = io->dbeta; b.dA_log = io->dA_log; b.dh0 = io->dh0;
   b.chunks = (const ChunkInfo*)(ws + pl.chunks.off);
@@ -297,6 +305,7 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   b.MqkT = ws + pl.MqkT.off;
   b.dstates = io->dstates ? io->dstates : (void*)(ws + pl.dstates.off);
   b.dAl_part = (float*)(ws + pl.dAl.off);
+  b.ddt_part = (float*)(ws + pl.ddt.off);
   b.h_saved = io->h_saved ? io->h_saved : (const void*)(ws + pl.hsaved.off);
   b.groups = (const GroupInfo*)(ws + pl.groups.off);
   b.grp_off = (const int*)(ws + pl.grp_off.off);
@@ -313,7 +322,7 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   if (!io->h_saved) {
     e = timed(5, s, [&] {
       return launch_fwd_ref(sh, b.seq_off, io->q, io->k, io->v, io->g_raw, io->beta, io->A_log,
-                            io->h0, nullptr, nullptr, (void*)b.h_saved, s);
+                            io->dt_bias, io->h0, nullptr, nullptr, (void*)b.h_saved, s);
     });
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -325,6 +334,10 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   if (e != hipSuccess) return hip_fail(e);
   e = timed(4, s, [&] { return launch_dalog(sh, b, s); });
   if (e != hipSuccess) return hip_fail(e);
+  if (io->ddt_bias) {
+    e = timed(4, s, [&] { return launch_ddt(sh, b, s); });
+    if (e != hipSuccess) return hip_fail(e);
+  }
   return KDA_OK;
 }
 

@@ -1,5 +1,5 @@
 // kda_fwd.hip -- chunk table, reference forward (chunk start states) and the
-// per-head dA_log reduction.
+// per-head dA_log and per-channel dt_bias reductions.
 #include "kda_dev.h"
 #include "kda_launch.h"
 
@@ -105,6 +105,7 @@ __global__ __launch_bounds__(64) void k_fwd_ref(const int* __restrict__ seq_off,
                                                 const float* __restrict__ g_raw,
                                                 const float* __restrict__ beta,
                                                 const float* __restrict__ A_log,
+                                                const float* __restrict__ dt_bias, float gu,
                                                 const float* __restrict__ h0, T* __restrict__ o,
                                                 float* __restrict__ ht, T* __restrict__ h_saved) {
   constexpr int NVS = D / 64;
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(64) void k_fwd_ref(const int* __restrict__ seq_off,
 #pragma unroll
     for (int i = 0; i < D; ++i) S[i] = 0.f;
   }
-  const float aA = __expf(A_log[h]);
+  // decay per token and key channel: exp(gu * g), g = -e^{A_log} softplus(g_raw + dt_bias)
+  const float aA = __expf(A_log[h]) * gu;
   const int c0 = seq_off[n];
   for (int tb = 0; tb < len; tb += TB) {
     const int nt = min(TB, len - tb);
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(64) void k_fwd_ref(const int* __restrict__ seq_off,
         size_t off = ((size_t)(start + tb + r) * H + h) * D + i;
         sk[r][i] = to_f(k[off]);
         sq[r][i] = to_f(q[off]);
-        sa[r][i] = __expf(-aA * softplus_f(g_raw[off]));
+        sa[r][i] = __expf(-aA * softplus_f(g_raw[off] + (dt_bias ? dt_bias[h * D + i] : 0.f)));
       }
     }
     if (j < nt) sb[j] = beta[(size_t)(start + tb + j) * H + h];
@@ -190,6 +192,16 @@ __global__ __launch_bounds__(256) void k_dalog(const float* __restrict__ part, i
   if (tid == 0) out[h] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// ddt_bias[h][i] = sum over chunks of the per chunk-head column sums of dg_raw (fixed
+// order: deterministic).  Block h, thread i; D threads.
+__global__ __launch_bounds__(128) void k_ddt(const float* __restrict__ part, int64_t NC, int H,
+                                             int D, float* __restrict__ out) {
+  const int h = blockIdx.x, i = threadIdx.x;
+  float acc = 0.f;
+  for (int64_t c = 0; c < NC; ++c) acc += part[(c * H + h) * D + i];
+  out[h * D + i] = acc;
+}
+
 hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, GroupInfo* groups,
                               int* grp_off, hipStream_t st) {
   hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, st, s.cu, s.N, s.T, s.gs, tab, seq_off,
@@ -200,30 +212,38 @@ hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, Grou
 template <typename T, int D>
 static hipError_t fwd_ref_t(const Shape& s, const int* seq_off, const void* q, const void* k,
                             const void* v, const float* g_raw, const float* beta,
-                            const float* A_log, const float* h0, void* o, float* ht,
-                            void* h_saved, hipStream_t st) {
+                            const float* A_log, const float* dt_bias, const float* h0, void* o,
+                            float* ht, void* h_saved, hipStream_t st) {
   dim3 grid((unsigned)(s.N * s.H * (D / 64)));
   hipLaunchKernelGGL((k_fwd_ref<T, D>), grid, dim3(64), 0, st, seq_off, s.cu, s.N, s.H, s.T,
-                     (const T*)q, (const T*)k, (const T*)v, g_raw, beta, A_log, h0, (T*)o, ht,
-                     (T*)h_saved);
+                     (const T*)q, (const T*)k, (const T*)v, g_raw, beta, A_log, dt_bias, s.gu, h0,
+                     (T*)o, ht, (T*)h_saved);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, const void* k,
                           const void* v, const float* g_raw, const float* beta,
-                          const float* A_log, const float* h0, void* o, float* ht,
-                          void* h_saved, hipStream_t st) {
+                          const float* A_log, const float* dt_bias, const float* h0, void* o,
+                          float* ht, void* h_saved, hipStream_t st) {
   if (s.N * s.H == 0) return hipSuccess;
   if (s.bf16) {
     if (s.D == 128)
-      return fwd_ref_t<bf16, 128>(s, seq_off, q, k, v, g_raw, beta, A_log, h0, o, ht, h_saved, st);
-    return fwd_ref_t<bf16, 64>(s, seq_off, q, k, v, g_raw, beta, A_log, h0, o, ht, h_saved, st);
+      return fwd_ref_t<bf16, 128>(s, seq_off, q, k, v, g_raw, beta, A_log, dt_bias, h0, o, ht,
+                                  h_saved, st);
+    return fwd_ref_t<bf16, 64>(s, seq_off, q, k, v, g_raw, beta, A_log, dt_bias, h0, o, ht,
+                               h_saved, st);
   }
-  return fwd_ref_t<float, 64>(s, seq_off, q, k, v, g_raw, beta, A_log, h0, o, ht, h_saved, st);
+  return fwd_ref_t<float, 64>(s, seq_off, q, k, v, g_raw, beta, A_log, dt_bias, h0, o, ht,
+                              h_saved, st);
 }
 
 hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   hipLaunchKernelGGL(k_dalog, dim3(s.H), dim3(256), 0, st, p.dAl_part, s.NC, s.H, p.dA_log);
+  return hipGetLastError();
+}
+
+hipError_t launch_ddt(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_ddt, dim3(s.H), dim3(s.D), 0, st, p.ddt_part, s.NC, s.H, s.D, p.ddt_bias);
   return hipGetLastError();
 }
 

@@ -96,10 +96,12 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const ChunkInfo* __restrict__ chunks, int NC, int H, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
     const float* __restrict__ g_raw, const float* __restrict__ beta,
-    const float* __restrict__ A_log, const T* __restrict__ h_saved,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias, int has_db, float gu,
+    const T* __restrict__ h_saved,
     const T* __restrict__ dstates, const T* __restrict__ INV,
     const T* __restrict__ MqkT, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
-    float* __restrict__ dg_raw, float* __restrict__ dbeta, float* __restrict__ dAl_part) {
+    float* __restrict__ dg_raw, float* __restrict__ dbeta, float* __restrict__ dAl_part,
+    float* __restrict__ ddt_part) {
   using L = GF<T, D>;
   using MM = Mma<T>;
   using MS = M16<T>;
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   // the intra phase is done, dO once the dq staging over its tile is read out.
   // g_raw of wave w's 16 channels in 16-byte quads: lane l holds rows 16 t + (l >> 2),
   // channels 16 w + 4 (l & 3) .. + 3, t = 0..3 (rows past the chunk: masked later)
-  f4 rg[4];
+  f4 rg[4], rdb;  // rdb: the gate bias of the same four channels
   float rbeta;
   // (t: this thread's index, passed in so that the address arithmetic is redone per
   // item rather than held across the loop)
@@ -202,6 +204,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       rg[t4] = *(const f4*)(grw + (size_t)(r < ci.len ? r : ci.len - 1) * rs);
     }
     rbeta = beta[((size_t)ci.t0 + (lane < ci.len ? lane : ci.len - 1)) * H + h];
+    rdb = *(const f4*)(dt_bias + (size_t)h * D + 16 * w + 4 * (lane & 3));  // always readable
   };
   auto issue_late = [&](int it, int t) {
     const int c = it % NC, h = it / NC;
@@ -216,6 +219,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   }
   settle(rg);  // waits for all of the first item's copies as well
   settle(rbeta);
+  settle(rdb);
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
   // thread indices re-derived per item so that the lane-dependent LDS addresses
   // below stay inside the loop instead of being held in registers across it
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const size_t hD = (size_t)h * D;
   const T* qh = q + t0 * rs + hD;
   const T* dSo = dstates + ch * DD;
-  const float aA = __expf(A_log[h]);
+  const float aA = __expf(A_log[h]) * gu;  // gu: natural-log decay per unit of the gate
   const int gch = 16 * w + cl;
   // state side: wave w owns the rows of block R1, value columns [64 half, +64)
   const int R1 = w / WPR, half = w % WPR;
@@ -251,12 +255,14 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
      // gates go into this wave's 16 channel rows of the tile (written and read back by
      // this wave only), then lane (g4, cl) sums channel 16 w + cl over rows 16 g4 .. + 15
      // and the sums of the earlier row parts come from the lanes that hold them
+    const f4 db = has_db ? rdb : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       const int r = 16 * t4 + (lane >> 2);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        sG[(16 * w + 4 * (lane & 3) + e) * PG + r] = r < Lr ? gate_log2(rg[t4][e], aA) : 0.f;
+        sG[(16 * w + 4 * (lane & 3) + e) * PG + r] =
+            r < Lr ? gate_log2(rg[t4][e] + db[e], aA) : 0.f;
     }
     float x[16];
 #pragma unroll
@@ -744,6 +750,16 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       if (r < Lr) dal += run * (d * 0.69314718055994531f);
     }
   }
+  {  // this item's column sum of dg_raw (channel ic), for ddt_bias; every lane stores
+    float sdt = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sdt += dG[rt][j];
+    sdt += __shfl_xor(sdt, 16);
+    sdt += __shfl_xor(sdt, 32);
+    ddt_part[ch * D + ic] = sdt;
+  }
   // dbeta second part, reduced over this wave's channels
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -794,6 +810,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   // wait at their first use would also cover this item's dq and dk stores.
   settle(rg);
   settle(rbeta);
+  settle(rdb);
   // dO over the dq staging, which is read out; issued after this item's last stores
   // so that the next item's first waits skip it
   if (nxt < items) issue_late(nxt, tid);
@@ -810,9 +827,10 @@ static hipError_t gradf_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const int grid = items < resident ? items : resident;
   hipLaunchKernelGGL((k_gradf<T, D>), dim3(grid), dim3(GF<T, D>::NT), 0, st, p.chunks, s.NC, s.H,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dO, p.g_raw,
-                     p.beta, p.A_log, (const T*)p.h_saved, (const T*)p.dstates,
+                     p.beta, p.A_log, p.dt_bias, p.has_db, s.gu, (const T*)p.h_saved,
+                     (const T*)p.dstates,
                      (const T*)p.INV, (const T*)p.MqkT, (T*)p.dq, (T*)p.dk,
-                     (T*)p.dv, p.dg_raw, p.dbeta, p.dAl_part);
+                     (T*)p.dv, p.dg_raw, p.dbeta, p.dAl_part, p.ddt_part);
   return hipGetLastError();
 }
 

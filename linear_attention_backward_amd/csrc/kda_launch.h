@@ -12,9 +12,14 @@ struct GroupInfo;
 struct BwdPtrs {
   const void *q, *k, *v, *dO;
   const float *g_raw, *beta, *A_log, *h0, *dht;
+  // per-channel gate bias [H,K]: always a readable address of at least H*K floats
+  // (g_raw when there is no bias); has_db = 0 makes the kernels use zero instead
+  const float* dt_bias;
+  int has_db;
   const void* h_saved;
   void *dq, *dk, *dv;
   float *dg_raw, *dbeta, *dA_log, *dh0;
+  float* ddt_bias;         // [H,K] or nullptr
   // workspace
   const ChunkInfo* chunks;
   const int* seq_off;      // [N+1] first chunk of every sequence
@@ -25,6 +30,7 @@ struct BwdPtrs {
   void* MqkT;              // [NC,H,64,64] act dtype: Mqk transposed
   void* dstates;           // [NC,H,K,V] act dtype: dL/dS at the end of every chunk
   float* dAl_part;         // [NC,H] per chunk-head partial sums for dA_log
+  float* ddt_part;         // [NC,H,K] per chunk-head column sums of dg_raw (for ddt_bias)
   const GroupInfo* groups; // [NG] chunk groups of the state-gradient scan
   const int* grp_off;      // [N+1] first group of every sequence
   void* Pg;                // [NG,H,K,K] act dtype: transition of every group (split scan only)
@@ -39,14 +45,15 @@ struct Shape {
   const int32_t* cu;  // device cu_seqlens or nullptr (uniform rows of T tokens)
   int gs;          // chunks per scan group; 0: one group per sequence
   int64_t NG;      // groups
+  float gu;        // natural-log decay per unit of the gate: 1, or ln 2 for log2 units
 };
 
 hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, GroupInfo* groups,
                               int* grp_off, hipStream_t st);
 hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, const void* k,
                           const void* v, const float* g_raw, const float* beta,
-                          const float* A_log, const float* h0, void* o, float* ht,
-                          void* h_saved, hipStream_t st);
+                          const float* A_log, const float* dt_bias, const float* h0, void* o,
+                          float* ht, void* h_saved, hipStream_t st);
 // Workgroups of `kernel` (block of `threads`) that the current device holds at
 // once: CU count times the per-CU occupancy; cached per device and kernel.  The
 // environment variable KDA_GRID_CAP, when set to n > 0, caps it at n.
@@ -56,5 +63,6 @@ hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st);
+hipError_t launch_ddt(const Shape& s, const BwdPtrs& p, hipStream_t st);
 
 }  // namespace kda

@@ -56,6 +56,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
                                                 const float* __restrict__ g_raw,
                                                 const float* __restrict__ beta,
                                                 const float* __restrict__ A_log,
+                                                const float* __restrict__ dt_bias, int has_db,
+                                                float gu,
                                                 T* __restrict__ Tm, T* __restrict__ PT,
                                                 float* __restrict__ eGT, T* __restrict__ INVo,
                                                 T* __restrict__ MqkTo) {
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   // (chunk, head) items with stride gridDim.x and holds the next item's g_raw,
   // beta, q and k in registers while it works on the current one. Rows beyond
   // the chunk are zero (q, k) or masked at the cumsum (g_raw).
-  float rg[16], rbeta;
+  float rg[16], rbeta, rdb;
   u32x4 rq[NLT], rk[NLT];
   // parts: 1 = g_raw rows 0-7 of the thread's 16 and beta, 2 = g_raw rows 8-15,
   // 4 = q, 8 = k.  A CU keeps a bounded number of cache lines in flight and a wave
@@ -115,7 +117,10 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       const float* rowp = gh + (unsigned)((r < ci.len ? r : ci.len - 1) * (int)rs);
       rg[rr] = rowp[lo];
     }
-    if (parts & 1) rbeta = beta[(size_t)(ci.t0 + ((t & 63) < ci.len ? (t & 63) : ci.len - 1)) * H + h];
+    if (parts & 1) {
+      rbeta = beta[(size_t)(ci.t0 + ((t & 63) < ci.len ? (t & 63) : ci.len - 1)) * H + h];
+      rdb = dt_bias[hD + lo];  // always a readable address; unused without a bias
+    }
     const T* qh = q + (size_t)ci.t0 * rs + hD;
     const T* kh = k + (size_t)ci.t0 * rs + hD;
 #pragma unroll
@@ -129,6 +134,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   auto settle_loads = [&]() {
     settle(rg);
     settle(rbeta);
+    settle(rdb);
     settle(rq);
     settle(rk);
   };
@@ -146,7 +152,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   const int nxt = it + (int)gridDim.x;
   const ChunkInfo cnx = chunks[(nxt < items ? nxt : it) % NC];  // early: scalar-load latency
   const size_t ch = (size_t)c * H + h;
-  const float aA = __expf(A_log[h]);
+  const float aA = __expf(A_log[h]) * gu;  // gu: natural-log decay per unit of the gate
+  const float db = has_db ? rdb : 0.f;
   if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
   // in-chunk cumulative gate (log2 units), natural: sG[r][i].  Thread (part, i) sums
   // channel i over rows 16 part .. + 15 in registers and publishes the part's total;
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int r = part * 16 + rr;
-      const float gv = gate_log2(rg[rr], aA);
+      const float gv = gate_log2(rg[rr] + db, aA);
       run += r < Lr ? gv : 0.f;
       gx[rr] = run;
     }
@@ -552,7 +559,8 @@ static hipError_t prep_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int grid = items < resident ? items : resident;
   hipLaunchKernelGGL((k_prep<T, D>), dim3(grid), dim3(PL<T, D>::NT), 0, st, p.chunks, s.NC, s.H, (const T*)p.q,
-                     (const T*)p.k, p.g_raw, p.beta, p.A_log, (T*)p.Tm, (T*)p.PT, p.eGT,
+                     (const T*)p.k, p.g_raw, p.beta, p.A_log, p.dt_bias, p.has_db, s.gu,
+                     (T*)p.Tm, (T*)p.PT, p.eGT,
                      (T*)p.INV, (T*)p.MqkT);
   return hipGetLastError();
 }

@@ -20,7 +20,7 @@ def to_gpu(inp: dict):
 
     g = dict(q=t(inp["q"], act), k=t(inp["k"], act), v=t(inp["v"], act), dO=t(inp["dO"], act),
              g_raw=t(inp["g_raw"]), beta=t(inp["beta"]), A_log=t(inp["A_log"]), h0=t(inp["h0"]),
-             dht=t(inp["dht"]))
+             dht=t(inp["dht"]), dt_bias=t(inp.get("dt_bias")))
     if not inp["varlen"]:
         B, T = inp["B"], inp["T"]
         for key in ("q", "k", "v", "dO", "g_raw"):
@@ -34,11 +34,12 @@ def run_gpu(inp: dict, use_h_saved=True, want_dstates=True):
     import torch
     g = to_gpu(inp)
     cu = inp["cu_seqlens"] if inp["varlen"] else None
+    gate = dict(dt_bias=g["dt_bias"], gate_log2=bool(inp.get("gate_log2", False)))
     fwd = K.kda_fwd_ref(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], h0=g["h0"],
-                        cu_seqlens=cu)
+                        cu_seqlens=cu, **gate)
     out = K.kda_bwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dO"],
                     h0=g["h0"], dht=g["dht"], h_saved=fwd["h_saved"] if use_h_saved else None,
-                    cu_seqlens=cu, want_dstates=want_dstates)
+                    cu_seqlens=cu, want_dstates=want_dstates, **gate)
     torch.cuda.synchronize()
     res = {}
     TT = inp["q"].shape[0]
@@ -69,7 +70,7 @@ def compare(res: dict, ref: dict, keys, tol: float, heads=None, label=""):
     report = {}
     for key in keys:
         got = res[key]
-        if heads is not None and key != "dA_log":
+        if heads is not None and key not in ("dA_log", "ddt_bias"):
             got = got[:, heads]
         elif heads is not None:
             got = got[heads]

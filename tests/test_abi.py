@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert K.abi_version() == 1
+    assert K.abi_version() == 2
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(K.status_string(code), str) and K.status_string(code)
 
@@ -51,6 +51,10 @@ def test_shape_validation():
     assert _ws(p)[0] == K.KDA_ERR_UNSUPPORTED
     n = ctypes.c_size_t(0)
     assert K.load_library().kda_workspace_size(ok.ref(), 5, ctypes.byref(n)) == -1
+    assert _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16, gate_units=K.KDA_GATE_LOG2))[0] == 0
+    bad = K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16)
+    bad.p.gate_units = 2
+    assert _ws(bad)[0] == K.KDA_ERR_INVALID_ARGUMENT
 
 
 def test_cu_seqlens_validation():
@@ -94,6 +98,12 @@ def test_bwd_rejects_bad_calls_without_launching():
     io.q = 258
     assert lib.kda_bwd(p.ref(), ctypes.byref(io), None, 0, None) == K.KDA_ERR_INVALID_ARGUMENT
     io.q = 256
+    io.dt_bias = 264  # the gate bias is read in 16-byte pieces
+    assert lib.kda_bwd(p.ref(), ctypes.byref(io), None, 0, None) == K.KDA_ERR_INVALID_ARGUMENT
+    io.dt_bias = None
+    io.ddt_bias = 258
+    assert lib.kda_bwd(p.ref(), ctypes.byref(io), None, 0, None) == K.KDA_ERR_INVALID_ARGUMENT
+    io.ddt_bias = None
     # workspace too small
     assert lib.kda_bwd(p.ref(), ctypes.byref(io), ctypes.c_void_p(256), 16, None) == \
         K.KDA_ERR_WORKSPACE_TOO_SMALL

@@ -36,7 +36,8 @@ def _check(name, heads=None, use_h_saved=True):
     ref["dstates"] = ref["dstates"]
     ref["h_saved"] = ref["states"]
     tol = KC.TOL[inp["dtype"]]
-    rep = KC.compare(res, ref, GRADS + INTER, tol, heads=heads, label=name)
+    keys = GRADS + INTER + (["ddt_bias"] if inp.get("dt_bias") is not None else [])
+    rep = KC.compare(res, ref, keys, tol, heads=heads, label=name)
     print("[errors] " + " ".join("%s=%.2e" % kv for kv in rep.items()), flush=True)
     return res
 
@@ -53,13 +54,20 @@ def test_parity_bf16(name):
     _check(name)
 
 
+@pytest.mark.parametrize("name", ["gate_bias_bf16", "gate_log2_fp32", "gate_log2_bf16"])
+def test_gate_variants(name):
+    """A per-channel gate bias inside the softplus (with its gradient, ddt_bias) and gates
+    in log2 units, in the reference forward and in every backward kernel."""
+    _check(name)
+
+
 @pytest.mark.parametrize("name,heads", [("train_bf16", [0, 21]), ("varlen_bf16", [7]),
                                         ("long_bf16", [5])])
 def test_parity_full_size_sampled(name, heads):
     _check(name, heads)
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "ragged_bf16"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "ragged_bf16", "gate_log2_fp32"])
 def test_state_recompute_path(name):
     """h_saved omitted: the library recomputes the chunk states in-stream."""
     _check(name, use_h_saved=False)
@@ -113,7 +121,7 @@ def test_split_scan_zero_length(monkeypatch):
 
 @pytest.mark.parametrize("name,cap", [("ragged_fp32", 3), ("ragged_bf16", 3),
                                       ("ragged_bf16_d64", 2), ("weak_decay_bf16", 5),
-                                      ("multi_ragged_bf16", 2)])
+                                      ("multi_ragged_bf16", 2), ("gate_bias_bf16", 3)])
 def test_persistent_walk(name, cap, monkeypatch):
     """Prep and the gradient pass with a grid of `cap` workgroups: each workgroup walks
     many (chunk, head) items and hands the prefetched tiles of the next item over
@@ -126,6 +134,7 @@ def test_persistent_walk(name, cap, monkeypatch):
     capped = KC.run_gpu(inp)
     ref = KC.oracle_for(inp)
     ref["h_saved"] = ref["states"]
-    KC.compare(capped, ref, GRADS + INTER, KC.TOL[inp["dtype"]], label=name + " capped")
-    for key in GRADS + ["dstates"]:
+    extra = ["ddt_bias"] if inp.get("dt_bias") is not None else []
+    KC.compare(capped, ref, GRADS + INTER + extra, KC.TOL[inp["dtype"]], label=name + " capped")
+    for key in GRADS + ["dstates"] + extra:
         assert np.array_equal(full[key], capped[key]), key
