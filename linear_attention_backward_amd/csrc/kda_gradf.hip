@@ -19,7 +19,8 @@
 //     dk_r = e^{G_T-G} dKr,  dk = dk_d + dk_i + dk_r
 //     dbeta_r += sum_s dL_rs A_rs = sum_i k_ri x2_ri
 //     dG = q.dq + k.(dk_d - dk_i - dk_r);  dG_last += sum_r k.dk_r + e^{G_T}.p
-//     dg = reverse cumsum of dG (rows);  dg_raw = dg . (-e^{A_log} sigmoid(g_raw))
+//     dg = reverse cumsum of dG (rows);  dg_raw = dg . gu (-e^{A_log} sigmoid(g_raw + dt_bias))
+//     (gu = 1, or ln 2 for a gate in log2 units);  ddt_bias = column sums of dg_raw
 //     dA_log partial = sum dg . g
 // The epilogue stays fp32 ([KB] B3: dk_d - dk_i - dk_r cancels strongly).  The
 // pairwise decays e^{G_r-G_s} never come from exp(-G) (it overflows): across 16-row
@@ -719,9 +720,10 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   dkr_col += __shfl_xor(dkr_col, 32);
   if (g4 == 3) dG[3][3] += dkr_col + ex2(gT) * pp;
   // reverse cumsum over r = 16 rt + 4 g4 + j; dG becomes dg_raw.  The gate's own
-  // derivative comes from the cumulative gate: with d = G_r - G_{r-1} = g_r log2(e),
-  // softplus(g_raw) = -g_r / e^{A_log} and sigmoid(g_raw) = 1 - e^{-softplus}, so
-  // dg_raw = dg . e^{A_log} (2^{d / e^{A_log}} - 1) and the dA_log term is dg . d ln 2.
+  // derivative comes from the cumulative gate: with aA = gu e^{A_log}, x = g_raw + dt_bias
+  // and d = G_r - G_{r-1} = -aA softplus(x) log2(e), softplus(x) = -d ln 2 / aA and
+  // sigmoid(x) = 1 - e^{-softplus(x)} = 1 - 2^{d / aA}, so dg_raw = dg . aA (2^{d / aA} - 1)
+  // and the dA_log term is dg . d ln 2 (dg here is the gradient of the natural-log decay).
   const float inv_aA = 1.f / aA;
   float carry = 0.f;
 #pragma unroll
