@@ -19,6 +19,9 @@
  *   g_t   = -exp(A_log[h]) * softplus(g_raw_t)              (per key channel, <= 0)
  *   S_t   = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
  *
+ * Optionally q and k are L2-normalised per token first ([KB] R1 / K1: the norm
+ * forward and its backward); the recurrence then runs on the normalised vectors.
+ *
  * Gate variants ([KB] part 2, the gate epilogue K1 and its dt_bias reduction): a
  * per-channel bias inside the softplus, and a gate given in log2 units (decay 2^g);
  * both live in the gate map and its chain rule below.
@@ -117,6 +120,37 @@ void kda_oracle_gate_backward(int64_t TT, int H, int K, const double* g_raw, con
       }
     dA_log[h] = acc;
   }
+}
+
+/* L2 normalisation of q or k per (token, head), over the D features:
+ *   xn = x * r,  r = 1 / sqrt(sum_i x_i^2 + eps),
+ * the reciprocal r kept for the backward ([KB] R1 computes it per row, K1 reuses
+ * it).  Its chain rule, from dxn = dL/dxn:
+ *   dx = r * (dxn - xn * (xn . dxn)). */
+void kda_oracle_l2norm(int64_t TT, int H, int D, const double* x, double eps, double* xn,
+                       double* r) {
+  for (int64_t t = 0; t < TT; ++t)
+    for (int h = 0; h < H; ++h) {
+      const double* a = x + IDX3(t, h, 0, H, D);
+      double ss = 0.0;
+      for (int i = 0; i < D; ++i) ss += a[i] * a[i];
+      double rr = 1.0 / sqrt(ss + eps);
+      r[(int64_t)t * H + h] = rr;
+      for (int i = 0; i < D; ++i) xn[IDX3(t, h, i, H, D)] = a[i] * rr;
+    }
+}
+
+void kda_oracle_l2norm_backward(int64_t TT, int H, int D, const double* xn, const double* r,
+                                const double* dxn, double* dx) {
+  for (int64_t t = 0; t < TT; ++t)
+    for (int h = 0; h < H; ++h) {
+      const double* a = xn + IDX3(t, h, 0, H, D);
+      const double* g = dxn + IDX3(t, h, 0, H, D);
+      double dot = 0.0;
+      for (int i = 0; i < D; ++i) dot += a[i] * g[i];
+      double rr = r[(int64_t)t * H + h];
+      for (int i = 0; i < D; ++i) dx[IDX3(t, h, i, H, D)] = rr * (g[i] - a[i] * dot);
+    }
 }
 
 /* One forward token step on a K x V state (row-major, V contiguous):

@@ -57,6 +57,10 @@ def _load():
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int
         lib.kda_oracle_gate.argtypes = [i64, i32, i32, P, P, P, ctypes.c_double, P]
+        lib.kda_oracle_l2norm.argtypes = [i64, i32, i32, P, ctypes.c_double, P, P]
+        lib.kda_oracle_l2norm.restype = None
+        lib.kda_oracle_l2norm_backward.argtypes = [i64, i32, i32, P, P, P, P]
+        lib.kda_oracle_l2norm_backward.restype = None
         lib.kda_oracle_gate.restype = None
         lib.kda_oracle_gate_backward.argtypes = [i64, i32, i32, P, P, P, ctypes.c_double, P, P, P,
                                                  P, P]
@@ -119,6 +123,29 @@ def gate_backward(g_raw, A_log, g, dg, dt_bias=None, log2_units=False):
     return dg_raw, dA, ddt
 
 
+L2NORM_EPS = 1e-6
+
+
+def l2norm(x, eps=L2NORM_EPS):
+    """xn = x / sqrt(sum_i x_i^2 + eps) per (token, head); returns (xn, r) with r the
+    reciprocal norm [TT, H]."""
+    x = _d(x)
+    TT, H, D = x.shape
+    xn = np.empty_like(x)
+    r = np.empty((TT, H))
+    _load().kda_oracle_l2norm(TT, H, D, _p(x), eps, _p(xn), _p(r))
+    return xn, r
+
+
+def l2norm_backward(xn, r, dxn):
+    """dx = r (dxn - xn (xn . dxn)) per (token, head)."""
+    xn, r, dxn = _d(xn), _d(r), _d(dxn)
+    TT, H, D = xn.shape
+    dx = np.empty_like(xn)
+    _load().kda_oracle_l2norm_backward(TT, H, D, _p(xn), _p(r), _p(dxn), _p(dx))
+    return dx
+
+
 def _forward(fn, q, k, v, g, beta, h0, cu, chunk, want_states, nthreads):
     q, k, v, g, beta, h0 = map(_d, (q, k, v, g, beta, h0))
     cu = np.ascontiguousarray(cu, dtype=np.int64)
@@ -174,21 +201,30 @@ def kda_backward(inp: dict, want_dstates=False, want_states=False, nthreads=0) -
     """Full backward from raw inputs (an input dict as produced by kda_inputs):
     gate, per-token backward, gate chain rule.  Returns fp64 arrays dq, dk, dv,
     dg_raw, dA_log, dbeta, dh0, ddt_bias (+ dstates / states on request).  Optional
-    entries: dt_bias [H, K] (added inside the softplus) and gate_log2 (the gate is in
-    log2 units: the decay per step is 2^g)."""
+    entries: dt_bias [H, K] (added inside the softplus), gate_log2 (the gate is in
+    log2 units: the decay per step is 2^g) and qk_l2norm (q and k are L2-normalised per
+    token first; dq, dk are then w.r.t. the raw q, k)."""
     gkw = dict(dt_bias=inp.get("dt_bias"), log2_units=bool(inp.get("gate_log2", False)))
     g = gate(inp["g_raw"], inp["A_log"], **gkw)
     cu = inp["cu_seqlens"]
-    out = backward(inp["q"], inp["k"], inp["v"], g, inp["beta"], inp["h0"], inp["dO"],
+    q, k = inp["q"], inp["k"]
+    norm = bool(inp.get("qk_l2norm", False))
+    if norm:
+        q, rq = l2norm(q)
+        k, rk = l2norm(k)
+    out = backward(q, k, inp["v"], g, inp["beta"], inp["h0"], inp["dO"],
                    inp["dht"], cu, chunk=inp.get("chunk", 64), want_dstates=want_dstates,
                    nthreads=nthreads)
+    if norm:
+        out["dq"] = l2norm_backward(q, rq, out["dq"])
+        out["dk"] = l2norm_backward(k, rk, out["dk"])
     dg_raw, dA, ddt = gate_backward(inp["g_raw"], inp["A_log"], g, out["dg"], **gkw)
     out["dg_raw"] = dg_raw
     out["dA_log"] = dA
     out["ddt_bias"] = ddt
     out["g"] = g
     if want_states:
-        o, ht, st = forward(inp["q"], inp["k"], inp["v"], g, inp["beta"], inp["h0"], cu,
+        o, ht, st = forward(q, k, inp["v"], g, inp["beta"], inp["h0"], cu,
                             chunk=inp.get("chunk", 64), want_states=True, nthreads=nthreads)
         out["o"], out["ht"], out["states"] = o, ht, st
     return out

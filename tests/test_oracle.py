@@ -43,7 +43,10 @@ def _loss(c, **over):
     d.update(over)
     g = O.gate(d["g_raw"], d["A_log"], dt_bias=d.get("dt_bias"),
                log2_units=bool(d.get("gate_log2", False)))
-    o, ht, _ = O.forward(d["q"], d["k"], d["v"], g, d["beta"], d["h0"], d["cu"], chunk=4,
+    q, k = d["q"], d["k"]
+    if d.get("qk_l2norm"):
+        q, k = O.l2norm(q)[0], O.l2norm(k)[0]
+    o, ht, _ = O.forward(q, k, d["v"], g, d["beta"], d["h0"], d["cu"], chunk=4,
                          want_states=False)
     L = float(np.sum(o * d["dO"]))
     if d["dht"] is not None:
@@ -274,7 +277,8 @@ def _as_inputs(c, **over):
     d.update(over)
     return dict(q=d["q"], k=d["k"], v=d["v"], g_raw=d["g_raw"], A_log=d["A_log"], beta=d["beta"],
                 h0=d["h0"], dO=d["dO"], dht=d["dht"], cu_seqlens=d["cu"], chunk=4,
-                dt_bias=d.get("dt_bias"), gate_log2=d.get("gate_log2", False))
+                dt_bias=d.get("dt_bias"), gate_log2=d.get("gate_log2", False),
+                qk_l2norm=d.get("qk_l2norm", False))
 
 
 _GRADS = ("dq", "dk", "dv", "dg_raw", "dA_log", "dbeta", "dh0")
@@ -336,6 +340,48 @@ def test_finite_differences_gate_variants(gate_log2):
     out = O.kda_backward(_as_inputs(c))
     eps = 1e-6
     for name, gname in (("dt_bias", "ddt_bias"), ("g_raw", "dg_raw"), ("A_log", "dA_log")):
+        x = c[name]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy()
+            xp[idx] += eps
+            xm = x.copy()
+            xm[idx] -= eps
+            num[idx] = (_loss(c, **{name: xp}) - _loss(c, **{name: xm})) / (2 * eps)
+        err = np.abs(num - out[gname]).max() / np.abs(num).max()
+        assert err < 1e-7, (name, err)
+
+
+def test_l2norm_against_library_routines():
+    """The per-token L2 normalisation against numpy, its chain rule against torch
+    autograd of the same map."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(27)
+    x = rng.standard_normal((9, 3, 5)) * rng.uniform(0.01, 10, size=(9, 3, 1))
+    xn, r = O.l2norm(x)
+    ref = x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + O.L2NORM_EPS)
+    np.testing.assert_allclose(xn, ref, rtol=1e-14)
+    np.testing.assert_allclose(r, 1.0 / np.sqrt(np.sum(x * x, axis=-1) + O.L2NORM_EPS), rtol=1e-14)
+    dxn = rng.standard_normal(x.shape)
+    xt = torch.tensor(x, requires_grad=True)
+    yt = xt * torch.rsqrt((xt * xt).sum(-1, keepdim=True) + O.L2NORM_EPS)
+    (yt * torch.tensor(dxn)).sum().backward()
+    np.testing.assert_allclose(O.l2norm_backward(xn, r, dxn), xt.grad.numpy(), rtol=1e-11,
+                               atol=1e-14)
+
+
+def test_finite_differences_qk_l2norm():
+    """With q and k L2-normalised inside the method, central differences of the loss
+    in the raw q and k match dq and dk (gate bias present, both gate units covered by
+    the other finite-difference tests)."""
+    c = _rand_case(28, [5, 7], H=2, K=4, V=3)
+    c["q"] = c["q"] * 3.0
+    c["k"] = c["k"] * 0.5 + 0.1
+    c["qk_l2norm"] = True
+    c["dt_bias"] = np.random.default_rng(29).standard_normal((2, 4))
+    out = O.kda_backward(_as_inputs(c))
+    eps = 1e-6
+    for name, gname in (("q", "dq"), ("k", "dk"), ("g_raw", "dg_raw"), ("beta", "dbeta")):
         x = c[name]
         num = np.zeros_like(x)
         for idx in np.ndindex(x.shape):
