@@ -10,7 +10,10 @@
  * gate is in log2 units: Diag(2^g_t) replaces Diag(exp g_t) (bwd-kernelB-beginner-
  * guide-full, R1, applies the gate with exp2; its K1 reduces ddt_bias).  kda_bwd
  * returns the gradients of  L = sum(dO . o) + sum(dht . S_T)  with respect to q, k, v,
- * g_raw, A_log, beta, h0 and dt_bias.  It is computed chunkwise (64 tokens):
+ * g_raw, A_log, beta, h0 and dt_bias.  With qk_l2norm = 1, q and k are first
+ * L2-normalised per (token, head), x / sqrt(sum x^2 + 1e-6) (R1 of the same guide;
+ * its K1 holds the norm's backward), and dq, dk are with respect to the raw q, k.
+ * It is computed chunkwise (64 tokens):
  * a serial reverse scan carries the state gradient dS back across chunks
  * ("Kernel A", bwd-ncu-and-optimization-playbook, section 3.5 on split-V), then a
  * data-parallel pass per chunk produces the per-token gradients, the gate
@@ -86,6 +89,7 @@ typedef struct kda_problem {
   const int32_t* cu_seqlens_host;
   const int32_t* cu_seqlens_dev;
   int gate_units;     /* KDA_GATE_LN or KDA_GATE_LOG2 (anything else: invalid) */
+  int qk_l2norm;      /* 0, or 1: L2-normalise q and k inside the method (see above) */
 } kda_problem;
 
 /* Device pointers for kda_bwd.  16-byte aligned. */
@@ -162,7 +166,8 @@ KDA_API int kda_abi_version(void);
  * waits for the recorded events, writes per-stage totals (milliseconds) and
  * launch counts for up to n stages, clears them, and returns the number of
  * stages.  Stages: 0 chunk table, 1 prep, 2 state-gradient scan, 3 gradient
- * pass, 4 dA_log reduction, 5 state recompute (h_saved == NULL).
+ * pass, 4 dA_log and dt_bias reductions, 5 state recompute (h_saved == NULL),
+ * 6 q/k L2 normalisation and its backward (qk_l2norm).
  * Not thread-safe; meant for benchmarks. */
 KDA_API int kda_timing_enable(int on);
 KDA_API int kda_timing_read(double* ms, int* launches, int n);

@@ -52,6 +52,7 @@ class Workload:
     fixed_lengths: Optional[tuple] = None  # explicit packed lengths
     dt_bias_std: float = 0.0  # >0: a per-(head, channel) gate bias of this scale
     gate_log2: bool = False   # gate in log2 units (decay 2^g per step)
+    qk_l2norm: bool = False   # q, k normalised inside the method: drawn raw (scale 2, 0.5)
 
     @property
     def tokens(self) -> int:
@@ -109,6 +110,17 @@ EXTRA = {
     "gate_log2_bf16": Workload("gate_log2_bf16", 3, 100, 3, 128, 128, "bf16", 1111,
                                h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0,
                                gate_log2=True),
+    # q, k L2-normalised inside the method (raw inputs of norm 2 sqrt(K) and sqrt(K) / 2)
+    "qk_norm_bf16": Workload("qk_norm_bf16", 1, 1 + 63 + 64 + 65 + 200, 4, 128, 128, "bf16",
+                             1112, varlen_seqs=5, fixed_lengths=(1, 63, 64, 65, 200),
+                             h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0,
+                             qk_l2norm=True),
+    "qk_norm_fp32": Workload("qk_norm_fp32", 2, 200, 2, 64, 64, "f32", 1113, h0_std=0.3,
+                             dht_std=1.0, alog_lo=-3.0, alog_hi=1.0, dt_bias_std=1.0,
+                             gate_log2=True, qk_l2norm=True),
+    "qk_norm_bf16_d64": Workload("qk_norm_bf16_d64", 2, 130, 2, 64, 64, "bf16", 1114,
+                                 h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0,
+                                 qk_l2norm=True),
 }
 
 
@@ -181,8 +193,12 @@ def make_inputs(wl: Workload) -> dict:
     cu[1:] = np.cumsum(lens)
 
     A_log = rng.uniform(wl.alog_lo, wl.alog_hi, size=H).astype(np.float32)
-    q = _l2norm(rng.standard_normal((TT, H, K), dtype=np.float32))
-    k = _l2norm(rng.standard_normal((TT, H, K), dtype=np.float32))
+    q = rng.standard_normal((TT, H, K), dtype=np.float32)
+    k = rng.standard_normal((TT, H, K), dtype=np.float32)
+    if wl.qk_l2norm:
+        q, k = q * np.float32(2.0), k * np.float32(0.5)
+    else:
+        q, k = _l2norm(q), _l2norm(k)
     v = rng.standard_normal((TT, H, V), dtype=np.float32)
     blog = rng.standard_normal((TT, H), dtype=np.float32)
     beta = (1.0 / (1.0 + np.exp(-blog.astype(np.float64)))).astype(np.float32)
@@ -204,7 +220,7 @@ def make_inputs(wl: Workload) -> dict:
     return dict(name=wl.name, dtype=wl.dtype, B=wl.B, T=wl.T, H=H, K=K, V=V, N=N,
                 chunk=CHUNK, cu_seqlens=cu, lens=lens, varlen=wl.varlen_seqs > 0,
                 q=q, k=k, v=v, dO=dO, g_raw=g_raw, beta=beta, A_log=A_log, h0=h0, dht=dht,
-                dt_bias=dt_bias, gate_log2=wl.gate_log2)
+                dt_bias=dt_bias, gate_log2=wl.gate_log2, qk_l2norm=wl.qk_l2norm)
 
 
 def select_heads(inp: dict, heads) -> dict:

@@ -27,7 +27,7 @@ KDA_GATE_LN = 0
 KDA_GATE_LOG2 = 1
 CHUNK = 64
 
-STAGES = ("chunk_table", "prep", "scan", "grad", "dalog", "recompute")
+STAGES = ("chunk_table", "prep", "scan", "grad", "dalog", "recompute", "l2norm")
 
 _P = ctypes.c_void_p
 
@@ -36,7 +36,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("K", ctypes.c_int),
                 ("V", ctypes.c_int), ("chunk", ctypes.c_int), ("act_dtype", ctypes.c_int),
                 ("num_seqs", ctypes.c_int), ("cu_seqlens_host", _P), ("cu_seqlens_dev", _P),
-                ("gate_units", ctypes.c_int)]
+                ("gate_units", ctypes.c_int), ("qk_l2norm", ctypes.c_int)]
 
 
 class BwdIO(ctypes.Structure):
@@ -111,14 +111,15 @@ def _stream_ptr(stream=None):
 class _Prob:
     """A kda_problem plus the host copy of cu_seqlens it points at."""
 
-    def __init__(self, B, T, H, K, V, dtype_code, cu_host=None, cu_dev=None, gate_units=0):
+    def __init__(self, B, T, H, K, V, dtype_code, cu_host=None, cu_dev=None, gate_units=0,
+                 qk_l2norm=0):
         self.cu_host = None
         if cu_host is not None:
             self.cu_host = (ctypes.c_int32 * len(cu_host))(*[int(x) for x in cu_host])
         self.p = Problem(B, T, H, K, V, CHUNK, dtype_code,
                          (len(cu_host) - 1) if cu_host is not None else 0,
                          ctypes.cast(self.cu_host, _P) if self.cu_host is not None else None,
-                         _ptr(cu_dev) if cu_dev is not None else None, gate_units)
+                         _ptr(cu_dev) if cu_dev is not None else None, gate_units, qk_l2norm)
 
     def ref(self):
         return ctypes.byref(self.p)
@@ -148,7 +149,7 @@ def _shape(q, v, cu_seqlens):
     return B, T, H, K, V
 
 
-def _make_prob(q, v, cu_seqlens, gate_log2=False):
+def _make_prob(q, v, cu_seqlens, gate_log2=False, qk_l2norm=False):
     import torch
     B, T, H, K, V = _shape(q, v, cu_seqlens)
     cu_host = cu_dev = None
@@ -157,7 +158,7 @@ def _make_prob(q, v, cu_seqlens, gate_log2=False):
                                     else cu_seqlens)]
         cu_dev = torch.tensor(cu_host, dtype=torch.int32, device=q.device)
     prob = _Prob(B, T, H, K, V, _dtype_code(q), cu_host, cu_dev,
-                 KDA_GATE_LOG2 if gate_log2 else KDA_GATE_LN)
+                 KDA_GATE_LOG2 if gate_log2 else KDA_GATE_LN, 1 if qk_l2norm else 0)
     prob.cu_dev_tensor = cu_dev  # keep alive
     return prob, (B, T, H, K, V)
 
@@ -182,12 +183,13 @@ def _require_cuda(*ts):
 
 def kda_fwd_ref(q, k, v, g_raw, beta, A_log, h0=None, cu_seqlens=None, want_o=True,
                 want_ht=True, want_states=True, stream=None, workspace=None, dt_bias=None,
-                gate_log2=False):
+                gate_log2=False, qk_l2norm=False):
     """Reference forward: returns dict(o, ht, h_saved).  dt_bias [H, K] (optional) is
-    added inside the softplus; gate_log2 = True takes the gate in log2 units."""
+    added inside the softplus; gate_log2 = True takes the gate in log2 units;
+    qk_l2norm = True L2-normalises q and k per token first."""
     import torch
     _require_cuda(q, k, v, g_raw, beta, A_log, h0, dt_bias)
-    prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens, gate_log2)
+    prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens, gate_log2, qk_l2norm)
     N = (len(prob.cu_host) - 1) if prob.cu_host is not None else B
     nc = num_chunks(prob)
     dev = q.device
@@ -210,10 +212,10 @@ class BwdPlan:
 
     def __init__(self, q, k, v, g_raw, beta, A_log, dO, h0=None, dht=None, h_saved=None,
                  cu_seqlens=None, want_dh0=True, want_dstates=False, dt_bias=None,
-                 gate_log2=False, want_ddt_bias=None):
+                 gate_log2=False, want_ddt_bias=None, qk_l2norm=False):
         import torch
         _require_cuda(q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved, dt_bias)
-        self.prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens, gate_log2)
+        self.prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens, gate_log2, qk_l2norm)
         N = (len(self.prob.cu_host) - 1) if self.prob.cu_host is not None else B
         dev = q.device
         self.inputs = (q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved, dt_bias)
@@ -249,11 +251,12 @@ class BwdPlan:
 
 
 def kda_bwd(q, k, v, g_raw, beta, A_log, dO, h0=None, dht=None, h_saved=None, cu_seqlens=None,
-            want_dh0=True, want_dstates=False, stream=None, dt_bias=None, gate_log2=False):
+            want_dh0=True, want_dstates=False, stream=None, dt_bias=None, gate_log2=False,
+            qk_l2norm=False):
     """Backward pass.  Returns dict(dq, dk, dv, dg_raw, dbeta, dA_log, dh0, dstates,
     ddt_bias); ddt_bias is produced when dt_bias is given."""
     plan = BwdPlan(q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved, cu_seqlens, want_dh0,
-                   want_dstates, dt_bias, gate_log2)
+                   want_dstates, dt_bias, gate_log2, qk_l2norm=qk_l2norm)
     plan.run(stream)
     return plan.outputs()
 

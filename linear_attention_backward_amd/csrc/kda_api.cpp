@@ -31,8 +31,10 @@ struct Plan {
   int64_t NC = 0;
   size_t es = 0;  // bytes per act element
   // workspace regions
-  Region chunks, seq_off, groups, grp_off, Tm, PT, eGT, INV, MqkT, dstates, dAl, ddt, Pg, Qg,
-      bnd, hsaved;
+  Region chunks, seq_off, qn, kn, rq, rk, groups, grp_off, Tm, PT, eGT, INV, MqkT, dstates, dAl,
+      ddt, Pg, Qg, bnd, hsaved;
+  int64_t rows = 0;  // tokens * heads
+  bool l2 = false;   // q, k L2-normalised inside the method
   size_t fwd_bytes = 0, bwd_bytes = 0;
 };
 
@@ -75,6 +77,7 @@ int validate_problem(const kda_problem* p) {
   if (p->B < 1 || p->T < 0 || p->H < 1 || p->K < 1 || p->V < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (p->chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (p->gate_units != KDA_GATE_LN && p->gate_units != KDA_GATE_LOG2) return KDA_ERR_INVALID_ARGUMENT;
+  if (p->qk_l2norm != 0 && p->qk_l2norm != 1) return KDA_ERR_INVALID_ARGUMENT;
   if (p->act_dtype != KDA_DTYPE_F32 && p->act_dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
   if (p->K != p->V) return KDA_ERR_UNSUPPORTED;
   if (p->act_dtype == KDA_DTYPE_BF16 && p->K != 64 && p->K != 128) return KDA_ERR_UNSUPPORTED;
@@ -124,6 +127,13 @@ int make_plan(const kda_problem* p, Plan* pl) {
   };
   take(pl->chunks, (size_t)pl->NC * sizeof(ChunkInfo));
   take(pl->seq_off, ((size_t)s.N + 1) * sizeof(int));
+  pl->rows = (int64_t)p->B * p->T * p->H;
+  pl->l2 = p->qk_l2norm == 1;
+  const size_t l2 = pl->l2 ? 1 : 0;
+  take(pl->qn, l2 * (size_t)pl->rows * D * pl->es);
+  take(pl->kn, l2 * (size_t)pl->rows * D * pl->es);
+  take(pl->rq, l2 * (size_t)pl->rows * 4);
+  take(pl->rk, l2 * (size_t)pl->rows * 4);
   pl->fwd_bytes = off;
   take(pl->groups, (size_t)s.NG * sizeof(GroupInfo));
   take(pl->grp_off, ((size_t)s.N + 1) * sizeof(int));
@@ -153,7 +163,7 @@ struct TimedLaunch {
 };
 bool g_timing = false;
 std::vector<TimedLaunch> g_events;
-constexpr int kStages = 6;
+constexpr int kStages = 7;
 
 template <typename F>
 hipError_t timed(int stage, hipStream_t st, F&& launch) {
@@ -261,7 +271,16 @@ int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, siz
   int* seq_off = (int*)(ws + pl.seq_off.off);
   hipError_t e = launch_chunk_table(pl.s, tab, seq_off, nullptr, nullptr, s);
   if (e != hipSuccess) return hip_fail(e);
-  e = launch_fwd_ref(pl.s, seq_off, io->q, io->k, io->v, io->g_raw, io->beta, io->A_log,
+  const void *q = io->q, *k = io->k;
+  if (pl.l2) {
+    q = ws + pl.qn.off;
+    k = ws + pl.kn.off;
+    e = launch_l2norm(pl.s, pl.rows, io->q, (void*)q, (float*)(ws + pl.rq.off), s);
+    if (e == hipSuccess)
+      e = launch_l2norm(pl.s, pl.rows, io->k, (void*)k, (float*)(ws + pl.rk.off), s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  e = launch_fwd_ref(pl.s, seq_off, q, k, io->v, io->g_raw, io->beta, io->A_log,
                      io->dt_bias, io->h0, io->o, io->ht, io->h_saved, s);
   if (e != hipSuccess) return hip_fail(e);
   return KDA_OK;
@@ -289,7 +308,9 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   BwdPtrs b;
-  b.q = io->q; b.k = io->k; b.v = io->v; b.dO = io->dO;
+  b.q = pl.l2 ? (const void*)(ws + pl.qn.off) : io->q;  // the normalised copies when asked
+  b.k = pl.l2 ? (const void*)(ws + pl.kn.off) : io->k;
+  b.v = io->v; b.dO = io->dO;
   b.g_raw = io->g_raw; b.beta = io->beta; b.A_log = io->A_log; b.h0 = io->h0; b.dht = io->dht;
   b.dt_bias = io->dt_bias ? io->dt_bias : io->g_raw;
   b.has_db = io->dt_bias != nullptr;
@@ -319,9 +340,18 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
                               (int*)b.grp_off, s);
   });
   if (e != hipSuccess) return hip_fail(e);
+  float* rq = (float*)(ws + pl.rq.off);
+  float* rk = (float*)(ws + pl.rk.off);
+  if (pl.l2) {
+    e = timed(6, s, [&] {
+      hipError_t x = launch_l2norm(sh, pl.rows, io->q, (void*)b.q, rq, s);
+      return x == hipSuccess ? launch_l2norm(sh, pl.rows, io->k, (void*)b.k, rk, s) : x;
+    });
+    if (e != hipSuccess) return hip_fail(e);
+  }
   if (!io->h_saved) {
     e = timed(5, s, [&] {
-      return launch_fwd_ref(sh, b.seq_off, io->q, io->k, io->v, io->g_raw, io->beta, io->A_log,
+      return launch_fwd_ref(sh, b.seq_off, b.q, b.k, io->v, io->g_raw, io->beta, io->A_log,
                             io->dt_bias, io->h0, nullptr, nullptr, (void*)b.h_saved, s);
     });
     if (e != hipSuccess) return hip_fail(e);
@@ -336,6 +366,13 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   if (e != hipSuccess) return hip_fail(e);
   if (io->ddt_bias) {
     e = timed(4, s, [&] { return launch_ddt(sh, b, s); });
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (pl.l2) {  // dq, dk came out with respect to the normalised q, k: project in place
+    e = timed(6, s, [&] {
+      hipError_t x = launch_l2norm_bwd(sh, pl.rows, b.q, rq, io->dq, s);
+      return x == hipSuccess ? launch_l2norm_bwd(sh, pl.rows, b.k, rk, io->dk, s) : x;
+    });
     if (e != hipSuccess) return hip_fail(e);
   }
   return KDA_OK;

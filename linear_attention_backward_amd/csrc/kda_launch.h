@@ -64,5 +64,11 @@ hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_ddt(const Shape& s, const BwdPtrs& p, hipStream_t st);
+// rows = tokens * heads of a [.., H, D] act-dtype tensor: xn = x / |x|, r = 1 / |x|; and
+// the backward dx = r (dx - xn (xn . dx)) in place
+hipError_t launch_l2norm(const Shape& s, int64_t rows, const void* x, void* xn, float* r,
+                         hipStream_t st);
+hipError_t launch_l2norm_bwd(const Shape& s, int64_t rows, const void* xn, const float* r,
+                             void* dx, hipStream_t st);
 
 }  // namespace kda

@@ -34,7 +34,8 @@ def run_gpu(inp: dict, use_h_saved=True, want_dstates=True):
     import torch
     g = to_gpu(inp)
     cu = inp["cu_seqlens"] if inp["varlen"] else None
-    gate = dict(dt_bias=g["dt_bias"], gate_log2=bool(inp.get("gate_log2", False)))
+    gate = dict(dt_bias=g["dt_bias"], gate_log2=bool(inp.get("gate_log2", False)),
+                qk_l2norm=bool(inp.get("qk_l2norm", False)))
     fwd = K.kda_fwd_ref(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], h0=g["h0"],
                         cu_seqlens=cu, **gate)
     out = K.kda_bwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dO"],

@@ -61,13 +61,20 @@ def test_gate_variants(name):
     _check(name)
 
 
+@pytest.mark.parametrize("name", ["qk_norm_bf16", "qk_norm_fp32", "qk_norm_bf16_d64"])
+def test_qk_l2norm(name):
+    """q and k L2-normalised inside the method (a pass before the kernels, the
+    projection of dq, dk after them), also with log2-unit gates and a gate bias."""
+    _check(name)
+
+
 @pytest.mark.parametrize("name,heads", [("train_bf16", [0, 21]), ("varlen_bf16", [7]),
                                         ("long_bf16", [5])])
 def test_parity_full_size_sampled(name, heads):
     _check(name, heads)
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "ragged_bf16", "gate_log2_fp32"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "ragged_bf16", "gate_log2_fp32", "qk_norm_fp32"])
 def test_state_recompute_path(name):
     """h_saved omitted: the library recomputes the chunk states in-stream."""
     _check(name, use_h_saved=False)
