@@ -174,6 +174,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="train_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dt-bias", action="store_true",
+                    help="method variant: a per-(head, channel) gate bias (and its gradient)")
+    ap.add_argument("--gate-log2", action="store_true",
+                    help="method variant: the gate in log2 units (decay 2^g)")
+    ap.add_argument("--qk-l2norm", action="store_true",
+                    help="method variant: q and k L2-normalised inside the method")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) so that "
                          "HBM counters can be scaled against a kernel of known traffic")
@@ -213,14 +219,17 @@ def main():
     wl = KI.get_workload(a.workload)
     t = time.perf_counter()
     inp = KI.make_inputs(wl)
+    variants = dict(dt_bias=a.dt_bias, gate_log2=a.gate_log2, qk_l2norm=a.qk_l2norm)
+    inp = KI.with_variants(inp, **variants)
     log("inputs generated in %.1f s" % (time.perf_counter() - t))
     g = KC.to_gpu(inp)
     cu = inp["cu_seqlens"] if inp["varlen"] else None
+    vk = dict(dt_bias=g["dt_bias"], gate_log2=inp["gate_log2"], qk_l2norm=inp["qk_l2norm"])
     fwd = K.kda_fwd_ref(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], h0=g["h0"],
-                        cu_seqlens=cu, want_o=False, want_ht=False)
+                        cu_seqlens=cu, want_o=False, want_ht=False, **vk)
     torch.cuda.synchronize()
     plan = K.BwdPlan(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dO"],
-                     h0=g["h0"], dht=g["dht"], h_saved=fwd["h_saved"], cu_seqlens=cu)
+                     h0=g["h0"], dht=g["dht"], h_saved=fwd["h_saved"], cu_seqlens=cu, **vk)
     stream = torch.cuda.current_stream()
     for _ in range(a.warmup):
         plan.run(stream)
@@ -272,6 +281,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": H, "K": D, "V": inp["V"],
                    "chunk": 64, "h_saved": "given", "parallelism": "single-gpu"},
+        **({"variants": [k for k, v in variants.items() if v]} if any(variants.values()) else {}),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "path_roofline": {"bound": "hbm", "algorithmic_bytes": path_bytes,

@@ -223,6 +223,19 @@ def make_inputs(wl: Workload) -> dict:
                 dt_bias=dt_bias, gate_log2=wl.gate_log2, qk_l2norm=wl.qk_l2norm)
 
 
+def with_variants(inp: dict, dt_bias=False, gate_log2=False, qk_l2norm=False) -> dict:
+    """The same inputs with method variants switched on: a per-(head, channel) gate bias
+    ~ N(0,1) from its own seeded stream, the gate in log2 units, q/k L2-normalised inside
+    the method."""
+    out = dict(inp)
+    if dt_bias and out.get("dt_bias") is None:
+        rng = np.random.default_rng(7001)
+        out["dt_bias"] = rng.standard_normal((inp["H"], inp["K"]), dtype=np.float32)
+    out["gate_log2"] = bool(out.get("gate_log2", False) or gate_log2)
+    out["qk_l2norm"] = bool(out.get("qk_l2norm", False) or qk_l2norm)
+    return out
+
+
 def select_heads(inp: dict, heads) -> dict:
     """Restrict an input dict to a subset of heads (copies)."""
     heads = list(heads)

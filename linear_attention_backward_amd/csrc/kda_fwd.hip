@@ -297,14 +297,35 @@ hipError_t launch_l2norm_bwd(const Shape& s, int64_t rows, const void* xn, const
   return l2norm_any(s, rows, nullptr, nullptr, nullptr, xn, r, dx, st);
 }
 
-// ddt_bias[h][i] = sum over chunks of the per chunk-head column sums of dg_raw (fixed
-// order: deterministic).  Block h, thread i; D threads.
-__global__ __launch_bounds__(128) void k_ddt(const float* __restrict__ part, int64_t NC, int H,
+// ddt_bias[h][i] = sum over chunks of the per chunk-head column sums of dg_raw, in a
+// fixed order (deterministic).  Block (h, 16-channel group); lane i + 16 l of the
+// block's 256 threads takes channel i and chunks l, l + 16, ... with four running
+// sums (chunk index mod 64), which are then added in a fixed order.
+__global__ __launch_bounds__(256) void k_ddt(const float* __restrict__ part, int64_t NC, int H,
                                              int D, float* __restrict__ out) {
-  const int h = blockIdx.x, i = threadIdx.x;
-  float acc = 0.f;
-  for (int64_t c = 0; c < NC; ++c) acc += part[(c * H + h) * D + i];
-  out[h * D + i] = acc;
+  __shared__ float red[16][17];
+  const int h = blockIdx.x, ch = 16 * blockIdx.y + (threadIdx.x & 15), l = threadIdx.x >> 4;
+  const float* src = part + (size_t)h * D + ch;
+  const size_t step = (size_t)H * D;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int64_t c = l;
+  for (; c + 48 < NC; c += 64) {
+    a0 += src[c * step];
+    a1 += src[(c + 16) * step];
+    a2 += src[(c + 32) * step];
+    a3 += src[(c + 48) * step];
+  }
+  if (c < NC) a0 += src[c * step];
+  if (c + 16 < NC) a1 += src[(c + 16) * step];
+  if (c + 32 < NC) a2 += src[(c + 32) * step];
+  red[l][threadIdx.x & 15] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (l == 0) {
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) acc += red[x][threadIdx.x & 15];
+    out[h * D + ch] = acc;
+  }
 }
 
 hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, GroupInfo* groups,
@@ -348,7 +369,8 @@ hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st) {
 }
 
 hipError_t launch_ddt(const Shape& s, const BwdPtrs& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_ddt, dim3(s.H), dim3(s.D), 0, st, p.ddt_part, s.NC, s.H, s.D, p.ddt_bias);
+  hipLaunchKernelGGL(k_ddt, dim3(s.H, s.D / 16), dim3(256), 0, st, p.ddt_part, s.NC, s.H, s.D,
+                     p.ddt_bias);
   return hipGetLastError();
 }
 

@@ -92,7 +92,9 @@ template <typename T, int D> struct GF {
   static_assert(N_SZ <= D * PN * ES, "dv staging fits the state tile");
 };
 
-template <typename T, int D>
+// GV: gate bias present or its gradient asked for; without it the bias is not read and
+// no column sums of dg_raw are formed.
+template <typename T, int D, bool GV>
 __global__ __launch_bounds__(4 * D) void k_gradf(
     const ChunkInfo* __restrict__ chunks, int NC, int H, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       rg[t4] = *(const f4*)(grw + (size_t)(r < ci.len ? r : ci.len - 1) * rs);
     }
     rbeta = beta[((size_t)ci.t0 + (lane < ci.len ? lane : ci.len - 1)) * H + h];
-    rdb = *(const f4*)(dt_bias + (size_t)h * D + 16 * w + 4 * (lane & 3));  // always readable
+    if constexpr (GV) rdb = *(const f4*)(dt_bias + (size_t)h * D + 16 * w + 4 * (lane & 3));
   };
   auto issue_late = [&](int it, int t) {
     const int c = it % NC, h = it / NC;
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   }
   settle(rg);  // waits for all of the first item's copies as well
   settle(rbeta);
-  settle(rdb);
+  if constexpr (GV) settle(rdb);
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
   // thread indices re-derived per item so that the lane-dependent LDS addresses
   // below stay inside the loop instead of being held in registers across it
@@ -256,7 +258,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
      // gates go into this wave's 16 channel rows of the tile (written and read back by
      // this wave only), then lane (g4, cl) sums channel 16 w + cl over rows 16 g4 .. + 15
      // and the sums of the earlier row parts come from the lanes that hold them
-    const f4 db = has_db ? rdb : f4{0.f, 0.f, 0.f, 0.f};
+    f4 db = f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (GV) db = has_db ? rdb : db;
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       const int r = 16 * t4 + (lane >> 2);
@@ -752,7 +755,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       if (r < Lr) dal += run * (d * 0.69314718055994531f);
     }
   }
-  {  // this item's column sum of dg_raw (channel ic), for ddt_bias; every lane stores
+  if constexpr (GV) {  // this item's column sum of dg_raw (channel ic), for ddt_bias; every lane stores
     float sdt = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -812,7 +815,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   // wait at their first use would also cover this item's dq and dk stores.
   settle(rg);
   settle(rbeta);
-  settle(rdb);
+  if constexpr (GV) settle(rdb);
   // dO over the dq staging, which is read out; issued after this item's last stores
   // so that the next item's first waits skip it
   if (nxt < items) issue_late(nxt, tid);
@@ -820,20 +823,25 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   }
 }
 
-template <typename T, int D>
-static hipError_t gradf_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+template <typename T, int D, bool GV>
+static hipError_t gradf_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const int items = s.NC * s.H;
   int resident = 0;
-  hipError_t e = resident_blocks((const void*)k_gradf<T, D>, GF<T, D>::NT, &resident);
+  hipError_t e = resident_blocks((const void*)k_gradf<T, D, GV>, GF<T, D>::NT, &resident);
   if (e != hipSuccess) return e;
   const int grid = items < resident ? items : resident;
-  hipLaunchKernelGGL((k_gradf<T, D>), dim3(grid), dim3(GF<T, D>::NT), 0, st, p.chunks, s.NC, s.H,
+  hipLaunchKernelGGL((k_gradf<T, D, GV>), dim3(grid), dim3(GF<T, D>::NT), 0, st, p.chunks, s.NC, s.H,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dO, p.g_raw,
                      p.beta, p.A_log, p.dt_bias, p.has_db, s.gu, (const T*)p.h_saved,
                      (const T*)p.dstates,
                      (const T*)p.INV, (const T*)p.MqkT, (T*)p.dq, (T*)p.dk,
                      (T*)p.dv, p.dg_raw, p.dbeta, p.dAl_part, p.ddt_part);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t gradf_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+  return p.has_db || p.ddt_bias ? gradf_v<T, D, true>(s, p, st) : gradf_v<T, D, false>(s, p, st);
 }
 
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st) {

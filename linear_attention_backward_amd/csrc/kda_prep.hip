@@ -50,7 +50,8 @@ template <typename T, int D> struct PL {
   static_assert(PTS_OFF + D * PPT * ES <= B_OFF, "staging fits the dead region");
 };
 
-template <typename T, int D>
+// GV: gate bias present (or its gradient asked for); without it the bias is not read.
+template <typename T, int D, bool GV>
 __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ chunks, int NC, int H,
                                                 const T* __restrict__ q, const T* __restrict__ k,
                                                 const float* __restrict__ g_raw,
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     }
     if (parts & 1) {
       rbeta = beta[(size_t)(ci.t0 + ((t & 63) < ci.len ? (t & 63) : ci.len - 1)) * H + h];
-      rdb = dt_bias[hD + lo];  // always a readable address; unused without a bias
+      if constexpr (GV) rdb = dt_bias[hD + lo];  // always a readable address
     }
     const T* qh = q + (size_t)ci.t0 * rs + hD;
     const T* kh = k + (size_t)ci.t0 * rs + hD;
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   auto settle_loads = [&]() {
     settle(rg);
     settle(rbeta);
-    settle(rdb);
+    if constexpr (GV) settle(rdb);
     settle(rq);
     settle(rk);
   };
@@ -153,7 +154,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   const ChunkInfo cnx = chunks[(nxt < items ? nxt : it) % NC];  // early: scalar-load latency
   const size_t ch = (size_t)c * H + h;
   const float aA = __expf(A_log[h]) * gu;  // gu: natural-log decay per unit of the gate
-  const float db = has_db ? rdb : 0.f;
+  float db = 0.f;
+  if constexpr (GV) db = has_db ? rdb : 0.f;
   if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
   // in-chunk cumulative gate (log2 units), natural: sG[r][i].  Thread (part, i) sums
   // channel i over rows 16 part .. + 15 in registers and publishes the part's total;
@@ -551,18 +553,23 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   }
 }
 
-template <typename T, int D>
-static hipError_t prep_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+template <typename T, int D, bool GV>
+static hipError_t prep_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const int items = s.NC * s.H;
   int resident = 0;
-  hipError_t e = resident_blocks((const void*)k_prep<T, D>, PL<T, D>::NT, &resident);
+  hipError_t e = resident_blocks((const void*)k_prep<T, D, GV>, PL<T, D>::NT, &resident);
   if (e != hipSuccess) return e;
   const int grid = items < resident ? items : resident;
-  hipLaunchKernelGGL((k_prep<T, D>), dim3(grid), dim3(PL<T, D>::NT), 0, st, p.chunks, s.NC, s.H, (const T*)p.q,
+  hipLaunchKernelGGL((k_prep<T, D, GV>), dim3(grid), dim3(PL<T, D>::NT), 0, st, p.chunks, s.NC, s.H, (const T*)p.q,
                      (const T*)p.k, p.g_raw, p.beta, p.A_log, p.dt_bias, p.has_db, s.gu,
                      (T*)p.Tm, (T*)p.PT, p.eGT,
                      (T*)p.INV, (T*)p.MqkT);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t prep_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+  return p.has_db || p.ddt_bias ? prep_v<T, D, true>(s, p, st) : prep_v<T, D, false>(s, p, st);
 }
 
 hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st) {
