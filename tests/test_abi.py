@@ -55,6 +55,15 @@ def test_shape_validation():
     bad = K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16)
     bad.p.gate_units = 2
     assert _ws(bad)[0] == K.KDA_ERR_INVALID_ARGUMENT
+    bad = K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16, qk_l2norm=2)
+    assert _ws(bad)[0] == K.KDA_ERR_INVALID_ARGUMENT
+    # the q/k L2 norm keeps normalised copies and reciprocal norms in the workspace
+    plain = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16))[1]
+    normed = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16, qk_l2norm=1))[1]
+    assert normed >= plain + 2 * 200 * 4 * 128 * 2 + 2 * 200 * 4 * 4
+    fwd_plain = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16), K.KDA_WS_FWD)[1]
+    fwd_normed = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16, qk_l2norm=1), K.KDA_WS_FWD)[1]
+    assert fwd_normed >= fwd_plain + 2 * 200 * 4 * 128 * 2
 
 
 def test_cu_seqlens_validation():
