@@ -12,6 +12,7 @@ workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -167,6 +168,59 @@ def summarize_profiles(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, c
     return out
 
 
+def bench_forward(a, K, torch, inp, g, cu, vk, wl, variants):
+    """kda_fwd timed over the whole call (chunk table, per-chunk pass, state scan), with
+    the reference forward timed once beside it."""
+    args = (g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"])
+    kw = dict(h0=g["h0"], cu_seqlens=cu, **vk)
+    stream = torch.cuda.current_stream()
+    prob = K._make_prob(g["q"], g["v"], cu, vk["gate_log2"], vk["qk_l2norm"])[0]
+    ws = torch.empty(max(K.workspace_size(prob, K.KDA_WS_FWD), 1), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(a.warmup):
+        K.kda_fwd(*args, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    res = K.kda_fwd(*args, workspace=ws, **kw)
+    io = K.FwdIO(*[K._ptr(x) for x in (g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"],
+                                       g["h0"], res["o"], res["ht"], res["h_saved"], g["dt_bias"])])
+    lib = K.load_library()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(a.steps):
+        K._check(lib.kda_fwd(prob.ref(), ctypes.byref(io), K._ptr(ws), ws.numel(),
+                             K._stream_ptr(stream)))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    e0.record(stream)
+    K.kda_fwd_ref(*args, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_ref = e0.elapsed_time(e1)
+    tokens = int(inp["q"].shape[0])
+    H, D = inp["H"], inp["K"]
+    es = 2 if inp["dtype"] == "bf16" else 4
+    # algorithmic bytes per token-head: q, k, v, g_raw, beta in; o and the chunk-start
+    # state (K x V per 64 tokens) out
+    per_th = 3 * D * es + 4 * D + 4 + D * es + D * D * es / 64
+    nbytes = per_th * tokens * H
+    achieved = nbytes / (ms / 1e3) / 1e9
+    log("kda_fwd: %.3f ms (kda_fwd_ref %.3f ms)" % (ms, ms_ref))
+    print(json.dumps({
+        "metric": "KDA forward tokens/s (o, ht, chunk-start states)", "value": tokens / (ms / 1e3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": inp["dtype"],
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": H, "K": D, "V": inp["V"],
+                   "chunk": 64, "parallelism": "single-gpu"},
+        **({"variants": [k for k, v in variants.items() if v]} if any(variants.values()) else {}),
+        "path_roofline": {"bound": "hbm", "algorithmic_bytes": nbytes, "achieved": achieved,
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS},
+        "reference_forward_ms": ms_ref}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +234,9 @@ def main():
                     help="method variant: the gate in log2 units (decay 2^g)")
     ap.add_argument("--qk-l2norm", action="store_true",
                     help="method variant: q and k L2-normalised inside the method")
+    ap.add_argument("--forward", action="store_true",
+                    help="time the production forward (kda_fwd: o, ht and the chunk-start "
+                         "states) instead of the backward; prints its own JSON line")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) so that "
                          "HBM counters can be scaled against a kernel of known traffic")
@@ -225,6 +282,9 @@ def main():
     g = KC.to_gpu(inp)
     cu = inp["cu_seqlens"] if inp["varlen"] else None
     vk = dict(dt_bias=g["dt_bias"], gate_log2=inp["gate_log2"], qk_l2norm=inp["qk_l2norm"])
+    if a.forward:
+        bench_forward(a, K, torch, inp, g, cu, vk, wl, variants)
+        return
     fwd = K.kda_fwd_ref(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], h0=g["h0"],
                         cu_seqlens=cu, want_o=False, want_ht=False, **vk)
     torch.cuda.synchronize()

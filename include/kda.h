@@ -138,11 +138,13 @@ typedef struct kda_fwd_io {
 } kda_fwd_io;
 
 #define KDA_WS_BWD 0
-#define KDA_WS_FWD 1
+#define KDA_WS_FWD 1     /* kda_fwd (also enough for kda_fwd_ref) */
+#define KDA_WS_FWD_REF 2 /* kda_fwd_ref */
 
-/* Bytes of workspace kda_bwd (which = KDA_WS_BWD) or kda_fwd_ref (KDA_WS_FWD)
- * needs for this problem.  Needs the host cu_seqlens when packed.  The bwd size
- * with h_saved == NULL is the one returned (it is the larger). */
+/* Bytes of workspace kda_bwd (which = KDA_WS_BWD), kda_fwd (KDA_WS_FWD) or
+ * kda_fwd_ref (KDA_WS_FWD_REF) needs for this problem.  Needs the host cu_seqlens
+ * when packed.  The bwd size with h_saved == NULL is the one returned (it is the
+ * larger). */
 KDA_API int kda_workspace_size(const kda_problem* p, int which, size_t* bytes);
 
 /* Total number of 64-token chunks NC over all sequences. */
@@ -152,9 +154,19 @@ KDA_API int kda_num_chunks(const kda_problem* p, int64_t* nchunks);
 KDA_API int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t ws_bytes,
             void* stream);
 
-/* Reference forward: o, ht and the per-chunk start states h_saved. */
+/* Reference forward: o, ht and the per-chunk start states h_saved (one work-item
+ * per (sequence, head, 64 value columns), token by token). */
 KDA_API int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t ws_bytes,
                 void* stream);
+
+/* Production forward, same arguments and results as kda_fwd_ref, in chunk form
+ * (bwd-kernelB-beginner-guide-full, part 2: the UT/WY quantities A, INV, W and
+ * Mqk): a data-parallel pass per chunk forms W = INV diag(beta) K e^G,
+ * Uv = INV diag(beta) V, Qd, Mqk, Kr and e^{G_T}; then one workgroup per (sequence,
+ * head) carries the state over its chunks, U = Uv - W S, O = Qd S + Mqk U,
+ * S <- e^{G_T} . S + Kr^T U.  o, ht and h_saved may each be NULL. */
+KDA_API int kda_fwd(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t ws_bytes,
+            void* stream);
 
 /* Text for a status code (for KDA_ERR_HIP: the last HIP error of this thread). */
 KDA_API const char* kda_status_string(int status);

@@ -23,6 +23,7 @@ KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 KDA_WS_BWD = 0
 KDA_WS_FWD = 1
+KDA_WS_FWD_REF = 2
 KDA_GATE_LN = 0
 KDA_GATE_LOG2 = 1
 CHUNK = 64
@@ -75,10 +76,11 @@ def load_library():
         lib.kda_num_chunks.argtypes = [PP, ctypes.POINTER(ctypes.c_int64)]
         lib.kda_bwd.argtypes = [PP, ctypes.POINTER(BwdIO), _P, ctypes.c_size_t, _P]
         lib.kda_fwd_ref.argtypes = [PP, ctypes.POINTER(FwdIO), _P, ctypes.c_size_t, _P]
+        lib.kda_fwd.argtypes = [PP, ctypes.POINTER(FwdIO), _P, ctypes.c_size_t, _P]
         lib.kda_timing_enable.argtypes = [ctypes.c_int]
         lib.kda_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int), ctypes.c_int]
-        for f in ("kda_workspace_size", "kda_num_chunks", "kda_bwd", "kda_fwd_ref",
+        for f in ("kda_workspace_size", "kda_num_chunks", "kda_bwd", "kda_fwd_ref", "kda_fwd",
                   "kda_timing_enable", "kda_timing_read"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -183,7 +185,7 @@ def _require_cuda(*ts):
 
 def kda_fwd_ref(q, k, v, g_raw, beta, A_log, h0=None, cu_seqlens=None, want_o=True,
                 want_ht=True, want_states=True, stream=None, workspace=None, dt_bias=None,
-                gate_log2=False, qk_l2norm=False):
+                gate_log2=False, qk_l2norm=False, _entry="kda_fwd_ref"):
     """Reference forward: returns dict(o, ht, h_saved).  dt_bias [H, K] (optional) is
     added inside the softplus; gate_log2 = True takes the gate in log2 units;
     qk_l2norm = True L2-normalises q and k per token first."""
@@ -196,14 +198,22 @@ def kda_fwd_ref(q, k, v, g_raw, beta, A_log, h0=None, cu_seqlens=None, want_o=Tr
     o = torch.empty_like(v) if want_o else None
     ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if want_ht else None
     hs = torch.empty((nc, H, K, V), dtype=q.dtype, device=dev) if want_states else None
-    ws_n = workspace_size(prob, KDA_WS_FWD)
+    ws_n = workspace_size(prob, KDA_WS_FWD_REF if _entry == "kda_fwd_ref" else KDA_WS_FWD)
     ws = workspace if workspace is not None else torch.empty(max(ws_n, 1), dtype=torch.uint8,
                                                              device=dev)
     io = FwdIO(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta), _ptr(A_log), _ptr(h0),
                _ptr(o), _ptr(ht), _ptr(hs), _ptr(dt_bias))
-    _check(load_library().kda_fwd_ref(prob.ref(), ctypes.byref(io), _ptr(ws), ws.numel(),
-                                      _stream_ptr(stream)))
+    _check(getattr(load_library(), _entry)(prob.ref(), ctypes.byref(io), _ptr(ws), ws.numel(),
+                                           _stream_ptr(stream)))
     return dict(o=o, ht=ht, h_saved=hs)
+
+
+def kda_fwd(q, k, v, g_raw, beta, A_log, h0=None, cu_seqlens=None, want_o=True, want_ht=True,
+            want_states=True, stream=None, workspace=None, dt_bias=None, gate_log2=False,
+            qk_l2norm=False):
+    """Production forward (chunk form), same arguments and results as kda_fwd_ref."""
+    return kda_fwd_ref(q, k, v, g_raw, beta, A_log, h0, cu_seqlens, want_o, want_ht, want_states,
+                       stream, workspace, dt_bias, gate_log2, qk_l2norm, _entry="kda_fwd")
 
 
 class BwdPlan:

@@ -33,6 +33,8 @@ struct Plan {
   // workspace regions
   Region chunks, seq_off, qn, kn, rq, rk, groups, grp_off, Tm, PT, eGT, INV, MqkT, dstates, dAl,
       ddt, Pg, Qg, bnd, hsaved;
+  Region fWn, fKrT, fUvT, fQd, fMq, fEgt;  // production forward (from fwd_bytes on)
+  size_t fwdp_bytes = 0;
   int64_t rows = 0;  // tokens * heads
   bool l2 = false;   // q, k L2-normalised inside the method
   size_t fwd_bytes = 0, bwd_bytes = 0;
@@ -151,6 +153,15 @@ int make_plan(const kda_problem* p, Plan* pl) {
   take(pl->bnd, split * NGH * D * D * 4);
   take(pl->hsaved, NCH * D * D * pl->es);
   pl->bwd_bytes = off;
+  // the production forward's per-chunk operands, after the reference forward's part
+  off = pl->fwd_bytes;
+  take(pl->fWn, NCH * 64 * D * pl->es);
+  take(pl->fKrT, NCH * D * 64 * pl->es);
+  take(pl->fUvT, NCH * D * 64 * pl->es);
+  take(pl->fQd, NCH * 64 * D * pl->es);
+  take(pl->fMq, NCH * 64 * 64 * pl->es);
+  take(pl->fEgt, NCH * D * 4);
+  pl->fwdp_bytes = off;
   return KDA_OK;
 }
 
@@ -245,11 +256,12 @@ int kda_num_chunks(const kda_problem* p, int64_t* nchunks) {
 }
 
 int kda_workspace_size(const kda_problem* p, int which, size_t* bytes) {
-  if (!bytes || (which != KDA_WS_BWD && which != KDA_WS_FWD)) return KDA_ERR_INVALID_ARGUMENT;
+  if (!bytes || (which != KDA_WS_BWD && which != KDA_WS_FWD && which != KDA_WS_FWD_REF))
+    return KDA_ERR_INVALID_ARGUMENT;
   Plan pl;
   int st = make_plan(p, &pl);
   if (st != KDA_OK) return st;
-  *bytes = which == KDA_WS_BWD ? pl.bwd_bytes : pl.fwd_bytes;
+  *bytes = which == KDA_WS_BWD ? pl.bwd_bytes : which == KDA_WS_FWD ? pl.fwdp_bytes : pl.fwd_bytes;
   return KDA_OK;
 }
 
@@ -282,6 +294,49 @@ int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, siz
   }
   e = launch_fwd_ref(pl.s, seq_off, q, k, io->v, io->g_raw, io->beta, io->A_log,
                      io->dt_bias, io->h0, io->o, io->ht, io->h_saved, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return KDA_OK;
+}
+
+int kda_fwd(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t ws_bytes,
+            void* stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != KDA_OK) return st;
+  if (!io || !io->q || !io->k || !io->v || !io->g_raw || !io->beta || !io->A_log)
+    return KDA_ERR_INVALID_ARGUMENT;
+  const void* al[] = {io->q, io->k, io->v, io->g_raw, io->h_saved, io->o, io->dt_bias};
+  for (const void* x : al)
+    if (!aligned16(x)) return KDA_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < pl.fwdp_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (pl.fwdp_bytes > 0 && !workspace) return KDA_ERR_INVALID_ARGUMENT;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  FwdPtrs f;
+  f.chunks = (const ChunkInfo*)(ws + pl.chunks.off);
+  f.seq_off = (const int*)(ws + pl.seq_off.off);
+  hipError_t e = launch_chunk_table(pl.s, (ChunkInfo*)f.chunks, (int*)f.seq_off, nullptr, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e);
+  f.q = io->q;
+  f.k = io->k;
+  if (pl.l2) {
+    f.q = ws + pl.qn.off;
+    f.k = ws + pl.kn.off;
+    e = launch_l2norm(pl.s, pl.rows, io->q, (void*)f.q, (float*)(ws + pl.rq.off), s);
+    if (e == hipSuccess)
+      e = launch_l2norm(pl.s, pl.rows, io->k, (void*)f.k, (float*)(ws + pl.rk.off), s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  f.v = io->v;
+  f.g_raw = io->g_raw; f.beta = io->beta; f.A_log = io->A_log; f.h0 = io->h0;
+  f.dt_bias = io->dt_bias ? io->dt_bias : io->g_raw;
+  f.has_db = io->dt_bias != nullptr;
+  f.Wn = ws + pl.fWn.off; f.KrT = ws + pl.fKrT.off; f.UvT = ws + pl.fUvT.off;
+  f.Qd = ws + pl.fQd.off; f.Mq = ws + pl.fMq.off; f.eGT = (float*)(ws + pl.fEgt.off);
+  f.o = io->o; f.ht = io->ht; f.h_saved = io->h_saved;
+  e = launch_fprep(pl.s, f, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_fscan(pl.s, f, s);
   if (e != hipSuccess) return hip_fail(e);
   return KDA_OK;
 }

@@ -38,6 +38,27 @@ struct BwdPtrs {
   float* bnd;              // [NG,H,K,V] state gradient at the end of every group (split scan only)
 };
 
+// Pointers of one production-forward call.
+struct FwdPtrs {
+  const void *q, *k, *v;
+  const float *g_raw, *beta, *A_log, *h0;
+  const float* dt_bias;  // always readable (g_raw without a bias); has_db selects it
+  int has_db;
+  const ChunkInfo* chunks;
+  const int* seq_off;
+  // per chunk-head operands (workspace), act dtype unless noted
+  void* Wn;    // [NC,H,64,K]  -W, W = INV diag(beta) K e^G
+  void* KrT;   // [NC,H,K,64]  (K e^{G_T - G})^T
+  void* UvT;   // [NC,H,V,64]  (INV diag(beta) V)^T
+  void* Qd;    // [NC,H,64,K]  Q e^G
+  void* Mq;    // [NC,H,64,64] Mqk
+  float* eGT;  // [NC,H,K]     e^{G_T}
+  // outputs
+  void* o;       // [B,T,H,V] or nullptr
+  float* ht;     // [N,H,K,V] or nullptr
+  void* h_saved; // [NC,H,K,V] or nullptr
+};
+
 struct Shape {
   int N, H, D, T;  // sequences, heads, K = V, tokens per row when not packed
   int64_t NC;      // total chunks
@@ -60,6 +81,8 @@ hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, con
 hipError_t resident_blocks(const void* kernel, int threads, int* out);
 
 hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st);
+hipError_t launch_fprep(const Shape& s, const FwdPtrs& p, hipStream_t st);
+hipError_t launch_fscan(const Shape& s, const FwdPtrs& p, hipStream_t st);
 hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st);

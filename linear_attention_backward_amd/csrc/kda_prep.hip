@@ -51,7 +51,9 @@ template <typename T, int D> struct PL {
 };
 
 // GV: gate bias present (or its gradient asked for); without it the bias is not read.
-template <typename T, int D, bool GV>
+// FWD: the forward's per-chunk operands instead of the backward's (see the end of the
+// item loop).
+template <typename T, int D, bool GV, bool FWD>
 __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ chunks, int NC, int H,
                                                 const T* __restrict__ q, const T* __restrict__ k,
                                                 const float* __restrict__ g_raw,
@@ -61,7 +63,10 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
                                                 float gu,
                                                 T* __restrict__ Tm, T* __restrict__ PT,
                                                 float* __restrict__ eGT, T* __restrict__ INVo,
-                                                T* __restrict__ MqkTo) {
+                                                T* __restrict__ MqkTo, const T* __restrict__ v,
+                                                T* __restrict__ Wn, T* __restrict__ KrT,
+                                                T* __restrict__ UvT, T* __restrict__ Qd,
+                                                T* __restrict__ Mq) {
   using L = PL<T, D>;
   using MM = Mma<T>;
   typedef typename MM::Frag Frag;
@@ -389,6 +394,15 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   if constexpr (NW == 4) kr_kd(tid, NT);
   __syncthreads();
   if (nxt < items) issue_loads(nxt, tid, cnx, 2 | 8);  // g_raw rows 8-15, k
+  u32x4 rv[NLT];  // forward: this item's v, put into the A tile as beta v once INV is formed
+  if constexpr (FWD) {
+    const T* vh = v + (size_t)chunks[c].t0 * rs + (size_t)h * D;
+#pragma unroll
+    for (int l = 0; l < NLT; ++l) {  // rows past the chunk: scaled by beta = 0 when stored
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      rv[l] = *(const u32x4*)(vh + (unsigned)(r < Lr ? r : Lr - 1) * (unsigned)rs + vv * EPV);
+    }
+  }
 
   // ---- INV = (I + L)^{-1}, L = diag(beta) A (strictly lower), blocked by 16.
   // Step 1: wave R < 4 inverts its unit lower-triangular diagonal block (forward
@@ -458,6 +472,19 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   __syncthreads();
 
   settle_loads();  // the next item's inputs, before this item's first stores
+  if constexpr (FWD) {  // beta v into the A tile (dead once INV is formed)
+    T* sVb = (T*)(smem + L::A_OFF);
+#pragma unroll
+    for (int l = 0; l < NLT; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      const T* e = (const T*)&rv[l];
+      const float br = sBeta[r];
+      T out[EPV];
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) out[j] = from_f<T>(br * to_f(e[j]));
+      *(u32x4*)(sVb + r * PN + vv * EPV) = *(const u32x4*)out;
+    }
+  }
 
   // ---- W = INV (beta Kd): wave w -> rows of block w % 4, columns [c0, c0 + DH)
   {
@@ -476,6 +503,74 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) store_c<T>(sW, PN, 16 * R, c0 + nt * 16, acc[nt], lane);
   }
+  if constexpr (FWD) {
+    __syncthreads();  // W formed; beta v in the A tile
+    // Uv = INV (beta V), rows of block w % 4, columns [c0, c0 + DH); written as Uv^T
+    // straight from the C tiles (a lane holds 4 consecutive rows of one column)
+    {
+      const int R = w & 3, c0 = (w >> 2) * DH;
+      const T* sVb = (const T*)(smem + L::A_OFF);
+      constexpr int NTW = DH / 16;
+      f4 acc[NTW];
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) acc[nt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < NKC; ++ks) {
+        const Frag a = MM::ld_perm_f32(sINV + (16 * R + cl) * PC, ks * KS, lane);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          acc[nt] = MM::mma(a, MM::ld_tr(sVb, PN, ks * KS, c0 + nt * 16, lane), acc[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        T u4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u4[j] = from_f<T>(acc[nt][j]);
+        T* dst = UvT + ch * D * 64 + (size_t)(c0 + nt * 16 + cl) * 64 + 16 * R + 4 * g4;
+        if constexpr (L::ES == 2) *(uint2*)dst = *(const uint2*)u4;
+        else *(uint4*)dst = *(const uint4*)u4;
+      }
+    }
+    // -W and Qd = Q e^G (natural rows)
+#pragma unroll
+    for (int l = 0; l < NLT; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      const u32x4 wv = *(const u32x4*)(sW + r * PN + vv * EPV);
+      const u32x4 qv = *(const u32x4*)(sQ + r * PN + vv * EPV);
+      const T* we = (const T*)&wv;
+      const T* qe = (const T*)&qv;
+      T wn[EPV], qd[EPV];
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) {
+        wn[j] = from_f<T>(-to_f(we[j]));
+        qd[j] = from_f<T>(to_f(qe[j]) * ex2(sG[r * PGN + vv * EPV + j]));
+      }
+      const size_t o = ch * 64 * D + (size_t)r * D + vv * EPV;
+      *(u32x4*)(Wn + o) = *(const u32x4*)wn;
+      *(u32x4*)(Qd + o) = *(const u32x4*)qd;
+    }
+    // Mqk (natural rows) and Kr^T, 8 elements per piece
+    for (int e = tid; e < 64 * 8; e += NT) {
+      const int r = e >> 3, c8 = (e & 7) * 8;
+      T tm[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tm[j] = from_f<T>(sM[r * PC + c8 + j]);
+#pragma unroll
+      for (int x = 0; x < 8 * L::ES / 16; ++x)
+        ((uint4*)(Mq + ch * 64 * 64 + r * 64 + c8))[x] = ((const uint4*)tm)[x];
+    }
+    for (int e = tid; e < D * 8; e += NT) {
+      const int i = e >> 3, r8 = (e & 7) * 8;
+      T kt[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kt[j] = sKr[(r8 + j) * PN + i];
+#pragma unroll
+      for (int x = 0; x < 8 * L::ES / 16; ++x)
+        ((uint4*)(KrT + ch * D * 64 + (size_t)i * 64 + r8))[x] = ((const uint4*)kt)[x];
+    }
+    if (tid < D) eGT[ch * D + tid] = ex2(sG[63 * PGN + tid]);
+    __syncthreads();  // the next item overwrites sG, sQ and sK (here read as W)
+  } else {
   // ---- INV and Mqk^T (act dtype, natural rows) for the gradient pass (which reads
   // INV^T out of its copy of INV)
   for (int e = tid; e < 64 * 8; e += NT) {
@@ -549,6 +644,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       *(uint4*)(dp + r * 64 + vv * EPV) = *(const uint4*)(sPT + r * PPT + vv * EPV);
     }
   }
+  }
   // the next item writes sG, sQ, sK and sBeta only: no reader of those is left
   }
 }
@@ -557,19 +653,44 @@ template <typename T, int D, bool GV>
 static hipError_t prep_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const int items = s.NC * s.H;
   int resident = 0;
-  hipError_t e = resident_blocks((const void*)k_prep<T, D, GV>, PL<T, D>::NT, &resident);
+  hipError_t e = resident_blocks((const void*)k_prep<T, D, GV, false>, PL<T, D>::NT, &resident);
   if (e != hipSuccess) return e;
   const int grid = items < resident ? items : resident;
-  hipLaunchKernelGGL((k_prep<T, D, GV>), dim3(grid), dim3(PL<T, D>::NT), 0, st, p.chunks, s.NC, s.H, (const T*)p.q,
+  hipLaunchKernelGGL((k_prep<T, D, GV, false>), dim3(grid), dim3(PL<T, D>::NT), 0, st, p.chunks, s.NC, s.H, (const T*)p.q,
                      (const T*)p.k, p.g_raw, p.beta, p.A_log, p.dt_bias, p.has_db, s.gu,
                      (T*)p.Tm, (T*)p.PT, p.eGT,
-                     (T*)p.INV, (T*)p.MqkT);
+                     (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool GV>
+static hipError_t fprep_v(const Shape& s, const FwdPtrs& p, hipStream_t st) {
+  const int items = s.NC * s.H;
+  int resident = 0;
+  hipError_t e = resident_blocks((const void*)k_prep<T, D, GV, true>, PL<T, D>::NT, &resident);
+  if (e != hipSuccess) return e;
+  const int grid = items < resident ? items : resident;
+  hipLaunchKernelGGL((k_prep<T, D, GV, true>), dim3(grid), dim3(PL<T, D>::NT), 0, st, p.chunks,
+                     s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta, p.A_log,
+                     p.dt_bias, p.has_db, s.gu, nullptr, nullptr, p.eGT, nullptr, nullptr,
+                     (const T*)p.v, (T*)p.Wn, (T*)p.KrT, (T*)p.UvT, (T*)p.Qd, (T*)p.Mq);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t prep_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   return p.has_db || p.ddt_bias ? prep_v<T, D, true>(s, p, st) : prep_v<T, D, false>(s, p, st);
+}
+
+template <typename T, int D>
+static hipError_t fprep_t(const Shape& s, const FwdPtrs& p, hipStream_t st) {
+  return p.has_db ? fprep_v<T, D, true>(s, p, st) : fprep_v<T, D, false>(s, p, st);
+}
+
+hipError_t launch_fprep(const Shape& s, const FwdPtrs& p, hipStream_t st) {
+  if (s.NC == 0) return hipSuccess;
+  if (s.bf16) return s.D == 128 ? fprep_t<bf16, 128>(s, p, st) : fprep_t<bf16, 64>(s, p, st);
+  return fprep_t<float, 64>(s, p, st);
 }
 
 hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st) {

@@ -287,6 +287,211 @@ __global__ __launch_bounds__(4 * D) void k_scan_bnd(const GroupInfo* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Forward state scan (the production forward).  Per (sequence, head), chunks first to
+// last, with U = INV diag(beta) (V - Kd S) written as X = Uv + Wn S (Wn = -W):
+//   h_saved(c) = S;   O = Qd S + Mqk X;   S <- e^{G_T} . S + Kr^T X,
+// and ht = S after the last chunk.  S is carried in fp32 MFMA accumulators with the
+// tiling of the backward scan (wave w: row tiles of row group w % 4, column tiles of
+// column group w / 4); X and O are 64 x V, wave w holding row tile w % 4 and the
+// column tiles of column group w / 4.  S and X go through LDS as natural tiles of T,
+// read back as B operands; O is staged in LDS and stored as 16-byte rows a step later.
+// The operands of the next chunk are loaded at the start of each step.
+template <typename T, int D>
+__global__ __launch_bounds__(4 * D) void k_fscan(
+    const ChunkInfo* __restrict__ chunks, const int* __restrict__ seq_off, int H,
+    const T* __restrict__ Wn, const T* __restrict__ KrT, const T* __restrict__ UvT,
+    const T* __restrict__ Qd, const T* __restrict__ Mq, const float* __restrict__ eGT,
+    const float* __restrict__ h0, T* __restrict__ o, float* __restrict__ ht,
+    T* __restrict__ h_saved) {
+  using L = SL<T, D>;
+  using MM = Mma<T>;
+  typedef typename MM::Frag Frag;
+  constexpr int NT = L::NT, RTW = L::RTW, CTW = L::CTW, PS = L::PS, PO = L::PO;
+  constexpr int KS = MM::KS;
+  constexpr int NKD = D / KS, NKC = 64 / KS;
+  constexpr int EPV = 16 / L::ES;
+  constexpr int VPR = D / EPV;       // 16-byte vectors per D-long row
+  constexpr int NLO = 64 * VPR / NT; // O vectors per thread
+  constexpr int NLS = D * VPR / NT;  // state vectors per thread
+  static_assert(64 * VPR % NT == 0 && D * VPR % NT == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) char smem[L::S_SZ + 2 * L::O_SZ];
+  T* sS = (T*)smem;
+  T* sX = (T*)(smem + L::S_SZ);
+  T* sO = (T*)(smem + L::S_SZ + L::O_SZ);
+
+  const int n = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, cl = lane & 15;
+  const int rgp = w & 3, cgp = w >> 2;
+  const int xr = w & 3;  // row tile of X and O
+  const size_t DD = (size_t)D * D;
+  const size_t uh = (size_t)n * H + h;
+  const int cb = seq_off[n], nck = seq_off[n + 1] - cb;
+  const size_t rs = (size_t)H * D;
+
+  f4 acc[RTW][CTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      const int i0 = (rgp * RTW + rt) * 16 + 4 * g4;
+      const int col = (cgp * CTW + ct) * 16 + cl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[rt][ct][j] = h0 ? h0[uh * DD + (size_t)(i0 + j) * D + col] : 0.f;
+    }
+
+  // One set of operand fragments, each part refilled for the next chunk right after its
+  // last use in the current step (so that it has most of a step to land).
+  Frag fw[NKD], fq[NKD], fm[NKC], fk[RTW][NKC];
+  f4 fuv[CTW], fe[RTW];
+  auto load_xo = [&](int cg) {  // operands of X and of Qd S
+    const size_t ch = (size_t)cg * H + h;
+    const int r = 16 * xr + cl;
+#pragma unroll
+    for (int kk = 0; kk < NKD; ++kk) {
+      fw[kk] = MM::ld_nat(Wn + ch * 64 * D + (size_t)r * D, kk * KS, lane);
+      fq[kk] = MM::ld_nat(Qd + ch * 64 * D + (size_t)r * D, kk * KS, lane);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {  // Uv rows 16 xr + 4 g4 .. + 3 of column col
+      const int col = (cgp * CTW + ct) * 16 + cl;
+      const T* src = UvT + ch * D * 64 + (size_t)col * 64 + 16 * xr + 4 * g4;
+      T u4[4];
+      if constexpr (L::ES == 2) *(uint2*)u4 = *(const uint2*)src;
+      else *(uint4*)u4 = *(const uint4*)src;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fuv[ct][j] = to_f(u4[j]);
+    }
+  };
+  auto load_m = [&](int cg) {
+    const size_t ch = (size_t)cg * H + h;
+#pragma unroll
+    for (int kk = 0; kk < NKC; ++kk)
+      fm[kk] = MM::ld_nat(Mq + ch * 4096 + (size_t)(16 * xr + cl) * 64, kk * KS, lane);
+  };
+  auto load_k = [&](int cg) {
+    const size_t ch = (size_t)cg * H + h;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int i = (rgp * RTW + rt) * 16 + cl;
+#pragma unroll
+      for (int kk = 0; kk < NKC; ++kk) fk[rt][kk] = MM::ld_nat(KrT + ch * D * 64 + (size_t)i * 64, kk * KS, lane);
+      fe[rt] = *(const f4*)(eGT + ch * D + (rgp * RTW + rt) * 16 + 4 * g4);
+    }
+  };
+  // O of chunk cg (staged in sO) out as 16-byte rows; rows past the chunk are not
+  // part of the sequence
+  auto store_o = [&](int cg) {
+    const ChunkInfo ci = chunks[cg];
+#pragma unroll
+    for (int l = 0; l < NLO; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      if (r < ci.len)
+        *(uint4*)(o + ((size_t)ci.t0 + r) * rs + (size_t)h * D + vv * EPV) =
+            *(const uint4*)(sO + r * PO + vv * EPV);
+    }
+  };
+  if (nck > 0) {
+    load_xo(cb);
+    load_m(cb);
+    load_k(cb);
+  }
+  for (int c = 0; c < nck; ++c) {
+    const int cg = cb + c;
+    const bool more = c + 1 < nck;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+        store_c<T>(sS, PS, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, acc[rt][ct], lane);
+    __syncthreads();
+    if (h_saved) {  // the state at the start of this chunk, 16-byte rows
+      T* dst = h_saved + ((size_t)cg * H + h) * DD;
+#pragma unroll
+      for (int l = 0; l < NLS; ++l) {
+        const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+        *(uint4*)(dst + (size_t)r * D + vv * EPV) = *(const uint4*)(sS + r * PS + vv * EPV);
+      }
+    }
+    if (o && c > 0) store_o(cg - 1);
+    // X = Uv + Wn S and the first part of O, Qd S (same B fragments)
+    f4 X[CTW], Oa[CTW];
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      X[ct] = fuv[ct];
+      Oa[ct] = zero4();
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKD; ++kk) {
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const Frag b = MM::ld_tr_nat(sS, PS, kk * KS, (cgp * CTW + ct) * 16, lane);
+        X[ct] = MM::mma(fw[kk], b, X[ct]);
+        if (o) Oa[ct] = MM::mma(fq[kk], b, Oa[ct]);
+      }
+    }
+    if (more) load_xo(cg + 1);
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) store_c<T>(sX, PO, 16 * xr, (cgp * CTW + ct) * 16, X[ct], lane);
+    __syncthreads();
+    if (o) {  // O += Mqk X, staged for the next step
+#pragma unroll
+      for (int kk = 0; kk < NKC; ++kk) {
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct)
+          Oa[ct] = MM::mma(fm[kk], MM::ld_tr_nat(sX, PO, kk * KS, (cgp * CTW + ct) * 16, lane), Oa[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) store_c<T>(sO, PO, 16 * xr, (cgp * CTW + ct) * 16, Oa[ct], lane);
+    }
+    if (more) load_m(cg + 1);
+    // S <- e^{G_T} . S + Kr^T X
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[rt][ct][j] *= fe[rt][j];
+#pragma unroll
+    for (int kk = 0; kk < NKC; ++kk) {
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const Frag b = MM::ld_tr_nat(sX, PO, kk * KS, (cgp * CTW + ct) * 16, lane);
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) acc[rt][ct] = MM::mma(fk[rt][kk], b, acc[rt][ct]);
+      }
+    }
+    if (more) load_k(cg + 1);
+  }
+  if (o && nck > 0) {
+    __syncthreads();  // the last chunk's O staging complete
+    store_o(cb + nck - 1);
+  }
+  if (ht) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+        store_c<float>(ht + uh * DD, D, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, acc[rt][ct],
+                       lane);
+  }
+}
+
+template <typename T, int D>
+static hipError_t fscan_t(const Shape& s, const FwdPtrs& p, hipStream_t st) {
+  hipLaunchKernelGGL((k_fscan<T, D>), dim3((unsigned)s.N, (unsigned)s.H), dim3(SL<T, D>::NT), 0, st,
+                     p.chunks, p.seq_off, s.H, (const T*)p.Wn, (const T*)p.KrT, (const T*)p.UvT,
+                     (const T*)p.Qd, (const T*)p.Mq, p.eGT, p.h0, (T*)p.o, p.ht, (T*)p.h_saved);
+  return hipGetLastError();
+}
+
+hipError_t launch_fscan(const Shape& s, const FwdPtrs& p, hipStream_t st) {
+  if (s.N * s.H == 0) return hipSuccess;
+  if (s.bf16) return s.D == 128 ? fscan_t<bf16, 128>(s, p, st) : fscan_t<bf16, 64>(s, p, st);
+  return fscan_t<float, 64>(s, p, st);
+}
+
 template <typename T, int D>
 static hipError_t scan_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const dim3 gg((unsigned)s.NG, (unsigned)s.H);

@@ -197,6 +197,19 @@ def backward(q, k, v, g, beta, h0, dO, dht, cu, chunk=64, want_dstates=False, nt
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=db, dh0=dh0, dstates=dst)
 
 
+def kda_forward(inp: dict, nthreads=0) -> dict:
+    """Forward from raw inputs (same optional entries as kda_backward): o, ht and the
+    states at every chunk start, by the per-token recurrence."""
+    gkw = dict(dt_bias=inp.get("dt_bias"), log2_units=bool(inp.get("gate_log2", False)))
+    g = gate(inp["g_raw"], inp["A_log"], **gkw)
+    q, k = inp["q"], inp["k"]
+    if inp.get("qk_l2norm", False):
+        q, k = l2norm(q)[0], l2norm(k)[0]
+    o, ht, st = forward(q, k, inp["v"], g, inp["beta"], inp["h0"], inp["cu_seqlens"],
+                        chunk=inp.get("chunk", 64), want_states=True, nthreads=nthreads)
+    return dict(o=o, ht=ht, states=st)
+
+
 def kda_backward(inp: dict, want_dstates=False, want_states=False, nthreads=0) -> dict:
     """Full backward from raw inputs (an input dict as produced by kda_inputs):
     gate, per-token backward, gate chain rule.  Returns fp64 arrays dq, dk, dv,

@@ -86,3 +86,30 @@ def oracle_for(inp: dict, heads=None, want_dstates=True, want_states=True):
     from oracle import oracle as O
     sub = KI.select_heads(inp, heads) if heads is not None else inp
     return O.kda_backward(sub, want_dstates=want_dstates, want_states=want_states)
+
+
+def run_gpu_fwd(inp: dict):
+    """The production forward through the C ABI: o, ht, h_saved as fp64 arrays."""
+    import linear_attention_backward_amd as K
+    import torch
+    g = to_gpu(inp)
+    cu = inp["cu_seqlens"] if inp["varlen"] else None
+    fwd = K.kda_fwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], h0=g["h0"],
+                    cu_seqlens=cu, dt_bias=g["dt_bias"],
+                    gate_log2=bool(inp.get("gate_log2", False)),
+                    qk_l2norm=bool(inp.get("qk_l2norm", False)))
+    torch.cuda.synchronize()
+    TT = inp["q"].shape[0]
+    res = {}
+    for key, val in fwd.items():
+        a = val.float().cpu().numpy().astype(np.float64)
+        if key == "o" and a.ndim == 4:
+            a = a.reshape(TT, *a.shape[2:])
+        res[key] = a
+    return res
+
+
+def oracle_fwd_for(inp: dict, heads=None):
+    from oracle import oracle as O
+    sub = KI.select_heads(inp, heads) if heads is not None else inp
+    return O.kda_forward(sub)

@@ -68,6 +68,25 @@ def test_qk_l2norm(name):
     _check(name)
 
 
+@pytest.mark.parametrize("name,heads", [
+    ("tiny_fp32", None), ("ragged_fp32", None), ("weak_decay_fp32", None),
+    ("single_token_fp32", None), ("single_seq_bf16", None), ("ragged_bf16", None),
+    ("ragged_bf16_d64", None), ("multi_ragged_bf16", None), ("strong_decay_bf16", None),
+    ("gate_bias_bf16", None), ("gate_log2_fp32", None), ("qk_norm_bf16", None),
+    ("train_bf16", [0, 21]), ("varlen_bf16", [7])])
+def test_forward_parity(name, heads):
+    """The production forward (kda_fwd) against the oracle's per-token recurrence:
+    outputs, final states and the states at every chunk start."""
+    print("\n[case] forward %s heads=%s" % (name, heads), flush=True)
+    inp = KI.make_inputs(KI.get_workload(name))
+    res = KC.run_gpu_fwd(inp)
+    ref = KC.oracle_fwd_for(inp, heads)
+    ref["h_saved"] = ref["states"]
+    rep = KC.compare(res, ref, ["o", "ht", "h_saved"], KC.TOL[inp["dtype"]], heads=heads,
+                     label="forward " + name)
+    print("[errors] " + " ".join("%s=%.2e" % kv for kv in rep.items()), flush=True)
+
+
 @pytest.mark.parametrize("name,heads", [("train_bf16", [0, 21]), ("varlen_bf16", [7]),
                                         ("long_bf16", [5])])
 def test_parity_full_size_sampled(name, heads):
