@@ -34,6 +34,7 @@ struct Plan {
   Region chunks, seq_off, qn, kn, rq, rk, groups, grp_off, Tm, PT, eGT, INV, MqkT, dstates, dAl,
       ddt, Pg, Qg, bnd, hsaved;
   Region fWn, fKrT, fUvT, fQd, fMq, fEgt;  // production forward (from fwd_bytes on)
+  Region rWn, rKrT, rUvT, rQd, rMq;        // the same operands for the in-stream recompute
   size_t fwdp_bytes = 0;
   int64_t rows = 0;  // tokens * heads
   bool l2 = false;   // q, k L2-normalised inside the method
@@ -152,6 +153,13 @@ int make_plan(const kda_problem* p, Plan* pl) {
   take(pl->Qg, split * NGH * D * D * 4);
   take(pl->bnd, split * NGH * D * D * 4);
   take(pl->hsaved, NCH * D * D * pl->es);
+  // the forward's per-chunk operands for the state recompute (only without h_saved; the
+  // recompute regions are the last ones)
+  take(pl->rWn, NCH * 64 * D * pl->es);
+  take(pl->rKrT, NCH * D * 64 * pl->es);
+  take(pl->rUvT, NCH * D * 64 * pl->es);
+  take(pl->rQd, NCH * 64 * D * pl->es);
+  take(pl->rMq, NCH * 64 * 64 * pl->es);
   pl->bwd_bytes = off;
   // the production forward's per-chunk operands, after the reference forward's part
   off = pl->fwd_bytes;
@@ -404,10 +412,19 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
     });
     if (e != hipSuccess) return hip_fail(e);
   }
-  if (!io->h_saved) {
+  if (!io->h_saved) {  // the chunk-start states by the production forward
+    FwdPtrs f;
+    f.q = b.q; f.k = b.k; f.v = io->v;
+    f.g_raw = io->g_raw; f.beta = io->beta; f.A_log = io->A_log; f.h0 = io->h0;
+    f.dt_bias = b.dt_bias; f.has_db = b.has_db;
+    f.chunks = b.chunks; f.seq_off = b.seq_off;
+    f.Wn = ws + pl.rWn.off; f.KrT = ws + pl.rKrT.off; f.UvT = ws + pl.rUvT.off;
+    f.Qd = ws + pl.rQd.off; f.Mq = ws + pl.rMq.off;
+    f.eGT = b.eGT;  // prep writes the same values again
+    f.o = nullptr; f.ht = nullptr; f.h_saved = (void*)b.h_saved;
     e = timed(5, s, [&] {
-      return launch_fwd_ref(sh, b.seq_off, b.q, b.k, io->v, io->g_raw, io->beta, io->A_log,
-                            io->dt_bias, io->h0, nullptr, nullptr, (void*)b.h_saved, s);
+      hipError_t x = launch_fprep(sh, f, s);
+      return x == hipSuccess ? launch_fscan(sh, f, s) : x;
     });
     if (e != hipSuccess) return hip_fail(e);
   }
