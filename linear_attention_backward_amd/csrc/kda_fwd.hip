@@ -33,21 +33,19 @@ __global__ __launch_bounds__(256) void k_chunk_table(const int32_t* __restrict__
     cnt += nck;
     gcnt += ngroups(nck);
   }
-  part[tid] = cnt;
-  gpart[tid] = gcnt;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0, grun = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int x = part[i], y = gpart[i];
-      part[i] = run;
-      gpart[i] = grun;
-      run += x;
-      grun += y;
+  // exclusive prefix sums over the 256 threads (inclusive scan by doubling, then shift)
+  int x = cnt, y = gcnt;
+  for (int d = 1; d < 256; d <<= 1) {
+    part[tid] = x;
+    gpart[tid] = y;
+    __syncthreads();
+    if (tid >= d) {
+      x += part[tid - d];
+      y += gpart[tid - d];
     }
+    __syncthreads();
   }
-  __syncthreads();
-  int off = part[tid], goff = gpart[tid];
+  int off = x - cnt, goff = y - gcnt;
   for (int n = n0; n < n1; ++n) {
     const int start = cu ? cu[n] : n * T;
     const int len = cu ? cu[n + 1] - cu[n] : T;
