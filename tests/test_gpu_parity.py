@@ -73,7 +73,7 @@ def test_qk_l2norm(name):
     ("single_token_fp32", None), ("single_seq_bf16", None), ("ragged_bf16", None),
     ("ragged_bf16_d64", None), ("multi_ragged_bf16", None), ("strong_decay_bf16", None),
     ("gate_bias_bf16", None), ("gate_log2_fp32", None), ("qk_norm_bf16", None),
-    ("train_bf16", [0, 21]), ("varlen_bf16", [7])])
+    ("train_bf16", [0, 21]), ("varlen_bf16", [7]), ("long_bf16", [5])])
 def test_forward_parity(name, heads):
     """The production forward (kda_fwd) against the oracle's per-token recurrence:
     outputs, final states and the states at every chunk start."""
