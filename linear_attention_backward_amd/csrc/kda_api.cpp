@@ -34,6 +34,7 @@ struct Plan {
   Region chunks, seq_off, qn, kn, rq, rk, groups, grp_off, Tm, PT, eGT, INV, MqkT, dstates, dAl,
       ddt, Pg, Qg, bnd, hsaved;
   Region fWn, fKrT, fUvT, fQd, fMq, fEgt;  // production forward (from fwd_bytes on)
+  Region fgroups, fgrp_off, fPg, fQg, fbnd;
   Region rWn, rKrT, rUvT, rQd, rMq;        // the same operands for the in-stream recompute
   size_t fwdp_bytes = 0;
   int64_t rows = 0;  // tokens * heads
@@ -163,6 +164,11 @@ int make_plan(const kda_problem* p, Plan* pl) {
   pl->bwd_bytes = off;
   // the production forward's per-chunk operands, after the reference forward's part
   off = pl->fwd_bytes;
+  take(pl->fgroups, (size_t)s.NG * sizeof(GroupInfo));
+  take(pl->fgrp_off, ((size_t)s.N + 1) * sizeof(int));
+  take(pl->fPg, split * NGH * D * D * pl->es);
+  take(pl->fQg, split * NGH * D * D * 4);
+  take(pl->fbnd, split * NGH * D * D * 4);
   take(pl->fWn, NCH * 64 * D * pl->es);
   take(pl->fKrT, NCH * D * 64 * pl->es);
   take(pl->fUvT, NCH * D * 64 * pl->es);
@@ -323,7 +329,13 @@ int kda_fwd(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t 
   FwdPtrs f;
   f.chunks = (const ChunkInfo*)(ws + pl.chunks.off);
   f.seq_off = (const int*)(ws + pl.seq_off.off);
-  hipError_t e = launch_chunk_table(pl.s, (ChunkInfo*)f.chunks, (int*)f.seq_off, nullptr, nullptr, s);
+  f.groups = (const GroupInfo*)(ws + pl.fgroups.off);
+  f.grp_off = (const int*)(ws + pl.fgrp_off.off);
+  f.Pg = ws + pl.fPg.off;
+  f.Qg = (float*)(ws + pl.fQg.off);
+  f.bnd = (float*)(ws + pl.fbnd.off);
+  hipError_t e = launch_chunk_table(pl.s, (ChunkInfo*)f.chunks, (int*)f.seq_off,
+                                    (GroupInfo*)f.groups, (int*)f.grp_off, s);
   if (e != hipSuccess) return hip_fail(e);
   f.q = io->q;
   f.k = io->k;
@@ -418,6 +430,8 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
     f.g_raw = io->g_raw; f.beta = io->beta; f.A_log = io->A_log; f.h0 = io->h0;
     f.dt_bias = b.dt_bias; f.has_db = b.has_db;
     f.chunks = b.chunks; f.seq_off = b.seq_off;
+    f.groups = b.groups; f.grp_off = b.grp_off;  // the split-scan regions, free until the scan
+    f.Pg = b.Pg; f.Qg = b.Qg; f.bnd = b.bnd;
     f.Wn = ws + pl.rWn.off; f.KrT = ws + pl.rKrT.off; f.UvT = ws + pl.rUvT.off;
     f.Qd = ws + pl.rQd.off; f.Mq = ws + pl.rMq.off;
     f.eGT = b.eGT;  // prep writes the same values again

@@ -46,6 +46,11 @@ struct FwdPtrs {
   int has_db;
   const ChunkInfo* chunks;
   const int* seq_off;
+  const GroupInfo* groups;  // chunk groups of the state scan (one per sequence unless split)
+  const int* grp_off;
+  void* Pg;                 // [NG,H,K,K] act dtype: group transitions (split scan only)
+  float* Qg;                // [NG,H,K,V] group offsets (split scan only)
+  float* bnd;               // [NG,H,K,V] state at the start of every group (split scan only)
   // per chunk-head operands (workspace), act dtype unless noted
   void* Wn;    // [NC,H,64,K]  -W, W = INV diag(beta) K e^G
   void* KrT;   // [NC,H,K,64]  (K e^{G_T - G})^T

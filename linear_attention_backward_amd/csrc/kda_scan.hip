@@ -214,9 +214,12 @@ __global__ __launch_bounds__(4 * D) void k_scanw(
     }
 }
 
-// Group boundaries of one (sequence, head): B = dht at the end of the last group;
-// going back, bnd[g] = B (the state at the end of group g), then B <- P_g B + Q_g.
-template <typename T, int D>
+// Group boundaries of one (sequence, head).  Backward (FWD = false): B = dht at the
+// end of the last group; going back, B <- P_g B + Q_g is the state gradient at the end
+// of the group before, stored as bnd of that group.  Forward (FWD = true): S = h0 at the
+// start of the first group; going forward, S <- P_g S + Q_g is the state at the start
+// of the next group, stored as its bnd.
+template <typename T, int D, bool FWD>
 __global__ __launch_bounds__(4 * D) void k_scan_bnd(const GroupInfo* __restrict__ groups,
                                                     const int* __restrict__ grp_off, int H,
                                                     const T* __restrict__ Pg,
@@ -248,9 +251,11 @@ __global__ __launch_bounds__(4 * D) void k_scan_bnd(const GroupInfo* __restrict_
         for (int j = 0; j < 4; ++j) acc[rt][ct][j] = src ? src[(size_t)(i0 + j) * D + col] : 0.f;
       }
   }
-  for (int gg = ng - 1; gg >= 1; --gg) {
+  for (int it = 0; it + 1 < ng; ++it) {
+    const int gg = FWD ? it : ng - 1 - it;  // the group whose map is applied
     const size_t gh = (size_t)(gb + gg) * H + h;
-    // the state at the end of group gb + gg - 1 is P_g B + Q_g
+    // backward: the state gradient at the end of group gg - 1 is P_g B + Q_g;
+    // forward: the state at the start of group gg + 1 is P_g S + Q_g
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(4 * D) void k_scan_bnd(const GroupInfo* __restrict_
       }
     }
     __syncthreads();
-    const size_t bh = (size_t)(gb + gg - 1) * H + h;
+    const size_t bh = (size_t)(gb + (FWD ? gg + 1 : gg - 1)) * H + h;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -296,14 +301,20 @@ __global__ __launch_bounds__(4 * D) void k_scan_bnd(const GroupInfo* __restrict_
 // column group w / 4); X and O are 64 x V, wave w holding row tile w % 4 and the
 // column tiles of column group w / 4.  S and X go through LDS as natural tiles of T,
 // read back as B operands; O is staged in LDS and stored as 16-byte rows a step later.
-// The operands of the next chunk are loaded at the start of each step.
-template <typename T, int D>
+// One workgroup per chunk group of a (sequence, head) (a whole sequence unless long
+// sequences are split): PQ = false scans the group from its true start state (h0 for
+// the first group, else bnd) and stores O, h_saved and, for the last group, ht;
+// PQ = true scans it without outputs, blockIdx.z = 0 from I without the Uv term (the
+// group's transition P_g, act dtype) and blockIdx.z = 1 from 0 (its offset Q_g, fp32),
+// so that the state after the group is P_g S + Q_g for the state S before it.
+template <typename T, int D, bool PQ>
 __global__ __launch_bounds__(4 * D) void k_fscan(
-    const ChunkInfo* __restrict__ chunks, const int* __restrict__ seq_off, int H,
+    const ChunkInfo* __restrict__ chunks, const GroupInfo* __restrict__ groups, int H,
     const T* __restrict__ Wn, const T* __restrict__ KrT, const T* __restrict__ UvT,
     const T* __restrict__ Qd, const T* __restrict__ Mq, const float* __restrict__ eGT,
-    const float* __restrict__ h0, T* __restrict__ o, float* __restrict__ ht,
-    T* __restrict__ h_saved) {
+    const float* __restrict__ h0, const float* __restrict__ bnd, T* __restrict__ o,
+    float* __restrict__ ht, T* __restrict__ h_saved, T* __restrict__ Pg,
+    float* __restrict__ Qg) {
   using L = SL<T, D>;
   using MM = Mma<T>;
   typedef typename MM::Frag Frag;
@@ -320,26 +331,42 @@ __global__ __launch_bounds__(4 * D) void k_fscan(
   T* sX = (T*)(smem + L::S_SZ);
   T* sO = (T*)(smem + L::S_SZ + L::O_SZ);
 
-  const int n = blockIdx.x, h = blockIdx.y;
+  const int gidx = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g4 = lane >> 4, cl = lane & 15;
   const int rgp = w & 3, cgp = w >> 2;
   const int xr = w & 3;  // row tile of X and O
   const size_t DD = (size_t)D * D;
-  const size_t uh = (size_t)n * H + h;
-  const int cb = seq_off[n], nck = seq_off[n + 1] - cb;
+  const GroupInfo gi = groups[gidx];
+  const size_t uh = (size_t)gi.seq * H + h;  // (sequence, head)
+  const size_t gh = (size_t)gidx * H + h;    // (group, head)
+  const int cb = gi.c0, nck = gi.cnt;
   const size_t rs = (size_t)H * D;
+  const bool trans = PQ && blockIdx.z == 0;  // transition: identity start, no Uv term
+  if constexpr (PQ) {  // no outputs in this pass
+    o = nullptr;
+    h_saved = nullptr;
+  }
 
   f4 acc[RTW][CTW];
+  {
+    const float* src = nullptr;
+    if constexpr (!PQ) src = (gi.flags & GRP_FIRST) ? (h0 ? h0 + uh * DD : nullptr) : bnd + gh * DD;
 #pragma unroll
-  for (int rt = 0; rt < RTW; ++rt)
+    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < CTW; ++ct) {
-      const int i0 = (rgp * RTW + rt) * 16 + 4 * g4;
-      const int col = (cgp * CTW + ct) * 16 + cl;
+      for (int ct = 0; ct < CTW; ++ct) {
+        const int i0 = (rgp * RTW + rt) * 16 + 4 * g4;
+        const int col = (cgp * CTW + ct) * 16 + cl;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[rt][ct][j] = h0 ? h0[uh * DD + (size_t)(i0 + j) * D + col] : 0.f;
-    }
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (PQ)
+            acc[rt][ct][j] = (trans && i0 + j == col) ? 1.f : 0.f;
+          else
+            acc[rt][ct][j] = src ? src[(size_t)(i0 + j) * D + col] : 0.f;
+        }
+      }
+  }
 
   // One set of operand fragments, each part refilled for the next chunk right after its
   // last use in the current step (so that it has most of a step to land).
@@ -361,7 +388,7 @@ __global__ __launch_bounds__(4 * D) void k_fscan(
       if constexpr (L::ES == 2) *(uint2*)u4 = *(const uint2*)src;
       else *(uint4*)u4 = *(const uint4*)src;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fuv[ct][j] = to_f(u4[j]);
+      for (int j = 0; j < 4; ++j) fuv[ct][j] = trans ? 0.f : to_f(u4[j]);
     }
   };
   auto load_m = [&](int cg) {
@@ -468,26 +495,44 @@ __global__ __launch_bounds__(4 * D) void k_fscan(
     __syncthreads();  // the last chunk's O staging complete
     store_o(cb + nck - 1);
   }
-  if (ht) {
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt)
+  for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < CTW; ++ct)
-        store_c<float>(ht + uh * DD, D, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, acc[rt][ct],
-                       lane);
-  }
+    for (int ct = 0; ct < CTW; ++ct) {
+      const int r0 = (rgp * RTW + rt) * 16, c0 = (cgp * CTW + ct) * 16;
+      if constexpr (PQ) {
+        if (trans) store_c<T>(Pg + gh * DD, D, r0, c0, acc[rt][ct], lane);
+        else store_c<float>(Qg + gh * DD, D, r0, c0, acc[rt][ct], lane);
+      } else {
+        if ((gi.flags & GRP_LAST) && ht) store_c<float>(ht + uh * DD, D, r0, c0, acc[rt][ct], lane);
+      }
+    }
 }
 
 template <typename T, int D>
 static hipError_t fscan_t(const Shape& s, const FwdPtrs& p, hipStream_t st) {
-  hipLaunchKernelGGL((k_fscan<T, D>), dim3((unsigned)s.N, (unsigned)s.H), dim3(SL<T, D>::NT), 0, st,
-                     p.chunks, p.seq_off, s.H, (const T*)p.Wn, (const T*)p.KrT, (const T*)p.UvT,
-                     (const T*)p.Qd, (const T*)p.Mq, p.eGT, p.h0, (T*)p.o, p.ht, (T*)p.h_saved);
+  if (s.gs > 0) {  // chunk groups side by side: P_g and Q_g, the boundaries, then the outputs
+    hipLaunchKernelGGL((k_fscan<T, D, true>), dim3((unsigned)s.NG, (unsigned)s.H, 2),
+                       dim3(SL<T, D>::NT), 0, st, p.chunks, p.groups, s.H, (const T*)p.Wn,
+                       (const T*)p.KrT, (const T*)p.UvT, (const T*)p.Qd, (const T*)p.Mq, p.eGT,
+                       nullptr, nullptr, nullptr, nullptr, nullptr, (T*)p.Pg, p.Qg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_scan_bnd<T, D, true>), dim3((unsigned)s.N, (unsigned)s.H),
+                       dim3(SL<T, D>::NT), 0, st, p.groups, p.grp_off, s.H, (const T*)p.Pg, p.Qg,
+                       p.h0, p.bnd);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_fscan<T, D, false>), dim3((unsigned)s.NG, (unsigned)s.H),
+                     dim3(SL<T, D>::NT), 0, st, p.chunks, p.groups, s.H, (const T*)p.Wn,
+                     (const T*)p.KrT, (const T*)p.UvT, (const T*)p.Qd, (const T*)p.Mq, p.eGT, p.h0,
+                     p.bnd, (T*)p.o, p.ht, (T*)p.h_saved, nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_fscan(const Shape& s, const FwdPtrs& p, hipStream_t st) {
-  if (s.N * s.H == 0) return hipSuccess;
+  if (s.NG == 0) return hipSuccess;
   if (s.bf16) return s.D == 128 ? fscan_t<bf16, 128>(s, p, st) : fscan_t<bf16, 64>(s, p, st);
   return fscan_t<float, 64>(s, p, st);
 }
@@ -502,7 +547,7 @@ static hipError_t scan_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
                        nullptr, nullptr, nullptr, nullptr, (T*)p.Pg, p.Qg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_scan_bnd<T, D>), dim3((unsigned)s.N, (unsigned)s.H),
+    hipLaunchKernelGGL((k_scan_bnd<T, D, false>), dim3((unsigned)s.N, (unsigned)s.H),
                        dim3(SL<T, D>::NT), 0, st, p.groups, p.grp_off, s.H,
                        (const T*)p.Pg, p.Qg, p.dht, p.bnd);
     e = hipGetLastError();

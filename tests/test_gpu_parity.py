@@ -133,6 +133,31 @@ def test_split_scan(name, group, monkeypatch):
     _check(name)
 
 
+@pytest.mark.parametrize("name,group", [("weak_decay_bf16", 3), ("weak_decay_fp32", 2),
+                                        ("ragged_bf16", 1), ("ragged_fp32", 3),
+                                        ("single_seq_bf16", 5), ("gate_log2_fp32", 2)])
+def test_forward_split_scan(name, group, monkeypatch):
+    """The production forward's state scan split into groups of a few chunks (group
+    maps from I and from 0, boundaries chained from h0, re-scan with outputs)."""
+    monkeypatch.setenv("KDA_SCAN_GROUP", str(group))
+    print("\n[case] forward split scan %s, %d chunks per group" % (name, group), flush=True)
+    inp = KI.make_inputs(KI.get_workload(name))
+    res = KC.run_gpu_fwd(inp)
+    ref = KC.oracle_fwd_for(inp)
+    ref["h_saved"] = ref["states"]
+    rep = KC.compare(res, ref, ["o", "ht", "h_saved"], KC.TOL[inp["dtype"]],
+                     label="forward split " + name)
+    print("[errors] " + " ".join("%s=%.2e" % kv for kv in rep.items()), flush=True)
+
+
+def test_recompute_with_split_scans(monkeypatch):
+    """Backward without h_saved and with split scans: the forward's split scan recomputes
+    the chunk-start states, the backward's split scan carries dS."""
+    monkeypatch.setenv("KDA_SCAN_GROUP", "2")
+    print("\n[case] recompute + split scans weak_decay_fp32", flush=True)
+    _check("weak_decay_fp32", use_h_saved=False)
+
+
 def test_split_scan_zero_length(monkeypatch):
     monkeypatch.setenv("KDA_SCAN_GROUP", "1")
     wl = KI.Workload("zero_len", 1, 0 + 70 + 0 + 5 + 64, 2, 128, 128, "bf16", 1200, varlen_seqs=4,
@@ -143,6 +168,8 @@ def test_split_scan_zero_length(monkeypatch):
     ref = KC.oracle_for(inp)
     ref["h_saved"] = ref["states"]
     KC.compare(res, ref, GRADS + INTER, KC.TOL["bf16"], label="zero_len split")
+    fres = KC.run_gpu_fwd(inp)  # the production forward's split scan, empty sequences too
+    KC.compare(fres, ref, ["o", "ht", "h_saved"], KC.TOL["bf16"], label="zero_len forward split")
 
 
 @pytest.mark.parametrize("name,cap", [("ragged_fp32", 3), ("ragged_bf16", 3),
