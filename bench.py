@@ -261,7 +261,7 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "repeats": 3}))
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU; this build has no multi-GPU path (--gpus %d)" % a.gpus,
+        print("bench.py measures one GPU; the library has no multi-GPU path (--gpus %d)" % a.gpus,
               file=sys.stderr)
         sys.exit(2)
 

@@ -31,7 +31,7 @@
  * dq, dk, dv, h_saved and dstates.  g_raw, beta, A_log, h0, dht, ht, dg_raw, dbeta,
  * dA_log and dh0 are always fp32.  All accumulation is fp32.
  *
- * Supported shapes in this build: chunk = 64; K == V; K in {64, 128} for bf16,
+ * Supported shapes: chunk = 64; K == V; K in {64, 128} for bf16,
  * K == 64 for fp32.  Anything else returns KDA_ERR_UNSUPPORTED.
  *
  * Ownership and synchronisation.  The caller owns every buffer (device memory)
@@ -64,7 +64,7 @@ extern "C" {
 #define KDA_OK 0
 #define KDA_ERR_INVALID_ARGUMENT (-1) /* NULL required pointer, bad size, misaligned
                                          pointer, non-monotone cu_seqlens, sum != T */
-#define KDA_ERR_UNSUPPORTED (-2)      /* shape or dtype outside this build */
+#define KDA_ERR_UNSUPPORTED (-2)      /* shape or dtype not supported */
 #define KDA_ERR_WORKSPACE_TOO_SMALL (-3)
 #define KDA_ERR_HIP (-4)              /* a HIP launch failed; kda_status_string(-4)
                                          then names the HIP error of this thread */
