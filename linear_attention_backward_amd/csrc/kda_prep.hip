@@ -36,7 +36,7 @@ template <typename T, int D> struct PL {
   static constexpr int K_OFF = Q_OFF + N_SZ;    // k, later W
   static constexpr int M_OFF = K_OFF + N_SZ;    // Mqk
   static constexpr int KR_OFF = M_OFF + C_SZ;   // Kr
-  static constexpr int A_OFF = KR_OFF + N_SZ;   // A
+  static constexpr int A_OFF = KR_OFF + N_SZ;   // L = diag(beta) A
   static constexpr int INV_OFF = A_OFF + C_SZ;  // INV
   static constexpr int KD_OFF = INV_OFF + C_SZ; // beta Kd
   static constexpr int SCR_OFF = KD_OFF + N_SZ; // INV block-substitution scratch
@@ -219,7 +219,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       *(uint4*)(sKd + r * PN + i0) = *(const uint4*)kd;
     }
   };
-  // ---- A and Mqk, by 16-row blocks.
+  // ---- A and Mqk, by 16-row blocks.  A goes to its tile with the rows scaled by
+  //   beta (L = diag(beta) A), the only form INV reads.
   //   offdiag(R, S0, S1): blocks (R, S), S0 <= S < S1 < R, anchored at the first row
   //   of block R; diag(R): block (R, R) and the zero blocks right of it.
   auto offdiag = [&](const int R, const int S0, const int S1) {
@@ -256,10 +257,11 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
         }
       }
     }
+    const f4 bt = *(const f4*)(sBeta + r0 + 4 * g4);  // beta of this lane's C rows
 #pragma unroll
     for (int S = 0; S < 3; ++S)
       if (S >= S0 && S < S1) {
-        store_c<float>(sA, PC, r0, 16 * S, accA[S], lane);
+        store_c<float>(sA, PC, r0, 16 * S, accA[S] * bt, lane);
         store_c<float>(sM, PC, r0, 16 * S, accM[S], lane);
       }
   };
@@ -362,10 +364,11 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
         }
       }
     }
+    const f4 bt = *(const f4*)(sBeta + r0 + 4 * g4);
 #pragma unroll
     for (int S = 0; S < 4; ++S) {
       if (S < R) continue;
-      const f4 a = S == R ? dA : zero4();
+      const f4 a = S == R ? dA * bt : zero4();
       const f4 m = S == R ? dM : zero4();
       store_c<float>(sA, PC, r0, 16 * S, a, lane);
       store_c<float>(sM, PC, r0, 16 * S, m, lane);
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
         const float xs = acc[s];
 #pragma unroll
         for (int r = s + 1; r < 16; ++r)
-          acc[r] -= sBeta[16 * R + r] * sA[(16 * R + r) * PC + 16 * R + s] * xs;
+          acc[r] -= sA[(16 * R + r) * PC + 16 * R + s] * xs;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sINV[(16 * R + r) * PC + 16 * R + lane] = acc[r];
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 #pragma unroll
         for (int kk = 0; kk < 16; kk += 4) {
           const int row = cl, kx = kk + g4;
-          const float a = sBeta[16 * R + row] * sA[(16 * R + row) * PC + 16 * J + kx];
+          const float a = sA[(16 * R + row) * PC + 16 * J + kx];
           const float b = sINV[(16 * J + kx) * PC + 16 * S + row];
           X = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, X, 0, 0, 0);
         }
