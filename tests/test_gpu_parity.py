@@ -111,6 +111,32 @@ def test_zero_length_sequences():
     KC.compare(res, ref, GRADS + INTER, KC.TOL["bf16"], label="zero_len")
 
 
+@pytest.mark.parametrize("name,mode", [("ragged_fp32", "mix"), ("ragged_bf16", "mix"),
+                                       ("ragged_fp32", "zero"), ("ragged_bf16", "zero")])
+def test_degenerate_beta(name, mode):
+    """beta exactly 0 (the token writes nothing: S_t = Diag(exp g_t) S_{t-1}, and k_t, v_t
+    have no gradient) and exactly 1 (the old value along k_t is fully replaced): on all
+    tokens ("zero") or on a random third each ("mix").  Backward and production forward."""
+    inp = KI.make_inputs(KI.get_workload(name))
+    b = inp["beta"]
+    if mode == "zero":
+        b = np.zeros_like(b)
+    else:
+        u = np.random.default_rng(4242).integers(0, 3, size=b.shape)
+        b = np.where(u == 0, 0.0, np.where(u == 1, 1.0, b)).astype(b.dtype)
+    inp = dict(inp, beta=b)
+    print("\n[case] degenerate beta %s %s" % (name, mode), flush=True)
+    res = KC.run_gpu(inp)
+    ref = KC.oracle_for(inp)
+    ref["h_saved"] = ref["states"]
+    tol = KC.TOL[inp["dtype"]]
+    if mode == "zero":
+        assert np.abs(ref["dk"]).max() == 0.0 and np.abs(ref["dv"]).max() == 0.0
+    KC.compare(res, ref, GRADS + INTER, tol, label="beta %s %s" % (name, mode))
+    fres = KC.run_gpu_fwd(inp)
+    KC.compare(fres, ref, ["o", "ht", "h_saved"], tol, label="beta %s %s forward" % (name, mode))
+
+
 def test_repeatable_bitwise():
     """Two runs give bit-identical outputs (no atomics, fixed reduction order)."""
     inp = KI.make_inputs(KI.get_workload("weak_decay_bf16"))
