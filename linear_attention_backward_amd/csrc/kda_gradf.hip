@@ -727,7 +727,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   // and d = G_r - G_{r-1} = -aA softplus(x) log2(e), softplus(x) = -d ln 2 / aA and
   // sigmoid(x) = 1 - e^{-softplus(x)} = 1 - 2^{d / aA}, so dg_raw = dg . aA (2^{d / aA} - 1)
   // and the dA_log term is dg . d ln 2 (dg here is the gradient of the natural-log decay).
-  const float inv_aA = 1.f / aA;
+  // With no decay (A_log -> -inf, or e^{A_log} below 1e-30) d is 0 and 1/aA would overflow:
+  // the factor is taken as 0 there, so dg_raw is 0 (its true size is below 1e-30 |dg|).
+  const float inv_aA = aA > 1e-30f ? 1.f / aA : 0.f;
   float carry = 0.f;
 #pragma unroll
   for (int rt = 3; rt >= 0; --rt) {

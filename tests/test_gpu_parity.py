@@ -137,6 +137,30 @@ def test_degenerate_beta(name, mode):
     KC.compare(fres, ref, ["o", "ht", "h_saved"], tol, label="beta %s %s forward" % (name, mode))
 
 
+@pytest.mark.parametrize("name", ["ragged_fp32", "multi_ragged_bf16"])
+def test_no_decay_heads(name):
+    """A_log = -inf on head 0 (g = 0 exactly: the plain delta rule) and, with three heads,
+    A_log = -95 on head 1 (e^{A_log} below the fp32 normal range): finite gradients equal to
+    the oracle's, dg_raw and dA_log zero on the no-decay head."""
+    inp = KI.make_inputs(KI.get_workload(name))
+    a = inp["A_log"].copy()
+    a[0] = -np.inf
+    if a.shape[0] > 2:
+        a[1] = -95.0
+    inp = dict(inp, A_log=a)
+    print("\n[case] no-decay heads %s" % name, flush=True)
+    res = KC.run_gpu(inp)
+    ref = KC.oracle_for(inp)
+    ref["h_saved"] = ref["states"]
+    for key in GRADS:
+        assert np.all(np.isfinite(res[key])), key
+    assert np.abs(ref["dg_raw"][:, 0]).max() == 0.0 and ref["dA_log"][0] == 0.0
+    KC.compare(res, ref, GRADS + INTER, KC.TOL[inp["dtype"]], label="no decay %s" % name)
+    fres = KC.run_gpu_fwd(inp)
+    KC.compare(fres, ref, ["o", "ht", "h_saved"], KC.TOL[inp["dtype"]],
+               label="no decay %s forward" % name)
+
+
 def test_repeatable_bitwise():
     """Two runs give bit-identical outputs (no atomics, fixed reduction order)."""
     inp = KI.make_inputs(KI.get_workload("weak_decay_bf16"))
