@@ -59,10 +59,13 @@ def path_bytes_per_token_head(D=128, es=2):
 
 
 def kernel_sources_digest():
+    """Digest of the device code (the .hip sources and the headers they include); the
+    host-side API file does not change what a kernel reads or writes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_backward_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 

@@ -32,7 +32,8 @@
  * dA_log and dh0 are always fp32.  All accumulation is fp32.
  *
  * Supported shapes: chunk = 64; K == V; K in {64, 128} for bf16,
- * K == 64 for fp32.  Anything else returns KDA_ERR_UNSUPPORTED.
+ * K == 64 for fp32; B*T*H < 2^31 (token-head rows and chunk-head items are indexed in
+ * 32 bits).  Anything else returns KDA_ERR_UNSUPPORTED.
  *
  * Ownership and synchronisation.  The caller owns every buffer (device memory)
  * and the stream.  The library allocates no device memory and keeps no pointer

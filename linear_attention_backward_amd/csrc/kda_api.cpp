@@ -97,6 +97,11 @@ int validate_problem(const kda_problem* p) {
     if (p->cu_seqlens_host[p->num_seqs] != p->T) return KDA_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)p->cu_seqlens_dev & 3) != 0) return KDA_ERR_INVALID_ARGUMENT;
   }
+  // the kernels index (chunk, head) work items and (token, head) rows in 32 bits
+  int64_t nc = 0;
+  count_chunks(p, &nc);
+  if (nc * p->H >= ((int64_t)1 << 31) || (int64_t)p->B * p->T * p->H >= ((int64_t)1 << 31))
+    return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 

@@ -46,6 +46,10 @@ def test_shape_validation():
     assert _ws(K._Prob(2, 100, 4, 64, 64, 7))[0] == K.KDA_ERR_UNSUPPORTED
     assert _ws(K._Prob(0, 100, 4, 64, 64, 0))[0] == K.KDA_ERR_INVALID_ARGUMENT
     assert _ws(K._Prob(1, 100, 0, 64, 64, 0))[0] == K.KDA_ERR_INVALID_ARGUMENT
+    # token-head rows past 32-bit indexing
+    assert _ws(K._Prob(1, 1 << 24, 127, 64, 64, 0))[0] == 0
+    assert _ws(K._Prob(1, 1 << 24, 128, 64, 64, 0))[0] == K.KDA_ERR_UNSUPPORTED
+    assert _ws(K._Prob(4, 1 << 22, 128, 64, 64, 0))[0] == K.KDA_ERR_UNSUPPORTED
     p = K._Prob(1, 100, 4, 64, 64, 0)
     p.p.chunk = 32
     assert _ws(p)[0] == K.KDA_ERR_UNSUPPORTED
