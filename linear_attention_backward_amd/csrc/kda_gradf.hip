@@ -168,7 +168,11 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 
   // ------------------------------------------------------------------ loads
   // Persistent: one workgroup fills a CU's LDS, so each workgroup walks the
-  // (chunk, head) items with stride gridDim.x and copies the next item's tiles
+  // (chunk, head) items with stride gridDim.x, head fastest (item = chunk * H + head:
+  // the workgroups in flight together read whole token rows of q, k, v, dO and g_raw,
+  // all heads of the same chunks, and write whole rows of the gradients; about 2%
+  // faster here than chunk-fastest order, which prep keeps: there it is the faster
+  // one), and copies the next item's tiles
   // straight into LDS as soon as their regions are dead: S_in and v when the key
   // side is done (they then land during the intra phase), k, g_raw and beta once
   // the intra phase is done, dO once the dq staging over its tile is read out.
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   // (part: 0 = all of S_in, v and INV; 1..3 = the pieces that the intra phase spreads over its
   // row tiles, so that the copies do not queue up ahead of the epilogue's loads and stores)
   auto issue_early = [&](int it, int t, int part) {
-    const int c = it % NC, h = it / NC;
+    const int c = it / H, h = it % H;
     const ChunkInfo ci = chunks[c];
     const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const T* sin = h_saved + ((size_t)c * H + h) * DD;
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     }
   };
   auto issue_front = [&](int it, int t) {
-    const int c = it % NC, h = it / NC;
+    const int c = it / H, h = it % H;
     const ChunkInfo ci = chunks[c];
     const size_t base = (size_t)ci.t0 * rs + (size_t)h * D;
     const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     if constexpr (GV) rdb = *(const f4*)(dt_bias + (size_t)h * D + 16 * w + 4 * (lane & 3));
   };
   auto issue_late = [&](int it, int t) {
-    const int c = it % NC, h = it / NC;
+    const int c = it / H, h = it % H;
     const ChunkInfo ci = chunks[c];
     g2l_tile<T, D, 64, NW>(lds0 + L::O_OFF, sO, dO + (size_t)ci.t0 * rs + (size_t)h * D, rs, ci.len,
                            __builtin_amdgcn_readfirstlane(t >> 6), t & 63);
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, cl = lane & 15;
-  const int c = it % NC, h = it / NC;
+  const int c = it / H, h = it % H;
   const int nxt = it + (int)gridDim.x;
   const ChunkInfo ci = chunks[c];
   const size_t t0 = ci.t0;

@@ -99,7 +99,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   const int tid0 = threadIdx.x;
 
   // Persistent: one workgroup fills a CU's LDS, so each workgroup walks the
-  // (chunk, head) items with stride gridDim.x and holds the next item's g_raw,
+  // (chunk, head) items with stride gridDim.x (chunk fastest: item = head * NC + chunk;
+  // head-fastest order measured slower here) and holds the next item's g_raw,
   // beta, q and k in registers while it works on the current one. Rows beyond
   // the chunk are zero (q, k) or masked at the cumsum (g_raw).
   float rg[16], rbeta, rdb;
