@@ -31,31 +31,37 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# Algorithmic bytes per token-head of each kernel's own compulsory traffic
-# (each operand read once, each result written once), bf16 activations,
-# K = V = 128, chunk 64.  Per chunk-head quantities are divided by 64.
+# Algorithmic bytes per token-head (bf16 activations, K = V = 128, chunk 64 unless given)
+# as the measurement plan counts them for the whole path: every input read once, every
+# output written once, the chunk-start state read once and the state gradient handed
+# from the scan to the gradient pass once (written, then read).  Per chunk-head
+# quantities are divided by 64.  Each byte is assigned to the kernel that moves it
+# compulsorily: the gradient pass reads every per-token input and the two states and
+# writes every per-token output; the scan writes the state-gradient hand-off; prep's
+# traffic (re-reads of q, k, g_raw, beta and its own intermediates) is all overhead.
 def kernel_bytes_per_token_head(D=128, es=2):
     act = D * es          # one activation row
     f32row = D * 4        # one fp32 row (g_raw, dg_raw)
     state = D * D * es / 64.0   # one K x V state per chunk
-    sq = 64 * 64 * es / 64.0    # one 64 x 64 matrix per chunk
     return {
-        # q, k, g_raw, beta -> Tm (KxK), PT (Kx64), eGT, INV, Mqk^T
-        "prep": 2 * act + f32row + 4 + state + D * 64 * es / 64.0 + D * 4 / 64.0 + 2 * sq,
-        # Tm, PT, eGT, dO -> dS_out
-        "scan": state + D * 64 * es / 64.0 + D * 4 / 64.0 + act + state,
-        # q, k, v, dO, g_raw, beta, S_in, dS_out, INV, Mqk^T
-        #   -> dq, dk, dv, dg_raw, dbeta, dA_log partial
-        "grad": 4 * act + f32row + 4 + 2 * state + 2 * sq + 3 * act + f32row + 4 + 4 / 64.0,
+        "prep": 0.0,
+        "scan": state,                                   # dS_out written
+        # q, k, v, dO, g_raw, beta in; S_in and dS_out in; dq, dk, dv, dg_raw, dbeta out
+        "grad": 4 * act + f32row + 4 + 2 * state + 3 * act + f32row + 4,
     }
 
 
-# The whole path's algorithmic bytes per token-head: inputs q, k, v, dO, g_raw,
-# beta read once, outputs dq, dk, dv, dg_raw, dbeta written once, the chunk start
-# state read once and the state gradient handed from the scan to the gradient
-# pass once (written + read).
 def path_bytes_per_token_head(D=128, es=2):
-    return 4 * D * es + D * 4 + 4 + 3 * D * es + D * 4 + 4 + D * D * es / 64.0 * 3
+    return sum(kernel_bytes_per_token_head(D, es).values())
+
+
+# Algorithmic MFMA work per chunk-head (C = 64, D = K = V): seven state contractions
+# (C x D x D each), eleven causal C x C x D products at half density, the 64 x 64
+# inverse (2 C^3 / 3); in FLOP.
+def path_flops_per_chunk_head(D=128, C=64):
+    w = C * D * D * 2
+    u = C * C * D * 2
+    return 7 * w + 5.5 * u + 2 * C ** 3 / 3
 
 
 def kernel_sources_digest():
@@ -69,23 +75,46 @@ def kernel_sources_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_stage):
-    """HBM traffic measured by rocprofv3 counters (profiles/traffic.json), only
-    if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _profile_json(name):
+    """A committed counter summary under profiles/, only if it was taken on the current
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", name)
     try:
         d = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if d.get("sources") != kernel_sources_digest():
-        return None
-    ent = d.get("kernels", {}).get(kernel_stage)
+    return d if d.get("sources") == kernel_sources_digest() else None
+
+
+def load_traffic(kernel_stage):
+    """HBM traffic measured by rocprofv3 counters (profiles/traffic.json), only
+    if it was taken on the current kernel sources."""
+    d = _profile_json("traffic.json")
+    ent = None if d is None else d.get("kernels", {}).get(kernel_stage)
     return None if ent is None else ent.get("bytes_per_launch")
+
+
+def load_counters(kernel_stage):
+    """SQ counter ratios of one kernel (profiles/counters.json), only if they were taken
+    on the current kernel sources."""
+    d = _profile_json("counters.json")
+    return None if d is None else d.get("kernels", {}).get(kernel_stage)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(inp, target_s=12.0):
     """Time the fp64 oracle on whole heads of the workload (every sequence of
-    each head), sized to roughly target_s seconds; scale to tokens/s."""
+    each head), sized to roughly target_s seconds; scale to tokens/s.  Returns the
+    record, the oracle's outputs and the heads it ran on (for the parity check)."""
     import numpy as np
     import kda_inputs as KI
     from oracle import oracle as O
@@ -105,15 +134,44 @@ def cpu_baseline(inp, target_s=12.0):
     est_per_head = per_token_head * TT / max(1, min(threads, units_per_head))
     nh = int(max(1, min(H, round(target_s / max(est_per_head, 1e-9)))))
     # keep all threads busy: whole heads, every sequence
-    sub = KI.select_heads(inp, list(range(nh)))
+    heads = list(range(nh))
+    sub = KI.select_heads(inp, heads)
     t = time.perf_counter()
-    O.kda_backward(sub)
+    ref = O.kda_backward(sub)
     dt = time.perf_counter() - t
     token_heads = TT * nh
     tok_s = token_heads / H / dt
-    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d heads x all %d tokens (%d token-heads), fp64, %.1f s"
-                      % (nh, H, TT, token_heads, dt)}
+    rec = {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": "%d of %d heads x all %d tokens (%d token-heads), fp64, %.1f s"
+                     % (nh, H, TT, token_heads, dt)}
+    return rec, ref, heads
+
+
+def parity_report(outs, ref, heads, inp, tol):
+    """max|gpu - oracle| / max|oracle| per output on the oracle's heads."""
+    import numpy as np
+    TT = inp["q"].shape[0]
+    rep = {}
+    for key in ("dq", "dk", "dv", "dg_raw", "dbeta", "dA_log", "dh0"):
+        val = outs.get(key)
+        if val is None or key not in ref:
+            continue
+        a = val.float().cpu().numpy().astype(np.float64)
+        if key in ("dq", "dk", "dv", "dg_raw"):
+            a = a.reshape(TT, a.shape[-2], a.shape[-1])[:, heads]
+        elif key == "dbeta":
+            a = a.reshape(TT, -1)[:, heads]
+        elif key == "dA_log":
+            a = a[heads]
+        else:
+            a = a[:, heads]
+        den = float(np.abs(ref[key]).max())
+        num = float(np.abs(a - ref[key]).max())
+        rep[key] = num / den if den > 0 else num
+    return {"metric": "max|gpu-oracle|/max|oracle| per output", "tol": tol,
+            "heads": "%d of %d" % (len(heads), inp["H"]), "max_rel_err": rep,
+            "pass": all(v <= tol for v in rep.values())}
 
 
 KERNEL_STAGE = (("k_prep", "prep"), ("k_scanw", "scan"), ("k_gradf", "grad"))
@@ -169,6 +227,58 @@ def summarize_profiles(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, c
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     return out
+
+
+N_XCD = 8       # GRBM_GUI_ACTIVE is reported once per XCD and summed in the CSV
+CU_NUM = 256
+SIMD_NUM = 1024
+
+
+def summarize_counters(csvs):
+    """Write profiles/counters.json from rocprofv3 --pmc CSVs of this benchmark (any split
+    of the counters below over passes): per backward kernel, the profiler's own ratios
+    VALU busy = SQ_ACTIVE_INST_VALU / (CUs x kernel cycles), MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x kernel cycles), MFMA FLOP = MOPS_BF16 x 512,
+    resident waves per SIMD = SQ_WAVE_CYCLES / (CUs x kernel cycles) and LDS bank-conflict
+    cycles / LDS-active cycles; kernel cycles = GRBM_GUI_ACTIVE / XCDs."""
+    vals = {}
+    for path in csvs:
+        for stage, cnt in _pmc_all(path).items():
+            vals.setdefault(stage, {}).update(cnt)
+    out = {"sources": kernel_sources_digest(),
+           "workload": "train_bf16 (B=8,T=4096,H=32,K=V=128,bf16)", "kernels": {}}
+    for stage, c in vals.items():
+        if "GRBM_GUI_ACTIVE" not in c:
+            continue
+        cyc = c["GRBM_GUI_ACTIVE"] / N_XCD
+        ent = {"kernel_cycles": cyc, "raw": c}
+        if "SQ_ACTIVE_INST_VALU" in c:
+            ent["valu_busy"] = c["SQ_ACTIVE_INST_VALU"] / (CU_NUM * cyc)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            ent["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMD_NUM * cyc)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            ent["mfma_flop_per_launch"] = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+        if "SQ_WAVE_CYCLES" in c:
+            ent["waves_per_simd"] = c["SQ_WAVE_CYCLES"] / (CU_NUM * cyc)
+        if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
+            ent["lds_bank_conflict_frac"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
+        out["kernels"][stage] = ent
+    with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
+def _pmc_all(csv_path):
+    """Average value of every counter per dispatch of every backward kernel stage."""
+    import csv
+    per = {}
+    for row in csv.DictReader(open(csv_path)):
+        stage = _stage_of(row["Kernel_Name"])
+        if stage is None:
+            continue
+        per.setdefault(stage, {}).setdefault(row["Counter_Name"], []).append(
+            float(row["Counter_Value"]))
+    return {st: {k: sum(v) / len(v) for k, v in d.items()} for st, d in per.items()}
 
 
 def bench_forward(a, K, torch, inp, g, cu, vk, wl, variants):
@@ -247,7 +357,13 @@ def main():
                                                              "CALIB_FETCH_CSV", "CALIB_WRITE_CSV"),
                     help="write profiles/traffic.json from rocprofv3 counter CSVs of this "
                          "benchmark and of --copy-calib 1024 (no GPU needed)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_CSV",
+                    help="write profiles/counters.json from rocprofv3 --pmc CSVs of this "
+                         "benchmark (SQ busy, MFMA, occupancy and LDS counters; no GPU needed)")
     a = ap.parse_args()
+    if a.summarize_counters:
+        print(json.dumps(summarize_counters(a.summarize_counters), indent=1))
+        return
     if a.summarize_traffic:
         print(json.dumps(summarize_profiles(*a.summarize_traffic, copy_mib=1024), indent=1))
         return
@@ -299,6 +415,9 @@ def main():
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    # per-kernel durations: HIP events around each launch, on the launch stream, inside
+    # the timed region (the library records them; read after the region)
+    K.timing_enable(True)
     t_wall = time.perf_counter()
     e0.record(stream)
     for _ in range(a.steps):
@@ -306,21 +425,32 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    st = K.timing_read()
+    K.timing_enable(False)
     ms = e0.elapsed_time(e1) / a.steps
     tokens = int(inp["q"].shape[0])
     value = tokens / (ms / 1e3)
     log("kda_bwd: %.3f ms/step (wall %.3f ms/step)" % (ms, t_wall * 1e3 / a.steps))
-
-    # per-kernel durations (HIP events around each launch, on the launch stream)
-    K.timing_enable(True)
-    nt = max(3, min(a.steps, 10))
-    for _ in range(nt):
-        plan.run(stream)
-    torch.cuda.synchronize()
-    st = K.timing_read()
-    K.timing_enable(False)
     per = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in st.items()}
     log("per-kernel ms: " + " ".join("%s=%.3f" % kv for kv in per.items() if kv[1] > 0))
+
+    # the same step with the last-level cache (256 MB MALL) flushed before each one by a
+    # 1 GiB write; each step timed on its own
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    nf = max(3, min(a.steps, 10))
+    fl = []
+    for _ in range(nf):
+        flush.zero_()
+        e0.record(stream)
+        plan.run(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fl.append(e0.elapsed_time(e1))
+    del flush
+    fl.sort()
+    ms_flushed = fl[len(fl) // 2]
+    log("kda_bwd with the MALL flushed before each step: %.3f ms (median of %d)" % (ms_flushed, nf))
+
     dom = max(("prep", "scan", "grad"), key=lambda s: per[s])
     H, D = inp["H"], inp["K"]
     es = 2 if inp["dtype"] == "bf16" else 4
@@ -329,6 +459,43 @@ def main():
     achieved = kb / (per[dom] / 1e3) / 1e9
     traffic = load_traffic(dom)
     path_bytes = path_bytes_per_token_head(D, es) * token_heads
+    # Which roofline binds: the path's MFMA work per algorithmic byte against the ridge
+    # point (bf16 peak / HBM peak).  The MFMA work is the counted one when counters for
+    # these sources are committed, else the algorithmic count.
+    ctr = {st_: load_counters(st_) for st_ in ("prep", "scan", "grad")}
+    chunk_heads = int(plan.nc) * H
+    if all(c is not None for c in ctr.values()):
+        flops = sum(c["mfma_flop_per_launch"] for c in ctr.values())
+        flops_src = "rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_BF16 (profiles/counters.json)"
+    else:
+        flops = path_flops_per_chunk_head(D) * chunk_heads
+        flops_src = "algorithmic count"
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    intensity = flops / path_bytes
+    bound = "mfma" if intensity > ridge else "hbm"
+    roof = {"bound": bound, "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "algorithmic_bytes_per_launch": kb,
+            "duration_ms": per[dom],
+            "duration_source": "mean of HIP-event durations of the %d launches in the timed "
+                               "region, on the launch stream" % a.steps,
+            "bound_from": {"flop_per_byte": intensity, "ridge_flop_per_byte": ridge,
+                           "flop_source": flops_src}}
+    c = ctr.get(dom)
+    if c is not None:
+        # what holds the kernel below its roofline, from its SQ counters
+        mfma_tflops = c["mfma_flop_per_launch"] / (per[dom] / 1e3) / 1e12
+        roof["counters"] = {"valu_busy": c["valu_busy"], "mfma_busy": c["mfma_busy"],
+                            "mfma_tflops": mfma_tflops,
+                            "mfma_frac_of_bf16_peak": mfma_tflops / BF16_PEAK_TFLOPS,
+                            "lds_bank_conflict_frac": c.get("lds_bank_conflict_frac"),
+                            "occupancy_waves_per_simd": c.get("waves_per_simd"),
+                            "hbm_frac_measured": (traffic / (per[dom] / 1e3) / 1e9 / HBM_PEAK_GBS
+                                                  if traffic else None)}
+        busy = {"valu-issue": c["valu_busy"], "mfma": c["mfma_busy"]}
+        if traffic:
+            busy["hbm"] = traffic / (per[dom] / 1e3) / 1e9 / HBM_PEAK_GBS
+        roof["limiter"] = max(busy, key=busy.get)
     out = {
         "metric": "KDA backward tokens/s (H=32,K=V=128,bf16)",
         "value": value,
@@ -345,15 +512,20 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": H, "K": D, "V": inp["V"],
                    "chunk": 64, "h_saved": "given", "parallelism": "single-gpu"},
         **({"variants": [k for k, v in variants.items() if v]} if any(variants.values()) else {}),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
-        "path_roofline": {"bound": "hbm", "algorithmic_bytes": path_bytes,
+        "roofline": roof,
+        "path_roofline": {"bound": bound, "algorithmic_bytes": path_bytes,
                           "achieved": path_bytes / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": path_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "kernel_ms": per,
+        "mall_flushed_ms_per_step": ms_flushed,
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp)
+        rec, ref, heads = cpu_baseline(inp)
+        out["cpu_baseline"] = rec
+        out["parity"] = parity_report(plan.outputs(), ref, heads, inp,
+                                      KC.TOL[inp["dtype"]])
+        log("parity vs oracle (%s): %s" % (out["parity"]["heads"], " ".join(
+            "%s=%.2e" % kv for kv in out["parity"]["max_rel_err"].items())))
     print(json.dumps(out), flush=True)
 
 

@@ -41,7 +41,9 @@
  * kda_workspace_size.  Calls are asynchronous on `stream` (a hipStream_t; NULL =
  * the default stream) and enqueue work only after every argument has been
  * validated: a non-OK return means nothing was launched.  Concurrent calls need
- * distinct workspaces.  Outputs are overwritten, never accumulated.
+ * distinct workspaces.  Outputs are overwritten, never accumulated.  No output may
+ * overlap an input, another output or the workspace, and the workspace may not overlap
+ * an input (KDA_ERR_INVALID_ARGUMENT otherwise; inputs may overlap one another).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -155,8 +157,13 @@ KDA_API int kda_num_chunks(const kda_problem* p, int64_t* nchunks);
 KDA_API int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t ws_bytes,
             void* stream);
 
-/* Reference forward: o, ht and the per-chunk start states h_saved (one work-item
- * per (sequence, head, 64 value columns), token by token). */
+/* Reference forward: o, ht and the per-chunk start states h_saved, by the per-token
+ * recurrence of the method above taken token by token (one work-item per (sequence,
+ * head, 64 value columns)).  The backward consumes the state saved at the start of
+ * every chunk (bwd-kernelB-beginner-guide-full, part 2, B0 and B2: the chunk-start
+ * state S_in that the state-side products and the p = rowsum(S_in . dS) term read).
+ * o, ht and h_saved may each be NULL.  Workspace: kda_workspace_size(KDA_WS_FWD_REF);
+ * errors as for kda_bwd. */
 KDA_API int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t ws_bytes,
                 void* stream);
 

@@ -183,6 +183,64 @@ def _require_cuda(*ts):
             raise ValueError("all tensors must be on the GPU")
 
 
+def _n_chunks_host(B, T, cu_seqlens):
+    """Chunk count for shape checks (the library's kda_num_chunks gives the same)."""
+    if cu_seqlens is None:
+        return B * ((T + CHUNK - 1) // CHUNK)
+    cu = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    return sum((cu[i + 1] - cu[i] + CHUNK - 1) // CHUNK for i in range(len(cu) - 1))
+
+
+def _validate(q, v, cu_seqlens, named, act_named=(), h_saved=None):
+    """Check every tensor against the shapes, dtypes and layout the kernels assume,
+    before anything reaches the library: the kernels read dense row-major memory of
+    exactly these sizes, so a wrong dtype would make them read past a buffer and a
+    strided view would be read as if it were dense.
+
+    named: (name, tensor, shape, dtype) with None tensors skipped; act_named: (name,
+    tensor) that must match q's shape-with-last-dim and dtype.  Returns (B, T, H, K, V, N).
+    """
+    import torch
+    B, T, H, K, V = _shape(q, v, cu_seqlens)
+    N = (len(cu_seqlens) - 1) if cu_seqlens is not None else B
+    lead = tuple(q.shape[:-1])
+    checks = [("q", q, lead + (K,), q.dtype)]
+    for name, t in act_named:
+        d = V if name in ("v", "dO") else K
+        checks.append((name, t, lead + (d,), q.dtype))
+    for name, t, shp, dt in named:
+        checks.append((name, t, shp(lead, B, T, H, K, V, N), dt))
+    if h_saved is not None:
+        checks.append(("h_saved", h_saved, (_n_chunks_host(B, T, cu_seqlens), H, K, V), q.dtype))
+    _dtype_code(q)
+    for name, t, shp, dt in checks:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.dtype != dt:
+            raise ValueError("%s must be %s, got %s" % (name, dt, t.dtype))
+        if tuple(t.shape) != tuple(shp):
+            raise ValueError("%s must have shape %s, got %s" % (name, tuple(shp), tuple(t.shape)))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous (dense row-major)" % name)
+    devs = {t.device for _, t, _, _ in checks if t is not None}
+    if len(devs) > 1:
+        raise ValueError("all tensors must be on one device, got %s" % sorted(map(str, devs)))
+    _require_cuda(*[t for _, t, _, _ in checks])
+    return B, T, H, K, V, N
+
+
+def _gate_specs(g_raw, beta, A_log, h0, dt_bias):
+    import torch
+    f32 = torch.float32
+    return [("g_raw", g_raw, lambda L, B, T, H, K, V, N: L + (K,), f32),
+            ("beta", beta, lambda L, B, T, H, K, V, N: L, f32),
+            ("A_log", A_log, lambda L, B, T, H, K, V, N: (H,), f32),
+            ("h0", h0, lambda L, B, T, H, K, V, N: (N, H, K, V), f32),
+            ("dt_bias", dt_bias, lambda L, B, T, H, K, V, N: (H, K), f32)]
+
+
 def kda_fwd_ref(q, k, v, g_raw, beta, A_log, h0=None, cu_seqlens=None, want_o=True,
                 want_ht=True, want_states=True, stream=None, workspace=None, dt_bias=None,
                 gate_log2=False, qk_l2norm=False, _entry="kda_fwd_ref"):
@@ -190,7 +248,11 @@ def kda_fwd_ref(q, k, v, g_raw, beta, A_log, h0=None, cu_seqlens=None, want_o=Tr
     added inside the softplus; gate_log2 = True takes the gate in log2 units;
     qk_l2norm = True L2-normalises q and k per token first."""
     import torch
-    _require_cuda(q, k, v, g_raw, beta, A_log, h0, dt_bias)
+    for name, t in (("g_raw", g_raw), ("beta", beta), ("A_log", A_log)):
+        if t is None:
+            raise ValueError("%s is required" % name)
+    _validate(q, v, cu_seqlens, _gate_specs(g_raw, beta, A_log, h0, dt_bias),
+              (("k", k), ("v", v)))
     prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens, gate_log2, qk_l2norm)
     N = (len(prob.cu_host) - 1) if prob.cu_host is not None else B
     nc = num_chunks(prob)
@@ -224,7 +286,12 @@ class BwdPlan:
                  cu_seqlens=None, want_dh0=True, want_dstates=False, dt_bias=None,
                  gate_log2=False, want_ddt_bias=None, qk_l2norm=False):
         import torch
-        _require_cuda(q, k, v, g_raw, beta, A_log, dO, h0, dht, h_saved, dt_bias)
+        for name, t in (("g_raw", g_raw), ("beta", beta), ("A_log", A_log), ("dO", dO)):
+            if t is None:
+                raise ValueError("%s is required" % name)
+        specs = _gate_specs(g_raw, beta, A_log, h0, dt_bias)
+        specs.append(("dht", dht, lambda L, B, T, H, K, V, N: (N, H, K, V), torch.float32))
+        _validate(q, v, cu_seqlens, specs, (("k", k), ("v", v), ("dO", dO)), h_saved=h_saved)
         self.prob, (B, T, H, K, V) = _make_prob(q, v, cu_seqlens, gate_log2, qk_l2norm)
         N = (len(self.prob.cu_host) - 1) if self.prob.cu_host is not None else B
         dev = q.device

@@ -186,6 +186,73 @@ int make_plan(const kda_problem* p, Plan* pl) {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
+// A device byte range [p, p + n); null or empty ranges never overlap anything.
+struct Span {
+  const void* p;
+  size_t n;
+};
+bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+// Outputs must not overlap inputs, each other or the workspace, and the workspace must
+// not overlap inputs: the kernels read inputs while other workgroups write outputs.
+bool aliased(const Span* in, int nin, const Span* out, int nout, const Span& ws) {
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i)
+      if (overlap(out[o], in[i])) return true;
+    for (int j = o + 1; j < nout; ++j)
+      if (overlap(out[o], out[j])) return true;
+    if (overlap(out[o], ws)) return true;
+  }
+  for (int i = 0; i < nin; ++i)
+    if (overlap(in[i], ws)) return true;
+  return false;
+}
+
+// Byte sizes of the tensors of one call (kda.h gives the shapes).
+struct Sizes {
+  size_t act_k, act_v, f32_k, rowsf, heads, hk, state_n, state_c;
+};
+Sizes sizes_of(const kda_problem* p, const Plan& pl) {
+  const size_t rows = (size_t)p->B * p->T * p->H;
+  const size_t N = pl.s.N, KV = (size_t)p->K * p->V;
+  Sizes z;
+  z.act_k = rows * p->K * pl.es;
+  z.act_v = rows * p->V * pl.es;
+  z.f32_k = rows * p->K * 4;
+  z.rowsf = rows * 4;
+  z.heads = (size_t)p->H * 4;
+  z.hk = (size_t)p->H * p->K * 4;
+  z.state_n = N * p->H * KV * 4;
+  z.state_c = (size_t)pl.NC * p->H * KV * pl.es;
+  return z;
+}
+
+bool fwd_aliased(const kda_problem* p, const Plan& pl, const kda_fwd_io* io, const void* ws,
+                 size_t ws_n) {
+  const Sizes z = sizes_of(p, pl);
+  const Span in[] = {{io->q, z.act_k}, {io->k, z.act_k}, {io->v, z.act_v}, {io->g_raw, z.f32_k},
+                     {io->beta, z.rowsf}, {io->A_log, z.heads}, {io->h0, z.state_n},
+                     {io->dt_bias, z.hk}};
+  const Span out[] = {{io->o, z.act_v}, {io->ht, z.state_n}, {io->h_saved, z.state_c}};
+  return aliased(in, 8, out, 3, Span{ws, ws_n});
+}
+
+bool bwd_aliased(const kda_problem* p, const Plan& pl, const kda_bwd_io* io, const void* ws,
+                 size_t ws_n) {
+  const Sizes z = sizes_of(p, pl);
+  const Span in[] = {{io->q, z.act_k},      {io->k, z.act_k},       {io->v, z.act_v},
+                     {io->g_raw, z.f32_k},  {io->beta, z.rowsf},    {io->A_log, z.heads},
+                     {io->h0, z.state_n},   {io->dO, z.act_v},      {io->dht, z.state_n},
+                     {io->h_saved, z.state_c}, {io->dt_bias, z.hk}};
+  const Span out[] = {{io->dq, z.act_k},    {io->dk, z.act_k},      {io->dv, z.act_v},
+                      {io->dg_raw, z.f32_k}, {io->dbeta, z.rowsf},  {io->dA_log, z.heads},
+                      {io->dh0, z.state_n}, {io->dstates, z.state_c}, {io->ddt_bias, z.hk}};
+  return aliased(in, 11, out, 9, Span{ws, ws_n});
+}
+
 // ---- optional per-stage timing
 struct TimedLaunch {
   int stage;
@@ -296,6 +363,7 @@ int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, siz
     return KDA_ERR_INVALID_ARGUMENT;
   if (ws_bytes < pl.fwd_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
   if (pl.fwd_bytes > 0 && !workspace) return KDA_ERR_INVALID_ARGUMENT;
+  if (fwd_aliased(p, pl, io, workspace, pl.fwd_bytes)) return KDA_ERR_INVALID_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   ChunkInfo* tab = (ChunkInfo*)(ws + pl.chunks.off);
@@ -329,6 +397,7 @@ int kda_fwd(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t 
     if (!aligned16(x)) return KDA_ERR_INVALID_ARGUMENT;
   if (ws_bytes < pl.fwdp_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
   if (pl.fwdp_bytes > 0 && !workspace) return KDA_ERR_INVALID_ARGUMENT;
+  if (fwd_aliased(p, pl, io, workspace, pl.fwdp_bytes)) return KDA_ERR_INVALID_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   FwdPtrs f;
@@ -380,10 +449,10 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   for (const void* x : al)
     if (!aligned16(x)) return KDA_ERR_INVALID_ARGUMENT;
   if (((uintptr_t)io->ddt_bias & 3) != 0) return KDA_ERR_INVALID_ARGUMENT;
-  size_t need = pl.bwd_bytes;
-  if (io->h_saved) need = pl.hsaved.off;  // the recompute region is the last one
+  const size_t need = io->h_saved ? pl.hsaved.off : pl.bwd_bytes;  // recompute region last
   if (ws_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && !workspace) return KDA_ERR_INVALID_ARGUMENT;
+  if (bwd_aliased(p, pl, io, workspace, need)) return KDA_ERR_INVALID_ARGUMENT;
 
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;

@@ -126,3 +126,45 @@ def test_bwd_rejects_bad_calls_without_launching():
 def test_binding_raises_on_error():
     with pytest.raises(K.KdaError):
         K._check(K.KDA_ERR_UNSUPPORTED)
+
+
+def test_aliasing_rejected_without_launching():
+    """Outputs may not overlap inputs, other outputs or the workspace (every call below
+    is rejected during validation, so none of these fake addresses is ever used)."""
+    lib = K.load_library()
+    p = K._Prob(1, 64, 2, 64, 64, K.KDA_DTYPE_F32)
+    st, need = _ws(p)
+    assert st == 0
+    base, step = 1 << 32, 1 << 28
+    fields = ("q", "k", "v", "g_raw", "beta", "A_log", "dO", "dq", "dk", "dv", "dg_raw",
+              "dbeta", "dA_log", "dh0", "h0", "dht")
+    ws = base + len(fields) * step
+
+    def io_with(**over):
+        io = K.BwdIO()
+        for i, f in enumerate(fields):
+            setattr(io, f, base + i * step)
+        for f, val in over.items():
+            setattr(io, f, val)
+        return io
+
+    addr = {f: base + i * step for i, f in enumerate(fields)}
+    for over in (dict(dq=addr["q"]),                       # output on an input
+                 dict(dv=addr["dO"] + 4096),               # partly on an input
+                 dict(dk=addr["dq"]),                      # two outputs
+                 dict(dA_log=addr["dbeta"] + 16),
+                 dict(dh0=addr["h0"]),
+                 dict(dg_raw=ws),                          # output in the workspace
+                 dict(beta=ws + 256)):                     # input in the workspace
+        io = io_with(**over)
+        assert lib.kda_bwd(p.ref(), ctypes.byref(io), ctypes.c_void_p(ws), need, None) == \
+            K.KDA_ERR_INVALID_ARGUMENT, over
+    fio = K.FwdIO()
+    for i, f in enumerate(("q", "k", "v", "g_raw", "beta", "A_log", "h0", "o", "ht",
+                           "h_saved")):
+        setattr(fio, f, base + i * step)
+    fio.o = fio.v  # the output o on the input v
+    st, need_f = _ws(p, K.KDA_WS_FWD)
+    for entry in ("kda_fwd", "kda_fwd_ref"):
+        assert getattr(lib, entry)(p.ref(), ctypes.byref(fio), ctypes.c_void_p(ws), need_f,
+                                   None) == K.KDA_ERR_INVALID_ARGUMENT, entry
