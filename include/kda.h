@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define KDA_API __attribute__((visibility("default")))
@@ -71,6 +71,8 @@ extern "C" {
 #define KDA_ERR_WORKSPACE_TOO_SMALL (-3)
 #define KDA_ERR_HIP (-4)              /* a HIP launch failed; kda_status_string(-4)
                                          then names the HIP error of this thread */
+#define KDA_ERR_SCRATCH_TOO_SMALL (-5) /* kda_bwd_noalloc: the problem needs more than
+                                          KDA_NOALLOC_SCRATCH_BYTES of workspace */
 
 #define KDA_DTYPE_F32 0
 #define KDA_DTYPE_BF16 1
@@ -175,6 +177,20 @@ KDA_API int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* worksp
  * S <- e^{G_T} . S + Kr^T U.  o, ht and h_saved may each be NULL. */
 KDA_API int kda_fwd(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t ws_bytes,
             void* stream);
+
+/* The backward pass for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): kda_bwd with its
+ * workspace taken from a static device array of KDA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends, instead of a caller
+ * workspace.  The caller still passes every input and output.  Problems whose workspace
+ * (kda_workspace_size, or less when h_saved is given) exceeds that size return
+ * KDA_ERR_SCRATCH_TOO_SMALL without launching; other errors as for kda_bwd.  Allocates
+ * nothing.  The first call on a device looks the array's device address up once (not
+ * allowed under stream capture: make one call on each device before capturing).  Every
+ * call on one GPU shares that GPU's array, so calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+KDA_API int kda_bwd_noalloc(const kda_problem* p, const kda_bwd_io* io, void* stream);
 
 /* Text for a status code (for KDA_ERR_HIP: the last HIP error of this thread). */
 KDA_API const char* kda_status_string(int status);

@@ -19,6 +19,8 @@ KDA_ERR_INVALID_ARGUMENT = -1
 KDA_ERR_UNSUPPORTED = -2
 KDA_ERR_WORKSPACE_TOO_SMALL = -3
 KDA_ERR_HIP = -4
+KDA_ERR_SCRATCH_TOO_SMALL = -5
+KDA_NOALLOC_SCRATCH_BYTES = 64 << 20
 KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 KDA_WS_BWD = 0
@@ -77,11 +79,12 @@ def load_library():
         lib.kda_bwd.argtypes = [PP, ctypes.POINTER(BwdIO), _P, ctypes.c_size_t, _P]
         lib.kda_fwd_ref.argtypes = [PP, ctypes.POINTER(FwdIO), _P, ctypes.c_size_t, _P]
         lib.kda_fwd.argtypes = [PP, ctypes.POINTER(FwdIO), _P, ctypes.c_size_t, _P]
+        lib.kda_bwd_noalloc.argtypes = [PP, ctypes.POINTER(BwdIO), _P]
         lib.kda_timing_enable.argtypes = [ctypes.c_int]
         lib.kda_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int), ctypes.c_int]
         for f in ("kda_workspace_size", "kda_num_chunks", "kda_bwd", "kda_fwd_ref", "kda_fwd",
-                  "kda_timing_enable", "kda_timing_read"):
+                  "kda_bwd_noalloc", "kda_timing_enable", "kda_timing_read"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -320,6 +323,12 @@ class BwdPlan:
     def run(self, stream=None):
         _check(load_library().kda_bwd(self.prob.ref(), ctypes.byref(self.io), _ptr(self.ws),
                                       self.ws.numel(), _stream_ptr(stream)))
+
+    def run_noalloc(self, stream=None):
+        """The same call through kda_bwd_noalloc: the library's static device scratch
+        instead of this plan's workspace (nothing is allocated)."""
+        _check(load_library().kda_bwd_noalloc(self.prob.ref(), ctypes.byref(self.io),
+                                              _stream_ptr(stream)))
 
     def outputs(self):
         return dict(dq=self.dq, dk=self.dk, dv=self.dv, dg_raw=self.dg_raw, dbeta=self.dbeta,

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["kda_fwd.hip", "kda_prep.hip", "kda_scan.hip", "kda_gradf.hip", "kda_api.cpp"]
+SOURCES = ["kda_fwd.hip", "kda_prep.hip", "kda_scan.hip", "kda_gradf.hip", "kda_api.cpp",
+           "kda_noalloc.hip"]
 
 
 def hipcc() -> str:

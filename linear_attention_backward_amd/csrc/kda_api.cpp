@@ -317,6 +317,14 @@ hipError_t resident_blocks(const void* kernel, int threads, int* out) {
   return hipSuccess;
 }
 
+int bwd_workspace_need(const kda_problem* p, bool has_h_saved, size_t* bytes) {
+  Plan pl;
+  const int st = make_plan(p, &pl);
+  if (st != KDA_OK) return st;
+  *bytes = has_h_saved ? pl.hsaved.off : pl.bwd_bytes;
+  return KDA_OK;
+}
+
 }  // namespace kda
 
 extern "C" {
@@ -330,6 +338,8 @@ const char* kda_status_string(int status) {
     case KDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case KDA_ERR_HIP: return g_hip_msg.empty() ? "HIP error" : g_hip_msg.c_str();
+    case KDA_ERR_SCRATCH_TOO_SMALL:
+      return "problem needs more scratch than kda_bwd_noalloc holds (KDA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda.h"
+
 namespace kda {
 
 struct ChunkInfo;
@@ -84,6 +86,9 @@ hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, con
 // once: CU count times the per-CU occupancy; cached per device and kernel.  The
 // environment variable KDA_GRID_CAP, when set to n > 0, caps it at n.
 hipError_t resident_blocks(const void* kernel, int threads, int* out);
+
+// Workspace bytes kda_bwd needs for this problem, with or without a caller's h_saved.
+int bwd_workspace_need(const struct ::kda_problem* p, bool has_h_saved, size_t* bytes);
 
 hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_fprep(const Shape& s, const FwdPtrs& p, hipStream_t st);

@@ -25,8 +25,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert K.abi_version() == 2
-    for code in (0, -1, -2, -3, -4, 7):
+    assert K.abi_version() == 3
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(K.status_string(code), str) and K.status_string(code)
 
 
@@ -168,3 +168,17 @@ def test_aliasing_rejected_without_launching():
     for entry in ("kda_fwd", "kda_fwd_ref"):
         assert getattr(lib, entry)(p.ref(), ctypes.byref(fio), ctypes.c_void_p(ws), need_f,
                                    None) == K.KDA_ERR_INVALID_ARGUMENT, entry
+
+
+def test_noalloc_rejects_oversized_without_launching():
+    """kda_bwd_noalloc refuses a problem whose workspace exceeds its static scratch
+    before it looks anything up on a device."""
+    lib = K.load_library()
+    io = K.BwdIO()
+    io.h_saved = 256
+    big = K._Prob(8, 4096, 32, 128, 128, K.KDA_DTYPE_BF16)
+    assert lib.kda_bwd_noalloc(big.ref(), ctypes.byref(io), None) == K.KDA_ERR_SCRATCH_TOO_SMALL
+    assert "scratch" in K.status_string(K.KDA_ERR_SCRATCH_TOO_SMALL)
+    assert lib.kda_bwd_noalloc(big.ref(), None, None) == K.KDA_ERR_INVALID_ARGUMENT
+    bad = K._Prob(8, 4096, 32, 96, 96, K.KDA_DTYPE_BF16)
+    assert lib.kda_bwd_noalloc(bad.ref(), ctypes.byref(io), None) == K.KDA_ERR_UNSUPPORTED
