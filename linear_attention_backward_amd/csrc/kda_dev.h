@@ -394,10 +394,10 @@ __device__ __forceinline__ void store_ct<float>(float* base, int pitch, int row0
 }
 
 // Direct global -> LDS copy of a [ROWS][D] tile of T (global row stride `rs`
-// elements) into an LDS tile of pitch D + 16 / sizeof(T) elements, i.e. one 16-byte
-// pad granule per row.  global_load_lds moves 16 bytes per lane and lands lane l at
-// the wave-uniform LDS base + 16 l, so each wave fills 64-granule slices of the
-// padded tile (wave w: slices w, w + NW, ...) without passing through registers.
+// elements) into an LDS tile of pitch D + PAD * 16 / sizeof(T) elements, i.e. PAD
+// 16-byte pad granules per row.  global_load_lds moves 16 bytes per lane and lands
+// lane l at the wave-uniform LDS base + 16 l, so each wave fills 64-granule slices of
+// the padded tile (wave w: slices w, w + NW, ...) without passing through registers.
 // Pad granules receive a copy of the row's last granule (never read); rows at or
 // beyond `valid` are zero-filled with ordinary LDS stores instead.  The caller
 // waits for vmcnt(0) and synchronises before the tile is read.
@@ -414,11 +414,11 @@ __device__ __forceinline__ void g2l16(const void* g, unsigned lds) {
 //   lds0: LDS byte address of the tile (wave-uniform), lds_tile: the same tile seen
 //   through a generic pointer (for the zero fill).
 //   [N0, N1): the part of the wave's slices to issue (a tile may be issued in parts).
-template <typename T, int D, int ROWS, int NW, int N0 = 0, int N1 = 1 << 20>
+template <typename T, int D, int ROWS, int NW, int N0 = 0, int N1 = 1 << 20, int PAD = 1>
 __device__ __forceinline__ void g2l_tile(unsigned lds0, T* lds_tile, const T* src, size_t rs,
                                          int valid, int w, int lane) {
   constexpr int GPR = D * (int)sizeof(T) / 16;  // data granules per row
-  constexpr int GP = GPR + 1;                   // granules per padded LDS row
+  constexpr int GP = GPR + PAD;                 // granules per padded LDS row
   constexpr int NG = ROWS * GP;
   constexpr int EPG = 16 / (int)sizeof(T);
   constexpr int NSL = (NG + 63) / 64;           // slices

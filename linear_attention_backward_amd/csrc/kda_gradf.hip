@@ -38,10 +38,18 @@ template <typename T, int D> struct GF {
   static constexpr int NT = NW * 64;
   static constexpr int WPR = NW / 4;  // waves per 16-row block in the state side
   static constexpr int ES = (int)sizeof(T);
+  // Row pitches.  gfx950 LDS has 64 banks of 4 bytes; 16- to 64-bit accesses are served
+  // 32 lanes per cycle and 128-bit ones 16 lanes per cycle (lanes 0-31 or 32-63, split by
+  // the parity of lane bits 2..4).  A bf16 row pitch of 32 (mod 256) bytes lets both the
+  // MFMA operand reads (16 rows x 16 bytes at one column) and the transposing reads
+  // (8 rows x 32 bytes per 32 lanes) hit 64 distinct banks; 16 bytes of padding leaves
+  // both 2-way conflicted (measured with rocprofv3 SQ_LDS_BANK_CONFLICT on probe kernels).
   static constexpr int PG = 68;                 // sG  [D][PG] fp32 (channel-major G)
-  static constexpr int PN = D + 16 / ES;        // natural [rows][D] tiles of T
-  static constexpr int PT = ES == 2 ? 72 : 68;  // [D][64] token-minor tiles of T
-  static constexpr int PC = ES == 2 ? 72 : 68;  // [64][64] tiles of T
+  static constexpr int NPAD = ES == 2 ? 2 : 1;  // 16-byte pad granules per natural row
+  static constexpr int PN = D + NPAD * 16 / ES; // natural [rows][D] tiles of T
+  static constexpr int PT = ES == 2 ? 80 : 68;  // [D][64] token-minor tiles of T
+  static constexpr int PC = ES == 2 ? 80 : 68;  // [64][64] tiles of T
+  static constexpr int CPAD = (PC - 64) * ES / 16;  // pad granules of a [64][PC] tile
   static constexpr int PDG = 20;                // fp32 diagonal-block tables [16][PDG]
   static constexpr int PR = D + 4;              // dg_raw staging [64][PR] fp32
   static constexpr int G_OFF = 0;
@@ -81,6 +89,8 @@ template <typename T, int D> struct GF {
   static constexpr int IV_OFF = ES == 2 ? DG_OFF : C_END;
   static constexpr int L_END = ES == 2 ? C_END : C_END + IV_SZ;
   static_assert(ES != 2 || IV_SZ <= DG_SZ, "INV fits the diagonal-table region");
+  // k (then dvcorr) and INV are both live through the state side
+  static_assert(K0_OFF + N_SZ <= IV_OFF || IV_OFF + IV_SZ <= K0_OFF, "k tile clear of INV");
   static constexpr int B_OFF = (L_END + 15) / 16 * 16;     // beta [64]
   static constexpr int DB1_OFF = B_OFF + 256;             // [WPR][64]
   static constexpr int DB2_OFF = DB1_OFF + WPR * 256;     // [NW][64]
@@ -189,13 +199,17 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const ChunkInfo ci = chunks[c];
     const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const T* sin = h_saved + ((size_t)c * H + h) * DD;
-    if (part == 0 || part == 1) g2l_tile<T, D, D, NW, 0, 2>(lds0 + L::S_OFF, sS, sin, D, D, w, lane);
-    if (part == 0 || part == 2) g2l_tile<T, D, D, NW, 2>(lds0 + L::S_OFF, sS, sin, D, D, w, lane);
+    if (part == 0 || part == 1)
+      g2l_tile<T, D, D, NW, 0, 2, L::NPAD>(lds0 + L::S_OFF, sS, sin, D, D, w, lane);
+    if (part == 0 || part == 2)
+      g2l_tile<T, D, D, NW, 2, 1 << 20, L::NPAD>(lds0 + L::S_OFF, sS, sin, D, D, w, lane);
     if (part == 0 || part == 3) {
-      g2l_tile<T, D, 64, NW>(lds0 + L::V_OFF, sV, v + (size_t)ci.t0 * rs + (size_t)h * D, rs,
+      g2l_tile<T, D, 64, NW, 0, 1 << 20, L::NPAD>(lds0 + L::V_OFF, sV,
+                                                  v + (size_t)ci.t0 * rs + (size_t)h * D, rs,
                              ci.len, w, lane);
-      g2l_tile<T, 64, 64, NW>(lds0 + L::IV_OFF, sIV, INV + ((size_t)c * H + h) * 4096, 64, 64, w,
-                              lane);
+      g2l_tile<T, 64, 64, NW, 0, 1 << 20, L::CPAD>(lds0 + L::IV_OFF, sIV,
+                                                   INV + ((size_t)c * H + h) * 4096, 64, 64, w,
+                                                   lane);
     }
   };
   auto issue_front = [&](int it, int t) {
@@ -203,7 +217,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const ChunkInfo ci = chunks[c];
     const size_t base = (size_t)ci.t0 * rs + (size_t)h * D;
     const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
-    g2l_tile<T, D, 64, NW>(lds0 + L::K0_OFF, sK0, k + base, rs, ci.len, w, lane);
+    g2l_tile<T, D, 64, NW, 0, 1 << 20, L::NPAD>(lds0 + L::K0_OFF, sK0, k + base, rs, ci.len, w,
+                                                lane);
     const float* grw = g_raw + base + 16 * w + 4 * (lane & 3);
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
@@ -216,8 +231,10 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   auto issue_late = [&](int it, int t) {
     const int c = it / H, h = it % H;
     const ChunkInfo ci = chunks[c];
-    g2l_tile<T, D, 64, NW>(lds0 + L::O_OFF, sO, dO + (size_t)ci.t0 * rs + (size_t)h * D, rs, ci.len,
-                           __builtin_amdgcn_readfirstlane(t >> 6), t & 63);
+    g2l_tile<T, D, 64, NW, 0, 1 << 20, L::NPAD>(lds0 + L::O_OFF, sO,
+                                                dO + (size_t)ci.t0 * rs + (size_t)h * D, rs,
+                                                ci.len, __builtin_amdgcn_readfirstlane(t >> 6),
+                                                t & 63);
   };
   if ((int)blockIdx.x < items) {
     issue_early(blockIdx.x, tid0, 0);
@@ -545,13 +562,31 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const f4 t = *(const f4*)(Gi + rb + 4 * m);
       Gb[4 * m] = t[0]; Gb[4 * m + 1] = t[1]; Gb[4 * m + 2] = t[2]; Gb[4 * m + 3] = t[3];
     }
+    // k and q of column ic, rows rb .. rb + 15: transposing reads of four rows each
+    // for bf16 (lane (g4, cl) receives rows rb + 4 m + e of column 16 w + cl)
+    if constexpr (L::ES == 2) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) kb[t] = to_f(sK[(rb + t) * PN + ic]);
+      for (int m = 0; m < 4; ++m) {
+        const bf16x4 t4 = ld_tr4(sK, PN, rb + 4 * m, 16 * w, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kb[4 * m + e] = (float)t4[e];
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) kb[t] = to_f(sK[(rb + t) * PN + ic]);
+    }
     const float* mb = dgM + g4 * DGB;
     const float* lb = dgL + g4 * DGB;
+    bf16x4 q4;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float qr = to_f(sQ[(rb + r) * PN + ic]);
+      float qr;
+      if constexpr (L::ES == 2) {
+        if (r % 4 == 0) q4 = ld_tr4(sQ, PN, rb + r, 16 * w, lane);
+        qr = (float)q4[r % 4];
+      } else {
+        qr = to_f(sQ[(rb + r) * PN + ic]);
+      }
       const float bkr = sBeta[rb + r] * kb[r];
       if (r > 0) {
         const float al = ex2(Gb[r] - Gb[r - 1]);
