@@ -116,6 +116,7 @@ int make_plan(const kda_problem* p, Plan* pl) {
   s.bf16 = p->act_dtype == KDA_DTYPE_BF16;
   s.cu = p->cu_seqlens_dev;
   s.gu = p->gate_units == KDA_GATE_LOG2 ? 0.69314718055994531f : 1.f;
+  s.qn = p->qk_l2norm == 1;
   count_chunks(p, &pl->NC);
   s.NC = pl->NC;
   s.gs = scan_group_size(p, s.N);
@@ -136,6 +137,9 @@ int make_plan(const kda_problem* p, Plan* pl) {
   };
   take(pl->chunks, (size_t)pl->NC * sizeof(ChunkInfo));
   take(pl->seq_off, ((size_t)s.N + 1) * sizeof(int));
+  const size_t common = off;
+  // the reference forward normalises q, k (qk_l2norm) into copies; kda_bwd and kda_fwd
+  // normalise inside their kernels and do not use these regions
   pl->rows = (int64_t)p->B * p->T * p->H;
   pl->l2 = p->qk_l2norm == 1;
   const size_t l2 = pl->l2 ? 1 : 0;
@@ -144,6 +148,7 @@ int make_plan(const kda_problem* p, Plan* pl) {
   take(pl->rq, l2 * (size_t)pl->rows * 4);
   take(pl->rk, l2 * (size_t)pl->rows * 4);
   pl->fwd_bytes = off;
+  off = common;
   take(pl->groups, (size_t)s.NG * sizeof(GroupInfo));
   take(pl->grp_off, ((size_t)s.N + 1) * sizeof(int));
   take(pl->Tm, NCH * D * D * pl->es);
@@ -167,8 +172,8 @@ int make_plan(const kda_problem* p, Plan* pl) {
   take(pl->rQd, NCH * 64 * D * pl->es);
   take(pl->rMq, NCH * 64 * 64 * pl->es);
   pl->bwd_bytes = off;
-  // the production forward's per-chunk operands, after the reference forward's part
-  off = pl->fwd_bytes;
+  // the production forward's per-chunk operands
+  off = common;
   take(pl->fgroups, (size_t)s.NG * sizeof(GroupInfo));
   take(pl->fgrp_off, ((size_t)s.N + 1) * sizeof(int));
   take(pl->fPg, split * NGH * D * D * pl->es);
@@ -180,7 +185,7 @@ int make_plan(const kda_problem* p, Plan* pl) {
   take(pl->fQd, NCH * 64 * D * pl->es);
   take(pl->fMq, NCH * 64 * 64 * pl->es);
   take(pl->fEgt, NCH * D * 4);
-  pl->fwdp_bytes = off;
+  pl->fwdp_bytes = std::max(off, pl->fwd_bytes);  // also enough for kda_fwd_ref
   return KDA_OK;
 }
 
@@ -266,8 +271,10 @@ template <typename F>
 hipError_t timed(int stage, hipStream_t st, F&& launch) {
   if (!g_timing) return launch();
   TimedLaunch t{stage, nullptr, nullptr};
-  hipEventCreate(&t.a);
-  hipEventCreate(&t.b);
+  // no system-scope release at the event: the launches it separates are on one stream and
+  // the host reads the times only after hipEventSynchronize
+  hipEventCreateWithFlags(&t.a, hipEventDisableSystemFence);
+  hipEventCreateWithFlags(&t.b, hipEventDisableSystemFence);
   hipEventRecord(t.a, st);
   hipError_t e = launch();
   hipEventRecord(t.b, st);
@@ -421,16 +428,8 @@ int kda_fwd(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t 
   hipError_t e = launch_chunk_table(pl.s, (ChunkInfo*)f.chunks, (int*)f.seq_off,
                                     (GroupInfo*)f.groups, (int*)f.grp_off, s);
   if (e != hipSuccess) return hip_fail(e);
-  f.q = io->q;
+  f.q = io->q;  // raw: with qk_l2norm the per-chunk pass normalises the rows itself
   f.k = io->k;
-  if (pl.l2) {
-    f.q = ws + pl.qn.off;
-    f.k = ws + pl.kn.off;
-    e = launch_l2norm(pl.s, pl.rows, io->q, (void*)f.q, (float*)(ws + pl.rq.off), s);
-    if (e == hipSuccess)
-      e = launch_l2norm(pl.s, pl.rows, io->k, (void*)f.k, (float*)(ws + pl.rk.off), s);
-    if (e != hipSuccess) return hip_fail(e);
-  }
   f.v = io->v;
   f.g_raw = io->g_raw; f.beta = io->beta; f.A_log = io->A_log; f.h0 = io->h0;
   f.dt_bias = io->dt_bias ? io->dt_bias : io->g_raw;
@@ -467,8 +466,8 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   BwdPtrs b;
-  b.q = pl.l2 ? (const void*)(ws + pl.qn.off) : io->q;  // the normalised copies when asked
-  b.k = pl.l2 ? (const void*)(ws + pl.kn.off) : io->k;
+  b.q = io->q;  // raw: with qk_l2norm prep and the gradient pass normalise the rows
+  b.k = io->k;
   b.v = io->v; b.dO = io->dO;
   b.g_raw = io->g_raw; b.beta = io->beta; b.A_log = io->A_log; b.h0 = io->h0; b.dht = io->dht;
   b.dt_bias = io->dt_bias ? io->dt_bias : io->g_raw;
@@ -499,15 +498,6 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
                               (int*)b.grp_off, s);
   });
   if (e != hipSuccess) return hip_fail(e);
-  float* rq = (float*)(ws + pl.rq.off);
-  float* rk = (float*)(ws + pl.rk.off);
-  if (pl.l2) {
-    e = timed(6, s, [&] {
-      hipError_t x = launch_l2norm(sh, pl.rows, io->q, (void*)b.q, rq, s);
-      return x == hipSuccess ? launch_l2norm(sh, pl.rows, io->k, (void*)b.k, rk, s) : x;
-    });
-    if (e != hipSuccess) return hip_fail(e);
-  }
   if (!io->h_saved) {  // the chunk-start states by the production forward
     FwdPtrs f;
     f.q = b.q; f.k = b.k; f.v = io->v;
@@ -536,13 +526,6 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   if (e != hipSuccess) return hip_fail(e);
   if (io->ddt_bias) {
     e = timed(4, s, [&] { return launch_ddt(sh, b, s); });
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  if (pl.l2) {  // dq, dk came out with respect to the normalised q, k: project in place
-    e = timed(6, s, [&] {
-      hipError_t x = launch_l2norm_bwd(sh, pl.rows, b.q, rq, io->dq, s);
-      return x == hipSuccess ? launch_l2norm_bwd(sh, pl.rows, b.k, rk, io->dk, s) : x;
-    });
     if (e != hipSuccess) return hip_fail(e);
   }
   return KDA_OK;

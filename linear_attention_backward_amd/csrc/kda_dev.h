@@ -488,6 +488,71 @@ __device__ __forceinline__ float sum64(float x) {
   return x;
 }
 
+// L2 normalisation of q and k per (token, head) (the Kernel-B guide, R1 computes the
+// reciprocal norm of every row once and its K1, the norm's backward, reuses it):
+//   xn = x r,  r = 1 / sqrt(sum_i x_i^2 + eps),   dx = r (dxn - xn (xn . dxn)).
+// A row of D elements is held by LPR consecutive lanes (one 16-byte piece each) that
+// form one DPP row (LPR = 16) or half row (LPR = 8).  Every kernel that normalises uses
+// these helpers, so the normalised values are bit-identical wherever they are formed.
+constexpr float kL2Eps = 1e-6f;
+template <int LPR> __device__ __forceinline__ float sum_group(float x) {
+  if constexpr (LPR == 16) return sum16(x);
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror: the 8 lanes of each half row
+  return x;
+}
+// Normalises the lane's piece of a row in place; returns the row's reciprocal norm.
+template <typename T, int LPR> __device__ __forceinline__ float l2n_piece(u32x4& piece) {
+  constexpr int EPV = 16 / (int)sizeof(T);
+  const T* e = (const T*)&piece;
+  float v[EPV];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPV; ++j) {
+    v[j] = to_f(e[j]);
+    ss += v[j] * v[j];
+  }
+  ss = sum_group<LPR>(ss);
+  const float rr = __builtin_amdgcn_rsqf(ss + kL2Eps);  // argument >= eps: no scaling needed
+  T out[EPV];
+#pragma unroll
+  for (int j = 0; j < EPV; ++j) out[j] = from_f<T>(v[j] * rr);
+  piece = *(const u32x4*)out;
+  return rr;
+}
+// xn = x rr for a raw piece whose row's reciprocal norm is already known (the same
+// rounding as l2n_piece).
+template <typename T> __device__ __forceinline__ u32x4 l2n_apply(u32x4 piece, float rr) {
+  constexpr int EPV = 16 / (int)sizeof(T);
+  const T* e = (const T*)&piece;
+  T out[EPV];
+#pragma unroll
+  for (int j = 0; j < EPV; ++j) out[j] = from_f<T>(to_f(e[j]) * rr);
+  return *(const u32x4*)out;
+}
+// The lane's share of xn . dxn.
+template <typename T> __device__ __forceinline__ float dot_piece(u32x4 xn, u32x4 dxn) {
+  constexpr int EPV = 16 / (int)sizeof(T);
+  const T* a = (const T*)&xn;
+  const T* g = (const T*)&dxn;
+  float d = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPV; ++j) d += to_f(a[j]) * to_f(g[j]);
+  return d;
+}
+// dx = rr (dxn - xn dot) for one piece.
+template <typename T>
+__device__ __forceinline__ u32x4 l2n_project(u32x4 xn, u32x4 dxn, float rr, float dot) {
+  constexpr int EPV = 16 / (int)sizeof(T);
+  const T* a = (const T*)&xn;
+  const T* g = (const T*)&dxn;
+  T out[EPV];
+#pragma unroll
+  for (int j = 0; j < EPV; ++j) out[j] = from_f<T>(rr * (to_f(g[j]) - to_f(a[j]) * dot));
+  return *(const u32x4*)out;
+}
+
 // Pitches (in elements) of the LDS tiles.  Natural token-major tiles [64][D] of T
 // get 16 bytes of row padding so that the 16 rows one MFMA operand reads start
 // in distinct 4-bank groups of the 64-bank LDS; transposed tiles [D][64] likewise.

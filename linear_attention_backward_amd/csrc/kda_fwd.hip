@@ -192,24 +192,12 @@ __global__ __launch_bounds__(256) void k_dalog(const float* __restrict__ part, i
 }
 
 // ---------------------------------------------------------------------------
-// Optional L2 normalisation of q and k per (token, head) (the Kernel-B guide, R1
-// computes the reciprocal norm of every row once and its K1, the norm's backward,
-// reuses it):
-//   xn = x r,  r = 1 / sqrt(sum_i x_i^2 + eps)       (eps = kL2Eps)
-// and, in place on the gradient with respect to xn,
-//   dx = r (dxn - xn (xn . dxn)).
-// A row of D elements is LPR lanes holding one 16-byte piece each; every lane of a
-// block works (rows past the end are clamped and not stored), so the DPP sums over
-// a lane group never see an idle lane.
-constexpr float kL2Eps = 1e-6f;
-template <int LPR> __device__ __forceinline__ float sum_group(float x) {
-  if constexpr (LPR == 16) return sum16(x);
-  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp_f<0x141>(x);  // row_half_mirror: the 8 lanes of each half row
-  return x;
-}
-
+// L2 normalisation of q and k per (token, head) for the reference forward:
+//   xn = x r,  r = 1 / sqrt(sum_i x_i^2 + eps)
+// (the backward and the production forward normalise inside their own kernels with the
+// same helpers).  A row of D elements is LPR lanes holding one 16-byte piece each; every
+// lane of a block works (rows past the end are clamped and not stored), so the DPP sums
+// over a lane group never see an idle lane.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_l2norm(const T* __restrict__ x, int64_t rows,
                                                 T* __restrict__ xn, float* __restrict__ r) {
@@ -219,80 +207,29 @@ __global__ __launch_bounds__(256) void k_l2norm(const T* __restrict__ x, int64_t
   const int64_t row0 = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int64_t row = row0 < rows ? row0 : rows - 1;
   const size_t o = (size_t)row * D + sub * EPV;
-  const uint4 raw = *(const uint4*)(x + o);
-  const T* e = (const T*)&raw;
-  float v[EPV];
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < EPV; ++j) {
-    v[j] = to_f(e[j]);
-    ss += v[j] * v[j];
-  }
-  ss = sum_group<LPR>(ss);
-  const float rr = 1.f / sqrtf(ss + kL2Eps);
-  T out[EPV];
-#pragma unroll
-  for (int j = 0; j < EPV; ++j) out[j] = from_f<T>(v[j] * rr);
+  u32x4 piece = *(const u32x4*)(x + o);
+  const float rr = l2n_piece<T, LPR>(piece);
   if (row0 < rows) {
-    *(uint4*)(xn + o) = *(const uint4*)out;
+    *(u32x4*)(xn + o) = piece;
     if (sub == 0) r[row] = rr;
   }
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_l2norm_bwd(const T* __restrict__ xn,
-                                                    const float* __restrict__ r, int64_t rows,
-                                                    T* __restrict__ dx) {
-  constexpr int EPV = 16 / (int)sizeof(T), LPR = D / EPV, RPB = 256 / LPR;
-  static_assert(LPR == 8 || LPR == 16, "row split");
-  const int sub = threadIdx.x % LPR;
-  const int64_t row0 = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int64_t row = row0 < rows ? row0 : rows - 1;
-  const size_t o = (size_t)row * D + sub * EPV;
-  const uint4 ra = *(const uint4*)(xn + o), rg = *(const uint4*)(dx + o);
-  const T* a = (const T*)&ra;
-  const T* g = (const T*)&rg;
-  float dot = 0.f;
-#pragma unroll
-  for (int j = 0; j < EPV; ++j) dot += to_f(a[j]) * to_f(g[j]);
-  dot = sum_group<LPR>(dot);
-  const float rr = r[row];
-  T out[EPV];
-#pragma unroll
-  for (int j = 0; j < EPV; ++j) out[j] = from_f<T>(rr * (to_f(g[j]) - to_f(a[j]) * dot));
-  if (row0 < rows) *(uint4*)(dx + o) = *(const uint4*)out;
-}
-
-template <typename T, int D>
-static hipError_t l2norm_t(int64_t rows, const void* x, void* xn, float* r, const void* xn_in,
-                           const float* r_in, void* dx, hipStream_t st) {
+static hipError_t l2norm_t(int64_t rows, const void* x, void* xn, float* r, hipStream_t st) {
   constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
   const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
-  if (x)
-    hipLaunchKernelGGL((k_l2norm<T, D>), grid, dim3(256), 0, st, (const T*)x, rows, (T*)xn, r);
-  else
-    hipLaunchKernelGGL((k_l2norm_bwd<T, D>), grid, dim3(256), 0, st, (const T*)xn_in, r_in, rows,
-                       (T*)dx);
+  hipLaunchKernelGGL((k_l2norm<T, D>), grid, dim3(256), 0, st, (const T*)x, rows, (T*)xn, r);
   return hipGetLastError();
-}
-
-static hipError_t l2norm_any(const Shape& s, int64_t rows, const void* x, void* xn, float* r,
-                             const void* xn_in, const float* r_in, void* dx, hipStream_t st) {
-  if (rows == 0) return hipSuccess;
-  if (s.bf16)
-    return s.D == 128 ? l2norm_t<bf16, 128>(rows, x, xn, r, xn_in, r_in, dx, st)
-                      : l2norm_t<bf16, 64>(rows, x, xn, r, xn_in, r_in, dx, st);
-  return l2norm_t<float, 64>(rows, x, xn, r, xn_in, r_in, dx, st);
 }
 
 hipError_t launch_l2norm(const Shape& s, int64_t rows, const void* x, void* xn, float* r,
                          hipStream_t st) {
-  return l2norm_any(s, rows, x, xn, r, nullptr, nullptr, nullptr, st);
-}
-
-hipError_t launch_l2norm_bwd(const Shape& s, int64_t rows, const void* xn, const float* r,
-                             void* dx, hipStream_t st) {
-  return l2norm_any(s, rows, nullptr, nullptr, nullptr, xn, r, dx, st);
+  if (rows == 0) return hipSuccess;
+  if (s.bf16)
+    return s.D == 128 ? l2norm_t<bf16, 128>(rows, x, xn, r, st)
+                      : l2norm_t<bf16, 64>(rows, x, xn, r, st);
+  return l2norm_t<float, 64>(rows, x, xn, r, st);
 }
 
 // ddt_bias[h][i] = sum over chunks of the per chunk-head column sums of dg_raw, in a

@@ -95,7 +95,8 @@ template <typename T, int D> struct GF {
   static constexpr int DB1_OFF = B_OFF + 256;             // [WPR][64]
   static constexpr int DB2_OFF = DB1_OFF + WPR * 256;     // [NW][64]
   static constexpr int RED_OFF = DB2_OFF + NW * 256;      // [NW]
-  static constexpr int TOTAL = RED_OFF + NW * 4;
+  static constexpr int RQ_OFF = RED_OFF + NW * 4;         // q/k reciprocal norms [2][64]
+  static constexpr int TOTAL = RQ_OFF + 2 * 64 * 4;
   static_assert(S_OFF >= I_END && K0_OFF >= DM_OFF, "prefetch tiles clear the intra phase");
   static_assert(TOTAL <= 160 * 1024, "LDS");
   static_assert(64 * PR * 4 <= G_SZ, "dg_raw staging fits the gate region");
@@ -103,8 +104,11 @@ template <typename T, int D> struct GF {
 };
 
 // GV: gate bias present or its gradient asked for; without it the bias is not read and
-// no column sums of dg_raw are formed.
-template <typename T, int D, bool GV>
+// no column sums of dg_raw are formed.  QN: q and k are L2-normalised per row inside the
+// pass (k in its LDS tile at the start of an item, q in registers on its way to LDS) and
+// dq, dk are projected back to the raw rows as they are written out, with the cached
+// reciprocal norms: dx = r (dxn - xn (xn . dxn)).
+template <typename T, int D, bool GV, bool QN>
 __global__ __launch_bounds__(4 * D) void k_gradf(
     const ChunkInfo* __restrict__ chunks, int NC, int H, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
@@ -152,6 +156,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   float* sDB1 = (float*)(smem + L::DB1_OFF);
   float* sDB2 = (float*)(smem + L::DB2_OFF);
   float* sRed = (float*)(smem + L::RED_OFF);
+  float* sRq = (float*)(smem + L::RQ_OFF);  // reciprocal norms of q, k rows (QN)
+  float* sRk = sRq + 64;
   // diagonal 16x16 blocks of dMqk and dL in fp32, natural: block R, row rr, col cc at
   // dg*[R * DGB + rr * DGP + cc]
   float* dgM;
@@ -242,6 +248,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     issue_late(blockIdx.x, tid0);
   }
   settle(rg);  // waits for all of the first item's copies as well
+  if constexpr (QN) __syncthreads();  // the first k tile is normalised in place below
   settle(rbeta);
   if constexpr (GV) settle(rdb);
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
@@ -275,6 +282,16 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     rD[l] = *(const u32x4*)(dSo + (size_t)r * D + sv * EPV);
   }
   if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
+  if constexpr (QN) {  // k rows normalised in place (rows past the chunk are zero)
+#pragma unroll
+    for (int l = 0; l < NLT; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+      u32x4 kv = *(const u32x4*)(sK0 + r * PN + sv * EPV);
+      const float rr = l2n_piece<T, VPR>(kv);
+      *(u32x4*)(sK0 + r * PN + sv * EPV) = kv;
+      if (sv == 0) sRk[r] = rr;
+    }
+  }
   {  // in-chunk cumulative gate (log2 units), channel-major: sG[i][r].  The per-token
      // gates go into this wave's 16 channel rows of the tile (written and read back by
      // this wave only), then lane (g4, cl) sums channel 16 w + cl over rows 16 g4 .. + 15
@@ -536,7 +553,12 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {  // q, k natural
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    *(u32x4*)(sQ + r * PN + sv * EPV) = rQ[l] & (r < Lr ? ~0u : 0u);
+    u32x4 qv = rQ[l];
+    if constexpr (QN) {
+      const float rr = l2n_piece<T, VPR>(qv);
+      if (sv == 0) sRq[r] = rr;
+    }
+    *(u32x4*)(sQ + r * PN + sv * EPV) = qv & (r < Lr ? ~0u : 0u);
     *(u32x4*)(sK + r * PN + sv * EPV) = rK[l];
   }
   __syncthreads();
@@ -757,6 +779,18 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     // the next item's S_in and v, in pieces (their tiles are clear of the intra phase)
     if (rt < 3 && nxt < items) issue_early(nxt, tid, rt + 1);
   }
+  // (QN) the raw q, k pieces that the output copies project with, issued now so that the
+  // reductions below hide their latency
+  u32x4 rawq[QN ? NLT : 1], rawk[QN ? NLT : 1];
+  if constexpr (QN) {
+#pragma unroll
+    for (int l = 0; l < NLT; ++l) {
+      const int idx = tid + l * NT, r0 = idx / VPR, sv = idx % VPR;
+      const size_t o = (t0 + (r0 < Lr ? r0 : Lr - 1)) * rs + hD + sv * EPV;
+      rawq[l] = *(const u32x4*)(q + o);
+      rawk[l] = *(const u32x4*)(k + o);
+    }
+  }
   // last row: sum_r k.dk_r + e^{G_T} p
   dkr_col += __shfl_xor(dkr_col, 16);
   dkr_col += __shfl_xor(dkr_col, 32);
@@ -827,8 +861,18 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const int idx = tid + l * NT, r0 = idx / VPR, sv = idx % VPR;
     const int r = r0 < Lr ? r0 : Lr - 1;
     const size_t o = (t0 + r) * rs + hD + sv * EPV;
-    *(u32x4*)(dq + o) = *(const u32x4*)(sDQ + r * PN + sv * EPV);
-    *(u32x4*)(dk + o) = *(const u32x4*)(sDK + r * PN + sv * EPV);
+    u32x4 vq = *(const u32x4*)(sDQ + r * PN + sv * EPV);
+    u32x4 vk = *(const u32x4*)(sDK + r * PN + sv * EPV);
+    if constexpr (QN) {  // back to the raw rows: dx = r (dxn - xn (xn . dxn)); the row's
+                         // VPR pieces are VPR consecutive lanes (one DPP row)
+      const float rrq = sRq[r], rrk = sRk[r];
+      const u32x4 qn = l2n_apply<T>(rawq[l], rrq);
+      const u32x4 kn = l2n_apply<T>(rawk[l], rrk);
+      vq = l2n_project<T>(qn, vq, rrq, sum_group<VPR>(dot_piece<T>(qn, vq)));
+      vk = l2n_project<T>(kn, vk, rrk, sum_group<VPR>(dot_piece<T>(kn, vk)));
+    }
+    *(u32x4*)(dq + o) = vq;
+    *(u32x4*)(dk + o) = vk;
   }
   if (tid < 64 && tid < Lr) {
     float s = 0.f;
@@ -864,14 +908,14 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   }
 }
 
-template <typename T, int D, bool GV>
+template <typename T, int D, bool GV, bool QN>
 static hipError_t gradf_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const int items = s.NC * s.H;
   int resident = 0;
-  hipError_t e = resident_blocks((const void*)k_gradf<T, D, GV>, GF<T, D>::NT, &resident);
+  hipError_t e = resident_blocks((const void*)k_gradf<T, D, GV, QN>, GF<T, D>::NT, &resident);
   if (e != hipSuccess) return e;
   const int grid = items < resident ? items : resident;
-  hipLaunchKernelGGL((k_gradf<T, D, GV>), dim3(grid), dim3(GF<T, D>::NT), 0, st, p.chunks, s.NC, s.H,
+  hipLaunchKernelGGL((k_gradf<T, D, GV, QN>), dim3(grid), dim3(GF<T, D>::NT), 0, st, p.chunks, s.NC, s.H,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dO, p.g_raw,
                      p.beta, p.A_log, p.dt_bias, p.has_db, s.gu, (const T*)p.h_saved,
                      (const T*)p.dstates,
@@ -882,7 +926,10 @@ static hipError_t gradf_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
 
 template <typename T, int D>
 static hipError_t gradf_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
-  return p.has_db || p.ddt_bias ? gradf_v<T, D, true>(s, p, st) : gradf_v<T, D, false>(s, p, st);
+  const bool gv = p.has_db || p.ddt_bias;
+  if (s.qn)
+    return gv ? gradf_v<T, D, true, true>(s, p, st) : gradf_v<T, D, false, true>(s, p, st);
+  return gv ? gradf_v<T, D, true, false>(s, p, st) : gradf_v<T, D, false, false>(s, p, st);
 }
 
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st) {

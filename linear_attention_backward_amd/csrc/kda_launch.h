@@ -74,6 +74,7 @@ struct Shape {
   int gs;          // chunks per scan group; 0: one group per sequence
   int64_t NG;      // groups
   float gu;        // natural-log decay per unit of the gate: 1, or ln 2 for log2 units
+  int qn;          // q and k L2-normalised inside the kernels (prep, gradient pass)
 };
 
 hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, GroupInfo* groups,
@@ -97,11 +98,8 @@ hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_ddt(const Shape& s, const BwdPtrs& p, hipStream_t st);
-// rows = tokens * heads of a [.., H, D] act-dtype tensor: xn = x / |x|, r = 1 / |x|; and
-// the backward dx = r (dx - xn (xn . dx)) in place
+// rows = tokens * heads of a [.., H, D] act-dtype tensor: xn = x / |x|, r = 1 / |x|
 hipError_t launch_l2norm(const Shape& s, int64_t rows, const void* x, void* xn, float* r,
                          hipStream_t st);
-hipError_t launch_l2norm_bwd(const Shape& s, int64_t rows, const void* xn, const float* r,
-                             void* dx, hipStream_t st);
 
 }  // namespace kda

@@ -52,8 +52,9 @@ template <typename T, int D> struct PL {
 
 // GV: gate bias present (or its gradient asked for); without it the bias is not read.
 // FWD: the forward's per-chunk operands instead of the backward's (see the end of the
-// item loop).
-template <typename T, int D, bool GV, bool FWD>
+// item loop).  QN: q and k are L2-normalised per row as they enter LDS (every quantity
+// below is then formed from the normalised rows).
+template <typename T, int D, bool GV, bool FWD, bool QN>
 __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ chunks, int NC, int H,
                                                 const T* __restrict__ q, const T* __restrict__ k,
                                                 const float* __restrict__ g_raw,
@@ -184,8 +185,13 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   for (int l = 0; l < NLT; ++l) {
     const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
     const unsigned m = r < Lr ? ~0u : 0u;
-    *(u32x4*)(sQ + r * PN + vv * EPV) = rq[l] & m;
-    *(u32x4*)(sK + r * PN + vv * EPV) = rk[l] & m;
+    u32x4 qv = rq[l], kv = rk[l];
+    if constexpr (QN) {  // a row is VPR consecutive lanes: one DPP (half) row
+      l2n_piece<T, VPR>(qv);
+      l2n_piece<T, VPR>(kv);
+    }
+    *(u32x4*)(sQ + r * PN + vv * EPV) = qv & m;
+    *(u32x4*)(sK + r * PN + vv * EPV) = kv & m;
   }
   __syncthreads();
   {
@@ -653,42 +659,49 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   }
 }
 
-template <typename T, int D, bool GV>
+template <typename T, int D, bool GV, bool QN>
 static hipError_t prep_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const int items = s.NC * s.H;
   int resident = 0;
-  hipError_t e = resident_blocks((const void*)k_prep<T, D, GV, false>, PL<T, D>::NT, &resident);
+  hipError_t e =
+      resident_blocks((const void*)k_prep<T, D, GV, false, QN>, PL<T, D>::NT, &resident);
   if (e != hipSuccess) return e;
   const int grid = items < resident ? items : resident;
-  hipLaunchKernelGGL((k_prep<T, D, GV, false>), dim3(grid), dim3(PL<T, D>::NT), 0, st, p.chunks, s.NC, s.H, (const T*)p.q,
-                     (const T*)p.k, p.g_raw, p.beta, p.A_log, p.dt_bias, p.has_db, s.gu,
-                     (T*)p.Tm, (T*)p.PT, p.eGT,
+  hipLaunchKernelGGL((k_prep<T, D, GV, false, QN>), dim3(grid), dim3(PL<T, D>::NT), 0, st,
+                     p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
+                     p.A_log, p.dt_bias, p.has_db, s.gu, (T*)p.Tm, (T*)p.PT, p.eGT,
                      (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool GV>
+template <typename T, int D, bool GV, bool QN>
 static hipError_t fprep_v(const Shape& s, const FwdPtrs& p, hipStream_t st) {
   const int items = s.NC * s.H;
   int resident = 0;
-  hipError_t e = resident_blocks((const void*)k_prep<T, D, GV, true>, PL<T, D>::NT, &resident);
+  hipError_t e =
+      resident_blocks((const void*)k_prep<T, D, GV, true, QN>, PL<T, D>::NT, &resident);
   if (e != hipSuccess) return e;
   const int grid = items < resident ? items : resident;
-  hipLaunchKernelGGL((k_prep<T, D, GV, true>), dim3(grid), dim3(PL<T, D>::NT), 0, st, p.chunks,
-                     s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta, p.A_log,
-                     p.dt_bias, p.has_db, s.gu, nullptr, nullptr, p.eGT, nullptr, nullptr,
-                     (const T*)p.v, (T*)p.Wn, (T*)p.KrT, (T*)p.UvT, (T*)p.Qd, (T*)p.Mq);
+  hipLaunchKernelGGL((k_prep<T, D, GV, true, QN>), dim3(grid), dim3(PL<T, D>::NT), 0, st,
+                     p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
+                     p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, p.eGT, nullptr,
+                     nullptr, (const T*)p.v, (T*)p.Wn, (T*)p.KrT, (T*)p.UvT, (T*)p.Qd,
+                     (T*)p.Mq);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t prep_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
-  return p.has_db || p.ddt_bias ? prep_v<T, D, true>(s, p, st) : prep_v<T, D, false>(s, p, st);
+  const bool gv = p.has_db || p.ddt_bias;
+  if (s.qn) return gv ? prep_v<T, D, true, true>(s, p, st) : prep_v<T, D, false, true>(s, p, st);
+  return gv ? prep_v<T, D, true, false>(s, p, st) : prep_v<T, D, false, false>(s, p, st);
 }
 
 template <typename T, int D>
 static hipError_t fprep_t(const Shape& s, const FwdPtrs& p, hipStream_t st) {
-  return p.has_db ? fprep_v<T, D, true>(s, p, st) : fprep_v<T, D, false>(s, p, st);
+  if (s.qn)
+    return p.has_db ? fprep_v<T, D, true, true>(s, p, st) : fprep_v<T, D, false, true>(s, p, st);
+  return p.has_db ? fprep_v<T, D, true, false>(s, p, st) : fprep_v<T, D, false, false>(s, p, st);
 }
 
 hipError_t launch_fprep(const Shape& s, const FwdPtrs& p, hipStream_t st) {

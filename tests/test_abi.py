@@ -61,13 +61,20 @@ def test_shape_validation():
     assert _ws(bad)[0] == K.KDA_ERR_INVALID_ARGUMENT
     bad = K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16, qk_l2norm=2)
     assert _ws(bad)[0] == K.KDA_ERR_INVALID_ARGUMENT
-    # the q/k L2 norm keeps normalised copies and reciprocal norms in the workspace
-    plain = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16))[1]
-    normed = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16, qk_l2norm=1))[1]
-    assert normed >= plain + 2 * 200 * 4 * 128 * 2 + 2 * 200 * 4 * 4
-    fwd_plain = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16), K.KDA_WS_FWD)[1]
-    fwd_normed = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16, qk_l2norm=1), K.KDA_WS_FWD)[1]
-    assert fwd_normed >= fwd_plain + 2 * 200 * 4 * 128 * 2
+    # the q/k L2 norm: kda_bwd and kda_fwd normalise inside their kernels (no extra
+    # workspace); the reference forward keeps normalised copies and reciprocal norms
+    for which in (K.KDA_WS_BWD, K.KDA_WS_FWD):
+        plain = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16), which)[1]
+        normed = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16, qk_l2norm=1), which)[1]
+        assert normed == plain, which
+    ref_plain = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16), K.KDA_WS_FWD_REF)[1]
+    ref_normed = _ws(K._Prob(2, 100, 4, 128, 128, K.KDA_DTYPE_BF16, qk_l2norm=1),
+                     K.KDA_WS_FWD_REF)[1]
+    assert ref_normed >= ref_plain + 2 * 200 * 4 * 128 * 2 + 2 * 200 * 4 * 4
+    for T in (1, 64, 1000):  # the production forward's workspace also serves kda_fwd_ref
+        for qn in (0, 1):
+            p = K._Prob(2, T, 4, 128, 128, K.KDA_DTYPE_BF16, qk_l2norm=qn)
+            assert _ws(p, K.KDA_WS_FWD)[1] >= _ws(p, K.KDA_WS_FWD_REF)[1]
 
 
 def test_cu_seqlens_validation():
