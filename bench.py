@@ -39,13 +39,14 @@ def log(*a):
 # compulsorily: the gradient pass reads every per-token input and the two states and
 # writes every per-token output; the scan writes the state-gradient hand-off; prep's
 # traffic (re-reads of q, k, g_raw, beta and its own intermediates) is all overhead.
-def kernel_bytes_per_token_head(D=128, es=2):
+# When prep runs the scan itself (fused), the hand-off is prep's.
+def kernel_bytes_per_token_head(D=128, es=2, fused=False):
     act = D * es          # one activation row
     f32row = D * 4        # one fp32 row (g_raw, dg_raw)
     state = D * D * es / 64.0   # one K x V state per chunk
     return {
-        "prep": 0.0,
-        "scan": state,                                   # dS_out written
+        "prep": state if fused else 0.0,
+        "scan": 0.0 if fused else state,                 # dS_out written
         # q, k, v, dO, g_raw, beta in; S_in and dS_out in; dq, dk, dv, dg_raw, dbeta out
         "grad": 4 * act + f32row + 4 + 2 * state + 3 * act + f32row + 4,
     }
@@ -455,14 +456,16 @@ def main():
     H, D = inp["H"], inp["K"]
     es = 2 if inp["dtype"] == "bf16" else 4
     token_heads = tokens * H
-    kb = kernel_bytes_per_token_head(D, es)[dom] * token_heads
+    fused = st["scan"][1] == 0  # prep ran the state-gradient scan itself
+    kb = kernel_bytes_per_token_head(D, es, fused)[dom] * token_heads
     achieved = kb / (per[dom] / 1e3) / 1e9
     traffic = load_traffic(dom)
     path_bytes = path_bytes_per_token_head(D, es) * token_heads
     # Which roofline binds: the path's MFMA work per algorithmic byte against the ridge
     # point (bf16 peak / HBM peak).  The MFMA work is the counted one when counters for
     # these sources are committed, else the algorithmic count.
-    ctr = {st_: load_counters(st_) for st_ in ("prep", "scan", "grad")}
+    ctr = {st_: load_counters(st_) for st_ in (("prep", "grad") if fused
+                                                else ("prep", "scan", "grad"))}
     chunk_heads = int(plan.nc) * H
     if all(c is not None for c in ctr.values()):
         flops = sum(c["mfma_flop_per_launch"] for c in ctr.values())
@@ -510,7 +513,9 @@ def main():
         "dtype": inp["dtype"],
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": H, "K": D, "V": inp["V"],
-                   "chunk": 64, "h_saved": "given", "parallelism": "single-gpu"},
+                   "chunk": 64, "h_saved": "given", "parallelism": "single-gpu",
+                   "kernels": "prep with the state-gradient scan inside, gradient pass"
+                   if fused else "prep, state-gradient scan, gradient pass"},
         **({"variants": [k for k, v in variants.items() if v]} if any(variants.values()) else {}),
         "roofline": roof,
         "path_roofline": {"bound": bound, "algorithmic_bytes": path_bytes,

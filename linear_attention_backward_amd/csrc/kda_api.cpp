@@ -76,6 +76,31 @@ int scan_group_size(const kda_problem* p, int N) {
   return mx > 128 ? 64 : 0;
 }
 
+// Chunks of every sequence when all sequences have the same number (>= 1), else 0.
+int64_t uniform_chunks(const kda_problem* p, int N) {
+  const int64_t first = seq_chunks(p, 0);
+  for (int n = 1; n < N; ++n)
+    if (seq_chunks(p, n) != first) return 0;
+  return first;
+}
+
+// Whether prep runs the state-gradient scan itself (one workgroup per (sequence, head)
+// unit, its chunks last to first): every sequence must have the same chunk count, and the
+// units must spread evenly over the resident workgroups.  KDA_PREPSCAN=0 / 1 forces the
+// separate kernels / the fused one (when the chunk counts allow it).
+int prepscan_chunks(const kda_problem* p, const Shape& s) {
+  const int64_t ncs = uniform_chunks(p, s.N);
+  if (ncs <= 0) return 0;
+  if (const char* env = std::getenv("KDA_PREPSCAN")) {
+    if (env[0] == '0') return 0;
+    if (env[0] == '1') return (int)ncs;
+  }
+  int grid = 0;
+  if (prepscan_grid(s, &grid) != hipSuccess || grid <= 0) return 0;
+  const int64_t units = (int64_t)s.N * s.H;
+  return units >= grid && (units % grid == 0 || units >= 8 * (int64_t)grid) ? (int)ncs : 0;
+}
+
 int validate_problem(const kda_problem* p) {
   if (!p) return KDA_ERR_INVALID_ARGUMENT;
   if (p->B < 1 || p->T < 0 || p->H < 1 || p->K < 1 || p->V < 1) return KDA_ERR_INVALID_ARGUMENT;
@@ -516,10 +541,15 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
     });
     if (e != hipSuccess) return hip_fail(e);
   }
-  e = timed(1, s, [&] { return launch_prep(sh, b, s); });
-  if (e != hipSuccess) return hip_fail(e);
-  e = timed(2, s, [&] { return launch_scan(sh, b, s); });
-  if (e != hipSuccess) return hip_fail(e);
+  if (const int ncs = prepscan_chunks(p, sh)) {  // prep with the scan inside
+    e = timed(1, s, [&] { return launch_prepscan(sh, b, ncs, s); });
+    if (e != hipSuccess) return hip_fail(e);
+  } else {
+    e = timed(1, s, [&] { return launch_prep(sh, b, s); });
+    if (e != hipSuccess) return hip_fail(e);
+    e = timed(2, s, [&] { return launch_scan(sh, b, s); });
+    if (e != hipSuccess) return hip_fail(e);
+  }
   e = timed(3, s, [&] { return launch_gradf(sh, b, s); });
   if (e != hipSuccess) return hip_fail(e);
   e = timed(4, s, [&] { return launch_dalog(sh, b, s); });

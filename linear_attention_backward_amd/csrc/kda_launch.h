@@ -95,6 +95,11 @@ hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_fprep(const Shape& s, const FwdPtrs& p, hipStream_t st);
 hipError_t launch_fscan(const Shape& s, const FwdPtrs& p, hipStream_t st);
 hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st);
+// prep with the reverse state-gradient scan inside (every sequence has ncs chunks): writes
+// INV, Mqk^T, dstates and dh0 instead of Tm, PT and exp(G_T)
+hipError_t launch_prepscan(const Shape& s, const BwdPtrs& p, int ncs, hipStream_t st);
+// workgroups of that kernel the current device holds at once
+hipError_t prepscan_grid(const Shape& s, int* grid);
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_ddt(const Shape& s, const BwdPtrs& p, hipStream_t st);

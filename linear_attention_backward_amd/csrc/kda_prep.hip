@@ -48,13 +48,26 @@ template <typename T, int D> struct PL {
   static constexpr int TMS_OFF = A_OFF;
   static constexpr int PTS_OFF = TMS_OFF + D * PTM * ES;
   static_assert(PTS_OFF + D * PPT * ES <= B_OFF, "staging fits the dead region");
+  // SCAN: the state tile [D][PSS] and the chunk's dO tile [64][PSS] (act dtype) over the
+  // gate, q, k, Mqk and Kr tiles, all dead once Tm and PT are staged.  32-byte row pads:
+  // the transposing B-operand reads of 8 consecutive rows hit 64 distinct banks.
+  static constexpr int PSS = D + 32 / ES;
+  static constexpr int SS_OFF = 0;
+  static constexpr int SO_OFF = SS_OFF + D * PSS * ES;
+  static_assert(SO_OFF + 64 * PSS * ES <= A_OFF, "scan tiles fit below the staging");
 };
 
 // GV: gate bias present (or its gradient asked for); without it the bias is not read.
 // FWD: the forward's per-chunk operands instead of the backward's (see the end of the
 // item loop).  QN: q and k are L2-normalised per row as they enter LDS (every quantity
 // below is then formed from the normalised rows).
-template <typename T, int D, bool GV, bool FWD, bool QN>
+// SCAN (backward only; every sequence has NCS chunks): the reverse state-gradient scan
+// runs inside this kernel instead of a separate one.  A workgroup owns whole (sequence,
+// head) units and walks each unit's chunks last to first, carrying dS (K x V, fp32, in
+// MFMA accumulators): after a chunk's Tm and PT are staged in LDS it stores dS_out of the
+// chunk and applies dS <- exp(G_T) . dS + Tm dS + PT dO, so Tm, PT and exp(G_T) never
+// go to memory.  dh0 is written after a unit's first chunk.
+template <typename T, int D, bool GV, bool FWD, bool QN, bool SCAN>
 __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ chunks, int NC, int H,
                                                 const T* __restrict__ q, const T* __restrict__ k,
                                                 const float* __restrict__ g_raw,
@@ -67,7 +80,10 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
                                                 T* __restrict__ MqkTo, const T* __restrict__ v,
                                                 T* __restrict__ Wn, T* __restrict__ KrT,
                                                 T* __restrict__ UvT, T* __restrict__ Qd,
-                                                T* __restrict__ Mq) {
+                                                T* __restrict__ Mq, const T* __restrict__ dO,
+                                                const float* __restrict__ dht,
+                                                T* __restrict__ dstates,
+                                                float* __restrict__ dh0, int NCS) {
   using L = PL<T, D>;
   using MM = Mma<T>;
   typedef typename MM::Frag Frag;
@@ -146,9 +162,29 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     settle(rq);
     settle(rk);
   };
-  if ((int)blockIdx.x < items) issue_loads(blockIdx.x, tid0, chunks[blockIdx.x % NC], 15);
+  // the j-th item of this workgroup (item = head * NC + chunk), or -1 past the end.
+  // SCAN: units u = blockIdx.x + k * gridDim.x (u = seq * H + head), chunks last to first.
+  auto item_of = [&](int j) -> int {
+    if constexpr (SCAN) {
+      const int u = (int)blockIdx.x + (j / NCS) * (int)gridDim.x;
+      if (u >= items / NCS) return -1;
+      const int n = u / H, hh = u % H;
+      return hh * NC + n * NCS + (NCS - 1 - j % NCS);
+    } else {
+      const int it = (int)blockIdx.x + j * (int)gridDim.x;
+      return it < items ? it : -1;
+    }
+  };
+  // SCAN: wave w owns the state rows of row group w % 4 and the columns of group w / 4
+  constexpr int SCW = NW / 4, SRT = D / 64, SCT = D / 16 / SCW;
+  constexpr int NLO = 64 * VPR / NT;  // dO vectors per thread
+  f4 sacc[SCAN ? SRT : 1][SCAN ? SCT : 1];
+  const int srg = (tid0 >> 6) & 3, scg = (tid0 >> 6) >> 2;
+  int jj = 0;
+  int first = item_of(0);
+  if (first >= 0) issue_loads(first, tid0, chunks[first % NC], 15);
   settle_loads();
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+  for (int it = first; it >= 0; ++jj) {
   // thread indices re-derived per item so that the lane-dependent LDS addresses
   // below stay inside the loop instead of being held in registers across it
   int tid = tid0;
@@ -157,13 +193,36 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   const int g4 = lane >> 4, cl = lane & 15;
   const int c = it % NC, h = it / NC;
   const int Lr = chunks[c].len;
-  const int nxt = it + (int)gridDim.x;
-  const ChunkInfo cnx = chunks[(nxt < items ? nxt : it) % NC];  // early: scalar-load latency
+  const int nxt = item_of(jj + 1);
+  const ChunkInfo cnx = chunks[(nxt >= 0 ? nxt : it) % NC];  // early: scalar-load latency
   const size_t ch = (size_t)c * H + h;
   const float aA = __expf(A_log[h]) * gu;  // gu: natural-log decay per unit of the gate
   float db = 0.f;
   if constexpr (GV) db = has_db ? rdb : 0.f;
   if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
+  u32x4 rdo[SCAN ? NLO : 1];  // SCAN: this chunk's dO rows (zero past the chunk)
+  if constexpr (SCAN) {
+    const int n = chunks[c].seq;
+    if (chunks[c].cidx == NCS - 1) {  // a unit's last chunk comes first: dS = dht
+      const float* src = dht ? dht + ((size_t)n * H + h) * D * D : nullptr;
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < SCT; ++ct) {
+          const int i0 = (srg * SRT + rt) * 16 + 4 * g4, col = (scg * SCT + ct) * 16 + cl;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sacc[rt][ct][j] = src ? src[(size_t)(i0 + j) * D + col] : 0.f;
+        }
+    }
+    const T* oh = dO + (size_t)chunks[c].t0 * rs + (size_t)h * D;
+#pragma unroll
+    for (int l = 0; l < NLO; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r < Lr) x = *(const u32x4*)(oh + (size_t)r * rs + vv * EPV);
+      rdo[l] = x;
+    }
+  }
   // in-chunk cumulative gate (log2 units), natural: sG[r][i].  Thread (part, i) sums
   // channel i over rows 16 part .. + 15 in registers and publishes the part's total;
   // after the barrier it adds the totals of the earlier parts and writes its rows.
@@ -202,7 +261,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     for (int rr = 0; rr < 16; ++rr) sG[(part * 16 + rr) * PGN + i] = gx[rr] + add;
   }
   __syncthreads();
-  if (nxt < items) issue_loads(nxt, tid, cnx, 1 | 4);  // g_raw rows 0-7, beta, q
+  if (nxt >= 0) issue_loads(nxt, tid, cnx, 1 | 4);  // g_raw rows 0-7, beta, q
 
   // Kr = K exp(G_T - G), beta Kd = beta K exp(G): natural tiles of T
   auto kr_kd = [&](int t, int n) {
@@ -403,7 +462,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   }
   if constexpr (NW == 4) kr_kd(tid, NT);
   __syncthreads();
-  if (nxt < items) issue_loads(nxt, tid, cnx, 2 | 8);  // g_raw rows 8-15, k
+  if (nxt >= 0) issue_loads(nxt, tid, cnx, 2 | 8);  // g_raw rows 8-15, k
   u32x4 rv[NLT];  // forward: this item's v, put into the A tile as beta v once INV is formed
   if constexpr (FWD) {
     const T* vh = v + (size_t)chunks[c].t0 * rs + (size_t)h * D;
@@ -637,6 +696,82 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       store_ct<T>(sPT, PPT, 16 * mt, 16 * w, pt, lane);  // sPT[i][r] = PT[i][r]
     }
   }
+  if constexpr (SCAN) {
+    // exp(G_T) of this lane's state rows, then the state and dO tiles over the dead ones
+    f4 eg[SRT];
+#pragma unroll
+    for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        eg[rt][j] = ex2(sG[63 * PGN + (srg * SRT + rt) * 16 + 4 * g4 + j]);
+    __syncthreads();  // Tm, PT staged; gate, q, k, Mqk and Kr tiles dead
+    T* sS = (T*)(smem + L::SS_OFF);
+    T* sO = (T*)(smem + L::SO_OFF);
+    constexpr int PSS = L::PSS;
+#pragma unroll
+    for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < SCT; ++ct)
+        store_c<T>(sS, PSS, (srg * SRT + rt) * 16, (scg * SCT + ct) * 16, sacc[rt][ct], lane);
+#pragma unroll
+    for (int l = 0; l < NLO; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      *(u32x4*)(sO + r * PSS + vv * EPV) = rdo[l];
+    }
+    __syncthreads();
+    {  // dS_out of this chunk (the state gradient at its end), 16-byte rows
+      T* dst = dstates + ch * D * D;
+#pragma unroll
+      for (int l = 0; l < D * VPR / NT; ++l) {
+        const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+        *(u32x4*)(dst + (size_t)r * D + vv * EPV) = *(const u32x4*)(sS + r * PSS + vv * EPV);
+      }
+    }
+    // dS <- exp(G_T) . dS + Tm dS + PT dO  (A: Tm / PT rows in the permuted k order,
+    // B: the state / dO tile read across its rows in the same order)
+#pragma unroll
+    for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < SCT; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[rt][ct][j] *= eg[rt][j];
+#pragma unroll
+    for (int kk = 0; kk < D / KS; ++kk) {
+      Frag a[SRT];
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt)
+        a[rt] = MM::ld_perm(sTm + ((srg * SRT + rt) * 16 + cl) * PTM, kk * KS, lane);
+#pragma unroll
+      for (int ct = 0; ct < SCT; ++ct) {
+        const Frag b = MM::ld_tr(sS, PSS, kk * KS, (scg * SCT + ct) * 16, lane);
+#pragma unroll
+        for (int rt = 0; rt < SRT; ++rt) sacc[rt][ct] = MM::mma(a[rt], b, sacc[rt][ct]);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKC; ++kk) {
+      Frag a[SRT];
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt)
+        a[rt] = MM::ld_perm(sPT + ((srg * SRT + rt) * 16 + cl) * PPT, kk * KS, lane);
+#pragma unroll
+      for (int ct = 0; ct < SCT; ++ct) {
+        const Frag b = MM::ld_tr(sO, PSS, kk * KS, (scg * SCT + ct) * 16, lane);
+#pragma unroll
+        for (int rt = 0; rt < SRT; ++rt) sacc[rt][ct] = MM::mma(a[rt], b, sacc[rt][ct]);
+      }
+    }
+    if (chunks[c].cidx == 0 && dh0) {  // the unit's first chunk: dh0 = dS
+      float* d0 = dh0 + ((size_t)chunks[c].seq * H + h) * D * D;
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < SCT; ++ct)
+          store_c<float>(d0, D, (srg * SRT + rt) * 16, (scg * SCT + ct) * 16, sacc[rt][ct],
+                         lane);
+    }
+    __syncthreads();  // the next item's gate, q and k tiles overwrite the state and dO tiles
+  } else {
   if (tid < D) eGT[ch * D + tid] = ex2(sG[63 * PGN + tid]);
   __syncthreads();
   {
@@ -655,7 +790,9 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     }
   }
   }
+  }
   // the next item writes sG, sQ, sK and sBeta only: no reader of those is left
+  it = nxt;
   }
 }
 
@@ -664,14 +801,57 @@ static hipError_t prep_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const int items = s.NC * s.H;
   int resident = 0;
   hipError_t e =
-      resident_blocks((const void*)k_prep<T, D, GV, false, QN>, PL<T, D>::NT, &resident);
+      resident_blocks((const void*)k_prep<T, D, GV, false, QN, false>, PL<T, D>::NT, &resident);
   if (e != hipSuccess) return e;
   const int grid = items < resident ? items : resident;
-  hipLaunchKernelGGL((k_prep<T, D, GV, false, QN>), dim3(grid), dim3(PL<T, D>::NT), 0, st,
+  hipLaunchKernelGGL((k_prep<T, D, GV, false, QN, false>), dim3(grid), dim3(PL<T, D>::NT), 0, st,
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, (T*)p.Tm, (T*)p.PT, p.eGT,
-                     (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+                     (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, 0);
   return hipGetLastError();
+}
+
+// prep with the state-gradient scan inside (every sequence has ncs chunks)
+template <typename T, int D, bool GV, bool QN>
+static hipError_t prepscan_v(const Shape& s, const BwdPtrs& p, int ncs, hipStream_t st) {
+  const int units = s.N * s.H;
+  int resident = 0;
+  hipError_t e =
+      resident_blocks((const void*)k_prep<T, D, GV, false, QN, true>, PL<T, D>::NT, &resident);
+  if (e != hipSuccess) return e;
+  const int grid = units < resident ? units : resident;
+  hipLaunchKernelGGL((k_prep<T, D, GV, false, QN, true>), dim3(grid), dim3(PL<T, D>::NT), 0, st,
+                     p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
+                     p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, nullptr,
+                     (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     (const T*)p.dO, p.dht, (T*)p.dstates, p.dh0, ncs);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t prepscan_t(const Shape& s, const BwdPtrs& p, int ncs, hipStream_t st) {
+  const bool gv = p.has_db || p.ddt_bias;
+  if (s.qn)
+    return gv ? prepscan_v<T, D, true, true>(s, p, ncs, st)
+              : prepscan_v<T, D, false, true>(s, p, ncs, st);
+  return gv ? prepscan_v<T, D, true, false>(s, p, ncs, st)
+            : prepscan_v<T, D, false, false>(s, p, ncs, st);
+}
+
+hipError_t launch_prepscan(const Shape& s, const BwdPtrs& p, int ncs, hipStream_t st) {
+  if (s.NC == 0) return hipSuccess;
+  if (s.bf16) return s.D == 128 ? prepscan_t<bf16, 128>(s, p, ncs, st)
+                                : prepscan_t<bf16, 64>(s, p, ncs, st);
+  return prepscan_t<float, 64>(s, p, ncs, st);
+}
+
+hipError_t prepscan_grid(const Shape& s, int* grid) {
+  const void* k = s.bf16 ? (s.D == 128 ? (const void*)k_prep<bf16, 128, false, false, false, true>
+                                       : (const void*)k_prep<bf16, 64, false, false, false, true>)
+                         : (const void*)k_prep<float, 64, false, false, false, true>;
+  const int nt = s.bf16 ? (s.D == 128 ? PL<bf16, 128>::NT : PL<bf16, 64>::NT) : PL<float, 64>::NT;
+  return resident_blocks(k, nt, grid);
 }
 
 template <typename T, int D, bool GV, bool QN>
@@ -679,14 +859,14 @@ static hipError_t fprep_v(const Shape& s, const FwdPtrs& p, hipStream_t st) {
   const int items = s.NC * s.H;
   int resident = 0;
   hipError_t e =
-      resident_blocks((const void*)k_prep<T, D, GV, true, QN>, PL<T, D>::NT, &resident);
+      resident_blocks((const void*)k_prep<T, D, GV, true, QN, false>, PL<T, D>::NT, &resident);
   if (e != hipSuccess) return e;
   const int grid = items < resident ? items : resident;
-  hipLaunchKernelGGL((k_prep<T, D, GV, true, QN>), dim3(grid), dim3(PL<T, D>::NT), 0, st,
+  hipLaunchKernelGGL((k_prep<T, D, GV, true, QN, false>), dim3(grid), dim3(PL<T, D>::NT), 0, st,
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, p.eGT, nullptr,
                      nullptr, (const T*)p.v, (T*)p.Wn, (T*)p.KrT, (T*)p.UvT, (T*)p.Qd,
-                     (T*)p.Mq);
+                     (T*)p.Mq, nullptr, nullptr, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -256,3 +256,36 @@ def test_persistent_walk(name, cap, monkeypatch):
     KC.compare(capped, ref, GRADS + INTER + extra, KC.TOL[inp["dtype"]], label=name + " capped")
     for key in GRADS + ["dstates"] + extra:
         assert np.array_equal(full[key], capped[key]), key
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "weak_decay_bf16", "weak_decay_fp32",
+                                  "multi_ragged_bf16", "qk_norm_fp32", "gate_log2_bf16",
+                                  "single_seq_bf16", "strong_decay_bf16", "qk_norm_bf16_d64"])
+def test_prep_with_scan(name, monkeypatch):
+    """Prep with the reverse state-gradient scan inside (one workgroup per (sequence,
+    head), its chunks last to first; no Tm / PT in memory), forced on for workloads whose
+    sequences all have the same chunk count: gradients, per-chunk dS and dh0 against the
+    oracle."""
+    monkeypatch.setenv("KDA_PREPSCAN", "1")
+    print("\n[case] prep with scan %s" % name, flush=True)
+    _check(name)
+
+
+@pytest.mark.parametrize("name,cap", [("weak_decay_bf16", 3), ("multi_ragged_bf16", 2),
+                                      ("weak_decay_fp32", 2), ("qk_norm_fp32", 3)])
+def test_prep_with_scan_capped(name, cap, monkeypatch):
+    """The same with the grid capped, so that every workgroup walks several units (the
+    state restarts from dht at each unit's last chunk, the next unit's inputs are fetched
+    during the current unit's first chunk): oracle parity, and bit-identical results to
+    the full grid and to the separate prep and scan kernels' per-chunk dS inputs."""
+    monkeypatch.setenv("KDA_PREPSCAN", "1")
+    inp = KI.make_inputs(KI.get_workload(name))
+    print("\n[case] prep with scan %s, grid capped at %d" % (name, cap), flush=True)
+    full = KC.run_gpu(inp)
+    monkeypatch.setenv("KDA_GRID_CAP", str(cap))
+    capped = KC.run_gpu(inp)
+    ref = KC.oracle_for(inp)
+    ref["h_saved"] = ref["states"]
+    KC.compare(capped, ref, GRADS + INTER, KC.TOL[inp["dtype"]], label=name + " capped")
+    for key in GRADS + ["dstates"]:
+        assert np.array_equal(full[key], capped[key]), key
