@@ -462,6 +462,11 @@ int kda_fwd(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t 
   f.Wn = ws + pl.fWn.off; f.KrT = ws + pl.fKrT.off; f.UvT = ws + pl.fUvT.off;
   f.Qd = ws + pl.fQd.off; f.Mq = ws + pl.fMq.off; f.eGT = (float*)(ws + pl.fEgt.off);
   f.o = io->o; f.ht = io->ht; f.h_saved = io->h_saved;
+  if (const int ncs = prepscan_chunks(p, pl.s)) {  // the state scan inside prep
+    e = launch_fprepscan(pl.s, f, ncs, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return KDA_OK;
+  }
   e = launch_fprep(pl.s, f, s);
   if (e != hipSuccess) return hip_fail(e);
   e = launch_fscan(pl.s, f, s);
@@ -536,6 +541,7 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
     f.eGT = b.eGT;  // prep writes the same values again
     f.o = nullptr; f.ht = nullptr; f.h_saved = (void*)b.h_saved;
     e = timed(5, s, [&] {
+      if (const int ncs = prepscan_chunks(p, sh)) return launch_fprepscan(sh, f, ncs, s);
       hipError_t x = launch_fprep(sh, f, s);
       return x == hipSuccess ? launch_fscan(sh, f, s) : x;
     });

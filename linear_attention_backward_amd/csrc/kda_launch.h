@@ -98,7 +98,11 @@ hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st);
 // prep with the reverse state-gradient scan inside (every sequence has ncs chunks): writes
 // INV, Mqk^T, dstates and dh0 instead of Tm, PT and exp(G_T)
 hipError_t launch_prepscan(const Shape& s, const BwdPtrs& p, int ncs, hipStream_t st);
-// workgroups of that kernel the current device holds at once
+// the production forward with the state scan inside prep's forward mode (every sequence
+// has ncs chunks): o, h_saved and ht without the per-chunk operands in memory
+hipError_t launch_fprepscan(const Shape& s, const FwdPtrs& p, int ncs, hipStream_t st);
+// workgroups of the backward one the current device holds at once (the forward one's is
+// the same: same LDS)
 hipError_t prepscan_grid(const Shape& s, int* grid);
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_dalog(const Shape& s, const BwdPtrs& p, hipStream_t st);

@@ -55,18 +55,27 @@ template <typename T, int D> struct PL {
   static constexpr int SS_OFF = 0;
   static constexpr int SO_OFF = SS_OFF + D * PSS * ES;
   static_assert(SO_OFF + 64 * PSS * ES <= A_OFF, "scan tiles fit below the staging");
+  // SCAN in forward mode: the state tile [D][PSS] and the X tile [64][PSS] over the beta v,
+  // INV, Kd and scratch tiles, dead once W and Uv are formed
+  static constexpr int FS_OFF = A_OFF;
+  static constexpr int FX_OFF = FS_OFF + D * PSS * ES;
+  static_assert(FX_OFF + 64 * PSS * ES <= B_OFF, "forward scan tiles fit");
 };
 
 // GV: gate bias present (or its gradient asked for); without it the bias is not read.
 // FWD: the forward's per-chunk operands instead of the backward's (see the end of the
 // item loop).  QN: q and k are L2-normalised per row as they enter LDS (every quantity
 // below is then formed from the normalised rows).
-// SCAN (backward only; every sequence has NCS chunks): the reverse state-gradient scan
-// runs inside this kernel instead of a separate one.  A workgroup owns whole (sequence,
-// head) units and walks each unit's chunks last to first, carrying dS (K x V, fp32, in
-// MFMA accumulators): after a chunk's Tm and PT are staged in LDS it stores dS_out of the
-// chunk and applies dS <- exp(G_T) . dS + Tm dS + PT dO, so Tm, PT and exp(G_T) never
-// go to memory.  dh0 is written after a unit's first chunk.
+// SCAN (every sequence has NCS chunks): the state scan runs inside this kernel instead
+// of a separate one.  A workgroup owns whole (sequence, head) units and walks each unit's
+// chunks, carrying the K x V state in fp32 MFMA accumulators.  Backward: chunks last to
+// first, the state gradient dS from dht: after a chunk's Tm and PT are staged in LDS it
+// stores dS_out of the chunk and applies dS <- exp(G_T) . dS + Tm dS + PT dO, so Tm, PT
+// and exp(G_T) never go to memory; dh0 after a unit's first chunk.  Forward: chunks first
+// to last, the state S from h0: with W and Uv = INV diag(beta) V formed (Uv kept in
+// registers) it stores h_saved, forms X = Uv - W S, O = Qd S + Mqk X and
+// S <- exp(G_T) . S + Kr^T X, and stores O; ht after a unit's last chunk.  In forward
+// mode the scan arguments are reused: dht = h0, dstates = h_saved, dh0 = ht.
 template <typename T, int D, bool GV, bool FWD, bool QN, bool SCAN>
 __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ chunks, int NC, int H,
                                                 const T* __restrict__ q, const T* __restrict__ k,
@@ -83,7 +92,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
                                                 T* __restrict__ Mq, const T* __restrict__ dO,
                                                 const float* __restrict__ dht,
                                                 T* __restrict__ dstates,
-                                                float* __restrict__ dh0, int NCS) {
+                                                float* __restrict__ dh0, int NCS,
+                                                T* __restrict__ o) {
   using L = PL<T, D>;
   using MM = Mma<T>;
   typedef typename MM::Frag Frag;
@@ -169,7 +179,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       const int u = (int)blockIdx.x + (j / NCS) * (int)gridDim.x;
       if (u >= items / NCS) return -1;
       const int n = u / H, hh = u % H;
-      return hh * NC + n * NCS + (NCS - 1 - j % NCS);
+      return hh * NC + n * NCS + (FWD ? j % NCS : NCS - 1 - j % NCS);
     } else {
       const int it = (int)blockIdx.x + j * (int)gridDim.x;
       return it < items ? it : -1;
@@ -203,7 +213,9 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   u32x4 rdo[SCAN ? NLO : 1];  // SCAN: this chunk's dO rows (zero past the chunk)
   if constexpr (SCAN) {
     const int n = chunks[c].seq;
-    if (chunks[c].cidx == NCS - 1) {  // a unit's last chunk comes first: dS = dht
+    // a unit's first chunk in walking order (backward: its last, dS = dht; forward: its
+    // first, S = h0)
+    if (chunks[c].cidx == (FWD ? 0 : NCS - 1)) {
       const float* src = dht ? dht + ((size_t)n * H + h) * D * D : nullptr;
 #pragma unroll
       for (int rt = 0; rt < SRT; ++rt)
@@ -214,13 +226,15 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
           for (int j = 0; j < 4; ++j) sacc[rt][ct][j] = src ? src[(size_t)(i0 + j) * D + col] : 0.f;
         }
     }
-    const T* oh = dO + (size_t)chunks[c].t0 * rs + (size_t)h * D;
+    if constexpr (!FWD) {
+      const T* oh = dO + (size_t)chunks[c].t0 * rs + (size_t)h * D;
 #pragma unroll
-    for (int l = 0; l < NLO; ++l) {
-      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (r < Lr) x = *(const u32x4*)(oh + (size_t)r * rs + vv * EPV);
-      rdo[l] = x;
+      for (int l = 0; l < NLO; ++l) {
+        const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (r < Lr) x = *(const u32x4*)(oh + (size_t)r * rs + vv * EPV);
+        rdo[l] = x;
+      }
     }
   }
   // in-chunk cumulative gate (log2 units), natural: sG[r][i].  Thread (part, i) sums
@@ -576,11 +590,11 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     __syncthreads();  // W formed; beta v in the A tile
     // Uv = INV (beta V), rows of block w % 4, columns [c0, c0 + DH); written as Uv^T
     // straight from the C tiles (a lane holds 4 consecutive rows of one column)
+    const int R = w & 3, c0 = (w >> 2) * DH;
+    constexpr int NTW = DH / 16;
+    f4 acc[NTW];  // Uv: rows 16 R + 4 g4 + j, columns c0 + 16 nt + cl
     {
-      const int R = w & 3, c0 = (w >> 2) * DH;
       const T* sVb = (const T*)(smem + L::A_OFF);
-      constexpr int NTW = DH / 16;
-      f4 acc[NTW];
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) acc[nt] = zero4();
 #pragma unroll
@@ -590,6 +604,113 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
         for (int nt = 0; nt < NTW; ++nt)
           acc[nt] = MM::mma(a, MM::ld_tr(sVb, PN, ks * KS, c0 + nt * 16, lane), acc[nt]);
       }
+    }
+    if constexpr (SCAN) {
+      // exp(G_T) of this lane's state rows
+      f4 eg[SRT];
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          eg[rt][j] = ex2(sG[63 * PGN + (srg * SRT + rt) * 16 + 4 * g4 + j]);
+      // Qd = Q e^G in place over q (each thread its own pieces)
+#pragma unroll
+      for (int l = 0; l < NLT; ++l) {
+        const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+        const u32x4 qv = *(const u32x4*)(sQ + r * PN + vv * EPV);
+        const T* qe = (const T*)&qv;
+        T qd[EPV];
+#pragma unroll
+        for (int j = 0; j < EPV; ++j) qd[j] = from_f<T>(to_f(qe[j]) * ex2(sG[r * PGN + vv * EPV + j]));
+        *(u32x4*)(sQ + r * PN + vv * EPV) = *(const u32x4*)qd;
+      }
+      T* sS = (T*)(smem + L::FS_OFF);
+      T* sX = (T*)(smem + L::FX_OFF);
+      constexpr int PSS = L::PSS;
+      __syncthreads();  // Uv formed: beta v, INV and Kd dead; Qd in place
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < SCT; ++ct)
+          store_c<T>(sS, PSS, (srg * SRT + rt) * 16, (scg * SCT + ct) * 16, sacc[rt][ct], lane);
+      __syncthreads();
+      if (dstates) {  // h_saved: the state at the start of this chunk, 16-byte rows
+        T* dst = dstates + ch * D * D;
+#pragma unroll
+        for (int l = 0; l < D * VPR / NT; ++l) {
+          const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+          *(u32x4*)(dst + (size_t)r * D + vv * EPV) = *(const u32x4*)(sS + r * PSS + vv * EPV);
+        }
+      }
+      // P = W S and the first part of O, Qd S (same B fragments); X = Uv - P
+      f4 P[NTW], Oa[NTW];
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) P[nt] = Oa[nt] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < D / KS; ++kk) {
+        const Frag aw = MM::load(sW + (16 * R + cl) * PN + kk * KS + g4 * KPL);
+        const Frag aq = MM::load(sQ + (16 * R + cl) * PN + kk * KS + g4 * KPL);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const Frag b = MM::ld_tr_nat(sS, PSS, kk * KS, c0 + nt * 16, lane);
+          P[nt] = MM::mma(aw, b, P[nt]);
+          Oa[nt] = MM::mma(aq, b, Oa[nt]);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) store_c<T>(sX, PSS, 16 * R, c0 + nt * 16, acc[nt] - P[nt], lane);
+      __syncthreads();  // X complete; the state tile is dead
+      // O += Mqk X;  S <- exp(G_T) . S + Kr^T X
+#pragma unroll
+      for (int kk = 0; kk < NKC; ++kk) {
+        const Frag am = MM::from_f32(sM + (16 * R + cl) * PC + kk * KS + g4 * KPL);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          Oa[nt] = MM::mma(am, MM::ld_tr_nat(sX, PSS, kk * KS, c0 + nt * 16, lane), Oa[nt]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < SCT; ++ct)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sacc[rt][ct][j] *= eg[rt][j];
+#pragma unroll
+      for (int kk = 0; kk < NKC; ++kk) {
+        Frag ak[SRT];
+#pragma unroll
+        for (int rt = 0; rt < SRT; ++rt) ak[rt] = MM::ld_tr_nat(sKr, PN, kk * KS, (srg * SRT + rt) * 16, lane);
+#pragma unroll
+        for (int ct = 0; ct < SCT; ++ct) {
+          const Frag b = MM::ld_tr_nat(sX, PSS, kk * KS, (scg * SCT + ct) * 16, lane);
+#pragma unroll
+          for (int rt = 0; rt < SRT; ++rt) sacc[rt][ct] = MM::mma(ak[rt], b, sacc[rt][ct]);
+        }
+      }
+      // O staged over the state tile (dead since X was formed), then out
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) store_c<T>(sS, PSS, 16 * R, c0 + nt * 16, Oa[nt], lane);
+      __syncthreads();
+      if (o) {  // rows past the chunk are not part of the sequence
+        T* oh = o + (size_t)chunks[c].t0 * rs + (size_t)h * D;
+#pragma unroll
+        for (int l = 0; l < NLT; ++l) {
+          const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+          if (r < Lr) *(u32x4*)(oh + (size_t)r * rs + vv * EPV) = *(const u32x4*)(sS + r * PSS + vv * EPV);
+        }
+      }
+      if (chunks[c].cidx == NCS - 1 && dh0) {  // ht after the unit's last chunk
+        float* d0 = dh0 + ((size_t)chunks[c].seq * H + h) * D * D;
+#pragma unroll
+        for (int rt = 0; rt < SRT; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < SCT; ++ct)
+            store_c<float>(d0, D, (srg * SRT + rt) * 16, (scg * SCT + ct) * 16, sacc[rt][ct],
+                           lane);
+      }
+      // the O staging is read out before the next item's A/Mqk phase writes over it (two
+      // barriers later); the gate, q and k tiles have no reader left
+    } else {
+    {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         T u4[4];
@@ -614,9 +735,9 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
         wn[j] = from_f<T>(-to_f(we[j]));
         qd[j] = from_f<T>(to_f(qe[j]) * ex2(sG[r * PGN + vv * EPV + j]));
       }
-      const size_t o = ch * 64 * D + (size_t)r * D + vv * EPV;
-      *(u32x4*)(Wn + o) = *(const u32x4*)wn;
-      *(u32x4*)(Qd + o) = *(const u32x4*)qd;
+      const size_t off = ch * 64 * D + (size_t)r * D + vv * EPV;
+      *(u32x4*)(Wn + off) = *(const u32x4*)wn;
+      *(u32x4*)(Qd + off) = *(const u32x4*)qd;
     }
     // Mqk (natural rows) and Kr^T, 8 elements per piece
     for (int e = tid; e < 64 * 8; e += NT) {
@@ -639,6 +760,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     }
     if (tid < D) eGT[ch * D + tid] = ex2(sG[63 * PGN + tid]);
     __syncthreads();  // the next item overwrites sG, sQ and sK (here read as W)
+    }
   } else {
   // ---- INV and Mqk^T (act dtype, natural rows) for the gradient pass (which reads
   // INV^T out of its copy of INV)
@@ -808,7 +930,7 @@ static hipError_t prep_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, (T*)p.Tm, (T*)p.PT, p.eGT,
                      (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, nullptr, nullptr, 0);
+                     nullptr, nullptr, nullptr, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 
@@ -825,7 +947,7 @@ static hipError_t prepscan_v(const Shape& s, const BwdPtrs& p, int ncs, hipStrea
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, nullptr,
                      (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     (const T*)p.dO, p.dht, (T*)p.dstates, p.dh0, ncs);
+                     (const T*)p.dO, p.dht, (T*)p.dstates, p.dh0, ncs, nullptr);
   return hipGetLastError();
 }
 
@@ -844,6 +966,39 @@ hipError_t launch_prepscan(const Shape& s, const BwdPtrs& p, int ncs, hipStream_
   if (s.bf16) return s.D == 128 ? prepscan_t<bf16, 128>(s, p, ncs, st)
                                 : prepscan_t<bf16, 64>(s, p, ncs, st);
   return prepscan_t<float, 64>(s, p, ncs, st);
+}
+
+// the production forward in one kernel: prep in forward mode with the state scan inside
+template <typename T, int D, bool GV, bool QN>
+static hipError_t fprepscan_v(const Shape& s, const FwdPtrs& p, int ncs, hipStream_t st) {
+  const int units = s.N * s.H;
+  int resident = 0;
+  hipError_t e =
+      resident_blocks((const void*)k_prep<T, D, GV, true, QN, true>, PL<T, D>::NT, &resident);
+  if (e != hipSuccess) return e;
+  const int grid = units < resident ? units : resident;
+  hipLaunchKernelGGL((k_prep<T, D, GV, true, QN, true>), dim3(grid), dim3(PL<T, D>::NT), 0, st,
+                     p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
+                     p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, (const T*)p.v, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, p.h0, (T*)p.h_saved, p.ht, ncs, (T*)p.o);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t fprepscan_t(const Shape& s, const FwdPtrs& p, int ncs, hipStream_t st) {
+  if (s.qn)
+    return p.has_db ? fprepscan_v<T, D, true, true>(s, p, ncs, st)
+                    : fprepscan_v<T, D, false, true>(s, p, ncs, st);
+  return p.has_db ? fprepscan_v<T, D, true, false>(s, p, ncs, st)
+                  : fprepscan_v<T, D, false, false>(s, p, ncs, st);
+}
+
+hipError_t launch_fprepscan(const Shape& s, const FwdPtrs& p, int ncs, hipStream_t st) {
+  if (s.NC == 0) return hipSuccess;
+  if (s.bf16) return s.D == 128 ? fprepscan_t<bf16, 128>(s, p, ncs, st)
+                                : fprepscan_t<bf16, 64>(s, p, ncs, st);
+  return fprepscan_t<float, 64>(s, p, ncs, st);
 }
 
 hipError_t prepscan_grid(const Shape& s, int* grid) {
@@ -866,7 +1021,7 @@ static hipError_t fprep_v(const Shape& s, const FwdPtrs& p, hipStream_t st) {
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, p.eGT, nullptr,
                      nullptr, (const T*)p.v, (T*)p.Wn, (T*)p.KrT, (T*)p.UvT, (T*)p.Qd,
-                     (T*)p.Mq, nullptr, nullptr, nullptr, nullptr, 0);
+                     (T*)p.Mq, nullptr, nullptr, nullptr, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 

@@ -289,3 +289,49 @@ def test_prep_with_scan_capped(name, cap, monkeypatch):
     KC.compare(capped, ref, GRADS + INTER, KC.TOL[inp["dtype"]], label=name + " capped")
     for key in GRADS + ["dstates"]:
         assert np.array_equal(full[key], capped[key]), key
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "weak_decay_bf16", "weak_decay_fp32",
+                                  "multi_ragged_bf16", "qk_norm_fp32", "gate_log2_bf16",
+                                  "single_seq_bf16", "strong_decay_bf16", "qk_norm_bf16_d64"])
+def test_forward_with_scan(name, monkeypatch):
+    """The production forward in one kernel (prep's forward mode carrying the state:
+    X = Uv - W S, O = Qd S + Mqk X, S <- e^{G_T} S + Kr^T X per chunk, no per-chunk operands
+    in memory), forced on for workloads with equal chunk counts per sequence: o, ht and the
+    chunk-start states against the oracle's per-token recurrence."""
+    monkeypatch.setenv("KDA_PREPSCAN", "1")
+    print("\n[case] forward with scan %s" % name, flush=True)
+    inp = KI.make_inputs(KI.get_workload(name))
+    res = KC.run_gpu_fwd(inp)
+    ref = KC.oracle_fwd_for(inp)
+    ref["h_saved"] = ref["states"]
+    rep = KC.compare(res, ref, ["o", "ht", "h_saved"], KC.TOL[inp["dtype"]],
+                     label="forward with scan " + name)
+    print("[errors] " + " ".join("%s=%.2e" % kv for kv in rep.items()), flush=True)
+
+
+@pytest.mark.parametrize("name,cap", [("weak_decay_bf16", 3), ("multi_ragged_bf16", 2),
+                                      ("qk_norm_fp32", 3)])
+def test_forward_with_scan_capped(name, cap, monkeypatch):
+    """The same with several units per workgroup (the state restarts from h0 at each
+    unit's first chunk): oracle parity and bit-identical results to the full grid."""
+    monkeypatch.setenv("KDA_PREPSCAN", "1")
+    inp = KI.make_inputs(KI.get_workload(name))
+    print("\n[case] forward with scan %s, grid capped at %d" % (name, cap), flush=True)
+    full = KC.run_gpu_fwd(inp)
+    monkeypatch.setenv("KDA_GRID_CAP", str(cap))
+    capped = KC.run_gpu_fwd(inp)
+    ref = KC.oracle_fwd_for(inp)
+    ref["h_saved"] = ref["states"]
+    KC.compare(capped, ref, ["o", "ht", "h_saved"], KC.TOL[inp["dtype"]], label=name + " capped")
+    for key in ("o", "ht", "h_saved"):
+        assert np.array_equal(full[key], capped[key]), key
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "weak_decay_bf16", "qk_norm_fp32"])
+def test_recompute_with_scans_in_prep(name, monkeypatch):
+    """kda_bwd without h_saved with both scans inside prep: the fused forward recomputes
+    the chunk-start states, the fused backward carries dS."""
+    monkeypatch.setenv("KDA_PREPSCAN", "1")
+    print("\n[case] recompute, scans inside prep, %s" % name, flush=True)
+    _check(name, use_h_saved=False)
