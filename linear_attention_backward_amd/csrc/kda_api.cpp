@@ -31,7 +31,7 @@ struct Plan {
   int64_t NC = 0;
   size_t es = 0;  // bytes per act element
   // workspace regions
-  Region chunks, seq_off, qn, kn, rq, rk, groups, grp_off, Tm, PT, eGT, INV, MqkT, dstates, dAl,
+  Region chunks, seq_off, order, qn, kn, rq, rk, groups, grp_off, Tm, PT, eGT, INV, MqkT, dstates, dAl,
       ddt, Pg, Qg, bnd, hsaved;
   Region fWn, fKrT, fUvT, fQd, fMq, fEgt;  // production forward (from fwd_bytes on)
   Region fgroups, fgrp_off, fPg, fQg, fbnd;
@@ -76,29 +76,43 @@ int scan_group_size(const kda_problem* p, int N) {
   return mx > 128 ? 64 : 0;
 }
 
-// Chunks of every sequence when all sequences have the same number (>= 1), else 0.
-int64_t uniform_chunks(const kda_problem* p, int N) {
-  const int64_t first = seq_chunks(p, 0);
-  for (int n = 1; n < N; ++n)
-    if (seq_chunks(p, n) != first) return 0;
-  return first;
-}
-
-// Whether prep runs the state-gradient scan itself (one workgroup per (sequence, head)
-// unit, its chunks last to first): every sequence must have the same chunk count, and the
-// units must spread evenly over the resident workgroups.  KDA_PREPSCAN=0 / 1 forces the
-// separate kernels / the fused one (when the chunk counts allow it).
-int prepscan_chunks(const kda_problem* p, const Shape& s) {
-  const int64_t ncs = uniform_chunks(p, s.N);
-  if (ncs <= 0) return 0;
+// Whether prep runs the state scans itself (one workgroup per (sequence, head) unit at a
+// time, walking its chunks).  The units, sorted by chunk count (longest first), are dealt
+// to the resident workgroups in a snake; that is used when every sequence has at least
+// one chunk, there are at least as many units as workgroups, and the busiest workgroup's
+// chunk count stays within 10% of the mean (the train workload: 256 units of 64 chunks on
+// 256 workgroups, exactly the mean; the varlen workload: 137 against 129).  Otherwise the
+// separate per-chunk pass and scan kernels, which spread single chunks over the GPU, are
+// better balanced.  KDA_PREPSCAN=0 / 1 forces the separate kernels / the fused ones (when
+// every sequence has a chunk).
+bool use_prepscan(const kda_problem* p, const Shape& s) {
+  if (s.N < 1 || s.N > kMaxOrderSeqs) return false;
+  std::vector<int> nck(s.N);
+  for (int n = 0; n < s.N; ++n) {
+    nck[n] = (int)seq_chunks(p, n);
+    if (nck[n] < 1) return false;
+  }
   if (const char* env = std::getenv("KDA_PREPSCAN")) {
-    if (env[0] == '0') return 0;
-    if (env[0] == '1') return (int)ncs;
+    if (env[0] == '0') return false;
+    if (env[0] == '1') return true;
   }
   int grid = 0;
-  if (prepscan_grid(s, &grid) != hipSuccess || grid <= 0) return 0;
+  if (prepscan_grid(s, &grid) != hipSuccess || grid <= 0) return false;
   const int64_t units = (int64_t)s.N * s.H;
-  return units >= grid && (units % grid == 0 || units >= 8 * (int64_t)grid) ? (int)ncs : 0;
+  if (units < grid) return false;
+  std::vector<int> order(s.N);
+  for (int n = 0; n < s.N; ++n) order[n] = n;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return nck[a] > nck[b]; });
+  std::vector<int64_t> load(grid, 0);
+  int64_t total = 0;
+  for (int64_t pos = 0; pos < units; ++pos) {
+    const int64_t k = pos / grid, r = pos % grid;
+    const int64_t g = (k & 1) ? grid - 1 - r : r;
+    load[g] += nck[order[pos / s.H]];
+    total += nck[order[pos / s.H]];
+  }
+  const int64_t mx = *std::max_element(load.begin(), load.end());
+  return (double)mx <= 1.1 * (double)total / grid;
 }
 
 int validate_problem(const kda_problem* p) {
@@ -162,6 +176,7 @@ int make_plan(const kda_problem* p, Plan* pl) {
   };
   take(pl->chunks, (size_t)pl->NC * sizeof(ChunkInfo));
   take(pl->seq_off, ((size_t)s.N + 1) * sizeof(int));
+  take(pl->order, (size_t)s.N * sizeof(int));  // sequences by chunk count (scans in prep)
   const size_t common = off;
   // the reference forward normalises q, k (qk_l2norm) into copies; kda_bwd and kda_fwd
   // normalise inside their kernels and do not use these regions
@@ -450,8 +465,10 @@ int kda_fwd(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t 
   f.Pg = ws + pl.fPg.off;
   f.Qg = (float*)(ws + pl.fQg.off);
   f.bnd = (float*)(ws + pl.fbnd.off);
+  const bool fused = use_prepscan(p, pl.s);
+  int* order = fused ? (int*)(ws + pl.order.off) : nullptr;
   hipError_t e = launch_chunk_table(pl.s, (ChunkInfo*)f.chunks, (int*)f.seq_off,
-                                    (GroupInfo*)f.groups, (int*)f.grp_off, s);
+                                    (GroupInfo*)f.groups, (int*)f.grp_off, s, order);
   if (e != hipSuccess) return hip_fail(e);
   f.q = io->q;  // raw: with qk_l2norm the per-chunk pass normalises the rows itself
   f.k = io->k;
@@ -462,8 +479,8 @@ int kda_fwd(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t 
   f.Wn = ws + pl.fWn.off; f.KrT = ws + pl.fKrT.off; f.UvT = ws + pl.fUvT.off;
   f.Qd = ws + pl.fQd.off; f.Mq = ws + pl.fMq.off; f.eGT = (float*)(ws + pl.fEgt.off);
   f.o = io->o; f.ht = io->ht; f.h_saved = io->h_saved;
-  if (const int ncs = prepscan_chunks(p, pl.s)) {  // the state scan inside prep
-    e = launch_fprepscan(pl.s, f, ncs, s);
+  if (fused) {  // the state scan inside prep
+    e = launch_fprepscan(pl.s, f, order, s);
     if (e != hipSuccess) return hip_fail(e);
     return KDA_OK;
   }
@@ -523,9 +540,11 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   b.bnd = (float*)(ws + pl.bnd.off);
   const Shape& sh = pl.s;
   hipError_t e;
+  const bool fused = use_prepscan(p, pl.s);
+  int* order = fused ? (int*)(ws + pl.order.off) : nullptr;
   e = timed(0, s, [&] {
     return launch_chunk_table(sh, (ChunkInfo*)b.chunks, (int*)b.seq_off, (GroupInfo*)b.groups,
-                              (int*)b.grp_off, s);
+                              (int*)b.grp_off, s, order);
   });
   if (e != hipSuccess) return hip_fail(e);
   if (!io->h_saved) {  // the chunk-start states by the production forward
@@ -541,14 +560,14 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
     f.eGT = b.eGT;  // prep writes the same values again
     f.o = nullptr; f.ht = nullptr; f.h_saved = (void*)b.h_saved;
     e = timed(5, s, [&] {
-      if (const int ncs = prepscan_chunks(p, sh)) return launch_fprepscan(sh, f, ncs, s);
+      if (fused) return launch_fprepscan(sh, f, order, s);
       hipError_t x = launch_fprep(sh, f, s);
       return x == hipSuccess ? launch_fscan(sh, f, s) : x;
     });
     if (e != hipSuccess) return hip_fail(e);
   }
-  if (const int ncs = prepscan_chunks(p, sh)) {  // prep with the scan inside
-    e = timed(1, s, [&] { return launch_prepscan(sh, b, ncs, s); });
+  if (fused) {  // prep with the scan inside
+    e = timed(1, s, [&] { return launch_prepscan(sh, b, order, s); });
     if (e != hipSuccess) return hip_fail(e);
   } else {
     e = timed(1, s, [&] { return launch_prep(sh, b, s); });

@@ -17,8 +17,10 @@ __global__ __launch_bounds__(256) void k_chunk_table(const int32_t* __restrict__
                                                      int gs, ChunkInfo* __restrict__ tab,
                                                      int* __restrict__ seq_off,
                                                      GroupInfo* __restrict__ groups,
-                                                     int* __restrict__ grp_off) {
+                                                     int* __restrict__ grp_off,
+                                                     int* __restrict__ order) {
   __shared__ int part[256], gpart[256];
+  __shared__ int snck[kMaxOrderSeqs];
   const int tid = threadIdx.x;
   const int per = (N + 255) / 256;
   const int n0 = min(N, tid * per), n1 = min(N, n0 + per);
@@ -81,6 +83,17 @@ __global__ __launch_bounds__(256) void k_chunk_table(const int32_t* __restrict__
   if (N == 0 && tid == 0) {
     seq_off[0] = 0;
     if (groups) grp_off[0] = 0;
+  }
+  if (order && N <= kMaxOrderSeqs) {
+    // the sequences sorted by chunk count, longest first (ties by index): order[rank] = n
+    for (int n = tid; n < N; n += 256) snck[n] = nchunks(n);
+    __syncthreads();
+    for (int n = tid; n < N; n += 256) {
+      const int a = snck[n];
+      int rank = 0;
+      for (int m = 0; m < N; ++m) rank += snck[m] > a || (snck[m] == a && m < n);
+      order[rank] = n;
+    }
   }
 }
 
@@ -264,9 +277,9 @@ __global__ __launch_bounds__(256) void k_ddt(const float* __restrict__ part, int
 }
 
 hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, GroupInfo* groups,
-                              int* grp_off, hipStream_t st) {
+                              int* grp_off, hipStream_t st, int* order) {
   hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, st, s.cu, s.N, s.T, s.gs, tab, seq_off,
-                     groups, grp_off);
+                     groups, grp_off, order);
   return hipGetLastError();
 }
 

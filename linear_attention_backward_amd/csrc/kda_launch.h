@@ -77,8 +77,11 @@ struct Shape {
   int qn;          // q and k L2-normalised inside the kernels (prep, gradient pass)
 };
 
+// order (optional, N ints): the sequences sorted by chunk count, longest first, for the
+// scans inside prep (at most kMaxOrderSeqs sequences)
+constexpr int kMaxOrderSeqs = 4096;
 hipError_t launch_chunk_table(const Shape& s, ChunkInfo* tab, int* seq_off, GroupInfo* groups,
-                              int* grp_off, hipStream_t st);
+                              int* grp_off, hipStream_t st, int* order = nullptr);
 hipError_t launch_fwd_ref(const Shape& s, const int* seq_off, const void* q, const void* k,
                           const void* v, const float* g_raw, const float* beta,
                           const float* A_log, const float* dt_bias, const float* h0, void* o,
@@ -95,12 +98,13 @@ hipError_t launch_prep(const Shape& s, const BwdPtrs& p, hipStream_t st);
 hipError_t launch_fprep(const Shape& s, const FwdPtrs& p, hipStream_t st);
 hipError_t launch_fscan(const Shape& s, const FwdPtrs& p, hipStream_t st);
 hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st);
-// prep with the reverse state-gradient scan inside (every sequence has ncs chunks): writes
-// INV, Mqk^T, dstates and dh0 instead of Tm, PT and exp(G_T)
-hipError_t launch_prepscan(const Shape& s, const BwdPtrs& p, int ncs, hipStream_t st);
-// the production forward with the state scan inside prep's forward mode (every sequence
-// has ncs chunks): o, h_saved and ht without the per-chunk operands in memory
-hipError_t launch_fprepscan(const Shape& s, const FwdPtrs& p, int ncs, hipStream_t st);
+// prep with the reverse state-gradient scan inside (every sequence has at least one chunk;
+// workgroups take (sequence, head) units from the chunk-count order `order` in a snake):
+// writes INV, Mqk^T, dstates and dh0 instead of Tm, PT and exp(G_T)
+hipError_t launch_prepscan(const Shape& s, const BwdPtrs& p, const int* order, hipStream_t st);
+// the production forward with the state scan inside prep's forward mode (same conditions):
+// o, h_saved and ht without the per-chunk operands in memory
+hipError_t launch_fprepscan(const Shape& s, const FwdPtrs& p, const int* order, hipStream_t st);
 // workgroups of the backward one the current device holds at once (the forward one's is
 // the same: same LDS)
 hipError_t prepscan_grid(const Shape& s, int* grid);

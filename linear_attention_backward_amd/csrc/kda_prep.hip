@@ -66,9 +66,12 @@ template <typename T, int D> struct PL {
 // FWD: the forward's per-chunk operands instead of the backward's (see the end of the
 // item loop).  QN: q and k are L2-normalised per row as they enter LDS (every quantity
 // below is then formed from the normalised rows).
-// SCAN (every sequence has NCS chunks): the state scan runs inside this kernel instead
-// of a separate one.  A workgroup owns whole (sequence, head) units and walks each unit's
-// chunks, carrying the K x V state in fp32 MFMA accumulators.  Backward: chunks last to
+// SCAN (every sequence has at least one chunk): the state scan runs inside this kernel
+// instead of a separate one.  A workgroup owns whole (sequence, head) units and walks
+// each unit's chunks, carrying the K x V state in fp32 MFMA accumulators.  The units,
+// sorted by chunk count (longest first: `order` holds the sequences in that order, heads
+// fastest), are dealt to the workgroups in a snake: unit k of workgroup g is position
+// k G + g for even k and k G + G - 1 - g for odd k, which pairs long units with short ones.  Backward: chunks last to
 // first, the state gradient dS from dht: after a chunk's Tm and PT are staged in LDS it
 // stores dS_out of the chunk and applies dS <- exp(G_T) . dS + Tm dS + PT dO, so Tm, PT
 // and exp(G_T) never go to memory; dh0 after a unit's first chunk.  Forward: chunks first
@@ -92,7 +95,9 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
                                                 T* __restrict__ Mq, const T* __restrict__ dO,
                                                 const float* __restrict__ dht,
                                                 T* __restrict__ dstates,
-                                                float* __restrict__ dh0, int NCS,
+                                                float* __restrict__ dh0,
+                                                const int* __restrict__ seq_off,
+                                                const int* __restrict__ order, int NS,
                                                 T* __restrict__ o) {
   using L = PL<T, D>;
   using MM = Mma<T>;
@@ -172,29 +177,62 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     settle(rq);
     settle(rk);
   };
-  // the j-th item of this workgroup (item = head * NC + chunk), or -1 past the end.
-  // SCAN: units u = blockIdx.x + k * gridDim.x (u = seq * H + head), chunks last to first.
-  auto item_of = [&](int j) -> int {
-    if constexpr (SCAN) {
-      const int u = (int)blockIdx.x + (j / NCS) * (int)gridDim.x;
-      if (u >= items / NCS) return -1;
-      const int n = u / H, hh = u % H;
-      return hh * NC + n * NCS + (FWD ? j % NCS : NCS - 1 - j % NCS);
-    } else {
-      const int it = (int)blockIdx.x + j * (int)gridDim.x;
-      return it < items ? it : -1;
+  // Items (item = head * NC + chunk) in this workgroup's order.  Without SCAN: items
+  // blockIdx.x, + gridDim.x, ...  With SCAN: a cursor over its units (k) and the chunk
+  // (cl, local to the sequence; first to last forward, last to first backward).
+  struct Cursor {
+    int it, k, n, hh, cl, nck;
+  };
+  auto unit_at = [&](Cursor& cu, int k) -> bool {  // unit k of this workgroup, if any
+    const int G = (int)gridDim.x, g = (int)blockIdx.x;
+    for (;; ++k) {
+      const int p = k * G + ((k & 1) ? G - 1 - g : g);
+      if (p >= NS * H) return false;
+      const int n = order[p / H];
+      const int nck = seq_off[n + 1] - seq_off[n];
+      if (nck == 0) continue;
+      cu.k = k;
+      cu.n = n;
+      cu.hh = p % H;
+      cu.nck = nck;
+      cu.cl = FWD ? 0 : nck - 1;
+      cu.it = cu.hh * NC + seq_off[n] + cu.cl;
+      return true;
     }
+  };
+  auto first_item = [&](Cursor& cu) -> void {
+    if constexpr (SCAN) {
+      if (!unit_at(cu, 0)) cu.it = -1;
+    } else {
+      cu.it = (int)blockIdx.x < items ? (int)blockIdx.x : -1;
+    }
+  };
+  auto next_item = [&](Cursor cu) -> Cursor {
+    if constexpr (SCAN) {
+      if (FWD ? cu.cl + 1 < cu.nck : cu.cl > 0) {
+        cu.cl += FWD ? 1 : -1;
+        cu.it = cu.hh * NC + seq_off[cu.n] + cu.cl;
+      } else if (!unit_at(cu, cu.k + 1)) {
+        cu.it = -1;
+      }
+    } else {
+      cu.it = cu.it + (int)gridDim.x < items ? cu.it + (int)gridDim.x : -1;
+    }
+    return cu;
   };
   // SCAN: wave w owns the state rows of row group w % 4 and the columns of group w / 4
   constexpr int SCW = NW / 4, SRT = D / 64, SCT = D / 16 / SCW;
   constexpr int NLO = 64 * VPR / NT;  // dO vectors per thread
   f4 sacc[SCAN ? SRT : 1][SCAN ? SCT : 1];
   const int srg = (tid0 >> 6) & 3, scg = (tid0 >> 6) >> 2;
-  int jj = 0;
-  int first = item_of(0);
-  if (first >= 0) issue_loads(first, tid0, chunks[first % NC], 15);
+  Cursor cur;
+  first_item(cur);
+  if (cur.it >= 0) issue_loads(cur.it, tid0, chunks[cur.it % NC], 15);
   settle_loads();
-  for (int it = first; it >= 0; ++jj) {
+  for (; cur.it >= 0;) {
+  const int it = cur.it;
+  const Cursor ncur = next_item(cur);
+  const int nxt = ncur.it;
   // thread indices re-derived per item so that the lane-dependent LDS addresses
   // below stay inside the loop instead of being held in registers across it
   int tid = tid0;
@@ -203,7 +241,6 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   const int g4 = lane >> 4, cl = lane & 15;
   const int c = it % NC, h = it / NC;
   const int Lr = chunks[c].len;
-  const int nxt = item_of(jj + 1);
   const ChunkInfo cnx = chunks[(nxt >= 0 ? nxt : it) % NC];  // early: scalar-load latency
   const size_t ch = (size_t)c * H + h;
   const float aA = __expf(A_log[h]) * gu;  // gu: natural-log decay per unit of the gate
@@ -215,7 +252,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     const int n = chunks[c].seq;
     // a unit's first chunk in walking order (backward: its last, dS = dht; forward: its
     // first, S = h0)
-    if (chunks[c].cidx == (FWD ? 0 : NCS - 1)) {
+    if (chunks[c].cidx == (FWD ? 0 : cur.nck - 1)) {
       const float* src = dht ? dht + ((size_t)n * H + h) * D * D : nullptr;
 #pragma unroll
       for (int rt = 0; rt < SRT; ++rt)
@@ -698,7 +735,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
           if (r < Lr) *(u32x4*)(oh + (size_t)r * rs + vv * EPV) = *(const u32x4*)(sS + r * PSS + vv * EPV);
         }
       }
-      if (chunks[c].cidx == NCS - 1 && dh0) {  // ht after the unit's last chunk
+      if (chunks[c].cidx == cur.nck - 1 && dh0) {  // ht after the sequence's last chunk
         float* d0 = dh0 + ((size_t)chunks[c].seq * H + h) * D * D;
 #pragma unroll
         for (int rt = 0; rt < SRT; ++rt)
@@ -883,7 +920,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
         for (int rt = 0; rt < SRT; ++rt) sacc[rt][ct] = MM::mma(a[rt], b, sacc[rt][ct]);
       }
     }
-    if (chunks[c].cidx == 0 && dh0) {  // the unit's first chunk: dh0 = dS
+    if (chunks[c].cidx == 0 && dh0) {  // the sequence's first chunk: dh0 = dS
       float* d0 = dh0 + ((size_t)chunks[c].seq * H + h) * D * D;
 #pragma unroll
       for (int rt = 0; rt < SRT; ++rt)
@@ -914,7 +951,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   }
   }
   // the next item writes sG, sQ, sK and sBeta only: no reader of those is left
-  it = nxt;
+  cur = ncur;
   }
 }
 
@@ -930,13 +967,14 @@ static hipError_t prep_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, (T*)p.Tm, (T*)p.PT, p.eGT,
                      (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, nullptr, nullptr, 0, nullptr);
+                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 
 // prep with the state-gradient scan inside (every sequence has ncs chunks)
 template <typename T, int D, bool GV, bool QN>
-static hipError_t prepscan_v(const Shape& s, const BwdPtrs& p, int ncs, hipStream_t st) {
+static hipError_t prepscan_v(const Shape& s, const BwdPtrs& p, const int* order,
+                             hipStream_t st) {
   const int units = s.N * s.H;
   int resident = 0;
   hipError_t e =
@@ -947,30 +985,33 @@ static hipError_t prepscan_v(const Shape& s, const BwdPtrs& p, int ncs, hipStrea
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, nullptr,
                      (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     (const T*)p.dO, p.dht, (T*)p.dstates, p.dh0, ncs, nullptr);
+                     (const T*)p.dO, p.dht, (T*)p.dstates, p.dh0, p.seq_off, order, s.N,
+                     nullptr);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t prepscan_t(const Shape& s, const BwdPtrs& p, int ncs, hipStream_t st) {
+static hipError_t prepscan_t(const Shape& s, const BwdPtrs& p, const int* order,
+                             hipStream_t st) {
   const bool gv = p.has_db || p.ddt_bias;
   if (s.qn)
-    return gv ? prepscan_v<T, D, true, true>(s, p, ncs, st)
-              : prepscan_v<T, D, false, true>(s, p, ncs, st);
-  return gv ? prepscan_v<T, D, true, false>(s, p, ncs, st)
-            : prepscan_v<T, D, false, false>(s, p, ncs, st);
+    return gv ? prepscan_v<T, D, true, true>(s, p, order, st)
+              : prepscan_v<T, D, false, true>(s, p, order, st);
+  return gv ? prepscan_v<T, D, true, false>(s, p, order, st)
+            : prepscan_v<T, D, false, false>(s, p, order, st);
 }
 
-hipError_t launch_prepscan(const Shape& s, const BwdPtrs& p, int ncs, hipStream_t st) {
+hipError_t launch_prepscan(const Shape& s, const BwdPtrs& p, const int* order, hipStream_t st) {
   if (s.NC == 0) return hipSuccess;
-  if (s.bf16) return s.D == 128 ? prepscan_t<bf16, 128>(s, p, ncs, st)
-                                : prepscan_t<bf16, 64>(s, p, ncs, st);
-  return prepscan_t<float, 64>(s, p, ncs, st);
+  if (s.bf16) return s.D == 128 ? prepscan_t<bf16, 128>(s, p, order, st)
+                                : prepscan_t<bf16, 64>(s, p, order, st);
+  return prepscan_t<float, 64>(s, p, order, st);
 }
 
 // the production forward in one kernel: prep in forward mode with the state scan inside
 template <typename T, int D, bool GV, bool QN>
-static hipError_t fprepscan_v(const Shape& s, const FwdPtrs& p, int ncs, hipStream_t st) {
+static hipError_t fprepscan_v(const Shape& s, const FwdPtrs& p, const int* order,
+                              hipStream_t st) {
   const int units = s.N * s.H;
   int resident = 0;
   hipError_t e =
@@ -981,24 +1022,25 @@ static hipError_t fprepscan_v(const Shape& s, const FwdPtrs& p, int ncs, hipStre
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, nullptr, nullptr,
                      nullptr, (const T*)p.v, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, p.h0, (T*)p.h_saved, p.ht, ncs, (T*)p.o);
+                     nullptr, p.h0, (T*)p.h_saved, p.ht, p.seq_off, order, s.N, (T*)p.o);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t fprepscan_t(const Shape& s, const FwdPtrs& p, int ncs, hipStream_t st) {
+static hipError_t fprepscan_t(const Shape& s, const FwdPtrs& p, const int* order,
+                              hipStream_t st) {
   if (s.qn)
-    return p.has_db ? fprepscan_v<T, D, true, true>(s, p, ncs, st)
-                    : fprepscan_v<T, D, false, true>(s, p, ncs, st);
-  return p.has_db ? fprepscan_v<T, D, true, false>(s, p, ncs, st)
-                  : fprepscan_v<T, D, false, false>(s, p, ncs, st);
+    return p.has_db ? fprepscan_v<T, D, true, true>(s, p, order, st)
+                    : fprepscan_v<T, D, false, true>(s, p, order, st);
+  return p.has_db ? fprepscan_v<T, D, true, false>(s, p, order, st)
+                  : fprepscan_v<T, D, false, false>(s, p, order, st);
 }
 
-hipError_t launch_fprepscan(const Shape& s, const FwdPtrs& p, int ncs, hipStream_t st) {
+hipError_t launch_fprepscan(const Shape& s, const FwdPtrs& p, const int* order, hipStream_t st) {
   if (s.NC == 0) return hipSuccess;
-  if (s.bf16) return s.D == 128 ? fprepscan_t<bf16, 128>(s, p, ncs, st)
-                                : fprepscan_t<bf16, 64>(s, p, ncs, st);
-  return fprepscan_t<float, 64>(s, p, ncs, st);
+  if (s.bf16) return s.D == 128 ? fprepscan_t<bf16, 128>(s, p, order, st)
+                                : fprepscan_t<bf16, 64>(s, p, order, st);
+  return fprepscan_t<float, 64>(s, p, order, st);
 }
 
 hipError_t prepscan_grid(const Shape& s, int* grid) {
@@ -1021,7 +1063,7 @@ static hipError_t fprep_v(const Shape& s, const FwdPtrs& p, hipStream_t st) {
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, p.eGT, nullptr,
                      nullptr, (const T*)p.v, (T*)p.Wn, (T*)p.KrT, (T*)p.UvT, (T*)p.Qd,
-                     (T*)p.Mq, nullptr, nullptr, nullptr, nullptr, 0, nullptr);
+                     (T*)p.Mq, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 

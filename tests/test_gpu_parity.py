@@ -247,6 +247,9 @@ def test_persistent_walk(name, cap, monkeypatch):
     full grid (an item's arithmetic does not depend on which workgroup runs it)."""
     inp = KI.make_inputs(KI.get_workload(name))
     print("\n[case] persistent walk %s, grid capped at %d" % (name, cap), flush=True)
+    # the separate prep and scan kernels in both runs (a capped grid can make the scans
+    # inside prep eligible; they have capped-grid tests of their own)
+    monkeypatch.setenv("KDA_PREPSCAN", "0")
     full = KC.run_gpu(inp)
     monkeypatch.setenv("KDA_GRID_CAP", str(cap))
     capped = KC.run_gpu(inp)
@@ -258,21 +261,26 @@ def test_persistent_walk(name, cap, monkeypatch):
         assert np.array_equal(full[key], capped[key]), key
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "weak_decay_bf16", "weak_decay_fp32",
-                                  "multi_ragged_bf16", "qk_norm_fp32", "gate_log2_bf16",
-                                  "single_seq_bf16", "strong_decay_bf16", "qk_norm_bf16_d64"])
+FUSED = ["tiny_fp32", "weak_decay_bf16", "weak_decay_fp32", "multi_ragged_bf16", "qk_norm_fp32",
+         "gate_log2_bf16", "single_seq_bf16", "strong_decay_bf16", "qk_norm_bf16_d64",
+         # packed sequences of different lengths (units sorted by chunk count, snake order)
+         "ragged_bf16", "ragged_fp32", "ragged_bf16_d64", "gate_bias_bf16", "gate_log2_fp32",
+         "qk_norm_bf16"]
+
+
+@pytest.mark.parametrize("name", FUSED)
 def test_prep_with_scan(name, monkeypatch):
     """Prep with the reverse state-gradient scan inside (one workgroup per (sequence,
-    head), its chunks last to first; no Tm / PT in memory), forced on for workloads whose
-    sequences all have the same chunk count: gradients, per-chunk dS and dh0 against the
-    oracle."""
+    head) unit at a time, its chunks last to first; no Tm / PT in memory), forced on:
+    gradients, per-chunk dS and dh0 against the oracle."""
     monkeypatch.setenv("KDA_PREPSCAN", "1")
     print("\n[case] prep with scan %s" % name, flush=True)
     _check(name)
 
 
 @pytest.mark.parametrize("name,cap", [("weak_decay_bf16", 3), ("multi_ragged_bf16", 2),
-                                      ("weak_decay_fp32", 2), ("qk_norm_fp32", 3)])
+                                      ("weak_decay_fp32", 2), ("qk_norm_fp32", 3),
+                                      ("ragged_bf16", 3), ("gate_bias_bf16", 2)])
 def test_prep_with_scan_capped(name, cap, monkeypatch):
     """The same with the grid capped, so that every workgroup walks several units (the
     state restarts from dht at each unit's last chunk, the next unit's inputs are fetched
@@ -291,9 +299,7 @@ def test_prep_with_scan_capped(name, cap, monkeypatch):
         assert np.array_equal(full[key], capped[key]), key
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "weak_decay_bf16", "weak_decay_fp32",
-                                  "multi_ragged_bf16", "qk_norm_fp32", "gate_log2_bf16",
-                                  "single_seq_bf16", "strong_decay_bf16", "qk_norm_bf16_d64"])
+@pytest.mark.parametrize("name", FUSED)
 def test_forward_with_scan(name, monkeypatch):
     """The production forward in one kernel (prep's forward mode carrying the state:
     X = Uv - W S, O = Qd S + Mqk X, S <- e^{G_T} S + Kr^T X per chunk, no per-chunk operands
@@ -311,7 +317,8 @@ def test_forward_with_scan(name, monkeypatch):
 
 
 @pytest.mark.parametrize("name,cap", [("weak_decay_bf16", 3), ("multi_ragged_bf16", 2),
-                                      ("qk_norm_fp32", 3)])
+                                      ("qk_norm_fp32", 3), ("ragged_fp32", 2),
+                                      ("gate_log2_fp32", 3)])
 def test_forward_with_scan_capped(name, cap, monkeypatch):
     """The same with several units per workgroup (the state restarts from h0 at each
     unit's first chunk): oracle parity and bit-identical results to the full grid."""
@@ -328,7 +335,7 @@ def test_forward_with_scan_capped(name, cap, monkeypatch):
         assert np.array_equal(full[key], capped[key]), key
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "weak_decay_bf16", "qk_norm_fp32"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "weak_decay_bf16", "qk_norm_fp32", "ragged_bf16"])
 def test_recompute_with_scans_in_prep(name, monkeypatch):
     """kda_bwd without h_saved with both scans inside prep: the fused forward recomputes
     the chunk-start states, the fused backward carries dS."""
