@@ -63,9 +63,16 @@ int64_t seq_chunks(const kda_problem* p, int n) {
   return (len + CH - 1) / CH;
 }
 
-// Chunks per group of the state-gradient scan.  A sequence of more than 128
-// chunks is scanned in groups of 64 (three passes, groups side by side); shorter
-// ones in one serial pass.  KDA_SCAN_GROUP=<chunks> overrides (0: never split).
+// Chunks per group of the state scans (backward and forward).  With few (sequence, head)
+// units the serial chain over a sequence's chunks leaves most CUs idle, so sequences are
+// split into groups (three passes: group maps side by side, the boundaries, the groups
+// again): the smallest power-of-two group size, at least 4 chunks, that keeps the
+// group-map pass within about 512 workgroups (two per CU).  Measured with one GPU on the
+// single-sequence workload (16 units of 32 chunks: scan 0.122 ms unsplit, 0.069 with groups
+// of 4, 0.080 with 8) and the long-context one (16 units of 2048 chunks: 2.20, 1.86, 1.66,
+// 1.54 and 2.10 ms with groups of 16 to 256).  With many units the GPU is full without
+// splitting; sequences of more than 128 chunks are then still cut into groups of 64.
+// KDA_SCAN_GROUP=<chunks> overrides (0: never split).
 int scan_group_size(const kda_problem* p, int N) {
   if (const char* env = std::getenv("KDA_SCAN_GROUP")) {
     const int v = std::atoi(env);
@@ -73,7 +80,14 @@ int scan_group_size(const kda_problem* p, int N) {
   }
   int64_t mx = 0;
   for (int n = 0; n < N; ++n) mx = std::max(mx, seq_chunks(p, n));
-  return mx > 128 ? 64 : 0;
+  const int64_t units = (int64_t)N * p->H;
+  if (units >= 256) return mx > 128 ? 64 : 0;
+  for (int64_t gs = 4; gs < mx; gs *= 2) {
+    int64_t ng = 0;
+    for (int n = 0; n < N; ++n) ng += (seq_chunks(p, n) + gs - 1) / gs;
+    if (ng * p->H * 2 <= 512) return (int)gs;
+  }
+  return 0;
 }
 
 // Whether prep runs the state scans itself (one workgroup per (sequence, head) unit at a

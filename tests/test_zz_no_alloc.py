@@ -75,7 +75,7 @@ def _run_both(lib, name, use_h_saved=True):
 
 
 def test_noalloc_matches_kda_bwd(lib):
-    _run_both(lib, "single_seq_bf16")      # 512 chunk-heads
+    _run_both(lib, "weak_decay_bf16")      # 128 chunk-heads, h0 / dht, split scans
     _run_both(lib, "ragged_bf16")          # smaller, on the scratch the first call left
     _run_both(lib, "gate_log2_fp32", use_h_saved=False)  # state recompute in the scratch
 
