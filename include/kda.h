@@ -33,7 +33,8 @@
  *
  * Supported shapes: chunk = 64; K == V; K in {64, 128} for bf16,
  * K == 64 for fp32; B*T*H < 2^31 (token-head rows and chunk-head items are indexed in
- * 32 bits).  Anything else returns KDA_ERR_UNSUPPORTED.
+ * 32 bits); H*K < 2^22 (a token row of fp32, H*K*4 bytes, stays below 2^24 bytes, so
+ * row offsets fit the 24-bit multiplier).  Anything else returns KDA_ERR_UNSUPPORTED.
  *
  * Ownership and synchronisation.  The caller owns every buffer (device memory)
  * and the stream.  The library allocates no device memory and keeps no pointer

@@ -140,6 +140,9 @@ int validate_problem(const kda_problem* p) {
   if (p->act_dtype == KDA_DTYPE_BF16 && p->K != 64 && p->K != 128) return KDA_ERR_UNSUPPORTED;
   if (p->act_dtype == KDA_DTYPE_F32 && p->K != 64) return KDA_ERR_UNSUPPORTED;
   if ((int64_t)p->B * p->T >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  // per-lane row offsets are formed on the 24-bit multiplier: a token row of fp32
+  // (H * K * 4 bytes) must stay below 2^24 bytes
+  if ((int64_t)p->H * p->K * 4 >= ((int64_t)1 << 24)) return KDA_ERR_UNSUPPORTED;
   const bool hv = p->cu_seqlens_host != nullptr, dv = p->cu_seqlens_dev != nullptr;
   if (hv != dv) return KDA_ERR_INVALID_ARGUMENT;
   if (hv) {

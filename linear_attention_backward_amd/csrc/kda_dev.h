@@ -402,37 +402,69 @@ __device__ __forceinline__ void store_ct<float>(float* base, int pitch, int row0
 // beyond `valid` are zero-filled with ordinary LDS stores instead.  The caller
 // waits for vmcnt(0) and synchronises before the tile is read.
 typedef __attribute__((address_space(3))) void lds_void;
-// One 16-byte global -> LDS copy per active lane: lane l writes LDS bytes
-// [lds + 16 l, lds + 16 l + 16) (lds: a wave-uniform LDS byte address, via M0).
+// Byte offset of row r for a row stride of rsb bytes, on the full-rate 24-bit multiplier
+// (a 32- or 64-bit product is a quarter-rate instruction).  The host keeps every row
+// stride below 2^24 bytes, and rows inside a chunk or a state tile are below 2^7, so
+// the product fits 31 bits.
+// (The operands are masked to 24 bits so that the compiler can see the range; a call of
+// the mul24 library function with an operand of unknown range becomes a full multiply.)
+__device__ __forceinline__ unsigned row_off(unsigned r, unsigned rsb) {
+  return (r & 0xffffffu) * (rsb & 0xffffffu);
+}
+// `base` (wave-uniform) plus a per-lane byte offset: the access can take the scalar-base
+// plus 32-bit vector-offset address form instead of a 64-bit add per lane.
+template <typename X> __device__ __forceinline__ X* at(X* base, unsigned off) {
+  return (X*)((char*)base + off);
+}
+template <typename X> __device__ __forceinline__ const X* at(const X* base, unsigned off) {
+  return (const X*)((const char*)base + off);
+}
+// floor(p / d) for 0 <= p < n as (p * m) >> 16 on the 24-bit multiplier (a division by
+// a constant otherwise becomes a quarter-rate high multiply); n and d are checked at
+// compile time.
+constexpr unsigned div24_m(int d) { return (65536u + (unsigned)d - 1) / (unsigned)d; }
+constexpr bool div24_exact(int d, int n) {
+  for (int p = 0; p < n; ++p)
+    if ((int)(((unsigned)p * div24_m(d)) >> 16) != p / d) return false;
+  return (unsigned)n * div24_m(d) < (1u << 24);
+}
+template <int d, int n> __device__ __forceinline__ unsigned div24(unsigned p) {
+  static_assert(div24_exact(d, n), "24-bit division exact over the range");
+  return ((p & 0xffffffu) * div24_m(d)) >> 16;
+}
+// One 16-byte global -> LDS copy per active lane: lane l reads 16 bytes at g + off
+// (g wave-uniform, in scalar registers; off this lane's byte offset) and writes LDS
+// bytes [lds + 16 l, lds + 16 l + 16) (lds: a wave-uniform LDS byte address, via M0).
 // Issued as inline asm so that the compiler does not hold every later LDS access
 // of the wave until the copy lands: a reader of the destination calls wait_vmem()
 // and then a workgroup barrier. The kernels that use it set M0 nowhere else.
-__device__ __forceinline__ void g2l16(const void* g, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+__device__ __forceinline__ void g2l16(const void* g, unsigned off, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
+               "s"(g), "s"(lds)
                : "memory");
 }
 //   lds0: LDS byte address of the tile (wave-uniform), lds_tile: the same tile seen
-//   through a generic pointer (for the zero fill).
+//   through a generic pointer (for the zero fill); src: the tile's first row (uniform),
+//   rs: its row stride in elements.
 //   [N0, N1): the part of the wave's slices to issue (a tile may be issued in parts).
 template <typename T, int D, int ROWS, int NW, int N0 = 0, int N1 = 1 << 20, int PAD = 1>
-__device__ __forceinline__ void g2l_tile(unsigned lds0, T* lds_tile, const T* src, size_t rs,
+__device__ __forceinline__ void g2l_tile(unsigned lds0, T* lds_tile, const T* src, unsigned rs,
                                          int valid, int w, int lane) {
   constexpr int GPR = D * (int)sizeof(T) / 16;  // data granules per row
   constexpr int GP = GPR + PAD;                 // granules per padded LDS row
   constexpr int NG = ROWS * GP;
-  constexpr int EPG = 16 / (int)sizeof(T);
   constexpr int NSL = (NG + 63) / 64;           // slices
   constexpr int NPW = (NSL + NW - 1) / NW;      // slices per wave (at most)
+  const unsigned rsb = rs * (unsigned)sizeof(T);
 #pragma unroll
   for (int n = N0; n < (N1 < NPW ? N1 : NPW); ++n) {
     const int base = (w + n * NW) * 64;
     if (base < NG) {
-      const int p = base + lane;
-      const int row = p / GP, gc = p - row * GP;
-      if (p < NG) {
-        if (row < valid) {
-          const T* g = src + (size_t)row * rs + (gc < GPR ? gc : GPR - 1) * EPG;
-          g2l16(g, lds0 + base * 16);
+      const unsigned p = (unsigned)(base + lane);
+      const unsigned row = div24<GP, NSL * 64>(p), gc = p - row * GP;
+      if (p < (unsigned)NG) {
+        if ((int)row < valid) {
+          g2l16(src, row_off(row, rsb) + (gc < GPR ? gc : GPR - 1) * 16, lds0 + base * 16);
         } else {
           unsigned z;  // made here: a zero quad kept across the caller's loop gets spilled
           asm volatile("v_mov_b32 %0, 0" : "=v"(z));

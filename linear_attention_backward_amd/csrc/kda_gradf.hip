@@ -211,8 +211,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       g2l_tile<T, D, D, NW, 2, 1 << 20, L::NPAD>(lds0 + L::S_OFF, sS, sin, D, D, w, lane);
     if (part == 0 || part == 3) {
       g2l_tile<T, D, 64, NW, 0, 1 << 20, L::NPAD>(lds0 + L::V_OFF, sV,
-                                                  v + (size_t)ci.t0 * rs + (size_t)h * D, rs,
-                             ci.len, w, lane);
+                                                  v + (size_t)ci.t0 * rs + (size_t)h * D,
+                                                  (unsigned)rs, ci.len, w, lane);
       g2l_tile<T, 64, 64, NW, 0, 1 << 20, L::CPAD>(lds0 + L::IV_OFF, sIV,
                                                    INV + ((size_t)c * H + h) * 4096, 64, 64, w,
                                                    lane);
@@ -223,23 +223,25 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const ChunkInfo ci = chunks[c];
     const size_t base = (size_t)ci.t0 * rs + (size_t)h * D;
     const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
-    g2l_tile<T, D, 64, NW, 0, 1 << 20, L::NPAD>(lds0 + L::K0_OFF, sK0, k + base, rs, ci.len, w,
-                                                lane);
-    const float* grw = g_raw + base + 16 * w + 4 * (lane & 3);
+    g2l_tile<T, D, 64, NW, 0, 1 << 20, L::NPAD>(lds0 + L::K0_OFF, sK0, k + base, (unsigned)rs,
+                                                ci.len, w, lane);
+    const unsigned gcol = (16 * w + 4 * (lane & 3)) * 4;
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       const int r = 16 * t4 + (lane >> 2);
-      rg[t4] = *(const f4*)(grw + (size_t)(r < ci.len ? r : ci.len - 1) * rs);
+      rg[t4] = *at((const f4*)(g_raw + base),
+                   row_off(r < ci.len ? r : ci.len - 1, (unsigned)rs * 4) + gcol);
     }
-    rbeta = beta[((size_t)ci.t0 + (lane < ci.len ? lane : ci.len - 1)) * H + h];
+    rbeta = *at(beta + (size_t)ci.t0 * H + h, row_off(lane < ci.len ? lane : ci.len - 1, H * 4));
     if constexpr (GV) rdb = *(const f4*)(dt_bias + (size_t)h * D + 16 * w + 4 * (lane & 3));
   };
   auto issue_late = [&](int it, int t) {
     const int c = it / H, h = it % H;
     const ChunkInfo ci = chunks[c];
     g2l_tile<T, D, 64, NW, 0, 1 << 20, L::NPAD>(lds0 + L::O_OFF, sO,
-                                                dO + (size_t)ci.t0 * rs + (size_t)h * D, rs,
-                                                ci.len, __builtin_amdgcn_readfirstlane(t >> 6),
+                                                dO + (size_t)ci.t0 * rs + (size_t)h * D,
+                                                (unsigned)rs, ci.len,
+                                                __builtin_amdgcn_readfirstlane(t >> 6),
                                                 t & 63);
   };
   if ((int)blockIdx.x < items) {
@@ -256,6 +258,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   // below stay inside the loop instead of being held in registers across it
   int tid = tid0;
   asm volatile("" : "+v"(tid));
+  tid &= NT - 1;  // its range, for the compiler (24-bit multiplies in the addresses below)
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, cl = lane & 15;
   const int c = it / H, h = it % H;
@@ -266,6 +269,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const size_t ch = (size_t)c * H + h;
   const size_t hD = (size_t)h * D;
   const T* qh = q + t0 * rs + hD;
+  const unsigned rsb = (unsigned)rs * L::ES;  // token row stride in bytes
   const T* dSo = dstates + ch * DD;
   const float aA = __expf(A_log[h]) * gu;  // gu: natural-log decay per unit of the gate
   const int gch = 16 * w + cl;
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
   for (int l = 0; l < NLS; ++l) {
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    rD[l] = *(const u32x4*)(dSo + (size_t)r * D + sv * EPV);
+    rD[l] = *at((const u32x4*)dSo, (unsigned)(r * D + sv * EPV) * L::ES);
   }
   if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
   if constexpr (QN) {  // k rows normalised in place (rows past the chunk are zero)
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
   for (int l = 0; l < NLT; ++l) {
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
-    rQ[l] = *(const u32x4*)(qh + (size_t)(r < Lr ? r : Lr - 1) * rs + sv * EPV);
+    rQ[l] = *at((const u32x4*)qh, row_off(r < Lr ? r : Lr - 1, rsb) + sv * 16);
   }
   __syncthreads();  // dvcorr and dv staged
   // Output copies: rows past the chunk store row Lr - 1 again (the same bytes as
@@ -482,7 +486,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   for (int l = 0; l < NLT; ++l) {  // dv out, 16-byte vectors
     const int idx = tid + l * NT, r0 = idx / VPR, sv = idx % VPR;
     const int r = r0 < Lr ? r0 : Lr - 1;
-    *(u32x4*)(dv + (t0 + r) * rs + hD + sv * EPV) = *(const u32x4*)(sDV + r * PN + sv * EPV);
+    *at((u32x4*)(dv + t0 * rs + hD), row_off(r, rsb) + sv * 16) =
+        *(const u32x4*)(sDV + r * PN + sv * EPV);
   }
 
   // --------------------------------------------------------------- key side
@@ -786,9 +791,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
     for (int l = 0; l < NLT; ++l) {
       const int idx = tid + l * NT, r0 = idx / VPR, sv = idx % VPR;
-      const size_t o = (t0 + (r0 < Lr ? r0 : Lr - 1)) * rs + hD + sv * EPV;
-      rawq[l] = *(const u32x4*)(q + o);
-      rawk[l] = *(const u32x4*)(k + o);
+      const unsigned o = row_off(r0 < Lr ? r0 : Lr - 1, rsb) + sv * 16;
+      rawq[l] = *at((const u32x4*)qh, o);
+      rawk[l] = *at((const u32x4*)(k + t0 * rs + hD), o);
     }
   }
   // last row: sum_r k.dk_r + e^{G_T} p
@@ -860,7 +865,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   for (int l = 0; l < NLT; ++l) {  // dq, dk out, 16-byte vectors
     const int idx = tid + l * NT, r0 = idx / VPR, sv = idx % VPR;
     const int r = r0 < Lr ? r0 : Lr - 1;
-    const size_t o = (t0 + r) * rs + hD + sv * EPV;
+    const unsigned o = row_off(r, rsb) + sv * 16;
     u32x4 vq = *(const u32x4*)(sDQ + r * PN + sv * EPV);
     u32x4 vk = *(const u32x4*)(sDK + r * PN + sv * EPV);
     if constexpr (QN) {  // back to the raw rows: dx = r (dxn - xn (xn . dxn)); the row's
@@ -871,8 +876,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       vq = l2n_project<T>(qn, vq, rrq, sum_group<VPR>(dot_piece<T>(qn, vq)));
       vk = l2n_project<T>(kn, vk, rrk, sum_group<VPR>(dot_piece<T>(kn, vk)));
     }
-    *(u32x4*)(dq + o) = vq;
-    *(u32x4*)(dk + o) = vk;
+    *at((u32x4*)(dq + t0 * rs + hD), o) = vq;
+    *at((u32x4*)(dk + t0 * rs + hD), o) = vk;
   }
   if (tid < 64 && tid < Lr) {
     float s = 0.f;
@@ -880,7 +885,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     for (int x = 0; x < WPR; ++x) s += sDB1[x * 64 + tid];
 #pragma unroll
     for (int x = 0; x < NW; ++x) s += sDB2[x * 64 + tid];
-    dbeta[(t0 + tid) * H + h] = s;
+    *at(dbeta + t0 * H + h, row_off(tid, H * 4)) = s;
   }
   if (tid == 0) {
     float s = 0.f;
@@ -893,7 +898,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   for (int l = 0; l < NLR; ++l) {  // dg_raw out, 16-byte vectors
     const int idx = tid + l * NT, r0 = idx / (D / 4), sv = idx % (D / 4);
     const int r = r0 < Lr ? r0 : Lr - 1;
-    *(f4*)(dg_raw + (t0 + r) * rs + hD + sv * 4) = *(const f4*)(sR + r * PR + sv * 4);
+    *at((f4*)(dg_raw + t0 * rs + hD), row_off(r, (unsigned)rs * 4) + sv * 16) =
+        *(const f4*)(sR + r * PR + sv * 4);
   }
   // The next item's g_raw and beta (and so, in issue order, its k, S_in, v and INV)
   // are waited for here, before the dO copy: the compiler does not see that copy, so a

@@ -237,6 +237,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   // below stay inside the loop instead of being held in registers across it
   int tid = tid0;
   asm volatile("" : "+v"(tid));
+  tid &= NT - 1;  // its range, for the compiler (24-bit multiplies in the addresses below)
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, cl = lane & 15;
   const int c = it % NC, h = it / NC;

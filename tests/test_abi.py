@@ -50,6 +50,9 @@ def test_shape_validation():
     assert _ws(K._Prob(1, 1 << 24, 127, 64, 64, 0))[0] == 0
     assert _ws(K._Prob(1, 1 << 24, 128, 64, 64, 0))[0] == K.KDA_ERR_UNSUPPORTED
     assert _ws(K._Prob(4, 1 << 22, 128, 64, 64, 0))[0] == K.KDA_ERR_UNSUPPORTED
+    # a token row of fp32 (H * K * 4 bytes) at or past 2^24 bytes
+    assert _ws(K._Prob(1, 64, (1 << 15) - 1, 128, 128, K.KDA_DTYPE_BF16))[0] == 0
+    assert _ws(K._Prob(1, 64, 1 << 15, 128, 128, K.KDA_DTYPE_BF16))[0] == K.KDA_ERR_UNSUPPORTED
     p = K._Prob(1, 100, 4, 64, 64, 0)
     p.p.chunk = 32
     assert _ws(p)[0] == K.KDA_ERR_UNSUPPORTED
