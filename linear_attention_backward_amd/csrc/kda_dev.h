@@ -512,13 +512,41 @@ __device__ __forceinline__ float sum16(float x) {
   x += dpp_f<0x140>(x);  // row_mirror
   return x;
 }
-// Sum over the whole wave.
-__device__ __forceinline__ float sum64(float x) {
-  x = sum16(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+// Lane swaps across the 16-lane rows of a wave (VALU, no LDS):
+//   swap32(a, b): lanes 32-63 of a <-> lanes 0-31 of b;
+//   swap16(a, b): lanes 16-31 of a <-> lanes 0-15 of b, lanes 48-63 of a <-> 32-47 of b.
+// Inline asm with both registers read and written: this compiler returns the first
+// register for both results of the swap builtins.  A swap that reads a register written
+// by a VALU instruction needs two wait states in between; the compiler cannot see into
+// the asm, so each swap brings its own (s_nop 1).
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+// rows_gather: r[k] = x of lane 16 k + (lane & 15), in every lane.
+__device__ __forceinline__ void rows_gather(float x, float (&r)[4]) {
+  float a = x, b = x;
+  swap32(a, b);  // a: rows 0 1 0 1, b: rows 2 3 2 3
+  float c = a, d = b;
+  swap16(a, c);  // a: row 0, c: row 1
+  swap16(b, d);  // b: row 2, d: row 3
+  r[0] = a;
+  r[1] = c;
+  r[2] = b;
+  r[3] = d;
+}
+// x summed over the four rows (the lanes l, l ^ 16, l ^ 32, l ^ 48), in every lane.
+__device__ __forceinline__ float sum_rows(float x) {
+  float a = x, b = x;
+  swap32(a, b);
+  float c = a + b, d = c;  // rows 0+2, 1+3, 0+2, 1+3
+  swap16(c, d);
+  return c + d;
+}
+// Sum over the whole wave.
+__device__ __forceinline__ float sum64(float x) { return sum_rows(sum16(x)); }
 
 // L2 normalisation of q and k per (token, head) (the Kernel-B guide, R1 computes the
 // reciprocal norm of every row once and its K1, the norm's backward, reuses it):

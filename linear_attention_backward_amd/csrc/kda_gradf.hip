@@ -322,8 +322,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       run += x[rr];
       x[rr] = run;
     }
-    const float t0p = __shfl(run, cl), t1p = __shfl(run, cl + 16), t2p = __shfl(run, cl + 32);
-    const float add = (g4 > 0 ? t0p : 0.f) + (g4 > 1 ? t1p : 0.f) + (g4 > 2 ? t2p : 0.f);
+    float tp[4];
+    rows_gather(run, tp);
+    const float add = (g4 > 0 ? tp[0] : 0.f) + (g4 > 1 ? tp[1] : 0.f) + (g4 > 2 ? tp[2] : 0.f);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
       *(f4*)(sG + gch * PG + g4 * 16 + 4 * qq) =
@@ -509,8 +510,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       aKd[rt] = MM::mma(MM::load(sDVC + r * PN + d0), bS[kk], aKd[rt]);
     }
   }
-  pp += __shfl_xor(pp, 16);
-  pp += __shfl_xor(pp, 32);
+  pp = sum_rows(pp);
   // dMqk = tril(dO U^T), dL = -stril(dvcorr U^T): wave -> rows of block R1,
   // column tiles [4/WPR * half, ...)
   constexpr int CTW = 4 / WPR;
@@ -647,16 +647,15 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     // to the C layout: lane (g4, cl) holds rows 16 g4 + t and wants rows
     // 16 rt + 4 g4 + j, i.e. a transpose of 4-row chunks across the four 16-lane rows
     // of the wave: one 32-lane swap stage and one 16-lane swap stage per element.
-    // The swaps are inline asm with both registers read and written: this compiler
-    // returns the first register for both results of the swap builtins.
+    // (swap32 / swap16: the lane swaps of the device helpers)
     auto exch = [&](const float (&src)[16], float (&dst)[4][4]) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x0 = src[e], x1 = src[4 + e], x2 = src[8 + e], x3 = src[12 + e];
-        asm volatile("v_permlane32_swap_b32 %0, %1" : "+v"(x0), "+v"(x2));
-        asm volatile("v_permlane32_swap_b32 %0, %1" : "+v"(x1), "+v"(x3));
-        asm volatile("v_permlane16_swap_b32 %0, %1" : "+v"(x0), "+v"(x1));
-        asm volatile("v_permlane16_swap_b32 %0, %1" : "+v"(x2), "+v"(x3));
+        swap32(x0, x2);
+        swap32(x1, x3);
+        swap16(x0, x1);
+        swap16(x2, x3);
         dst[0][e] = x0;
         dst[1][e] = x1;
         dst[2][e] = x2;
@@ -713,6 +712,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       Gr[0] = t[0]; Gr[1] = t[1]; Gr[2] = t[2]; Gr[3] = t[3];
     }
     f4 X1a = zero4(), X2a = zero4(), Za = zero4();
+    // e^{G_r} and e^{G_T - G_r} of this lane's rows, taken from the anchored row factors
+    // below where a tile has them (a product of two factors <= 1: no overflow)
+    float eGr[4], eTr[4];
     if (rt > 0) {
       const float ga = Gi[r0];
 #pragma unroll
@@ -733,12 +735,17 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
           }
         }
       }
+      const float eGa = ex2(ga);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float sc = ex2(Gr[j] - ga);
         X1a[j] *= sc;
         X2a[j] *= sc;
+        eGr[j] = sc * eGa;
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) eGr[j] = ex2(Gr[j]);
     }
     if (rt < 3) {
       const float gb = Gi[r0 + 16];
@@ -757,8 +764,16 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
           for (int j = 0; j < 4; ++j) Za[j] = fmaf(m, p[j], Za[j]);
         }
       }
+      const float eTb = ex2(gT - gb);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Za[j] *= ex2(gb - Gr[j]);
+      for (int j = 0; j < 4; ++j) {
+        const float sc = ex2(gb - Gr[j]);
+        Za[j] *= sc;
+        eTr[j] = sc * eTb;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) eTr[j] = ex2(gT - Gr[j]);
     }
     // combine and form the gate gradient of this tile
     const int rb = r0 + 4 * g4;
@@ -768,13 +783,13 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const float kr = to_f(sK[r * PN + ic]);
       const float qr = to_f(sQ[r * PN + ic]);
       const float br = sBeta[r];
-      const float eG = ex2(Gr[j]);
+      const float eG = eGr[j];
       const float x1 = X1a[j] + x1d[rt][j];
       const float x2 = X2a[j] + x2d[rt][j];
       const float dki = Za[j] + zd[rt][j];
       const float dqv = eG * aQd[rt][j] + x1;
       const float dkd = br * (-eG * aKd[rt][j] + x2);
-      const float dkr = ex2(gT - Gr[j]) * aKr[rt][j];
+      const float dkr = eTr[j] * aKr[rt][j];
       dG[rt][j] = qr * dqv + kr * (dkd - dki - dkr);
       dkr_col += kr * dkr;
       dbp[rt][j] = kr * x2;
@@ -797,8 +812,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     }
   }
   // last row: sum_r k.dk_r + e^{G_T} p
-  dkr_col += __shfl_xor(dkr_col, 16);
-  dkr_col += __shfl_xor(dkr_col, 32);
+  dkr_col = sum_rows(dkr_col);
   if (g4 == 3) dG[3][3] += dkr_col + ex2(gT) * pp;
   // reverse cumsum over r = 16 rt + 4 g4 + j; dG becomes dg_raw.  The gate's own
   // derivative comes from the cumulative gate: with aA = gu e^{A_log}, x = g_raw + dt_bias
@@ -812,8 +826,9 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
 #pragma unroll
   for (int rt = 3; rt >= 0; --rt) {
     const float tot = dG[rt][0] + dG[rt][1] + dG[rt][2] + dG[rt][3];
-    const float t0v = __shfl(tot, cl), t1 = __shfl(tot, cl + 16);
-    const float t2 = __shfl(tot, cl + 32), t3 = __shfl(tot, cl + 48);
+    float tr[4];
+    rows_gather(tot, tr);
+    const float t0v = tr[0], t1 = tr[1], t2 = tr[2], t3 = tr[3];
     float run = carry;
     if (g4 < 3) run += t3;
     if (g4 < 2) run += t2;
@@ -841,8 +856,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) sdt += dG[rt][j];
-    sdt += __shfl_xor(sdt, 16);
-    sdt += __shfl_xor(sdt, 32);
+    sdt = sum_rows(sdt);
     ddt_part[ch * D + ic] = sdt;
   }
   // dbeta second part, reduced over this wave's channels
