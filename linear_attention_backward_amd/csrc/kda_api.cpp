@@ -559,6 +559,9 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   hipError_t e;
   const bool fused = use_prepscan(p, pl.s);
   int* order = fused ? (int*)(ws + pl.order.off) : nullptr;
+  // with the scan inside prep, prep hands dU to the gradient pass in the Tm region (Tm and
+  // PT are not formed in that mode; the region holds NC*H*K*K >= NC*H*64*V elements)
+  b.dU = fused ? b.Tm : nullptr;
   e = timed(0, s, [&] {
     return launch_chunk_table(sh, (ChunkInfo*)b.chunks, (int*)b.seq_off, (GroupInfo*)b.groups,
                               (int*)b.grp_off, s, order);

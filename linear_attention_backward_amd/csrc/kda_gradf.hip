@@ -107,8 +107,10 @@ template <typename T, int D> struct GF {
 // no column sums of dg_raw are formed.  QN: q and k are L2-normalised per row inside the
 // pass (k in its LDS tile at the start of an item, q in registers on its way to LDS) and
 // dq, dk are projected back to the raw rows as they are written out, with the cached
-// reciprocal norms: dx = r (dxn - xn (xn . dxn)).
-template <typename T, int D, bool GV, bool QN>
+// reciprocal norms: dx = r (dxn - xn (xn . dxn)).  DU: dU = Mqk^T dO + Kr dS_out comes
+// from memory (prep forms it when the state scan runs inside prep) instead of being
+// formed here, which also drops the Kr fragments and the Mqk^T loads.
+template <typename T, int D, bool GV, bool QN, bool DU>
 __global__ __launch_bounds__(4 * D) void k_gradf(
     const ChunkInfo* __restrict__ chunks, int NC, int H, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const float* __restrict__ A_log, const float* __restrict__ dt_bias, int has_db, float gu,
     const T* __restrict__ h_saved,
     const T* __restrict__ dstates, const T* __restrict__ INV,
-    const T* __restrict__ MqkT, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
+    const T* __restrict__ MqkT, const T* __restrict__ dUin, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
     float* __restrict__ dg_raw, float* __restrict__ dbeta, float* __restrict__ dAl_part,
     float* __restrict__ ddt_part) {
   using L = GF<T, D>;
@@ -285,6 +287,14 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
     rD[l] = *at((const u32x4*)dSo, (unsigned)(r * D + sv * EPV) * L::ES);
   }
+  u32x4 rU[DU ? NLT : 1];  // DU: this chunk's dU rows
+  if constexpr (DU) {
+#pragma unroll
+    for (int l = 0; l < NLT; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+      rU[l] = *at((const u32x4*)(dUin + ch * 64 * D), (unsigned)(r * D + sv * EPV) * L::ES);
+    }
+  }
   if (tid < 64) sBeta[tid] = tid < Lr ? rbeta : 0.f;
   if constexpr (QN) {  // k rows normalised in place (rows past the chunk are zero)
 #pragma unroll
@@ -337,30 +347,34 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   Frag kf[NKD];                              // raw k of row arow (permuted k order)
 #pragma unroll
   for (int kk = 0; kk < NKD; ++kk) kf[kk] = MM::ld_perm(sK0 + arow * PN, kk * KS, lane);
-  Frag fI[NKC], fIT[NKC], fMT[NKC];          // rows arow of INV, INV^T, Mqk^T
+  Frag fI[NKC], fIT[NKC], fMT[DU ? 1 : NKC];  // rows arow of INV, INV^T, Mqk^T
 #pragma unroll
   for (int ks = 0; ks < NKC; ++ks) {
     fI[ks] = MM::load(sIV + arow * PC + ks * KS + g4 * KPL);
-    fMT[ks] = MM::ld_perm(MqkT + ch * 4096 + arow * 64, ks * KS, lane);
-    fIT[ks] = MM::ld_tr_nat(sIV, PC, ks * KS, 16 * R1, lane);  // row arow of INV^T
+    if constexpr (DU) {  // row arow of INV^T, permuted order (dU is read across its rows)
+      fIT[ks] = MM::ld_tr(sIV, PC, ks * KS, 16 * R1, lane);
+    } else {
+      fMT[ks] = MM::ld_perm(MqkT + ch * 4096 + arow * 64, ks * KS, lane);
+      fIT[ks] = MM::ld_tr_nat(sIV, PC, ks * KS, 16 * R1, lane);
+    }
   }
 
   // ------------------------------------------------------------- state side
   // decayed key rows of this lane: Kd = K e^G (for Y), Kr = K e^{G_T - G} (for dU)
-  Frag akd[NKD], akr[NKD];
+  Frag akd[NKD], akr[DU ? 1 : NKD];
 #pragma unroll
   for (int kk = 0; kk < NKD; ++kk) {
     float kd[KPL], kr[KPL];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       const int i = kk * KS + MM::kperm(g4, j);
-      const float gg = sG[i * PG + arow], gt = sG[i * PG + 63];
+      const float gg = sG[i * PG + arow];
       const float kv = MM::elem(kf[kk], j);
       kd[j] = kv * ex2(gg);
-      kr[j] = kv * ex2(gt - gg);
+      if constexpr (!DU) kr[j] = kv * ex2(sG[i * PG + 63] - gg);
     }
     akd[kk] = MM::from_vals(kd);
-    akr[kk] = MM::from_vals(kr);
+    if constexpr (!DU) akr[kk] = MM::from_vals(kr);
   }
   // Y = V - Kd S_in
   f4 Y[4];
@@ -412,7 +426,13 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   }
   wait_vmem();      // (dO: already waited for by the dS_out stores, which follow it)
   __syncthreads();  // dS_out in place; U complete; (beta Y)^T dead
-  {  // dU = Mqk^T dO + Kr dS_out  ->  dU^T
+  if constexpr (DU) {  // dU from memory, natural rows, over the dead (beta Y)^T
+#pragma unroll
+    for (int l = 0; l < NLT; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, sv = idx % VPR;
+      *(u32x4*)(sYT + r * PN + sv * EPV) = rU[l];
+    }
+  } else {  // dU = Mqk^T dO + Kr dS_out  ->  dU^T
     f4 dU[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) dU[nt] = zero4();
@@ -450,7 +470,8 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const Frag a = fIT[ks];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const Frag b = MM::load(sYT + (64 * half + nt * 16 + cl) * PT + ks * KS + g4 * KPL);
+        const Frag b = DU ? MM::ld_tr(sYT, PN, ks * KS, 64 * half + nt * 16, lane)
+                          : MM::load(sYT + (64 * half + nt * 16 + cl) * PT + ks * KS + g4 * KPL);
         dvc[nt] = MM::mma(a, b, dvc[nt]);
       }
     }
@@ -928,28 +949,32 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   }
 }
 
-template <typename T, int D, bool GV, bool QN>
+template <typename T, int D, bool GV, bool QN, bool DU>
 static hipError_t gradf_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const int items = s.NC * s.H;
   int resident = 0;
-  hipError_t e = resident_blocks((const void*)k_gradf<T, D, GV, QN>, GF<T, D>::NT, &resident);
+  hipError_t e = resident_blocks((const void*)k_gradf<T, D, GV, QN, DU>, GF<T, D>::NT, &resident);
   if (e != hipSuccess) return e;
   const int grid = items < resident ? items : resident;
-  hipLaunchKernelGGL((k_gradf<T, D, GV, QN>), dim3(grid), dim3(GF<T, D>::NT), 0, st, p.chunks, s.NC, s.H,
-                     (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dO, p.g_raw,
-                     p.beta, p.A_log, p.dt_bias, p.has_db, s.gu, (const T*)p.h_saved,
-                     (const T*)p.dstates,
-                     (const T*)p.INV, (const T*)p.MqkT, (T*)p.dq, (T*)p.dk,
-                     (T*)p.dv, p.dg_raw, p.dbeta, p.dAl_part, p.ddt_part);
+  hipLaunchKernelGGL((k_gradf<T, D, GV, QN, DU>), dim3(grid), dim3(GF<T, D>::NT), 0, st, p.chunks,
+                     s.NC, s.H, (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.dO,
+                     p.g_raw, p.beta, p.A_log, p.dt_bias, p.has_db, s.gu, (const T*)p.h_saved,
+                     (const T*)p.dstates, (const T*)p.INV, (const T*)p.MqkT, (const T*)p.dU,
+                     (T*)p.dq, (T*)p.dk, (T*)p.dv, p.dg_raw, p.dbeta, p.dAl_part, p.ddt_part);
   return hipGetLastError();
+}
+
+template <typename T, int D, bool DU>
+static hipError_t gradf_d(const Shape& s, const BwdPtrs& p, hipStream_t st) {
+  const bool gv = p.has_db || p.ddt_bias;
+  if (s.qn)
+    return gv ? gradf_v<T, D, true, true, DU>(s, p, st) : gradf_v<T, D, false, true, DU>(s, p, st);
+  return gv ? gradf_v<T, D, true, false, DU>(s, p, st) : gradf_v<T, D, false, false, DU>(s, p, st);
 }
 
 template <typename T, int D>
 static hipError_t gradf_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
-  const bool gv = p.has_db || p.ddt_bias;
-  if (s.qn)
-    return gv ? gradf_v<T, D, true, true>(s, p, st) : gradf_v<T, D, false, true>(s, p, st);
-  return gv ? gradf_v<T, D, true, false>(s, p, st) : gradf_v<T, D, false, false>(s, p, st);
+  return p.dU ? gradf_d<T, D, true>(s, p, st) : gradf_d<T, D, false>(s, p, st);
 }
 
 hipError_t launch_gradf(const Shape& s, const BwdPtrs& p, hipStream_t st) {

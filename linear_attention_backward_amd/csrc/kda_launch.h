@@ -31,6 +31,10 @@ struct BwdPtrs {
   void* INV;               // [NC,H,64,64] act dtype: (I + diag(beta) A)^{-1}
   void* MqkT;              // [NC,H,64,64] act dtype: Mqk transposed
   void* dstates;           // [NC,H,K,V] act dtype: dL/dS at the end of every chunk
+  // [NC,H,64,V] act dtype: dU = Mqk^T dO + Kr dS_out of every chunk, written by prep when
+  // the state scan runs inside it (then over Tm, which that mode does not use) and read
+  // by the gradient pass; nullptr: the gradient pass forms dU itself
+  void* dU;
   float* dAl_part;         // [NC,H] per chunk-head partial sums for dA_log
   float* ddt_part;         // [NC,H,K] per chunk-head column sums of dg_raw (for ddt_bias)
   const GroupInfo* groups; // [NG] chunk groups of the state-gradient scan

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
                                                 float* __restrict__ dh0,
                                                 const int* __restrict__ seq_off,
                                                 const int* __restrict__ order, int NS,
-                                                T* __restrict__ o) {
+                                                T* __restrict__ o, T* __restrict__ dUo) {
   using L = PL<T, D>;
   using MM = Mma<T>;
   typedef typename MM::Frag Frag;
@@ -904,6 +904,15 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       for (int nt = 0; nt < NTW; ++nt) store_c<T>(sX, PSX, 16 * R, c0 + nt * 16, -acc[nt], lane);
     }
     __syncthreads();  // X complete
+    if (dUo) {  // dU = -X for the gradient pass, natural [64][D] rows (sign bits flipped)
+      constexpr unsigned SGN = L::ES == 2 ? 0x80008000u : 0x80000000u;
+      T* dst = dUo + ch * 64 * D;
+#pragma unroll
+      for (int l = 0; l < NLT; ++l) {
+        const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+        *(u32x4*)(dst + r * D + vv * EPV) = *(const u32x4*)(sX + r * PSX + vv * EPV) ^ SGN;
+      }
+    }
     // dS <- e^{G_T} . dS + Qd^T dO + W^T X  (A: Qd^T / W^T rows, read across the q / W
     // tiles; B: the dO / X tiles read across their rows, in the same order)
 #pragma unroll
@@ -1009,7 +1018,7 @@ static hipError_t prep_v(const Shape& s, const BwdPtrs& p, hipStream_t st) {
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, (T*)p.Tm, (T*)p.PT, p.eGT,
                      (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr);
+                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -1028,7 +1037,7 @@ static hipError_t prepscan_v(const Shape& s, const BwdPtrs& p, const int* order,
                      p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, nullptr,
                      (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                      (const T*)p.dO, p.dht, (T*)p.dstates, p.dh0, p.seq_off, order, s.N,
-                     nullptr);
+                     nullptr, (T*)p.dU);
   return hipGetLastError();
 }
 
@@ -1064,7 +1073,8 @@ static hipError_t fprepscan_v(const Shape& s, const FwdPtrs& p, const int* order
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, nullptr, nullptr,
                      nullptr, (const T*)p.v, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, p.h0, (T*)p.h_saved, p.ht, p.seq_off, order, s.N, (T*)p.o);
+                     nullptr, p.h0, (T*)p.h_saved, p.ht, p.seq_off, order, s.N, (T*)p.o,
+                     nullptr);
   return hipGetLastError();
 }
 
@@ -1105,7 +1115,8 @@ static hipError_t fprep_v(const Shape& s, const FwdPtrs& p, hipStream_t st) {
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, p.eGT, nullptr,
                      nullptr, (const T*)p.v, (T*)p.Wn, (T*)p.KrT, (T*)p.UvT, (T*)p.Qd,
-                     (T*)p.Mq, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr);
+                     (T*)p.Mq, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr,
+                     nullptr);
   return hipGetLastError();
 }
 
