@@ -512,6 +512,19 @@ __device__ __forceinline__ float sum16(float x) {
   x += dpp_f<0x140>(x);  // row_mirror
   return x;
 }
+// sum16 of N values at once, one DPP stage over all of them before the next: the
+// independent adds between dependent ones stand in for the wait states a DPP read of a
+// just-written register needs.
+template <int N> __device__ __forceinline__ void sum16_n(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f<0xB1>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f<0x4E>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f<0x141>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f<0x140>(x[i]);
+}
 // Lane swaps across the 16-lane rows of a wave (VALU, no LDS):
 //   swap32(a, b): lanes 32-63 of a <-> lanes 0-31 of b;
 //   swap16(a, b): lanes 16-31 of a <-> lanes 0-15 of b, lanes 48-63 of a <-> 32-47 of b.

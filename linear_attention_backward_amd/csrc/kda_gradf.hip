@@ -487,10 +487,10 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       }
       store_c<T>(sDV, PN, 16 * R1, 64 * half + nt * 16, dvv, lane);
     }
+    sum16_n(db);
+    if (cl == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float s = sum16(db[j]);
-      if (cl == 0) sDB1[half * 64 + crow + j] = s;
+      for (int j = 0; j < 4; ++j) sDB1[half * 64 + crow + j] = db[j];
     }
   }
   // q for the intra-chunk phase (registers now, LDS once its tile is free); rows
@@ -881,13 +881,20 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
     ddt_part[ch * D + ic] = sdt;
   }
   // dbeta second part, reduced over this wave's channels
+  {
+    float db2[16];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float s = sum16(dbp[rt][j]);
-      if (cl == 0) sDB2[w * 64 + rt * 16 + g4 * 4 + j] = s;
+      for (int j = 0; j < 4; ++j) db2[rt * 4 + j] = dbp[rt][j];
+    sum16_n(db2);
+    if (cl == 0) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sDB2[w * 64 + rt * 16 + g4 * 4 + j] = db2[rt * 4 + j];
     }
+  }
   dal = sum64(dal);
   if (lane == 0) sRed[w] = dal;
   __syncthreads();  // dq, dk staged; the gate tile is dead

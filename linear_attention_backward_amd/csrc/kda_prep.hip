@@ -468,11 +468,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
               pm[p] += qq4[a_] * kb;
             }
         }
-#pragma unroll
-        for (int p = 0; p < 10; ++p) {
-          pa[p] = sum16(pa[p]);
-          pm[p] = sum16(pm[p]);
-        }
+        sum16_n(pa);
+        sum16_n(pm);
         // C layout: lane holds rows 4 sb + j, column cl; the diagonal sub-block of
         // those rows has columns 4 sb .. 4 sb + 3.
         if ((cl >> 2) == sb) {
@@ -807,26 +804,27 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     }
   } else {
   // ---- INV and Mqk^T (act dtype, natural rows) for the gradient pass (which reads
-  // INV^T out of its copy of INV)
+  // INV^T out of its copy of INV).  With the scan inside, Mqk^T is not stored: its only
+  // use there is dU, which this kernel forms and hands over.
   for (int e = tid; e < 64 * 8; e += NT) {
     const int r = e >> 3, c8 = (e & 7) * 8;
     float a[8], m[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       a[j] = sINV[r * PC + c8 + j];
-      m[j] = sM[(c8 + j) * PC + r];
+      if constexpr (!SCAN) m[j] = sM[(c8 + j) * PC + r];
     }
     T ta[8], tm[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       ta[j] = from_f<T>(a[j]);
-      tm[j] = from_f<T>(m[j]);
+      if constexpr (!SCAN) tm[j] = from_f<T>(m[j]);
     }
     const size_t o = ch * 64 * 64 + r * 64 + c8;
 #pragma unroll
     for (int v = 0; v < 8 * L::ES / 16; ++v) {
       ((uint4*)(INVo + o))[v] = ((const uint4*)ta)[v];
-      ((uint4*)(MqkTo + o))[v] = ((const uint4*)tm)[v];
+      if constexpr (!SCAN) ((uint4*)(MqkTo + o))[v] = ((const uint4*)tm)[v];
     }
   }
   __syncthreads();
@@ -1035,7 +1033,7 @@ static hipError_t prepscan_v(const Shape& s, const BwdPtrs& p, const int* order,
   hipLaunchKernelGGL((k_prep<T, D, GV, false, QN, true>), dim3(grid), dim3(PL<T, D>::NT), 0, st,
                      p.chunks, s.NC, s.H, (const T*)p.q, (const T*)p.k, p.g_raw, p.beta,
                      p.A_log, p.dt_bias, p.has_db, s.gu, nullptr, nullptr, nullptr,
-                     (T*)p.INV, (T*)p.MqkT, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     (T*)p.INV, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                      (const T*)p.dO, p.dht, (T*)p.dstates, p.dh0, p.seq_off, order, s.N,
                      nullptr, (T*)p.dU);
   return hipGetLastError();
