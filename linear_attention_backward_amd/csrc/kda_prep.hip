@@ -112,6 +112,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   constexpr int KS = MM::KS, KPL = MM::KPL;
   constexpr int PGN = L::PGN, PN = L::PN, PC = L::PC, PTM = L::PTM, PPT = L::PPT;
   constexpr int NKC = 64 / KS;
+  // backward scan mode with eight waves: Qd is formed by the waves INV step 1 leaves idle
+  constexpr bool QD_EARLY = SCAN && !FWD && NW == 8;
   constexpr int DH = D / HALVES;           // columns of W per wave
   constexpr int EPV = 16 / L::ES;          // elements per 16-byte vector
   constexpr int VPR = D / EPV;             // vectors per D-long row
@@ -554,6 +556,20 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       const int r = e >> 6, col = e & 63;
       if (col >= 16 * (R + 1)) sINV[(16 * R + r) * PC + col] = 0.f;
     }
+  } else if constexpr (QD_EARLY) {
+    // waves 4-7, idle in this step: Qd = Q e^G in place over q for the scan step's Qd^T dO
+    // (with the scan inside, nothing else reads q once A and Mqk are formed)
+#pragma unroll
+    for (int e = tid - NT / 2; e < 64 * VPR; e += NT / 2) {
+      const int r = e / VPR, vv = e % VPR;
+      const u32x4 qv = *(const u32x4*)(sQ + r * PN + vv * EPV);
+      const T* qe = (const T*)&qv;
+      T qd[EPV];
+#pragma unroll
+      for (int j = 0; j < EPV; ++j)
+        qd[j] = from_f<T>(to_f(qe[j]) * ex2(sG[r * PGN + vv * EPV + j]));
+      *(u32x4*)(sQ + r * PN + vv * EPV) = *(const u32x4*)qd;
+    }
   }
   __syncthreads();
   // Step 2: wave S < 3 fills column block S below the diagonal, top to bottom:
@@ -838,7 +854,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
     T* sX = (T*)(smem + L::SX_OFF);
     constexpr int PSS = L::PSS, PSX = L::PSX;
     // e^{G_T} of this lane's state rows; Qd = Q e^G in place over q (each thread its own
-    // pieces); the state and dO tiles over the dead A, INV, Kd and scratch tiles
+    // pieces; with eight waves already formed during INV step 1); the state and dO tiles
+    // over the dead A, INV, Kd and scratch tiles
     f4 eg[SRT];
 #pragma unroll
     for (int rt = 0; rt < SRT; ++rt)
@@ -846,7 +863,7 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       for (int j = 0; j < 4; ++j)
         eg[rt][j] = ex2(sG[63 * PGN + (srg * SRT + rt) * 16 + 4 * g4 + j]);
 #pragma unroll
-    for (int l = 0; l < NLT; ++l) {
+    for (int l = 0; l < (QD_EARLY ? 0 : NLT); ++l) {
       const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
       const u32x4 qv = *(const u32x4*)(sQ + r * PN + vv * EPV);
       const T* qe = (const T*)&qv;
