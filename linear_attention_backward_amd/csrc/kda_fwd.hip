@@ -49,18 +49,9 @@ __global__ __launch_bounds__(256) void k_chunk_table(const int32_t* __restrict__
   }
   int off = x - cnt, goff = y - gcnt;
   for (int n = n0; n < n1; ++n) {
-    const int start = cu ? cu[n] : n * T;
     const int len = cu ? cu[n + 1] - cu[n] : T;
     const int nck = (len + CH - 1) / CH;
     seq_off[n] = off;
-    for (int c = 0; c < nck; ++c) {
-      ChunkInfo e;
-      e.t0 = start + c * CH;
-      e.len = min(CH, len - c * CH);
-      e.seq = n;
-      e.cidx = c;
-      tab[off + c] = e;
-    }
     if (groups) {
       const int ng = ngroups(nck);
       grp_off[n] = goff;
@@ -83,6 +74,27 @@ __global__ __launch_bounds__(256) void k_chunk_table(const int32_t* __restrict__
   if (N == 0 && tid == 0) {
     seq_off[0] = 0;
     if (groups) grp_off[0] = 0;
+  }
+  // the chunk entries, all threads over all chunks (a long sequence has thousands): the
+  // sequence of chunk i is the last n with seq_off[n] <= i (seq_off is visible to the
+  // whole block after the barrier)
+  __syncthreads();
+  const int total = N > 0 ? seq_off[N] : 0;
+  for (int i = tid; i < total; i += 256) {
+    int lo = 0, hi = N - 1;  // seq_off[lo] <= i < seq_off[hi + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seq_off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int n = lo, c = i - seq_off[n];
+    const int start = cu ? cu[n] : n * T;
+    const int len = cu ? cu[n + 1] - cu[n] : T;
+    ChunkInfo e;
+    e.t0 = start + c * CH;
+    e.len = min(CH, len - c * CH);
+    e.seq = n;
+    e.cidx = c;
+    tab[i] = e;
   }
   if (order && N <= kMaxOrderSeqs) {
     // the sequences sorted by chunk count, longest first (ties by index): order[rank] = n
