@@ -112,8 +112,8 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
   constexpr int KS = MM::KS, KPL = MM::KPL;
   constexpr int PGN = L::PGN, PN = L::PN, PC = L::PC, PTM = L::PTM, PPT = L::PPT;
   constexpr int NKC = 64 / KS;
-  // backward scan mode with eight waves: Qd is formed by the waves INV step 1 leaves idle
-  constexpr bool QD_EARLY = SCAN && !FWD && NW == 8;
+  // scan mode with eight waves: Qd is formed by the waves INV step 1 leaves idle
+  constexpr bool QD_EARLY = SCAN && NW == 8;
   constexpr int DH = D / HALVES;           // columns of W per wave
   constexpr int EPV = 16 / L::ES;          // elements per 16-byte vector
   constexpr int VPR = D / EPV;             // vectors per D-long row
@@ -557,8 +557,9 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
       if (col >= 16 * (R + 1)) sINV[(16 * R + r) * PC + col] = 0.f;
     }
   } else if constexpr (QD_EARLY) {
-    // waves 4-7, idle in this step: Qd = Q e^G in place over q for the scan step's Qd^T dO
-    // (with the scan inside, nothing else reads q once A and Mqk are formed)
+    // waves 4-7, idle in this step: Qd = Q e^G in place over q for the scan step (Qd^T dO
+    // backward, Qd S forward; with the scan inside, nothing else reads q once A and Mqk
+    // are formed)
 #pragma unroll
     for (int e = tid - NT / 2; e < 64 * VPR; e += NT / 2) {
       const int r = e / VPR, vv = e % VPR;
@@ -670,9 +671,10 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           eg[rt][j] = ex2(sG[63 * PGN + (srg * SRT + rt) * 16 + 4 * g4 + j]);
-      // Qd = Q e^G in place over q (each thread its own pieces)
+      // Qd = Q e^G in place over q (each thread its own pieces; with eight waves already
+      // formed during INV step 1)
 #pragma unroll
-      for (int l = 0; l < NLT; ++l) {
+      for (int l = 0; l < (QD_EARLY ? 0 : NLT); ++l) {
         const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
         const u32x4 qv = *(const u32x4*)(sQ + r * PN + vv * EPV);
         const T* qe = (const T*)&qv;
@@ -747,12 +749,15 @@ __global__ __launch_bounds__(4 * D) void k_prep(const ChunkInfo* __restrict__ ch
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) store_c<T>(sS, PSS, 16 * R, c0 + nt * 16, Oa[nt], lane);
       __syncthreads();
-      if (o) {  // rows past the chunk are not part of the sequence
+      if (o) {  // rows past the chunk store row Lr - 1 again (the same bytes as the lane that
+                // owns it), so that every lane issues the same stores
         T* oh = o + (size_t)chunks[c].t0 * rs + (size_t)h * D;
 #pragma unroll
         for (int l = 0; l < NLT; ++l) {
-          const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
-          if (r < Lr) *(u32x4*)(oh + (size_t)r * rs + vv * EPV) = *(const u32x4*)(sS + r * PSS + vv * EPV);
+          const int idx = tid + l * NT, r0 = idx / VPR, vv = idx % VPR;
+          const int r = r0 < Lr ? r0 : Lr - 1;
+          *at((u32x4*)oh, row_off(r, (unsigned)rs * L::ES) + vv * 16) =
+              *(const u32x4*)(sS + r * PSS + vv * EPV);
         }
       }
       if (chunks[c].cidx == cur.nck - 1 && dh0) {  // ht after the sequence's last chunk
