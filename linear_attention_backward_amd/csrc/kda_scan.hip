@@ -22,6 +22,8 @@
 //      before the group is P_g B_g + Q_g for the state B_g at its end;
 //   2. per (sequence, head), the group boundaries B_g from the last group back;
 //   3. every group again from its true boundary, storing dS_out of every chunk.
+#include <cstdlib>
+
 #include "kda_dev.h"
 #include "kda_launch.h"
 
@@ -211,6 +213,156 @@ __global__ __launch_bounds__(4 * D) void k_scanw(
       } else {
         if ((gi.flags & GRP_FIRST) && dh0) store_c<float>(dh0 + uh * DD, D, r0, c0, acc[rt][ct], lane);
       }
+    }
+}
+
+// Group maps of the split scan with the transition and the offset in one workgroup per
+// (group, head): P_g from I without the dO terms and Q_g from 0 with them, so that every
+// chunk's Tm is read once for both (k_scanw<PQ> runs them as separate workgroups, which
+// takes two rounds of the GPU once there are more groups than CUs).  Both states and the
+// chunk's dO tile go through LDS as natural tiles of T; with three of them the tiles are
+// single-buffered (two barriers per chunk), while the next chunk's operands load into the
+// other register set.
+template <typename T, int D>
+__global__ __launch_bounds__(4 * D) void k_scanpq(
+    const ChunkInfo* __restrict__ chunks, const GroupInfo* __restrict__ groups, int H,
+    const T* __restrict__ Tm, const T* __restrict__ PT, const float* __restrict__ eGT,
+    const T* __restrict__ dO, T* __restrict__ Pg, float* __restrict__ Qg) {
+  using L = SL<T, D>;
+  using MM = Mma<T>;
+  typedef typename MM::Frag Frag;
+  constexpr int NT = L::NT, RTW = L::RTW, CTW = L::CTW, PS = L::PS, PO = L::PO;
+  constexpr int KS = MM::KS;
+  constexpr int NKD = D / KS, NKC = 64 / KS;
+  constexpr int EPV = 16 / L::ES;
+  constexpr int VPR = D / EPV;                 // 16-byte vectors per D-long row
+  constexpr int NLO = 64 * VPR / NT;           // dO vectors per thread
+  static_assert(64 * VPR % NT == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::S_SZ + L::O_SZ];
+  T* sP = (T*)smem;
+  T* sQ = (T*)(smem + L::S_SZ);
+  T* sO = (T*)(smem + 2 * L::S_SZ);
+
+  const int g = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, cl = lane & 15;
+  const int rgp = w & 3, cgp = w >> 2;
+  const GroupInfo gi = groups[g];
+  const size_t DD = (size_t)D * D;
+  const size_t gh = (size_t)g * H + h;  // (group, head)
+
+  f4 ap[RTW][CTW], aq[RTW][CTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      const int i0 = (rgp * RTW + rt) * 16 + 4 * g4;
+      const int col = (cgp * CTW + ct) * 16 + cl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ap[rt][ct][j] = i0 + j == col ? 1.f : 0.f;
+        aq[rt][ct][j] = 0.f;
+      }
+    }
+  auto load_a = [&](int cgl, Frag (&A)[RTW][NKD], Frag (&P)[RTW][NKC], f4 (&E)[RTW]) {
+    const size_t ch = (size_t)cgl * H + h;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int i = (rgp * RTW + rt) * 16 + cl;
+#pragma unroll
+      for (int kk = 0; kk < NKD; ++kk) A[rt][kk] = MM::ld_nat(Tm + ch * DD + (size_t)i * D, kk * KS, lane);
+#pragma unroll
+      for (int kk = 0; kk < NKC; ++kk) P[rt][kk] = MM::ld_nat(PT + ch * D * 64 + (size_t)i * 64, kk * KS, lane);
+      E[rt] = *(const f4*)(eGT + ch * D + (rgp * RTW + rt) * 16 + 4 * g4);
+    }
+  };
+  auto load_do = [&](int cgl, u32x4 (&R)[NLO]) {  // rows past the chunk: zero
+    const ChunkInfo ci = chunks[cgl];
+#pragma unroll
+    for (int l = 0; l < NLO; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r < ci.len) x = *(const u32x4*)(dO + ((size_t)(ci.t0 + r) * H + h) * D + vv * EPV);
+      R[l] = x;
+    }
+  };
+  // One chunk, last to first: issue the next chunk's loads, publish both states and this
+  // chunk's dO, then P <- exp(G_T) . P + Tm P and Q <- exp(G_T) . Q + Tm Q + PT dO.
+  auto step = [&](int cc, Frag (&ta)[RTW][NKD], Frag (&pa)[RTW][NKC], f4 (&eg)[RTW],
+                  u32x4 (&ro)[NLO], Frag (&tn)[RTW][NKD], Frag (&pn)[RTW][NKC], f4 (&en)[RTW],
+                  u32x4 (&rn)[NLO]) {
+    const int cgl = gi.c0 + cc;
+    if (cc > 0) {
+      load_a(cgl - 1, tn, pn, en);
+      load_do(cgl - 1, rn);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        store_c<T>(sP, PS, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, ap[rt][ct], lane);
+        store_c<T>(sQ, PS, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, aq[rt][ct], lane);
+      }
+#pragma unroll
+    for (int l = 0; l < NLO; ++l) {
+      const int idx = tid + l * NT, r = idx / VPR, vv = idx % VPR;
+      *(u32x4*)(sO + r * PO + vv * EPV) = ro[l];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ap[rt][ct][j] *= eg[rt][j];
+          aq[rt][ct][j] *= eg[rt][j];
+        }
+#pragma unroll
+    for (int kk = 0; kk < NKD; ++kk) {
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const Frag bp = MM::ld_tr_nat(sP, PS, kk * KS, (cgp * CTW + ct) * 16, lane);
+        const Frag bq = MM::ld_tr_nat(sQ, PS, kk * KS, (cgp * CTW + ct) * 16, lane);
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+          ap[rt][ct] = MM::mma(ta[rt][kk], bp, ap[rt][ct]);
+          aq[rt][ct] = MM::mma(ta[rt][kk], bq, aq[rt][ct]);
+        }
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKC; ++kk) {
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const Frag b = MM::ld_tr_nat(sO, PO, kk * KS, (cgp * CTW + ct) * 16, lane);
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) aq[rt][ct] = MM::mma(pa[rt][kk], b, aq[rt][ct]);
+      }
+    }
+    __syncthreads();  // the tiles are read before the next chunk writes them
+  };
+  Frag ta0[RTW][NKD], pa0[RTW][NKC], ta1[RTW][NKD], pa1[RTW][NKC];
+  f4 eg0[RTW], eg1[RTW];
+  u32x4 ro0[NLO], ro1[NLO];
+  int cc = gi.cnt - 1;
+  if (cc >= 0) {
+    load_a(gi.c0 + cc, ta0, pa0, eg0);
+    load_do(gi.c0 + cc, ro0);
+  }
+  for (; cc >= 1; cc -= 2) {
+    step(cc, ta0, pa0, eg0, ro0, ta1, pa1, eg1, ro1);
+    step(cc - 1, ta1, pa1, eg1, ro1, ta0, pa0, eg0, ro0);
+  }
+  if (cc == 0) step(0, ta0, pa0, eg0, ro0, ta1, pa1, eg1, ro1);
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      const int r0 = (rgp * RTW + rt) * 16;
+      const int c0 = (cgp * CTW + ct) * 16;
+      store_c<T>(Pg + gh * DD, D, r0, c0, ap[rt][ct], lane);
+      store_c<float>(Qg + gh * DD, D, r0, c0, aq[rt][ct], lane);
     }
 }
 
@@ -541,11 +693,24 @@ template <typename T, int D>
 static hipError_t scan_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
   const dim3 gg((unsigned)s.NG, (unsigned)s.H);
   if (s.gs > 0) {
-    hipLaunchKernelGGL((k_scanw<T, D, true>), dim3((unsigned)s.NG, (unsigned)s.H, 2),
-                       dim3(SL<T, D>::NT), 0, st, p.chunks,
-                       p.groups, s.H, (const T*)p.Tm, (const T*)p.PT, p.eGT, (const T*)p.dO,
-                       nullptr, nullptr, nullptr, nullptr, (T*)p.Pg, p.Qg);
-    hipError_t e = hipGetLastError();
+    // the group maps: transition and offset in separate workgroups while both fit one
+    // round of the GPU, else in one workgroup per (group, head) (each Tm read once);
+    // KDA_SCANPQ=0 / 1 forces the separate / the joint form
+    int resident = 0;
+    hipError_t e = resident_blocks((const void*)k_scanw<T, D, true>, SL<T, D>::NT, &resident);
+    if (e != hipSuccess) return e;
+    bool joint = 2 * (int64_t)s.NG * s.H > resident;
+    if (const char* env = std::getenv("KDA_SCANPQ")) joint = std::atoi(env) != 0;
+    if (joint) {
+      hipLaunchKernelGGL((k_scanpq<T, D>), gg, dim3(SL<T, D>::NT), 0, st, p.chunks, p.groups, s.H,
+                         (const T*)p.Tm, (const T*)p.PT, p.eGT, (const T*)p.dO, (T*)p.Pg, p.Qg);
+    } else {
+      hipLaunchKernelGGL((k_scanw<T, D, true>), dim3((unsigned)s.NG, (unsigned)s.H, 2),
+                         dim3(SL<T, D>::NT), 0, st, p.chunks,
+                         p.groups, s.H, (const T*)p.Tm, (const T*)p.PT, p.eGT, (const T*)p.dO,
+                         nullptr, nullptr, nullptr, nullptr, (T*)p.Pg, p.Qg);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_scan_bnd<T, D, false>), dim3((unsigned)s.N, (unsigned)s.H),
                        dim3(SL<T, D>::NT), 0, st, p.groups, p.grp_off, s.H,

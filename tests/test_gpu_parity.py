@@ -194,7 +194,22 @@ def test_split_scan(name, group, monkeypatch):
     boundaries, re-scan from the boundaries) against the oracle; weak decay keeps
     the cross-group terms large."""
     monkeypatch.setenv("KDA_SCAN_GROUP", str(group))
+    monkeypatch.setenv("KDA_SCANPQ", "0")
     print("\n[case] split scan %s, %d chunks per group" % (name, group), flush=True)
+    _check(name)
+
+
+@pytest.mark.parametrize("name,group", [("weak_decay_bf16", 3), ("weak_decay_fp32", 2),
+                                        ("ragged_bf16", 1), ("ragged_bf16_d64", 2),
+                                        ("multi_ragged_bf16", 1), ("single_seq_bf16", 5)])
+def test_split_scan_joint_maps(name, group, monkeypatch):
+    """The split scan with each group's transition and offset formed by one workgroup
+    (the form chosen by itself once separate workgroups would need more than one round
+    of the GPU, as on the long-context workload), forced here on small cases."""
+    monkeypatch.setenv("KDA_SCAN_GROUP", str(group))
+    monkeypatch.setenv("KDA_SCANPQ", "1")
+    print("\n[case] split scan, joint group maps, %s, %d chunks per group" % (name, group),
+          flush=True)
     _check(name)
 
 
