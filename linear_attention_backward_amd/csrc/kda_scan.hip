@@ -661,14 +661,171 @@ __global__ __launch_bounds__(4 * D) void k_fscan(
     }
 }
 
+// Group maps of the forward's split scan with the transition and the offset in one
+// workgroup per (group, head): P from I without the Uv term, Q from 0 with it,
+//   X_P = Wn P,  X_Q = Uv + Wn Q,  P <- e^{G_T} . P + Kr^T X_P,  Q <- e^{G_T} . Q + Kr^T X_Q,
+// so that each chunk's Wn and Kr^T fragments are read once for both.  The two states
+// and the two X tiles go through LDS (two barriers per chunk); each operand part is
+// refilled for the next chunk right after its last use.
+template <typename T, int D>
+__global__ __launch_bounds__(4 * D) void k_fscanpq(
+    const ChunkInfo* __restrict__ chunks, const GroupInfo* __restrict__ groups, int H,
+    const T* __restrict__ Wn, const T* __restrict__ KrT, const T* __restrict__ UvT,
+    const float* __restrict__ eGT, T* __restrict__ Pg, float* __restrict__ Qg) {
+  using L = SL<T, D>;
+  using MM = Mma<T>;
+  typedef typename MM::Frag Frag;
+  constexpr int RTW = L::RTW, CTW = L::CTW, PS = L::PS, PO = L::PO;
+  constexpr int KS = MM::KS;
+  constexpr int NKD = D / KS, NKC = 64 / KS;
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::S_SZ + 2 * L::O_SZ];
+  T* sP = (T*)smem;
+  T* sQ = (T*)(smem + L::S_SZ);
+  T* sXP = (T*)(smem + 2 * L::S_SZ);
+  T* sXQ = (T*)(smem + 2 * L::S_SZ + L::O_SZ);
+
+  const int gidx = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, cl = lane & 15;
+  const int rgp = w & 3, cgp = w >> 2;
+  const int xr = w & 3;  // row tile of X
+  const size_t DD = (size_t)D * D;
+  const GroupInfo gi = groups[gidx];
+  const size_t gh = (size_t)gidx * H + h;  // (group, head)
+  const int cb = gi.c0, nck = gi.cnt;
+
+  f4 ap[RTW][CTW], aq[RTW][CTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      const int i0 = (rgp * RTW + rt) * 16 + 4 * g4;
+      const int col = (cgp * CTW + ct) * 16 + cl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ap[rt][ct][j] = i0 + j == col ? 1.f : 0.f;
+        aq[rt][ct][j] = 0.f;
+      }
+    }
+  Frag fw[NKD], fk[RTW][NKC];
+  f4 fuv[CTW], fe[RTW];
+  auto load_x = [&](int cg) {  // operands of X: Wn rows and Uv
+    const size_t ch = (size_t)cg * H + h;
+    const int r = 16 * xr + cl;
+#pragma unroll
+    for (int kk = 0; kk < NKD; ++kk) fw[kk] = MM::ld_nat(Wn + ch * 64 * D + (size_t)r * D, kk * KS, lane);
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {  // Uv rows 16 xr + 4 g4 .. + 3 of column col
+      const int col = (cgp * CTW + ct) * 16 + cl;
+      const T* src = UvT + ch * D * 64 + (size_t)col * 64 + 16 * xr + 4 * g4;
+      T u4[4];
+      if constexpr (L::ES == 2) *(uint2*)u4 = *(const uint2*)src;
+      else *(uint4*)u4 = *(const uint4*)src;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fuv[ct][j] = to_f(u4[j]);
+    }
+  };
+  auto load_k = [&](int cg) {
+    const size_t ch = (size_t)cg * H + h;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int i = (rgp * RTW + rt) * 16 + cl;
+#pragma unroll
+      for (int kk = 0; kk < NKC; ++kk) fk[rt][kk] = MM::ld_nat(KrT + ch * D * 64 + (size_t)i * 64, kk * KS, lane);
+      fe[rt] = *(const f4*)(eGT + ch * D + (rgp * RTW + rt) * 16 + 4 * g4);
+    }
+  };
+  if (nck > 0) {
+    load_x(cb);
+    load_k(cb);
+  }
+  for (int c = 0; c < nck; ++c) {
+    const int cg = cb + c;
+    const bool more = c + 1 < nck;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        store_c<T>(sP, PS, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, ap[rt][ct], lane);
+        store_c<T>(sQ, PS, (rgp * RTW + rt) * 16, (cgp * CTW + ct) * 16, aq[rt][ct], lane);
+      }
+    __syncthreads();
+    f4 XP[CTW], XQ[CTW];
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      XP[ct] = zero4();
+      XQ[ct] = fuv[ct];
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKD; ++kk) {
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        XP[ct] = MM::mma(fw[kk], MM::ld_tr_nat(sP, PS, kk * KS, (cgp * CTW + ct) * 16, lane), XP[ct]);
+        XQ[ct] = MM::mma(fw[kk], MM::ld_tr_nat(sQ, PS, kk * KS, (cgp * CTW + ct) * 16, lane), XQ[ct]);
+      }
+    }
+    if (more) load_x(cg + 1);
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      store_c<T>(sXP, PO, 16 * xr, (cgp * CTW + ct) * 16, XP[ct], lane);
+      store_c<T>(sXQ, PO, 16 * xr, (cgp * CTW + ct) * 16, XQ[ct], lane);
+    }
+    __syncthreads();  // X tiles complete; the state tiles are dead
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ap[rt][ct][j] *= fe[rt][j];
+          aq[rt][ct][j] *= fe[rt][j];
+        }
+#pragma unroll
+    for (int kk = 0; kk < NKC; ++kk) {
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const Frag bp = MM::ld_tr_nat(sXP, PO, kk * KS, (cgp * CTW + ct) * 16, lane);
+        const Frag bq = MM::ld_tr_nat(sXQ, PO, kk * KS, (cgp * CTW + ct) * 16, lane);
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+          ap[rt][ct] = MM::mma(fk[rt][kk], bp, ap[rt][ct]);
+          aq[rt][ct] = MM::mma(fk[rt][kk], bq, aq[rt][ct]);
+        }
+      }
+    }
+    if (more) load_k(cg + 1);
+  }
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      const int r0 = (rgp * RTW + rt) * 16, c0 = (cgp * CTW + ct) * 16;
+      store_c<T>(Pg + gh * DD, D, r0, c0, ap[rt][ct], lane);
+      store_c<float>(Qg + gh * DD, D, r0, c0, aq[rt][ct], lane);
+    }
+}
+
 template <typename T, int D>
 static hipError_t fscan_t(const Shape& s, const FwdPtrs& p, hipStream_t st) {
   if (s.gs > 0) {  // chunk groups side by side: P_g and Q_g, the boundaries, then the outputs
-    hipLaunchKernelGGL((k_fscan<T, D, true>), dim3((unsigned)s.NG, (unsigned)s.H, 2),
-                       dim3(SL<T, D>::NT), 0, st, p.chunks, p.groups, s.H, (const T*)p.Wn,
-                       (const T*)p.KrT, (const T*)p.UvT, (const T*)p.Qd, (const T*)p.Mq, p.eGT,
-                       nullptr, nullptr, nullptr, nullptr, nullptr, (T*)p.Pg, p.Qg);
-    hipError_t e = hipGetLastError();
+    // (P_g and Q_g in one workgroup per (group, head) when separate ones would need more
+    // than one round of the GPU; KDA_SCANPQ=0 / 1 forces either form)
+    int resident = 0;
+    hipError_t e = resident_blocks((const void*)k_fscan<T, D, true>, SL<T, D>::NT, &resident);
+    if (e != hipSuccess) return e;
+    bool joint = 2 * (int64_t)s.NG * s.H > resident;
+    if (const char* env = std::getenv("KDA_SCANPQ")) joint = std::atoi(env) != 0;
+    if (joint) {
+      hipLaunchKernelGGL((k_fscanpq<T, D>), dim3((unsigned)s.NG, (unsigned)s.H),
+                         dim3(SL<T, D>::NT), 0, st, p.chunks, p.groups, s.H, (const T*)p.Wn,
+                         (const T*)p.KrT, (const T*)p.UvT, p.eGT, (T*)p.Pg, p.Qg);
+    } else {
+      hipLaunchKernelGGL((k_fscan<T, D, true>), dim3((unsigned)s.NG, (unsigned)s.H, 2),
+                         dim3(SL<T, D>::NT), 0, st, p.chunks, p.groups, s.H, (const T*)p.Wn,
+                         (const T*)p.KrT, (const T*)p.UvT, (const T*)p.Qd, (const T*)p.Mq, p.eGT,
+                         nullptr, nullptr, nullptr, nullptr, nullptr, (T*)p.Pg, p.Qg);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_scan_bnd<T, D, true>), dim3((unsigned)s.N, (unsigned)s.H),
                        dim3(SL<T, D>::NT), 0, st, p.groups, p.grp_off, s.H, (const T*)p.Pg, p.Qg,

@@ -216,11 +216,15 @@ def test_split_scan_joint_maps(name, group, monkeypatch):
 @pytest.mark.parametrize("name,group", [("weak_decay_bf16", 3), ("weak_decay_fp32", 2),
                                         ("ragged_bf16", 1), ("ragged_fp32", 3),
                                         ("single_seq_bf16", 5), ("gate_log2_fp32", 2)])
-def test_forward_split_scan(name, group, monkeypatch):
+@pytest.mark.parametrize("joint", [0, 1])
+def test_forward_split_scan(name, group, joint, monkeypatch):
     """The production forward's state scan split into groups of a few chunks (group
-    maps from I and from 0, boundaries chained from h0, re-scan with outputs)."""
+    maps from I and from 0, boundaries chained from h0, re-scan with outputs); the maps
+    as separate workgroups (joint = 0) and both in one workgroup (joint = 1)."""
     monkeypatch.setenv("KDA_SCAN_GROUP", str(group))
-    print("\n[case] forward split scan %s, %d chunks per group" % (name, group), flush=True)
+    monkeypatch.setenv("KDA_SCANPQ", str(joint))
+    print("\n[case] forward split scan %s, %d chunks per group, joint maps %d"
+          % (name, group, joint), flush=True)
     inp = KI.make_inputs(KI.get_workload(name))
     res = KC.run_gpu_fwd(inp)
     ref = KC.oracle_fwd_for(inp)
