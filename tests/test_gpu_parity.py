@@ -213,6 +213,26 @@ def test_split_scan_joint_maps(name, group, monkeypatch):
     _check(name)
 
 
+@pytest.mark.parametrize("name,group", [("weak_decay_bf16", 3), ("ragged_fp32", 2),
+                                        ("multi_ragged_bf16", 1)])
+def test_joint_maps_bitwise(name, group, monkeypatch):
+    """The joint and the separate group maps run the same products in the same order
+    (each map's accumulation, its bf16 state tiles), so the backward's and the
+    forward's results agree bit for bit between the two forms."""
+    monkeypatch.setenv("KDA_SCAN_GROUP", str(group))
+    inp = KI.make_inputs(KI.get_workload(name))
+    print("\n[case] joint vs separate group maps, %s, %d chunks per group" % (name, group),
+          flush=True)
+    out = {}
+    for joint in (0, 1):
+        monkeypatch.setenv("KDA_SCANPQ", str(joint))
+        out[joint] = (KC.run_gpu(inp), KC.run_gpu(inp, use_h_saved=False), KC.run_gpu_fwd(inp))
+    keys = (GRADS + ["dstates"], GRADS + ["dstates"], ["o", "ht", "h_saved"])
+    for a, b, ks in zip(out[0], out[1], keys):
+        for key in ks:
+            assert np.array_equal(a[key], b[key]), key
+
+
 @pytest.mark.parametrize("name,group", [("weak_decay_bf16", 3), ("weak_decay_fp32", 2),
                                         ("ragged_bf16", 1), ("ragged_fp32", 3),
                                         ("single_seq_bf16", 5), ("gate_log2_fp32", 2)])
