@@ -64,11 +64,19 @@ NAMES = ["ragged_bf16", "multi_ragged_bf16", "zero_len", "qk_norm_bf16", "ragged
 
 
 @pytest.mark.parametrize("name", NAMES)
-def test_backward_writes_stay_in_bounds(name):
+@pytest.mark.parametrize("fused", [None, "1"])
+def test_backward_writes_stay_in_bounds(name, fused, monkeypatch):
+    """fused = "1": the state scan inside prep (which writes dU into the workspace) and
+    the gradient pass that reads it; None: the path the library picks (separate
+    kernels for these small cases)."""
     import torch
     import linear_attention_backward_amd as K
+    if fused is not None:
+        if name == "zero_len":
+            pytest.skip("the scan inside prep needs a chunk in every sequence")
+        monkeypatch.setenv("KDA_PREPSCAN", fused)
     inp = _inputs(name)
-    print("\n[case] canary backward %s" % name, flush=True)
+    print("\n[case] canary backward %s prepscan=%s" % (name, fused), flush=True)
     g = KC.to_gpu(inp)
     cu = inp["cu_seqlens"] if inp["varlen"] else None
     gate = dict(dt_bias=g["dt_bias"], gate_log2=bool(inp.get("gate_log2", False)),
