@@ -14,6 +14,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import os
 import sys
@@ -65,14 +66,24 @@ def path_flops_per_chunk_head(D=128, C=64):
     return 7 * w + 5.5 * u + 2 * C ** 3 / 3
 
 
+def _code_only(text):
+    """C++ source without comments and with whitespace collapsed (a comment edit does not
+    change the code a profile was taken on).  The kernels hold no string literal with
+    comment markers in it."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_sources_digest():
-    """Digest of the device code (the .hip sources and the headers they include); the
-    host-side API file does not change what a kernel reads or writes."""
+    """Digest of the device code (the .hip sources and the headers they include, comments
+    and whitespace aside); the host-side API file does not change what a kernel reads or
+    writes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_backward_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

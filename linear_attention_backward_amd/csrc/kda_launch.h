@@ -25,11 +25,12 @@ struct BwdPtrs {
   // workspace
   const ChunkInfo* chunks;
   const int* seq_off;      // [N+1] first chunk of every sequence
+  // Tm, PT, exp(G_T): formed by prep for the separate scan kernels only
   void* Tm;                // [NC,H,K,K] act dtype : -W^T Kr (low-rank part of the chunk transition)
   void* PT;                // [NC,H,K,64] act dtype: (Qd - Mqk W)^T
   float* eGT;              // [NC,H,K]  exp(G_T)
   void* INV;               // [NC,H,64,64] act dtype: (I + diag(beta) A)^{-1}
-  void* MqkT;              // [NC,H,64,64] act dtype: Mqk transposed
+  void* MqkT;              // [NC,H,64,64] act dtype: Mqk transposed (separate kernels only)
   void* dstates;           // [NC,H,K,V] act dtype: dL/dS at the end of every chunk
   // [NC,H,64,V] act dtype: dU = Mqk^T dO + Kr dS_out of every chunk, written by prep when
   // the state scan runs inside it (then over Tm, which that mode does not use) and read
@@ -104,7 +105,7 @@ hipError_t launch_fscan(const Shape& s, const FwdPtrs& p, hipStream_t st);
 hipError_t launch_scan(const Shape& s, const BwdPtrs& p, hipStream_t st);
 // prep with the reverse state-gradient scan inside (every sequence has at least one chunk;
 // workgroups take (sequence, head) units from the chunk-count order `order` in a snake):
-// writes INV, Mqk^T, dstates and dh0 instead of Tm, PT and exp(G_T)
+// writes INV, dstates, dU (into p.dU) and dh0 instead of Tm, PT, exp(G_T) and Mqk^T
 hipError_t launch_prepscan(const Shape& s, const BwdPtrs& p, const int* order, hipStream_t st);
 // the production forward with the state scan inside prep's forward mode (same conditions):
 // o, h_saved and ht without the per-chunk operands in memory
