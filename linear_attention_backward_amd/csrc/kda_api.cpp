@@ -328,15 +328,27 @@ template <typename F>
 hipError_t timed(int stage, hipStream_t st, F&& launch) {
   if (!g_timing) return launch();
   TimedLaunch t{stage, nullptr, nullptr};
+  auto drop = [&] {
+    if (t.a) (void)hipEventDestroy(t.a);
+    if (t.b) (void)hipEventDestroy(t.b);
+  };
   // no system-scope release at the event: the launches it separates are on one stream and
   // the host reads the times only after hipEventSynchronize
-  hipEventCreateWithFlags(&t.a, hipEventDisableSystemFence);
-  hipEventCreateWithFlags(&t.b, hipEventDisableSystemFence);
-  hipEventRecord(t.a, st);
-  hipError_t e = launch();
-  hipEventRecord(t.b, st);
-  g_events.push_back(t);
-  return e;
+  hipError_t e = hipEventCreateWithFlags(&t.a, hipEventDisableSystemFence);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&t.b, hipEventDisableSystemFence);
+  if (e == hipSuccess) e = hipEventRecord(t.a, st);
+  if (e != hipSuccess) {  // the launch is not made: the caller reports the error
+    drop();
+    return e;
+  }
+  e = launch();
+  const hipError_t r = hipEventRecord(t.b, st);
+  if (e == hipSuccess && r == hipSuccess) {
+    g_events.push_back(t);
+    return hipSuccess;
+  }
+  drop();
+  return e != hipSuccess ? e : r;
 }
 
 int hip_fail(hipError_t e) {
@@ -620,8 +632,8 @@ int kda_timing_read(double* ms, int* launches, int n) {
       tot[t.stage] += x;
       cnt[t.stage] += 1;
     }
-    hipEventDestroy(t.a);
-    hipEventDestroy(t.b);
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
   }
   g_events.clear();
   for (int i = 0; i < n && i < kStages; ++i) {

@@ -122,7 +122,7 @@ __device__ __forceinline__ float softplus_f(float x) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(64) void k_fwd_ref(const int* __restrict__ seq_off,
-                                                const int32_t* __restrict__ cu, int N, int H,
+                                                const int32_t* __restrict__ cu, int H,
                                                 int Tn, const T* __restrict__ q,
                                                 const T* __restrict__ k,
                                                 const T* __restrict__ v,
@@ -301,7 +301,7 @@ static hipError_t fwd_ref_t(const Shape& s, const int* seq_off, const void* q, c
                             const float* A_log, const float* dt_bias, const float* h0, void* o,
                             float* ht, void* h_saved, hipStream_t st) {
   dim3 grid((unsigned)(s.N * s.H * (D / 64)));
-  hipLaunchKernelGGL((k_fwd_ref<T, D>), grid, dim3(64), 0, st, seq_off, s.cu, s.N, s.H, s.T,
+  hipLaunchKernelGGL((k_fwd_ref<T, D>), grid, dim3(64), 0, st, seq_off, s.cu, s.H, s.T,
                      (const T*)q, (const T*)k, (const T*)v, g_raw, beta, A_log, dt_bias, s.gu, h0,
                      (T*)o, ht, (T*)h_saved);
   return hipGetLastError();

@@ -372,8 +372,7 @@ __global__ __launch_bounds__(4 * D) void k_scanpq(
 // start of the first group; going forward, S <- P_g S + Q_g is the state at the start
 // of the next group, stored as its bnd.
 template <typename T, int D, bool FWD>
-__global__ __launch_bounds__(4 * D) void k_scan_bnd(const GroupInfo* __restrict__ groups,
-                                                    const int* __restrict__ grp_off, int H,
+__global__ __launch_bounds__(4 * D) void k_scan_bnd(const int* __restrict__ grp_off, int H,
                                                     const T* __restrict__ Pg,
                                                     const float* __restrict__ Qg,
                                                     const float* __restrict__ dht,
@@ -669,9 +668,9 @@ __global__ __launch_bounds__(4 * D) void k_fscan(
 // refilled for the next chunk right after its last use.
 template <typename T, int D>
 __global__ __launch_bounds__(4 * D) void k_fscanpq(
-    const ChunkInfo* __restrict__ chunks, const GroupInfo* __restrict__ groups, int H,
-    const T* __restrict__ Wn, const T* __restrict__ KrT, const T* __restrict__ UvT,
-    const float* __restrict__ eGT, T* __restrict__ Pg, float* __restrict__ Qg) {
+    const GroupInfo* __restrict__ groups, int H, const T* __restrict__ Wn,
+    const T* __restrict__ KrT, const T* __restrict__ UvT, const float* __restrict__ eGT,
+    T* __restrict__ Pg, float* __restrict__ Qg) {
   using L = SL<T, D>;
   using MM = Mma<T>;
   typedef typename MM::Frag Frag;
@@ -817,8 +816,8 @@ static hipError_t fscan_t(const Shape& s, const FwdPtrs& p, hipStream_t st) {
     if (const char* env = std::getenv("KDA_SCANPQ")) joint = std::atoi(env) != 0;
     if (joint) {
       hipLaunchKernelGGL((k_fscanpq<T, D>), dim3((unsigned)s.NG, (unsigned)s.H),
-                         dim3(SL<T, D>::NT), 0, st, p.chunks, p.groups, s.H, (const T*)p.Wn,
-                         (const T*)p.KrT, (const T*)p.UvT, p.eGT, (T*)p.Pg, p.Qg);
+                         dim3(SL<T, D>::NT), 0, st, p.groups, s.H, (const T*)p.Wn, (const T*)p.KrT,
+                         (const T*)p.UvT, p.eGT, (T*)p.Pg, p.Qg);
     } else {
       hipLaunchKernelGGL((k_fscan<T, D, true>), dim3((unsigned)s.NG, (unsigned)s.H, 2),
                          dim3(SL<T, D>::NT), 0, st, p.chunks, p.groups, s.H, (const T*)p.Wn,
@@ -828,7 +827,7 @@ static hipError_t fscan_t(const Shape& s, const FwdPtrs& p, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_scan_bnd<T, D, true>), dim3((unsigned)s.N, (unsigned)s.H),
-                       dim3(SL<T, D>::NT), 0, st, p.groups, p.grp_off, s.H, (const T*)p.Pg, p.Qg,
+                       dim3(SL<T, D>::NT), 0, st, p.grp_off, s.H, (const T*)p.Pg, p.Qg,
                        p.h0, p.bnd);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -870,7 +869,7 @@ static hipError_t scan_t(const Shape& s, const BwdPtrs& p, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_scan_bnd<T, D, false>), dim3((unsigned)s.N, (unsigned)s.H),
-                       dim3(SL<T, D>::NT), 0, st, p.groups, p.grp_off, s.H,
+                       dim3(SL<T, D>::NT), 0, st, p.grp_off, s.H,
                        (const T*)p.Pg, p.Qg, p.dht, p.bnd);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
