@@ -64,7 +64,9 @@ extern "C" {
 #define KDA_API
 #endif
 
-/* Status codes.  0 = success; negative = error (no work enqueued). */
+/* Status codes.  0 = success; negative = error.  Validation errors (-1, -2, -3, -5) are
+ * returned before anything is enqueued; with KDA_ERR_HIP the launches before the failing
+ * one may already be on the stream, and the outputs are then undefined. */
 #define KDA_OK 0
 #define KDA_ERR_INVALID_ARGUMENT (-1) /* NULL required pointer, bad size, misaligned
                                          pointer, non-monotone cu_seqlens, sum != T */
