@@ -293,6 +293,29 @@ def _pmc_all(csv_path):
     return {st: {k: sum(v) / len(v) for k, v in d.items()} for st, d in per.items()}
 
 
+def time_graph(torch, plan, stream, steps):
+    """ms per kda_bwd call replayed from a HIP graph captured once (torch.cuda.CUDAGraph)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):  # torch runs captured work once on a side stream first
+        plan.run(side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.run(torch.cuda.current_stream())
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def bench_forward(a, K, torch, inp, g, cu, vk, wl, variants):
     """kda_fwd timed over the whole call (chunk table, per-chunk pass, state scan), with
     the reference forward timed once beside it."""
@@ -359,6 +382,8 @@ def main():
                     help="method variant: the gate in log2 units (decay 2^g)")
     ap.add_argument("--qk-l2norm", action="store_true",
                     help="method variant: q and k L2-normalised inside the method")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the backward step replayed from a HIP graph captured once")
     ap.add_argument("--forward", action="store_true",
                     help="time the production forward (kda_fwd: o, ht and the chunk-start "
                          "states) instead of the backward; prints its own JSON line")
@@ -463,6 +488,14 @@ def main():
     ms_flushed = fl[len(fl) // 2]
     log("kda_bwd with the MALL flushed before each step: %.3f ms (median of %d)" % (ms_flushed, nf))
 
+    # --graph: the same step captured once into a HIP graph and replayed (the library
+    # enqueues kernels only): what a caller that replays its backward saves in launch
+    # overhead
+    ms_graph = None
+    if a.graph:
+        ms_graph = time_graph(torch, plan, stream, a.steps)
+        log("kda_bwd replayed as a HIP graph: %.3f ms/step" % ms_graph)
+
     dom = max(("prep", "scan", "grad"), key=lambda s: per[s])
     H, D = inp["H"], inp["K"]
     es = 2 if inp["dtype"] == "bf16" else 4
@@ -534,6 +567,7 @@ def main():
                           "unit": "GB/s", "frac": path_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "kernel_ms": per,
         "mall_flushed_ms_per_step": ms_flushed,
+        **({"graph_replay_ms_per_step": ms_graph} if ms_graph is not None else {}),
     }
     if not a.no_cpu_baseline:
         rec, ref, heads = cpu_baseline(inp)

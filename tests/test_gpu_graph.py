@@ -1,0 +1,106 @@
+"""kda_bwd captured into a HIP graph (through torch.cuda.CUDAGraph) and replayed.
+
+The library enqueues kernels only (no memory set, copy, allocation or host
+synchronisation inside a call), so one call can be captured and replayed; every
+replay must reproduce the eager call bit for bit (the kernels are deterministic).
+Each replay follows eager work of the program's own (a second plan's eager call and
+an overwrite of the graph's outputs), with a synchronisation in between, and is
+checked against the eager result."""
+import numpy as np
+import pytest
+
+import kda_inputs as KI
+from tests import kda_case as KC
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_backward_amd as K
+    K.load_library()
+
+
+def _plan(inp, use_h_saved=True):
+    import linear_attention_backward_amd as K
+    import torch
+    g = KC.to_gpu(inp)
+    cu = inp["cu_seqlens"] if inp["varlen"] else None
+    vk = dict(dt_bias=g["dt_bias"], gate_log2=bool(inp.get("gate_log2", False)),
+              qk_l2norm=bool(inp.get("qk_l2norm", False)))
+    hs = None
+    if use_h_saved:
+        hs = K.kda_fwd_ref(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"],
+                           h0=g["h0"], cu_seqlens=cu, want_o=False, want_ht=False,
+                           **vk)["h_saved"]
+    torch.cuda.synchronize()
+    plan = K.BwdPlan(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dO"],
+                     h0=g["h0"], dht=g["dht"], h_saved=hs, cu_seqlens=cu, want_dstates=True,
+                     **vk)
+    return plan, g
+
+
+def _snapshot(plan):
+    return {k: v.clone() for k, v in plan.outputs().items() if v is not None}
+
+
+@pytest.mark.parametrize("name,env,use_h_saved", [
+    ("tiny_fp32", {}, True),
+    ("ragged_bf16", {}, True),                       # separate prep and scan kernels
+    ("weak_decay_bf16", {"KDA_PREPSCAN": "1"}, True),  # the scan inside prep
+    ("single_seq_bf16", {}, True),                   # split scan (groups of chunks)
+    ("gate_bias_bf16", {}, False),                   # with the in-stream state recompute
+    ("qk_norm_fp32", {"KDA_PREPSCAN": "1"}, False),
+])
+def test_graph_replay_matches_eager(name, env, use_h_saved, monkeypatch):
+    import torch
+    for key, val in env.items():
+        monkeypatch.setenv(key, val)
+    print("\n[case] graph %s env=%s h_saved=%s" % (name, env, use_h_saved), flush=True)
+    inp = KI.make_inputs(KI.get_workload(name))
+    plan, _ = _plan(inp, use_h_saved)
+    other, _ = _plan(KI.make_inputs(KI.get_workload("tiny_fp32")))
+    stream = torch.cuda.current_stream()
+    plan.run(stream)
+    torch.cuda.synchronize()
+    ref = _snapshot(plan)
+
+    # capture (torch wants the captured work run once on a side stream first)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        plan.run(side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.run(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        for t in plan.outputs().values():  # eager overwrite: the replay must rewrite all
+            if t is not None:
+                t.fill_(float("nan"))
+        other.run(stream)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for key, want in ref.items():
+            got = plan.outputs()[key]
+            assert torch.equal(got, want), "%s replay %d: %s differs" % (name, rep, key)
+    # and the result is still the oracle's (replays reproduce a checked call)
+    res = {k: v.float().cpu().numpy().astype(np.float64) for k, v in ref.items()}
+    TT = inp["q"].shape[0]
+    for key in ("dq", "dk", "dv", "dg_raw"):
+        if res[key].ndim == 4:
+            res[key] = res[key].reshape(TT, *res[key].shape[2:])
+    if res["dbeta"].ndim == 3:
+        res["dbeta"] = res["dbeta"].reshape(TT, -1)
+    oref = KC.oracle_for(inp)
+    keys = ["dq", "dk", "dv", "dg_raw", "dbeta", "dA_log", "dh0", "dstates"]
+    if inp.get("dt_bias") is not None:
+        keys.append("ddt_bias")
+    KC.compare(res, oref, keys, KC.TOL[inp["dtype"]], label=name + " graph")
