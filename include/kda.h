@@ -158,7 +158,11 @@ KDA_API int kda_workspace_size(const kda_problem* p, int which, size_t* bytes);
 /* Total number of 64-token chunks NC over all sequences. */
 KDA_API int kda_num_chunks(const kda_problem* p, int64_t* nchunks);
 
-/* The backward pass (see the method above). */
+/* The backward pass (see the method above).  kda_bwd, kda_fwd_ref and kda_fwd only
+ * enqueue kernels on `stream` (no allocation, memory set, copy or host
+ * synchronisation), so a call may be captured into a HIP graph and replayed while its
+ * pointers, workspace and problem stay valid; kernels are deterministic, so replays
+ * reproduce the call bit for bit. */
 KDA_API int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t ws_bytes,
             void* stream);
 
