@@ -1,4 +1,4 @@
-"""kda_bwd captured into a HIP graph (through torch.cuda.CUDAGraph) and replayed.
+"""kda_bwd and kda_fwd captured into a HIP graph (through torch.cuda.CUDAGraph) and replayed.
 
 The library enqueues kernels only (no memory set, copy, allocation or host
 synchronisation inside a call), so one call can be captured and replayed; every
@@ -104,3 +104,59 @@ def test_graph_replay_matches_eager(name, env, use_h_saved, monkeypatch):
     if inp.get("dt_bias") is not None:
         keys.append("ddt_bias")
     KC.compare(res, oref, keys, KC.TOL[inp["dtype"]], label=name + " graph")
+
+
+@pytest.mark.parametrize("name,env", [
+    ("tiny_fp32", {}),
+    ("ragged_bf16", {}),                        # per-chunk pass, then the state scan
+    ("weak_decay_bf16", {"KDA_PREPSCAN": "1"}),  # the state scan inside prep
+    ("single_seq_bf16", {}),                    # split scan
+])
+def test_graph_replay_forward(name, env, monkeypatch):
+    """kda_fwd captured and replayed: o, ht and h_saved bitwise equal to the eager call."""
+    import ctypes
+    import linear_attention_backward_amd as K
+    import torch
+    for key, val in env.items():
+        monkeypatch.setenv(key, val)
+    print("\n[case] graph forward %s env=%s" % (name, env), flush=True)
+    inp = KI.make_inputs(KI.get_workload(name))
+    g = KC.to_gpu(inp)
+    cu = inp["cu_seqlens"] if inp["varlen"] else None
+    vk = dict(dt_bias=g["dt_bias"], gate_log2=bool(inp.get("gate_log2", False)),
+              qk_l2norm=bool(inp.get("qk_l2norm", False)))
+    prob = K._make_prob(g["q"], g["v"], cu, vk["gate_log2"], vk["qk_l2norm"])[0]
+    ws = torch.empty(max(K.workspace_size(prob, K.KDA_WS_FWD), 1), dtype=torch.uint8,
+                     device="cuda")
+    res = K.kda_fwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], h0=g["h0"],
+                    cu_seqlens=cu, workspace=ws, **vk)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in res.items()}
+    io = K.FwdIO(*[K._ptr(x) for x in (g["q"], g["k"], g["v"], g["g_raw"], g["beta"],
+                                       g["A_log"], g["h0"], res["o"], res["ht"],
+                                       res["h_saved"], g["dt_bias"])])
+    lib = K.load_library()
+
+    def call(stream):
+        K._check(lib.kda_fwd(prob.ref(), ctypes.byref(io), K._ptr(ws), ws.numel(),
+                             K._stream_ptr(stream)))
+
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        call(side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in res.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for key, want in ref.items():
+            assert torch.equal(res[key], want), "%s replay %d: %s differs" % (name, rep, key)
