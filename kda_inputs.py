@@ -121,6 +121,9 @@ EXTRA = {
     "qk_norm_bf16_d64": Workload("qk_norm_bf16_d64", 2, 130, 2, 64, 64, "bf16", 1114,
                                  h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0,
                                  qk_l2norm=True),
+    # the training shape with the other supported head sizes (measurement: bench.py --workload)
+    "train_bf16_d64": Workload("train_bf16_d64", 8, 4096, 32, 64, 64, "bf16", 1115),
+    "train_fp32_d64": Workload("train_fp32_d64", 8, 4096, 32, 64, 64, "f32", 1116),
 }
 
 
