@@ -86,9 +86,11 @@ def test_forward_parity(name, heads):
     print("[errors] " + " ".join("%s=%.2e" % kv for kv in rep.items()), flush=True)
 
 
-@pytest.mark.parametrize("name", ["train_bf16", "varlen_bf16", "long_bf16"])
+@pytest.mark.parametrize("name", ["train_bf16", "varlen_bf16", "long_bf16", "train_bf16_d64",
+                                  "train_fp32_d64"])
 def test_parity_full_size(name):
-    """The three large workloads at full size, every head and every sequence: the
+    """The three large workloads at full size, and the training shape at K = V = 64 in bf16
+    and fp32 (four waves per workgroup), every head and every sequence: the
     backward (with the reference forward's chunk-start states, in the launch
     configuration the benchmark times), the reference forward and the production
     forward (its split state scan on the long-context workload), all against one
