@@ -100,7 +100,9 @@ typedef struct kda_problem {
   int qk_l2norm;      /* 0, or 1: L2-normalise q and k inside the method (see above) */
 } kda_problem;
 
-/* Device pointers for kda_bwd.  16-byte aligned. */
+/* Device pointers for kda_bwd.  16-byte aligned.  With no tokens at all (B*T == 0) the
+ * per-token tensors ([B,T,...]) may be NULL: then dh0 = dht, dA_log = 0 and ddt_bias = 0
+ * (kda_fwd_ref and kda_fwd likewise give ht = h0). */
 typedef struct kda_bwd_io {
   /* inputs */
   const void* q;        /* [B,T,H,K] act_dtype */

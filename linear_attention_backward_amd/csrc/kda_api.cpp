@@ -442,7 +442,9 @@ int kda_fwd_ref(const kda_problem* p, const kda_fwd_io* io, void* workspace, siz
   Plan pl;
   int st = make_plan(p, &pl);
   if (st != KDA_OK) return st;
-  if (!io || !io->q || !io->k || !io->v || !io->g_raw || !io->beta || !io->A_log)
+  // per-token tensors may be NULL when there are no tokens (nothing reads them then)
+  const bool tok = (int64_t)p->B * p->T > 0;
+  if (!io || (tok && (!io->q || !io->k || !io->v || !io->g_raw || !io->beta)) || !io->A_log)
     return KDA_ERR_INVALID_ARGUMENT;
   if (!aligned16(io->q) || !aligned16(io->k) || !aligned16(io->v) || !aligned16(io->h_saved) ||
       !aligned16(io->dt_bias))
@@ -476,7 +478,8 @@ int kda_fwd(const kda_problem* p, const kda_fwd_io* io, void* workspace, size_t 
   Plan pl;
   int st = make_plan(p, &pl);
   if (st != KDA_OK) return st;
-  if (!io || !io->q || !io->k || !io->v || !io->g_raw || !io->beta || !io->A_log)
+  const bool tok = (int64_t)p->B * p->T > 0;  // per-token tensors may be NULL without tokens
+  if (!io || (tok && (!io->q || !io->k || !io->v || !io->g_raw || !io->beta)) || !io->A_log)
     return KDA_ERR_INVALID_ARGUMENT;
   const void* al[] = {io->q, io->k, io->v, io->g_raw, io->h_saved, io->o, io->dt_bias};
   for (const void* x : al)
@@ -526,8 +529,11 @@ int kda_bwd(const kda_problem* p, const kda_bwd_io* io, void* workspace, size_t 
   int st = make_plan(p, &pl);
   if (st != KDA_OK) return st;
   if (!io) return KDA_ERR_INVALID_ARGUMENT;
-  if (!io->q || !io->k || !io->v || !io->g_raw || !io->beta || !io->A_log || !io->dO || !io->dq ||
-      !io->dk || !io->dv || !io->dg_raw || !io->dbeta || !io->dA_log)
+  // per-token tensors (inputs and gradients) may be NULL when there are no tokens
+  const bool tok = (int64_t)p->B * p->T > 0;
+  if ((tok && (!io->q || !io->k || !io->v || !io->g_raw || !io->beta || !io->dO || !io->dq ||
+               !io->dk || !io->dv || !io->dg_raw || !io->dbeta)) ||
+      !io->A_log || !io->dA_log)
     return KDA_ERR_INVALID_ARGUMENT;
   const void* al[] = {io->q, io->k, io->v, io->dO, io->g_raw, io->h_saved, io->h0, io->dht,
                       io->dq, io->dk, io->dv, io->dg_raw, io->dh0, io->dstates, io->dt_bias};

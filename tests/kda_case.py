@@ -25,7 +25,7 @@ def to_gpu(inp: dict):
         B, T = inp["B"], inp["T"]
         for key in ("q", "k", "v", "dO", "g_raw"):
             g[key] = g[key].reshape(B, T, *g[key].shape[1:])
-        g["beta"] = g["beta"].reshape(B, T, -1)
+        g["beta"] = g["beta"].reshape(B, T, inp["H"])
     return g
 
 
@@ -52,7 +52,7 @@ def run_gpu(inp: dict, use_h_saved=True, want_dstates=True):
         if key in ("dq", "dk", "dv", "dg_raw", "o") and a.ndim == 4:
             a = a.reshape(TT, *a.shape[2:])
         if key == "dbeta" and a.ndim == 3:
-            a = a.reshape(TT, -1)
+            a = a.reshape(TT, a.shape[-1])
         res[key] = a
     return res
 

@@ -383,3 +383,28 @@ def test_recompute_with_scans_in_prep(name, monkeypatch):
     monkeypatch.setenv("KDA_PREPSCAN", "1")
     print("\n[case] recompute, scans inside prep, %s" % name, flush=True)
     _check(name, use_h_saved=False)
+
+
+@pytest.mark.parametrize("wl", [
+    KI.Workload("empty_batch_fp32", 2, 0, 2, 64, 64, "f32", 1300, h0_std=0.3, dht_std=1.0,
+                dt_bias_std=1.0),
+    KI.Workload("empty_seqs_bf16", 1, 0, 3, 128, 128, "bf16", 1301, varlen_seqs=3,
+                fixed_lengths=(0, 0, 0), h0_std=0.3, dht_std=1.0, gate_log2=True,
+                qk_l2norm=True),
+], ids=lambda w: w.name)
+@pytest.mark.parametrize("use_h_saved", [True, False])
+def test_no_tokens(wl, use_h_saved):
+    """No tokens at all (an empty batch, or packed sequences that are all empty): nothing
+    per token to compute; dh0 = dht, ht = h0, dA_log = 0 and ddt_bias = 0, as the oracle
+    gives, from the backward, the reference forward and the production forward."""
+    print("\n[case] no tokens %s h_saved=%s" % (wl.name, use_h_saved), flush=True)
+    inp = KI.make_inputs(wl)
+    res = KC.run_gpu(inp, use_h_saved=use_h_saved)
+    fres = KC.run_gpu_fwd(inp)
+    ref = KC.oracle_for(inp)
+    extra = ["ddt_bias"] if inp.get("dt_bias") is not None else []
+    for key in ["dh0", "dA_log", "ht"] + extra:
+        assert np.array_equal(res[key], ref[key]), key
+    assert np.array_equal(fres["ht"], ref["ht"])
+    for key in ("dq", "dk", "dv", "dg_raw", "dbeta", "o"):
+        assert res[key].size == 0, key
