@@ -408,3 +408,48 @@ def test_no_tokens(wl, use_h_saved):
     assert np.array_equal(fres["ht"], ref["ht"])
     for key in ("dq", "dk", "dv", "dg_raw", "dbeta", "o"):
         assert res[key].size == 0, key
+
+
+def test_max_row_stride():
+    """The largest token row the library accepts, H*K just under 2^22 (H = 32767,
+    K = V = 128, bf16: an fp32 g_raw row of 16 MiB less 512 bytes), over one full chunk
+    with h0 and dht: the 24-bit row-offset arithmetic of the kernels at its limit.
+    Backward (fused with the scan: 32767 units), reference and production forward;
+    compared with the oracle on four heads spread over the row (heads are independent)."""
+    import linear_attention_backward_amd as K
+    import torch
+    wl = KI.Workload("max_row_bf16", 1, 64, 32767, 128, 128, "bf16", 1400, h0_std=0.3,
+                     dht_std=1.0)
+    print("\n[case] max row stride: H=%d K=%d T=%d" % (wl.H, wl.K, wl.T), flush=True)
+    inp = KI.make_inputs(wl)
+    heads = [0, 1, 16383, 32766]
+    g = KC.to_gpu(inp)
+    fwd = K.kda_fwd_ref(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], h0=g["h0"])
+    out = K.kda_bwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dO"],
+                    h0=g["h0"], dht=g["dht"], h_saved=fwd["h_saved"], want_dstates=True)
+    pf = K.kda_fwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], h0=g["h0"])
+    torch.cuda.synchronize()
+    print("[gpu done] max row stride", flush=True)
+    hi = torch.tensor(heads, device="cuda")
+
+    def pick(t, axis):
+        return t.index_select(axis, hi).float().cpu().numpy().astype(np.float64)
+
+    res = {k: pick(out[k], 2).reshape(64, len(heads), -1) for k in ("dq", "dk", "dv", "dg_raw")}
+    res["dbeta"] = pick(out["dbeta"], 2).reshape(64, len(heads))
+    res["dA_log"] = pick(out["dA_log"], 0)
+    res["dstates"] = pick(out["dstates"], 1)
+    res["dh0"] = pick(out["dh0"], 1)
+    res["h_saved"] = pick(fwd["h_saved"], 1)
+    res["o"] = pick(fwd["o"], 2).reshape(64, len(heads), -1)
+    res["ht"] = pick(fwd["ht"], 1)
+    fres = {"o": pick(pf["o"], 2).reshape(64, len(heads), -1), "ht": pick(pf["ht"], 1),
+            "h_saved": pick(pf["h_saved"], 1)}
+    del g, fwd, out, pf
+    ref = KC.oracle_for(inp, heads)
+    ref["h_saved"] = ref["states"]
+    tol = KC.TOL["bf16"]
+    rep = KC.compare(res, ref, ["dq", "dk", "dv", "dg_raw", "dbeta", "dA_log", "dh0",
+                                "dstates", "h_saved", "o", "ht"], tol, label="max row stride")
+    print("[errors] " + " ".join("%s=%.2e" % kv for kv in rep.items()), flush=True)
+    KC.compare(fres, ref, ["o", "ht", "h_saved"], tol, label="max row stride forward")
