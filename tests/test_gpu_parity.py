@@ -453,3 +453,29 @@ def test_max_row_stride():
                                 "dstates", "h_saved", "o", "ht"], tol, label="max row stride")
     print("[errors] " + " ".join("%s=%.2e" % kv for kv in rep.items()), flush=True)
     KC.compare(fres, ref, ["o", "ht", "h_saved"], tol, label="max row stride forward")
+
+
+@pytest.mark.parametrize("n,lo,dtype,D,env", [
+    (5000, 0, "bf16", 64, {}),                       # more sequences than the fused scan orders
+    (4096, 1, "f32", 64, {"KDA_PREPSCAN": "1"}),      # the most the fused scan orders
+], ids=["5000_seqs_bf16", "4096_seqs_fp32_fused"])
+def test_many_sequences(n, lo, dtype, D, env, monkeypatch):
+    """Thousands of short packed sequences (lengths 0-99 or 1-99 tokens, empty ones
+    included): the chunk table and its longest-first unit order at and past their largest
+    size, the per-sequence state scans, dh0 of every sequence."""
+    for key, val in env.items():
+        monkeypatch.setenv(key, val)
+    rng = np.random.default_rng(1500 + n)
+    lens = tuple(int(x) for x in rng.integers(lo, 100, size=n))
+    wl = KI.Workload("seqs%d" % n, 1, sum(lens), 2, D, D, dtype, 1500 + n, varlen_seqs=n,
+                     fixed_lengths=lens, h0_std=0.3, dht_std=1.0, alog_lo=-3.0, alog_hi=1.0)
+    print("\n[case] %d sequences, %d tokens, env=%s" % (n, sum(lens), env), flush=True)
+    inp = KI.make_inputs(wl)
+    res = KC.run_gpu(inp)
+    fres = KC.run_gpu_fwd(inp)
+    ref = KC.oracle_for(inp)
+    ref["h_saved"] = ref["states"]
+    tol = KC.TOL[dtype]
+    rep = KC.compare(res, ref, GRADS + INTER, tol, label=wl.name)
+    print("[errors] " + " ".join("%s=%.2e" % kv for kv in rep.items()), flush=True)
+    KC.compare(fres, ref, ["o", "ht", "h_saved"], tol, label=wl.name + " forward")
