@@ -96,7 +96,8 @@ template <typename T, int D> struct GF {
   static constexpr int DB2_OFF = DB1_OFF + WPR * 256;     // [NW][64]
   static constexpr int RED_OFF = DB2_OFF + NW * 256;      // [NW]
   static constexpr int RQ_OFF = RED_OFF + NW * 4;         // q/k reciprocal norms [2][64]
-  static constexpr int TOTAL = RQ_OFF + 2 * 64 * 4;
+  static constexpr int MD_OFF = RQ_OFF + 2 * 64 * 4;      // diagonal of dMqk [64] fp32
+  static constexpr int TOTAL = MD_OFF + 64 * 4;
   static_assert(S_OFF >= I_END && K0_OFF >= DM_OFF, "prefetch tiles clear the intra phase");
   static_assert(TOTAL <= 160 * 1024, "LDS");
   static_assert(64 * PR * 4 <= G_SZ, "dg_raw staging fits the gate region");
@@ -160,6 +161,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   float* sRed = (float*)(smem + L::RED_OFF);
   float* sRq = (float*)(smem + L::RQ_OFF);  // reciprocal norms of q, k rows (QN)
   float* sRk = sRq + 64;
+  float* sMd = (float*)(smem + L::MD_OFF);  // dMqk_rr of every row
   // diagonal 16x16 blocks of dMqk and dL in fp32, natural: block R, row rr, col cc at
   // dg*[R * DGB + rr * DGP + cc]
   float* dgM;
@@ -561,6 +563,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const int r = crow + j;
       m[j] = s <= r ? am[st][j] : 0.f;
       l[j] = s < r ? -al[st][j] : 0.f;
+      if (s == r) sMd[r] = m[j];
     }
     store_c<T>(sDM, PC, 16 * R1, (CTW * half + st) * 16, m, lane);
     store_c<T>(sDL, PC, 16 * R1, (CTW * half + st) * 16, l, lane);
@@ -598,9 +601,13 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
   const float* Gi = sG + ic * PG;  // G of channel ic, by row
   const int n0 = 16 * w;           // first key channel of this wave
   const float gT = Gi[63];
-  // (1) diagonal blocks: lane -> block g4 of channel ic (dec[s] = e^{G_r - G_s}).  x1_r = sum_{s<=r} dMqk_rs
-  //     k_s e^{G_r-G_s}, x2_r = the same with dL, z_s = sum_{r>=s} (dMqk_rs q_r +
-  //     beta_r dL_rs k_r) e^{G_r-G_s}; all rows and columns inside the block.
+  // (1) diagonal blocks: lane -> block g4 of channel ic (dec[s] = e^{G_r - G_s}).  x1_r =
+  //     sum_{s<r} dMqk_rs k_s e^{G_r-G_s}, x2_r = the same with dL, z_s = sum_{r>s}
+  //     (dMqk_rs q_r + beta_r dL_rs k_r) e^{G_r-G_s}; all rows and columns inside the
+  //     block, the pairs r = s left out: their terms, dMqk_rr k_r in dq and dMqk_rr q_r
+  //     in dk, carry no decay and cancel exactly in the gate gradient, so they are added
+  //     to dq and dk alone (the gate gradient is formed without them, and is exactly 0
+  //     where every decay between two tokens underflows).
   float x1d[4][4], x2d[4][4], zd[4][4];  // C layout: rows 16 rt + 4 g4 + j
   {
     const int rb = 16 * g4;
@@ -656,7 +663,7 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       }
       float a1 = 0.f, a2 = 0.f;
 #pragma unroll
-      for (int s = 0; s <= r; ++s) {
+      for (int s = 0; s < r; ++s) {
         const float kd = kb[s] * dec[s];
         a1 = fmaf(mv[s], kd, a1);
         a2 = fmaf(lv[s], kd, a2);
@@ -811,11 +818,12 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const float dqv = eG * aQd[rt][j] + x1;
       const float dkd = br * (-eG * aKd[rt][j] + x2);
       const float dkr = eTr[j] * aKr[rt][j];
+      const float mrr = sMd[r];  // the pair r = s
       dG[rt][j] = qr * dqv + kr * (dkd - dki - dkr);
       dkr_col += kr * dkr;
       dbp[rt][j] = kr * x2;
-      sDQ[r * PN + ic] = from_f<T>(dqv);
-      sDK[r * PN + ic] = from_f<T>(dkd + dki + dkr);
+      sDQ[r * PN + ic] = from_f<T>(fmaf(mrr, kr, dqv));
+      sDK[r * PN + ic] = from_f<T>(dkd + fmaf(mrr, qr, dki) + dkr);
     }
     // the next item's S_in and v, in pieces (their tiles are clear of the intra phase)
     if (rt < 3 && nxt < items) issue_early(nxt, tid, rt + 1);

@@ -479,3 +479,26 @@ def test_many_sequences(n, lo, dtype, D, env, monkeypatch):
     rep = KC.compare(res, ref, GRADS + INTER, tol, label=wl.name)
     print("[errors] " + " ".join("%s=%.2e" % kv for kv in rep.items()), flush=True)
     KC.compare(fres, ref, ["o", "ht", "h_saved"], tol, label=wl.name + " forward")
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
+def test_extreme_decay(dtype, D):
+    """A_log = 10 (e^A_log = 22026) with g_raw around 2: per-token log decays of about
+    -5e4, every decay factor between two tokens underflows to 0 and the cumulative gate
+    reaches -1e7 within a chunk; each token sees only its own write.  dg, dA_log and dh0
+    are exactly 0 in the oracle; the kernels must not turn the huge cumulative gates into
+    inf or NaN anywhere."""
+    wl = KI.Workload("extreme_decay", 1, 200, 2, D, D, dtype, 1600, alog_lo=10.0, alog_hi=10.0,
+                     graw_mean=2.0, h0_std=0.3, dht_std=1.0)
+    print("\n[case] extreme decay %s" % dtype, flush=True)
+    inp = KI.make_inputs(wl)
+    res = KC.run_gpu(inp)
+    fres = KC.run_gpu_fwd(inp)
+    ref = KC.oracle_for(inp)
+    ref["h_saved"] = ref["states"]
+    tol = KC.TOL[dtype]
+    for key, val in list(res.items()) + [("f_" + k, v) for k, v in fres.items()]:
+        assert np.isfinite(val).all(), key
+    rep = KC.compare(res, ref, GRADS + INTER, tol, label="extreme decay")
+    print("[errors] " + " ".join("%s=%.2e" % kv for kv in rep.items()), flush=True)
+    KC.compare(fres, ref, ["o", "ht", "h_saved"], tol, label="extreme decay forward")
