@@ -819,8 +819,11 @@ __global__ __launch_bounds__(4 * D) void k_gradf(
       const float dkd = br * (-eG * aKd[rt][j] + x2);
       const float dkr = eTr[j] * aKr[rt][j];
       const float mrr = sMd[r];  // the pair r = s
-      dG[rt][j] = qr * dqv + kr * (dkd - dki - dkr);
-      dkr_col += kr * dkr;
+      // the last row's own e^{G_T - G_r} carries no decay either: its two terms in the
+      // gate gradient (-k dk_r here, +k dk_r in the last row's sum) are left out together
+      const float dkg = r == 63 ? 0.f : dkr;
+      dG[rt][j] = qr * dqv + kr * (dkd - dki - dkg);
+      dkr_col += kr * dkg;
       dbp[rt][j] = kr * x2;
       sDQ[r * PN + ic] = from_f<T>(fmaf(mrr, kr, dqv));
       sDK[r * PN + ic] = from_f<T>(dkd + fmaf(mrr, qr, dki) + dkr);
