@@ -160,3 +160,38 @@ def test_graph_replay_forward(name, env, monkeypatch):
         torch.cuda.synchronize()
         for key, want in ref.items():
             assert torch.equal(res[key], want), "%s replay %d: %s differs" % (name, rep, key)
+
+
+def test_concurrent_calls_from_threads():
+    """Two host threads calling kda_bwd at once, each on its own stream with its own
+    workspace (the library keeps no per-call state; its only shared state, the occupancy
+    cache, is locked): every result bitwise equal to the same call made alone."""
+    import threading
+    import torch
+    plans = [_plan(KI.make_inputs(KI.get_workload(n)))[0] for n in ("ragged_bf16", "tiny_fp32")]
+    refs = []
+    for p in plans:
+        p.run(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        refs.append(_snapshot(p))
+    streams = [torch.cuda.Stream() for _ in plans]
+    errors = []
+
+    def work(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(8):
+                    plans[i].run(streams[i])
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(plans))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for p, ref in zip(plans, refs):
+        for key, want in ref.items():
+            assert torch.equal(p.outputs()[key], want), key
