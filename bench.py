@@ -197,8 +197,9 @@ def _stage_of(name):
 
 
 def _pmc_kib(csv_path, counter):
-    """Average counter value (KiB) per dispatch of every backward kernel stage; the
-    scan stage sums its launches (group maps and the scan proper) per step."""
+    """Average counter value (KiB) per dispatch of every backward kernel stage (one row of
+    the rocprofv3 CSV per dispatch; the dispatches of all kernels of a stage averaged
+    together)."""
     import csv
     per = {}
     for row in csv.DictReader(open(csv_path)):
@@ -218,10 +219,12 @@ def _copy_kib(csv_path, counter):
     return sum(vals) / len(vals)
 
 
-def summarize_profiles(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, copy_mib):
-    """Write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of
-    this benchmark and of its --copy-calib mode (a copy of copy_mib MiB): each counter
-    is scaled by (bytes the copy moves) / (what the counter read for it)."""
+def summarize_profiles(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, copy_mib,
+                       out_path=None):
+    """Write profiles/traffic.json (or out_path) from rocprofv3 --pmc FETCH_SIZE /
+    WRITE_SIZE runs of this benchmark and of its --copy-calib mode (a copy of copy_mib
+    MiB): each counter is scaled by (bytes the copy moves) / (what the counter read for
+    it)."""
     nbytes = copy_mib << 20
     fs = nbytes / (_copy_kib(calib_fetch_csv, "FETCH_SIZE") * 1024.0)
     ws = nbytes / (_copy_kib(calib_write_csv, "WRITE_SIZE") * 1024.0)
@@ -235,7 +238,7 @@ def summarize_profiles(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, c
         wb = wk[stage] * 1024.0 * ws
         out["kernels"][stage] = {"fetch_kib_raw": fk[stage], "write_kib_raw": wk[stage],
                                  "read_bytes": rb, "write_bytes": wb, "bytes_per_launch": rb + wb}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = out_path or os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     return out
@@ -246,8 +249,8 @@ CU_NUM = 256
 SIMD_NUM = 1024
 
 
-def summarize_counters(csvs):
-    """Write profiles/counters.json from rocprofv3 --pmc CSVs of this benchmark (any split
+def summarize_counters(csvs, out_path=None):
+    """Write profiles/counters.json (or out_path) from rocprofv3 --pmc CSVs of this benchmark (any split
     of the counters below over passes): per backward kernel, the profiler's own ratios
     VALU busy = SQ_ACTIVE_INST_VALU / (CUs x kernel cycles), MFMA busy =
     SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x kernel cycles), MFMA FLOP = MOPS_BF16 x 512,
@@ -275,7 +278,7 @@ def summarize_counters(csvs):
         if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
             ent["lds_bank_conflict_frac"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
         out["kernels"][stage] = ent
-    with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
+    with open(out_path or os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
         json.dump(out, f, indent=1)
     return out
 
